@@ -1,0 +1,291 @@
+"""Throughput of Fibonacci-offset sparse attention, forward + backward, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one batch: for each of the 16 layers of the paper's
+model shape (B = 32, L = 1024, 8 query / 2 key-value heads, head dim 64, bfloat16 storage, W = 12,
+Fibonacci base, linear stagger alpha_l = 0.5 + l/15), the forward call (RoPE'd keys, attention,
+lse) and the backward call (dq, dk, dv). Each layer has its own input set in HBM (16 sets, more
+than the 256 MB Infinity Cache holds), resident before timing starts. The same protocol is then
+run once more at the 4x extrapolation shape (B = 8, L = 4096, coprime stagger) and reported under
+"l4096".
+
+Prints one JSON line on stdout. Progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import multiprocessing as mp
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, 8 TB/s
+FP32_VALU_PEAK_TFLOPS = 78.6    # 256 CU x 2.4 GHz x 64 lanes x 2 (FMA), scalar fp32 (no packed ops)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------------------------------------
+# CPU baseline: the float64 oracle as it stands, on the host's cores, on a bounded sample.
+# ------------------------------------------------------------------------------------------------
+
+def _oracle_unit(args):
+    name, layer, b = args
+    import numpy as np  # noqa: F401
+    from oracle import fibattn_oracle as O
+    w = workloads.WORKLOADS[name]
+    q, k, v, do = workloads.draw(w, layer, B=b + 1, with_grad=True)
+    q, k, v, do = [x[b:b + 1].double().numpy() for x in (q, k, v, do)]
+    fn = {"fixed": O.alpha_fixed, "linear": O.alpha_linear, "coprime": O.alpha_coprime}[w.schedule]
+    alpha = fn(layer, w.n_layers)
+    base = O.FIB_BASE if w.base == "fib" else O.POW2_BASE_1024
+    O.forward(q, k, v, alpha, w.W, base)
+    O.backward(q, k, v, do, alpha, w.W, base)
+    return 1
+
+
+def cpu_baseline(name: str, budget_s: float = 15.0):
+    w = workloads.WORKLOADS[name]
+    workers = min(16, len(os.sched_getaffinity(0)))
+    # (layer, repeat) units, each on batch element 0 of that layer's inputs: the oracle's cost does
+    # not depend on the values, and a B = 1 draw keeps input generation out of the way
+    units = [(name, layer, 0) for _ in range(w.B) for layer in range(w.n_layers)]
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    done = 0
+    with ctx.Pool(workers) as pool:
+        it = pool.imap_unordered(_oracle_unit, units)
+        for _ in it:
+            done += 1
+            if time.perf_counter() - t0 > budget_s and done % workers == 0:
+                break
+        wall = time.perf_counter() - t0
+        pool.terminate()
+    qh = done * w.L * w.Hq
+    cpu = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": qh / wall, "unit": "queries*heads/s (fwd+bwd)", "cores": workers, "kind": "oracle",
+        "sample": f"{done} (layer, batch element 0) units of {name}, each a float64 forward + backward at "
+                  f"B=1, L={w.L}, {wall:.1f} s wall on {workers} worker processes ({cpu}, {platform.machine()})",
+    }
+
+
+# ------------------------------------------------------------------------------------------------
+# GPU timing
+# ------------------------------------------------------------------------------------------------
+
+class Layers:
+    """Per-layer inputs, outputs and shared workspaces for one workload, resident on the GPU."""
+
+    def __init__(self, fa, w, dev):
+        self.fa, self.w, self.dev = fa, w, dev
+        base = fa.fibattn_base_offsets(fa.BASE_FIB if w.base == "fib" else fa.BASE_POW2, 1024)
+        self.base = base
+        code = {"fixed": fa.SCHEDULE_FIXED, "linear": fa.SCHEDULE_LINEAR, "coprime": fa.SCHEDULE_COPRIME}
+        self.alphas, self.dadt = [], []
+        thetas = workloads.draw_theta(w.n_layers).tolist() if w.schedule == "learned" else None
+        for layer in range(w.n_layers):
+            if thetas is not None:
+                a, d = fa.fibattn_alpha_from_theta(thetas[layer])
+            else:
+                a, d = fa.fibattn_alpha_schedule(code[w.schedule], layer, w.n_layers), 0.0
+            self.alphas.append(a)
+            self.dadt.append(d)
+        # d(alpha) only where every rung is interpolated (the learned schedule); static schedules
+        # need no alpha gradient
+        self.want_dalpha = []
+        for a in self.alphas:
+            kind = fa.fibattn_plan(a, w.W, base)[0]
+            self.want_dalpha.append(w.schedule == "learned" and bool((kind == fa.INTERP).all()))
+        self.inputs = []
+        for layer in range(w.n_layers):
+            q, k, v, do = workloads.draw(w, layer, with_grad=True)
+            self.inputs.append(tuple(x.to(dev) for x in (q, k, v, do)))
+            log(f"  inputs of layer {layer} resident")
+        B, L, Hq, Hkv, D = w.B, w.L, w.Hq, w.Hkv, w.D
+        self.o = [torch.empty(B, Hq, L, D, dtype=w.torch_dtype, device=dev) for _ in range(w.n_layers)]
+        self.lse = [torch.empty(B, Hq, L, dtype=torch.float32, device=dev) for _ in range(w.n_layers)]
+        self.ws_f = torch.empty(fa.fibattn_fwd_workspace_bytes(B, L, Hkv), dtype=torch.uint8, device=dev)
+        self.ws_b = torch.empty(fa.fibattn_bwd_workspace_bytes(B, L, Hq, Hkv, D, w.W, len(base)),
+                                dtype=torch.uint8, device=dev)
+
+    def fwd(self, layer):
+        q, k, v, _ = self.inputs[layer]
+        self.fa.fibattn_fwd(q, k, v, self.alphas[layer], self.w.W, self.base, o=self.o[layer],
+                            lse=self.lse[layer], workspace=self.ws_f)
+
+    def rope(self, layer):
+        self.fa.fibattn_rope_keys(self.inputs[layer][1], self.ws_f)
+
+    def attend(self, layer):
+        q, _, v, _ = self.inputs[layer]
+        self.fa.fibattn_fwd_attend(q, v, self.alphas[layer], self.w.W, self.base, self.ws_f, self.o[layer],
+                                   self.lse[layer])
+
+    def bwd(self, layer):
+        q, k, v, do = self.inputs[layer]
+        return self.fa.fibattn_bwd(q, k, v, self.o[layer], self.lse[layer], do, self.alphas[layer], self.w.W,
+                                   self.base, dalpha_dtheta=self.dadt[layer],
+                                   want_dalpha=self.want_dalpha[layer], workspace=self.ws_b)
+
+    def step(self):
+        for layer in range(self.w.n_layers):
+            self.fwd(layer)
+            self.bwd(layer)
+
+
+def time_steps(net: Layers, steps: int, warmup: int):
+    for _ in range(warmup):
+        net.step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        net.step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def time_stages(net: Layers, sweeps: int):
+    """Average duration of each stage, from HIP events on the stream the kernels run on."""
+    n = net.w.n_layers
+    tot = {"rope_keys": 0.0, "fwd_attend": 0.0, "bwd": 0.0}
+    for _ in range(sweeps):
+        for layer in range(n):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record()
+            net.rope(layer)
+            ev[1].record()
+            net.attend(layer)
+            ev[2].record()
+            net.bwd(layer)
+            ev[3].record()
+            torch.cuda.synchronize()
+            tot["rope_keys"] += ev[0].elapsed_time(ev[1])
+            tot["fwd_attend"] += ev[1].elapsed_time(ev[2])
+            tot["bwd"] += ev[2].elapsed_time(ev[3])
+    return {k: v / (sweeps * n) for k, v in tot.items()}
+
+
+def measure(fa, name: str, steps: int, warmup: int, dev):
+    w = workloads.WORKLOADS[name]
+    log(f"[{name}] allocating inputs")
+    net = Layers(fa, w, dev)
+    log(f"[{name}] warmup {warmup} + timed {steps} steps")
+    ms_step, wall = time_steps(net, steps, warmup)
+    log(f"[{name}] {ms_step:.3f} ms per step; timing stages")
+    st = time_stages(net, 3)
+    qh = w.B * w.L * w.Hq
+    eb = 2 if w.dtype == "bf16" else 4
+    fwd_bytes = (2 * w.Hq + 2 * w.Hkv) * w.B * w.L * w.D * eb + qh * 4           # q, k, v, o, lse
+    bwd_bytes = (3 * w.Hq + 2 * w.Hkv) * w.B * w.L * w.D * eb + qh * 4 \
+        + (w.Hq + 2 * w.Hkv) * w.B * w.L * w.D * eb                            # + dq, dk, dv
+    fwd_ms = st["rope_keys"] + st["fwd_attend"]
+    res = {
+        "ms_per_step": ms_step,
+        "wall_s": wall,
+        "qh_per_s": w.n_layers * qh / (ms_step * 1e-3),
+        "fwd": {"ms_per_call": fwd_ms, "qh_per_s": qh / (fwd_ms * 1e-3),
+                "GB_per_s": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
+                "frac_hbm_peak": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "algorithmic_bytes": fwd_bytes},
+        "bwd": {"ms_per_call": st["bwd"], "qh_per_s": qh / (st["bwd"] * 1e-3),
+                "GB_per_s": bwd_bytes / (st["bwd"] * 1e-3) / 1e9,
+                "frac_hbm_peak": bwd_bytes / (st["bwd"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "algorithmic_bytes": bwd_bytes},
+        "kernels_ms": st,
+        "attend_bytes": fwd_bytes,
+    }
+    del net
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="l1024_linear_bf16")
+    ap.add_argument("--long-workload", default="l4096_coprime_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the float64 oracle on the host cores")
+        cpu = cpu_baseline(args.workload)
+        log(f"cpu baseline: {cpu['value']:.0f} q*h/s on {cpu['cores']} cores")
+
+    import fibonacci_offset_sparse_amd as fa
+    dev = torch.device("cuda:0")
+    main_res = measure(fa, args.workload, args.steps, args.warmup, dev)
+    long_res = None if args.no_long else measure(fa, args.long_workload, max(3, args.steps // 4), 1, dev)
+
+    w = workloads.WORKLOADS[args.workload]
+    att_ms = main_res["kernels_ms"]["fwd_attend"]
+    achieved = main_res["attend_bytes"] / (att_ms * 1e-3) / 1e9
+    line = {
+        "metric": "fwd+bwd queries*heads/sec (and fwd HBM GB/s, % of peak)",
+        "value": main_res["qh_per_s"],
+        "unit": "queries*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": w.B, "L": w.L, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "W": w.W, "base": w.base, "schedule": w.schedule, "layers": w.n_layers,
+                   "pass": "fwd+bwd", "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "fwd_attend_kernel", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "avg_launch_ms": att_ms,
+                     "algorithmic_bytes_per_launch": main_res["attend_bytes"]},
+        "fwd": main_res["fwd"],
+        "bwd": main_res["bwd"],
+        "kernels_ms": main_res["kernels_ms"],
+        "cpu_baseline": cpu,
+    }
+    if long_res is not None:
+        lw = workloads.WORKLOADS[args.long_workload]
+        line["l4096"] = {"workload": args.long_workload, "B": lw.B, "L": lw.L, "ms_per_step": long_res["ms_per_step"],
+                         "qh_per_s": long_res["qh_per_s"], "fwd": long_res["fwd"], "bwd": long_res["bwd"],
+                         "kernels_ms": long_res["kernels_ms"]}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,262 @@
+"""Python binding of libfibattn.so: Fibonacci-offset sparse attention on MI355X (gfx950).
+
+Argument marshalling only. Every step of the forward and backward pass runs in the library's
+HIP kernels; PyTorch supplies device memory and the current stream. The functions carry the
+names of the C entry points in include/fibattn.h. Importing this package fails if the library
+has not been built (python -m fibonacci_offset_sparse_amd.build).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfibattn.so")
+
+F32, BF16 = 0, 1
+DUP, INT, INTERP = 0, 1, 2
+BASE_FIB, BASE_POW2 = 0, 1
+SCHEDULE_FIXED, SCHEDULE_LINEAR, SCHEDULE_COPRIME = 0, 1, 2
+MAX_W, MAX_K = 31, 32
+
+_c_i32, _c_u8, _c_f32, _c_f64 = ctypes.c_int32, ctypes.c_uint8, ctypes.c_float, ctypes.c_double
+_c_ptr, _c_size = ctypes.c_void_p, ctypes.c_size_t
+_P = ctypes.POINTER
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m fibonacci_offset_sparse_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "fibattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "fibattn_last_error": (ctypes.c_char_p, []),
+        "fibattn_base_offsets": (ctypes.c_int, [_c_i32, _c_i32, _P(_c_i32), _c_i32, _P(_c_i32)]),
+        "fibattn_alpha_schedule": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _P(_c_f64)]),
+        "fibattn_alpha_from_theta": (ctypes.c_int, [_c_f64, _P(_c_f64), _P(_c_f64)]),
+        "fibattn_plan": (ctypes.c_int, [_c_f64, _c_i32, _P(_c_i32), _c_i32, _P(_c_u8), _P(_c_i32),
+                                         _P(_c_f32), _P(_c_i32)]),
+        "fibattn_fwd_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+        "fibattn_fwd": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_f64, _c_i32, _P(_c_i32), _c_i32,
+                                        _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f64,
+                                        _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
+        "fibattn_rope_keys": (ctypes.c_int, [_c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f64,
+                                              _c_ptr, _c_size, _c_ptr]),
+        "fibattn_fwd_attend": (ctypes.c_int, [_c_ptr, _c_ptr, _c_f64, _c_i32, _P(_c_i32), _c_i32,
+                                               _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f64,
+                                               _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
+        "fibattn_bwd_workspace_bytes": (_c_size, [_c_i32] * 8),
+        "fibattn_bwd": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_f64, _c_i32,
+                                        _P(_c_i32), _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                        _c_i32, _c_f64, _c_f64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                        _c_ptr, _c_ptr, _c_size, _c_ptr]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class FibAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def fibattn_status_string(status: int) -> str:
+    return lib.fibattn_status_string(status).decode()
+
+
+def fibattn_last_error() -> str:
+    return lib.fibattn_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise FibAttnError(status, f"{fibattn_status_string(status)}: {fibattn_last_error()}")
+
+
+def _i32_array(values: Sequence[int]):
+    values = [int(x) for x in values]
+    return (_c_i32 * max(1, len(values)))(*values), len(values)
+
+
+# ------------------------------------------------------------------------------------------------
+# Host-only entry points (no GPU needed)
+# ------------------------------------------------------------------------------------------------
+
+def fibattn_base_offsets(base: int = BASE_FIB, pow2_max: int = 1024) -> Tuple[int, ...]:
+    out = (_c_i32 * MAX_K)()
+    n = _c_i32()
+    _check(lib.fibattn_base_offsets(base, pow2_max, out, MAX_K, ctypes.byref(n)))
+    return tuple(out[: n.value])
+
+
+def fibattn_alpha_schedule(schedule: int, layer: int, n_layers: int) -> float:
+    a = _c_f64()
+    _check(lib.fibattn_alpha_schedule(schedule, layer, n_layers, ctypes.byref(a)))
+    return a.value
+
+
+def fibattn_alpha_from_theta(theta: float) -> Tuple[float, float]:
+    a, d = _c_f64(), _c_f64()
+    _check(lib.fibattn_alpha_from_theta(float(theta), ctypes.byref(a), ctypes.byref(d)))
+    return a.value, d.value
+
+
+def fibattn_plan(alpha: float, W: int, offsets: Sequence[int]):
+    """(kind uint8[K], floor int32[K], t float32[K], reach int32[K]) of the offset plan."""
+    offs, K = _i32_array(offsets)
+    kind = np.zeros(max(K, 1), np.uint8)
+    fl = np.zeros(max(K, 1), np.int32)
+    t = np.zeros(max(K, 1), np.float32)
+    reach = np.zeros(max(K, 1), np.int32)
+    _check(lib.fibattn_plan(float(alpha), int(W), offs, K,
+                            kind.ctypes.data_as(_P(_c_u8)), fl.ctypes.data_as(_P(_c_i32)),
+                            t.ctypes.data_as(_P(_c_f32)), reach.ctypes.data_as(_P(_c_i32))))
+    return kind[:K], fl[:K], t[:K], reach[:K]
+
+
+def fibattn_fwd_workspace_bytes(B: int, L: int, Hkv: int, D: int = 64, dtype: int = BF16) -> int:
+    return int(lib.fibattn_fwd_workspace_bytes(B, L, Hkv, D, dtype))
+
+
+def fibattn_bwd_workspace_bytes(B: int, L: int, Hq: int, Hkv: int, D: int, W: int, K: int,
+                                dtype: int = BF16) -> int:
+    return int(lib.fibattn_bwd_workspace_bytes(B, L, Hq, Hkv, D, W, K, dtype))
+
+
+# ------------------------------------------------------------------------------------------------
+# Device entry points
+# ------------------------------------------------------------------------------------------------
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str, shape, dtype) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, H, L, D]")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device, stream) -> int:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _shapes(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, L, D]")
+    B, Hq, L, D = q.shape
+    return B, Hq, L, D, k.shape[1]
+
+
+def _workspace(ws: Optional[torch.Tensor], nbytes: int, device) -> torch.Tensor:
+    if ws is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if not ws.is_cuda or ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace must be a GPU tensor of at least {nbytes} bytes")
+    return ws
+
+
+def fibattn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, W: int,
+                offsets: Sequence[int], rope_theta: float = 1e4, o: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, need_lse: bool = True,
+                workspace: Optional[torch.Tensor] = None, stream=None):
+    """o [B, Hq, L, D] (and lse [B, Hq, L] float32 when need_lse) of the sparse attention."""
+    B, Hq, L, D, Hkv = _shapes(q, k)
+    dt = _dtype_code(q)
+    args = [_dev(q, "q", (B, Hq, L, D), q.dtype), _dev(k, "k", (B, Hkv, L, D), q.dtype),
+            _dev(v, "v", (B, Hkv, L, D), q.dtype)]
+    o = torch.empty_like(q) if o is None else o
+    if need_lse and lse is None:
+        lse = torch.empty(B, Hq, L, dtype=torch.float32, device=q.device)
+    optr = _dev(o, "o", (B, Hq, L, D), q.dtype)
+    lptr = _dev(lse, "lse", (B, Hq, L), torch.float32) if lse is not None else None
+    nbytes = fibattn_fwd_workspace_bytes(B, L, Hkv, D, dt)
+    ws = _workspace(workspace, nbytes, q.device)
+    offs, K = _i32_array(offsets)
+    with torch.cuda.device(q.device):
+        _check(lib.fibattn_fwd(*args, float(alpha), int(W), offs, K, B, L, Hq, Hkv, D, dt,
+                               float(rope_theta), optr, lptr, ws.data_ptr(), ws.numel(),
+                               _stream(q.device, stream)))
+    return o, lse
+
+
+def fibattn_rope_keys(k: torch.Tensor, workspace: torch.Tensor, rope_theta: float = 1e4, stream=None):
+    """First forward stage: rotated keys into `workspace` (for timing the stages apart)."""
+    B, Hkv, L, D = k.shape
+    dt = _dtype_code(k)
+    _dev(k, "k", (B, Hkv, L, D), k.dtype)
+    with torch.cuda.device(k.device):
+        _check(lib.fibattn_rope_keys(k.data_ptr(), B, L, Hkv, D, dt, float(rope_theta),
+                                     workspace.data_ptr(), workspace.numel(), _stream(k.device, stream)))
+
+
+def fibattn_fwd_attend(q: torch.Tensor, v: torch.Tensor, alpha: float, W: int, offsets: Sequence[int],
+                       workspace: torch.Tensor, o: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                       rope_theta: float = 1e4, stream=None):
+    """Second forward stage; reads the rotated keys fibattn_rope_keys left in `workspace`."""
+    B, Hq, L, D = q.shape
+    Hkv = v.shape[1]
+    dt = _dtype_code(q)
+    _dev(q, "q", (B, Hq, L, D), q.dtype)
+    _dev(v, "v", (B, Hkv, L, D), q.dtype)
+    _dev(o, "o", (B, Hq, L, D), q.dtype)
+    lptr = _dev(lse, "lse", (B, Hq, L), torch.float32) if lse is not None else None
+    offs, K = _i32_array(offsets)
+    with torch.cuda.device(q.device):
+        _check(lib.fibattn_fwd_attend(q.data_ptr(), v.data_ptr(), float(alpha), int(W), offs, K, B, L, Hq,
+                                      Hkv, D, dt, float(rope_theta), o.data_ptr(), lptr,
+                                      workspace.data_ptr(), workspace.numel(), _stream(q.device, stream)))
+
+
+def fibattn_bwd(q, k, v, o, lse, dout, alpha: float, W: int, offsets: Sequence[int],
+                rope_theta: float = 1e4, dalpha_dtheta: float = 0.0, want_dalpha: bool = False,
+                workspace: Optional[torch.Tensor] = None, stream=None):
+    """(dq, dk, dv, dalpha, dtheta); dalpha and dtheta are float32[1] GPU tensors or None."""
+    B, Hq, L, D, Hkv = _shapes(q, k)
+    dt = _dtype_code(q)
+    ptrs = [_dev(q, "q", (B, Hq, L, D), q.dtype), _dev(k, "k", (B, Hkv, L, D), q.dtype),
+            _dev(v, "v", (B, Hkv, L, D), q.dtype), _dev(o, "o", (B, Hq, L, D), q.dtype),
+            _dev(lse, "lse", (B, Hq, L), torch.float32), _dev(dout, "dout", (B, Hq, L, D), q.dtype)]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    da = torch.empty(1, dtype=torch.float32, device=q.device) if want_dalpha else None
+    dth = torch.empty(1, dtype=torch.float32, device=q.device) if want_dalpha else None
+    offs, K = _i32_array(offsets)
+    nbytes = fibattn_bwd_workspace_bytes(B, L, Hq, Hkv, D, W, K, dt)
+    ws = _workspace(workspace, nbytes, q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.fibattn_bwd(*ptrs, float(alpha), int(W), offs, K, B, L, Hq, Hkv, D, dt,
+                               float(rope_theta), float(dalpha_dtheta), dq.data_ptr(), dk.data_ptr(),
+                               dv.data_ptr(), da.data_ptr() if da is not None else None,
+                               dth.data_ptr() if dth is not None else None, ws.data_ptr(), ws.numel(),
+                               _stream(q.device, stream)))
+    return dq, dk, dv, da, dth
+
+
+__all__ = [
+    "fibattn_status_string", "fibattn_last_error", "fibattn_base_offsets", "fibattn_alpha_schedule",
+    "fibattn_alpha_from_theta", "fibattn_plan", "fibattn_fwd_workspace_bytes", "fibattn_fwd",
+    "fibattn_rope_keys", "fibattn_fwd_attend", "fibattn_bwd_workspace_bytes", "fibattn_bwd",
+    "FibAttnError", "lib", "LIB_PATH",
+]

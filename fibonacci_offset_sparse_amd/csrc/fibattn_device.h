@@ -1,0 +1,98 @@
+// Device helpers for the gfx950 kernels: storage-type conversion, row loads and stores,
+// accurate RoPE angles, and the workgroup mapping. Included by the .hip files only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "fibattn_internal.h"
+
+namespace fibattn {
+
+using bf16_t = uint16_t;  // bfloat16 storage
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bfloat16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Four consecutive elements starting at p, as float.
+template <typename T> __device__ __forceinline__ float4 load4(const T* p);
+template <> __device__ __forceinline__ float4 load4<float>(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+}
+template <> __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
+    uint2 w = *reinterpret_cast<const uint2*>(p);
+    return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+}
+
+template <typename T> __device__ __forceinline__ void store4(T* p, float4 x);
+template <> __device__ __forceinline__ void store4<float>(float* p, float4 x) {
+    *reinterpret_cast<float4*>(p) = x;
+}
+template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 x) {
+    *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
+}
+
+// A 64-element row into registers.
+template <typename T> __device__ __forceinline__ void load_row(const T* p, float (&x)[kD]) {
+#pragma unroll
+    for (int c = 0; c < kD / 4; ++c) {
+        float4 v = load4<T>(p + 4 * c);
+        x[4 * c + 0] = v.x;
+        x[4 * c + 1] = v.y;
+        x[4 * c + 2] = v.z;
+        x[4 * c + 3] = v.w;
+    }
+}
+
+template <typename T> __device__ __forceinline__ void store_row(T* p, const float (&x)[kD]) {
+#pragma unroll
+    for (int c = 0; c < kD / 4; ++c)
+        store4<T>(p + 4 * c, make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]));
+}
+
+// cos and sin of pos * omega_j. The angle is reduced in revolutions with an exact
+// product (fma) against omega_j / (2 pi) held as hi + lo, so the reduction error stays near
+// 2^-25 revolutions for every position below 2^24, then sincosf evaluates the reduced angle.
+__device__ __forceinline__ void rope_cos_sin(int pos, float hi, float lo, float& c, float& s) {
+    const float fp = static_cast<float>(pos);
+    const float prod = fp * hi;
+    const float err = fmaf(fp, hi, -prod);
+    const float frac = (prod - rintf(prod)) + fmaf(fp, lo, err);
+    sincosf(frac * 6.28318530717958647692f, &s, &c);
+}
+
+// Rotate (x_j, x_{j+32}) by the angle whose cos/sin are cs[j].
+__device__ __forceinline__ void rope_apply(float (&x)[kD], const float2* cs) {
+#pragma unroll
+    for (int j = 0; j < kPairs; ++j) {
+        const float2 r = cs[j];
+        const float a = x[j], b = x[j + kPairs];
+        x[j] = a * r.x - b * r.y;
+        x[j + kPairs] = b * r.x + a * r.y;
+    }
+}
+
+// Transpose of the rotation (used for gradients).
+__device__ __forceinline__ void rope_apply_t(float (&x)[kD], const float2* cs) {
+#pragma unroll
+    for (int j = 0; j < kPairs; ++j) {
+        const float2 r = cs[j];
+        const float a = x[j], b = x[j + kPairs];
+        x[j] = a * r.x + b * r.y;
+        x[j + kPairs] = b * r.x - a * r.y;
+    }
+}
+
+}  // namespace fibattn

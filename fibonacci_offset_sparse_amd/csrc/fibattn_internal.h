@@ -1,0 +1,79 @@
+// Internal declarations shared by the host library and the gfx950 kernels of libfibattn.so.
+// Nothing here is part of the C ABI (include/fibattn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace fibattn {
+
+constexpr int kD = 64;        // head dimension the kernels take
+constexpr int kPairs = 32;    // RoPE pairs (j, j + 32)
+constexpr int kTile = 64;     // query (or key) positions per workgroup
+constexpr int kMaxWin = 32;   // window slots 0..W with W <= 31
+constexpr int kMaxOff = 32;   // base rungs
+
+// One kept offset of the plan (DUP rungs are removed before launch).
+struct OffsetSlot {
+    int32_t a;       // distance of the nearer row, floor(d)
+    float t;         // weight of the farther row a + 1 (0 for an integral offset)
+    int32_t interp;  // 1: interpolated, valid for i >= a + 1; 0: integral, valid for i >= a
+    int32_t f;       // base rung (d(alpha) weight)
+};
+
+// RoPE frequencies omega_j / (2 pi) as an unevaluated float sum hi + lo (double accuracy).
+struct RopeFreq {
+    float hi[kPairs];
+    float lo[kPairs];
+};
+
+struct RopeKeysArgs {
+    const void* k;   // [B*Hkv, L, 64] storage type
+    float* krot;     // [B*Hkv, L, 64] float32
+    int32_t n_bh;    // B * Hkv
+    int32_t L;
+    RopeFreq fr;
+};
+
+struct FwdArgs {
+    const void* q;       // [B, Hq, L, 64]
+    const void* v;       // [B, Hkv, L, 64]
+    const float* krot;   // [B, Hkv, L, 64] float32, rotated
+    void* o;             // [B, Hq, L, 64]
+    float* lse;          // [B, Hq, L] or nullptr
+    int32_t B, L, Hq, Hkv, G, W, n_off;
+    float qscale;        // log2(e) / sqrt(D): scores kept in base 2
+    RopeFreq fr;
+    OffsetSlot off[kMaxOff];
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* v;
+    const void* o;
+    const float* lse;
+    const void* dout;
+    const float* krot;   // [B, Hkv, L, 64] float32 (workspace)
+    float* qrot;         // [B, Hq, L, 64] float32 (workspace)
+    float* pbuf;         // [B, Hq, S, L] softmax weights (workspace)
+    float* dsbuf;        // [B, Hq, S, L] score gradients, already times 1/sqrt(D) (workspace)
+    float* partial;      // [n_wg, kMaxOff] per-workgroup sums of d(loss)/dt (workspace)
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dalpha;
+    float* dtheta;
+    int32_t B, L, Hq, Hkv, G, W, n_off, S;
+    int32_t n_wg;        // workgroups of the query-centric kernel
+    float scale;         // 1/sqrt(D)
+    float dalpha_dtheta;
+    RopeFreq fr;
+    OffsetSlot off[kMaxOff];
+};
+
+hipError_t launch_rope_keys(int dtype, const RopeKeysArgs& a, hipStream_t s);
+hipError_t launch_fwd_attend(int dtype, const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd(int dtype, const BwdArgs& a, bool want_dalpha, hipStream_t s);
+int bwd_query_workgroups(int B, int L, int Hkv, int G);
+
+}  // namespace fibattn

@@ -1,0 +1,187 @@
+/*
+ * fibattn.h - C ABI of libfibattn.so: depth-staggered Fibonacci-offset sparse self-attention,
+ * forward and backward, on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is defined in "Depth-Staggered Fibonacci Spacing for Sparse Attention: Static
+ * Schedules Beat Learned Dilation and Extrapolate Where Dense Attention Fails" (C. A. Capps,
+ * arXiv 2606.28560). Section references below are to that paper.
+ *
+ * What is computed (§2 "Attended set"). Query i of head h attends to
+ *   - the dense causal window of distances {0, 1, ..., W} (self included), and
+ *   - one slot per base rung f_k at distance d_k = alpha * f_k, read by linear interpolation:
+ *       key = (1 - t) * krot[i - a] + t * krot[i - a - 1],  a = floor(d_k),  t = d_k - a,
+ *     and likewise for the value row (values are not rotated).
+ * q and k are rotated by RoPE at their own (integer) positions before the gather, with
+ * half-split pairs (j, j + D/2) and frequency rope_theta^(-2j/D). Scores are scaled by 1/sqrt(D),
+ * softmax runs over the valid slots, and query head h reads key-value head h / (Hq / Hkv) (GQA,
+ * §3 "Models and training").
+ *
+ * Slot rules where the paper leaves the detail open (the offset plan, fibattn_plan):
+ *   - d_k is computed in double; if |d_k - rint(d_k)| <= 1e-9 it is snapped to rint(d_k);
+ *   - an integral d_k <= W is DUP: dropped, the window already holds that distance;
+ *   - an integral d_k > W is INT: row i - d_k, valid for i >= d_k;
+ *   - otherwise INTERP: valid for i >= floor(d_k) + 1 (the farther row exists).
+ * The kernels never read a row before 0 or at or beyond L.
+ *
+ * Layout: every tensor is contiguous [B, H, L, D] (H = Hq for q, o, do, dq; Hkv for k, v, dk,
+ * dv). lse is [B, Hq, L] float32 (natural log). D must be 64.
+ * Storage types: FIBATTN_F32 (float32 everywhere) or FIBATTN_BF16 (bfloat16 q, k, v, o, do, dq,
+ * dk, dv; arithmetic is float32).
+ *
+ * Ownership and execution. All buffers belong to the caller. Device pointers must stay valid
+ * until the stream reaches the work. `offsets` is a host array, read during the call and not
+ * kept. The library keeps no allocation and no state between calls; calls are asynchronous on
+ * `stream` (a hipStream_t; NULL is the null stream) and are re-entrant. Outputs are overwritten,
+ * never accumulated.
+ *
+ * Errors. Arguments are checked on the host before anything is launched; on error no work is
+ * queued and an error status is returned. fibattn_last_error() gives the calling thread's last
+ * error text. Nothing aborts or throws across this boundary.
+ */
+#ifndef FIBATTN_H
+#define FIBATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FIBATTN_OK = 0,
+    FIBATTN_ERR_INVALID = 1,      /* an argument is out of its domain */
+    FIBATTN_ERR_UNSUPPORTED = 2,  /* valid, but not implemented here (e.g. D != 64, W > 31) */
+    FIBATTN_ERR_WORKSPACE = 3,    /* workspace pointer missing or smaller than required */
+    FIBATTN_ERR_HIP = 4           /* a HIP call or kernel launch failed */
+} fibattn_status_t;
+
+typedef enum { FIBATTN_F32 = 0, FIBATTN_BF16 = 1 } fibattn_dtype_t;
+
+typedef enum { FIBATTN_DUP = 0, FIBATTN_INT = 1, FIBATTN_INTERP = 2 } fibattn_offset_kind_t;
+
+typedef enum { FIBATTN_BASE_FIB = 0, FIBATTN_BASE_POW2 = 1 } fibattn_base_t;
+
+typedef enum {
+    FIBATTN_SCHEDULE_FIXED = 0,
+    FIBATTN_SCHEDULE_LINEAR = 1,
+    FIBATTN_SCHEDULE_COPRIME = 2
+} fibattn_schedule_t;
+
+/* Largest window W and number of base rungs K the kernels take. */
+#define FIBATTN_MAX_W 31
+#define FIBATTN_MAX_K 32
+
+/* Text of a status code (static storage). */
+const char* fibattn_status_string(fibattn_status_t status);
+
+/* The calling thread's last error message ("" if none). Valid until the thread's next call. */
+const char* fibattn_last_error(void);
+
+/*
+ * Base rungs (§2 "Attended set" for the Fibonacci list 1, 2, 3, 5, ..., 987, K = 15; §2 "Control
+ * base" for the power-of-two control 1, 2, 4, ..., up to pow2_max inclusive).
+ * out: host int32[capacity]; *count receives K. pow2_max is ignored for the Fibonacci base.
+ * Errors: INVALID for a NULL pointer, an unknown base, pow2_max < 1, or capacity < K.
+ */
+fibattn_status_t fibattn_base_offsets(int32_t base, int32_t pow2_max, int32_t* out,
+                                      int32_t capacity, int32_t* count);
+
+/*
+ * Per-layer alpha of a static schedule (§2 "Per-layer scalar"): fixed 1; linear
+ * 0.5 + layer / (n_layers - 1); coprime: the linear value of layer (7 * layer mod n_layers).
+ * Errors: INVALID for NULL alpha, an unknown schedule, n_layers < 2, layer outside
+ * [0, n_layers), or (coprime) n_layers sharing a factor with 7.
+ */
+fibattn_status_t fibattn_alpha_schedule(int32_t schedule, int32_t layer, int32_t n_layers,
+                                        double* alpha);
+
+/*
+ * Learned schedule (§2 "Per-layer scalar"): alpha = 0.5 + sigmoid(theta), and the factor
+ * dalpha/dtheta = sigmoid(theta) (1 - sigmoid(theta)) that turns d(alpha) into d(theta).
+ * Either output may be NULL. Errors: INVALID for a non-finite theta.
+ */
+fibattn_status_t fibattn_alpha_from_theta(double theta, double* alpha, double* dalpha_dtheta);
+
+/*
+ * Offset plan: the slot table the kernels use, host-only and GPU-free (§2 "Attended set").
+ * For each rung k: kind_out[k] (fibattn_offset_kind_t), floor_out[k] = a, t_out[k] = t rounded
+ * to float32 (0 for INT and DUP), reach_out[k] = first query index at which the slot is valid.
+ * All outputs are host arrays of K entries. Errors: INVALID for NULL pointers (when K > 0),
+ * K outside [0, 32], W < 0, a non-finite or non-positive alpha, or offsets not strictly
+ * increasing from >= 1; UNSUPPORTED if some alpha * f_k exceeds 2^30.
+ */
+fibattn_status_t fibattn_plan(double alpha, int32_t W, const int32_t* offsets, int32_t K,
+                              uint8_t* kind_out, int32_t* floor_out, float* t_out,
+                              int32_t* reach_out);
+
+/* Bytes of device workspace fibattn_fwd needs (rotated keys). */
+size_t fibattn_fwd_workspace_bytes(int32_t B, int32_t L, int32_t Hkv, int32_t D, int32_t dtype);
+
+/*
+ * Forward pass (§2 "Attended set", "Implementation note"; shapes §3 "Models and training").
+ * q: device [B, Hq, L, D]; k, v: device [B, Hkv, L, D]; all of storage type `dtype`.
+ * o: device [B, Hq, L, D] of `dtype` (written). lse: device float32 [B, Hq, L] (written) or
+ * NULL when no backward pass will follow.
+ * workspace: device, >= fibattn_fwd_workspace_bytes(...) bytes, scratch for this call only.
+ * Queues two kernels on `stream`: fibattn_rope_keys, then fibattn_fwd_attend.
+ * Errors: INVALID (NULL pointers, B/L/Hq/Hkv < 1, Hq % Hkv != 0, W < 0, K outside [0, 32],
+ * bad alpha, bad offsets, unknown dtype, rope_theta not finite and > 0), UNSUPPORTED (D != 64,
+ * W > 31, L > 2^20), WORKSPACE, HIP.
+ */
+fibattn_status_t fibattn_fwd(const void* q, const void* k, const void* v, double alpha,
+                             int32_t W, const int32_t* offsets, int32_t K, int32_t B, int32_t L,
+                             int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype, double rope_theta,
+                             void* o, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * First stage of fibattn_fwd, exposed so that each kernel can be timed on its own: rotate
+ * every key row at its position into the workspace. Same arguments and errors as fibattn_fwd.
+ */
+fibattn_status_t fibattn_rope_keys(const void* k, int32_t B, int32_t L, int32_t Hkv, int32_t D,
+                                   int32_t dtype, double rope_theta, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
+ * Second stage of fibattn_fwd: the attention itself. Reads the rotated keys that
+ * fibattn_rope_keys left in `workspace` (same k shape, dtype and rope_theta), so it must follow
+ * it on the same stream with the workspace untouched in between.
+ */
+fibattn_status_t fibattn_fwd_attend(const void* q, const void* v, double alpha, int32_t W,
+                                    const int32_t* offsets, int32_t K, int32_t B, int32_t L,
+                                    int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
+                                    double rope_theta, void* o, float* lse,
+                                    const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace fibattn_bwd needs. */
+size_t fibattn_bwd_workspace_bytes(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D,
+                                   int32_t W, int32_t K, int32_t dtype);
+
+/*
+ * Backward pass: gradients of sum(do * o) for the forward above (§2 "Attended set": the
+ * interpolation keeps a gradient to alpha; §2 "Per-layer scalar": alpha = 0.5 + sigmoid(theta)).
+ * Inputs: q, k, v, o (the forward's output), lse (the forward's float32 lse), dout = do, all
+ * device, same shapes and storage type as the forward.
+ * Outputs (device, overwritten): dq [B, Hq, L, D], dk, dv [B, Hkv, L, D] of `dtype`;
+ * dalpha float32[1] or NULL; dtheta float32[1] or NULL, set to dalpha * dalpha_dtheta (pass the
+ * factor from fibattn_alpha_from_theta for the learned schedule).
+ * d(alpha) takes the slope of each interpolated read in alpha; integral offsets (INT, DUP)
+ * contribute nothing, so when dalpha or dtheta is requested and some rung is integral the call
+ * returns UNSUPPORTED.
+ * workspace: device, >= fibattn_bwd_workspace_bytes(...) bytes.
+ * Errors: as fibattn_fwd, plus UNSUPPORTED as above.
+ */
+fibattn_status_t fibattn_bwd(const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, double alpha, int32_t W,
+                             const int32_t* offsets, int32_t K, int32_t B, int32_t L, int32_t Hq,
+                             int32_t Hkv, int32_t D, int32_t dtype, double rope_theta,
+                             double dalpha_dtheta, void* dq, void* dk, void* dv, float* dalpha,
+                             float* dtheta, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FIBATTN_H */

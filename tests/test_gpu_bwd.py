@@ -1,0 +1,151 @@
+"""GPU parity of the backward pass against the float64 oracle (needs an MI355X).
+
+dq, dk, dv per element; d(alpha) and d(theta) per layer. Cases: the tiny workload (integral
+offsets, no d(alpha)), float32 interpolated cases, every layer of the learned-alpha workload at a
+reduced size, the learned workload at full size (sampled batch elements for dq/dk/dv, the full
+batch for d(theta)), GQA group sizes, ragged lengths, and bitwise determinism.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import fibattn_oracle as O
+from parity import check, check_f32
+
+pytestmark = pytest.mark.gpu
+
+fa = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global fa
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fibonacci_offset_sparse_amd as m
+    fa = m
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+DALPHA_RTOL = {torch.float32: 1e-5, torch.bfloat16: 1e-3}
+
+
+def run(q, k, v, do, alpha, W, base, want_dalpha, dadt=0.0):
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x.to(dev) for x in (q, k, v, do))
+    o, lse = fa.fibattn_fwd(q, k, v, alpha, W, base)
+    dq, dk, dv, da, dth = fa.fibattn_bwd(q, k, v, o, lse, do, alpha, W, base, dalpha_dtheta=dadt,
+                                         want_dalpha=want_dalpha)
+    torch.cuda.synchronize()
+    out = [dq.cpu(), dk.cpu(), dv.cpu()]
+    out += [float(da.item()) if da is not None else None, float(dth.item()) if dth is not None else None]
+    return out
+
+
+def compare(q, k, v, do, alpha, W, base, what, want_dalpha=True, bsel=None, dadt=0.0):
+    dq, dk, dv, da, dth = run(q, k, v, do, alpha, W, base, want_dalpha, dadt)
+    n64 = [x.double().numpy() for x in (q, k, v, do)]
+    if bsel is not None:
+        n64 = [x[bsel] for x in n64]
+        dq, dk, dv = dq[bsel], dk[bsel], dv[bsel]
+    rq, rk, rv, ra = O.backward(*n64, alpha, W, base)
+    check(dq, rq, q.dtype, what=f"{what} dq")
+    check(dk, rk, q.dtype, what=f"{what} dk")
+    check(dv, rv, q.dtype, what=f"{what} dv")
+    if want_dalpha and bsel is None:
+        tol = DALPHA_RTOL[q.dtype]
+        assert abs(da - ra) <= tol * max(abs(ra), 1e-3), f"{what} dalpha {da} vs {ra}"
+        if dadt:
+            assert abs(dth - ra * dadt) <= tol * max(abs(ra * dadt), 1e-3), f"{what} dtheta {dth} vs {ra * dadt}"
+    return da
+
+
+def randn(shape, seed, dtype=torch.float32):
+    return workloads.randn_like_seeded(shape, seed, dtype)
+
+
+def test_tiny_workload_integral_offsets():
+    w = workloads.WORKLOADS["tiny_fixed_f32"]
+    q, k, v, do = workloads.draw(w, 0)
+    say("bwd tiny workload fp32 alpha=1")
+    compare(q, k, v, do, 1.0, w.W, O.FIB_BASE, "tiny", want_dalpha=False)
+
+
+@pytest.mark.parametrize("alpha,W,L", [(0.73, 6, 64), (1.21, 3, 200), (0.5 + 1e-3, 12, 130), (1.49, 10, 1100)])
+def test_fp32_interpolated(alpha, W, L):
+    q, k, v, do = randn((2, 8, L, 64), 21), randn((2, 2, L, 64), 22), randn((2, 2, L, 64), 23), randn((2, 8, L, 64), 24)
+    say(f"bwd fp32 alpha={alpha} W={W} L={L}")
+    compare(q, k, v, do, alpha, W, O.FIB_BASE, f"a={alpha}")
+
+
+def test_learned_workload_every_layer_reduced():
+    w = workloads.WORKLOADS["l1024_learned_bf16"]
+    theta = workloads.draw_theta(w.n_layers).tolist()
+    for layer, th in enumerate(theta):
+        alpha, dadt = O.alpha_from_theta(th), O.dalpha_dtheta(th)
+        B, L = (2, 200) if layer % 2 == 0 else (1, 1100)
+        q, k, v, do = workloads.draw(w, layer, B=B, L=L)
+        say(f"bwd learned layer {layer} theta={th!r} B={B} L={L}")
+        compare(q, k, v, do, alpha, w.W, O.FIB_BASE, f"learned/{layer}", dadt=dadt)
+
+
+@pytest.mark.parametrize("layer", [0, 9])
+def test_learned_workload_full_size(layer):
+    w = workloads.WORKLOADS["l1024_learned_bf16"]
+    th = float(workloads.draw_theta(w.n_layers)[layer])
+    alpha, dadt = O.alpha_from_theta(th), O.dalpha_dtheta(th)
+    q, k, v, do = workloads.draw(w, layer)
+    say(f"bwd learned full size layer {layer} B={w.B} L={w.L}")
+    # dq, dk, dv on three batch elements (batch elements never mix)
+    compare(q, k, v, do, alpha, w.W, O.FIB_BASE, f"full/{layer}", bsel=[0, w.B // 2, w.B - 1], dadt=dadt)
+    # d(alpha) is a sum over the batch: the oracle's per-element sums added up
+    dq, dk, dv, da, dth = run(q, k, v, do, alpha, w.W, O.FIB_BASE, True, dadt)
+    ref = 0.0
+    for b in range(w.B):
+        ref += O.backward(*[x[b:b + 1].double().numpy() for x in (q, k, v, do)], alpha, w.W, O.FIB_BASE)[3]
+    assert abs(da - ref) <= 1e-3 * abs(ref), (da, ref)
+    assert abs(dth - ref * dadt) <= 1e-3 * abs(ref * dadt), (dth, ref * dadt)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 1), (6, 2)])
+def test_gqa_group_sizes(Hq, Hkv):
+    L = 150
+    q, k, v, do = randn((1, Hq, L, 64), 31), randn((1, Hkv, L, 64), 32), randn((1, Hkv, L, 64), 33), randn((1, Hq, L, 64), 34)
+    say(f"bwd Hq={Hq} Hkv={Hkv}")
+    compare(q, k, v, do, 0.83, 4, O.FIB_BASE, f"Hq={Hq} Hkv={Hkv}")
+
+
+@pytest.mark.parametrize("L", [1, 65, 333])
+def test_ragged_lengths_bf16(L):
+    d = torch.bfloat16
+    q, k, v, do = randn((2, 8, L, 64), 41, d), randn((2, 2, L, 64), 42, d), randn((2, 2, L, 64), 43, d), randn((2, 8, L, 64), 44, d)
+    say(f"bwd ragged L={L}")
+    compare(q, k, v, do, 0.67, 9, O.FIB_BASE, f"L={L}")
+
+
+def test_integral_offsets_with_pow2_base_and_window_extremes():
+    L = 260
+    q, k, v, do = randn((1, 8, L, 64), 51), randn((1, 2, L, 64), 52), randn((1, 2, L, 64), 53), randn((1, 8, L, 64), 54)
+    say("bwd pow2 alpha=1 W=0 / W=31 / no offsets")
+    compare(q, k, v, do, 1.0, 0, O.POW2_BASE_1024, "pow2 W=0", want_dalpha=False)
+    compare(q, k, v, do, 1.0, 31, O.FIB_BASE, "fib W=31", want_dalpha=False)
+    compare(q, k, v, do, 1.0, 5, [], "no offsets", want_dalpha=False)
+
+
+def test_bitwise_determinism():
+    w = workloads.WORKLOADS["l1024_learned_bf16"]
+    q, k, v, do = workloads.draw(w, 2, B=4)
+    alpha = O.alpha_from_theta(float(workloads.draw_theta(16)[2]))
+    say("bwd determinism B=4 L=1024")
+    a = run(q, k, v, do, alpha, w.W, O.FIB_BASE, True)
+    b = run(q, k, v, do, alpha, w.W, O.FIB_BASE, True)
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(x, y)
+    assert a[3] == b[3]

@@ -1,0 +1,174 @@
+"""GPU parity of the forward pass against the float64 oracle (needs an MI355X).
+
+Cases: every workload's layer calls at reduced sizes that span several tiles and a ragged tail,
+every workload at full size (sampled batch elements, since rows of different batch elements never
+mix), edge cases (tiny and ragged L, W = 0 and 31, no offsets, 32 offsets, GQA groups 1, 2, 8,
+alphas that put every offset below one row or beyond L), NaN guard rows around K and V, bitwise
+determinism and a non-default stream.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import fibattn_oracle as O
+from parity import check, check_f32
+
+pytestmark = pytest.mark.gpu
+
+fa = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global fa
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fibonacci_offset_sparse_amd as m
+    fa = m
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def base_of(w):
+    return O.FIB_BASE if w.base == "fib" else O.POW2_BASE_1024
+
+
+def alphas_of(w):
+    if w.schedule == "learned":
+        return [O.alpha_from_theta(float(t)) for t in workloads.draw_theta(w.n_layers)]
+    fn = {"fixed": O.alpha_fixed, "linear": O.alpha_linear, "coprime": O.alpha_coprime}[w.schedule]
+    return [fn(l, w.n_layers) for l in range(w.n_layers)]
+
+
+def run_fwd(q, k, v, alpha, W, base, **kw):
+    dev = torch.device("cuda:0")
+    o, lse = fa.fibattn_fwd(q.to(dev), k.to(dev), v.to(dev), alpha, W, base, **kw)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def compare(q, k, v, alpha, W, base, what, bsel=None):
+    o, lse = run_fwd(q, k, v, alpha, W, base)
+    if bsel is not None:
+        q, k, v, o, lse = q[bsel], k[bsel], v[bsel], o[bsel], lse[bsel]
+    o_ref, lse_ref = O.forward(q.double().numpy(), k.double().numpy(), v.double().numpy(), alpha, W, base)
+    check(o, o_ref, q.dtype, what=f"{what} o")
+    check_f32(lse, lse_ref, what=f"{what} lse")
+
+
+def test_tiny_workload():
+    w = workloads.WORKLOADS["tiny_fixed_f32"]
+    q, k, v, _ = workloads.draw(w, 0)
+    say("tiny workload B=1 L=64 fp32 alpha=1 W=6")
+    compare(q, k, v, 1.0, w.W, base_of(w), "tiny")
+
+
+@pytest.mark.parametrize("name", list(workloads.WORKLOADS))
+def test_every_layer_at_reduced_size(name):
+    w = workloads.WORKLOADS[name]
+    base = base_of(w)
+    for layer, alpha in enumerate(alphas_of(w)):
+        B, L = (2, 200) if layer % 2 == 0 else (1, 1100)
+        q, k, v = workloads.draw(w, layer, B=B, L=L, with_grad=False)
+        say(f"{name} layer {layer} alpha={alpha!r} B={B} L={L}")
+        compare(q, k, v, alpha, w.W, base, f"{name}/{layer}")
+
+
+@pytest.mark.parametrize("name", [n for n in workloads.WORKLOADS if n != "tiny_fixed_f32"])
+def test_full_size_sampled_batches(name):
+    w = workloads.WORKLOADS[name]
+    base = base_of(w)
+    alphas = alphas_of(w)
+    for layer in (0, w.n_layers // 2 + 1, w.n_layers - 1):
+        q, k, v = workloads.draw(w, layer, with_grad=False)
+        bsel = sorted({0, w.B // 2, w.B - 1})
+        say(f"{name} full size layer {layer} B={w.B} L={w.L}, checking batches {bsel}")
+        compare(q, k, v, alphas[layer], w.W, base, f"{name}/{layer}", bsel=bsel)
+
+
+def randn(shape, seed, dtype=torch.float32):
+    return workloads.randn_like_seeded(shape, seed, dtype)
+
+
+@pytest.mark.parametrize("L", [1, 2, 63, 64, 65, 129, 1000])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_ragged_lengths(L, dtype):
+    q, k, v = randn((2, 8, L, 64), 1, dtype), randn((2, 2, L, 64), 2, dtype), randn((2, 2, L, 64), 3, dtype)
+    say(f"ragged L={L} {dtype}")
+    compare(q, k, v, 0.77, 5, O.FIB_BASE, f"L={L}")
+
+
+@pytest.mark.parametrize("W,offsets,alpha", [
+    (0, O.FIB_BASE, 1.0), (0, O.FIB_BASE, 0.61), (31, O.FIB_BASE, 1.0), (31, O.FIB_BASE, 1.13),
+    (4, [], 1.0), (4, list(range(1, 33)), 1.0), (4, list(range(1, 33)), 0.93),
+    (3, O.FIB_BASE, 0.001), (3, O.FIB_BASE, 10.5), (2, O.POW2_BASE_1024, 1.5),
+])
+def test_window_and_offset_extremes(W, offsets, alpha):
+    L = 300
+    q, k, v = randn((1, 8, L, 64), 4), randn((1, 2, L, 64), 5), randn((1, 2, L, 64), 6)
+    say(f"W={W} K={len(offsets)} alpha={alpha}")
+    compare(q, k, v, alpha, W, offsets, f"W={W} K={len(offsets)} a={alpha}")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (4, 2), (8, 1), (6, 2), (3, 3)])
+def test_gqa_group_sizes(Hq, Hkv):
+    L = 150
+    q, k, v = randn((2, Hq, L, 64), 7), randn((2, Hkv, L, 64), 8), randn((2, Hkv, L, 64), 9)
+    say(f"Hq={Hq} Hkv={Hkv}")
+    compare(q, k, v, 0.88, 6, O.FIB_BASE, f"Hq={Hq} Hkv={Hkv}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_nan_guard_rows_are_never_read(dtype):
+    L, pad = 400, 4096
+    dev = torch.device("cuda:0")
+    q = randn((1, 8, L, 64), 10, dtype)
+    k, v = randn((1, 1, L, 64), 11, dtype), randn((1, 1, L, 64), 12, dtype)
+    q8 = q[:, :4].contiguous()
+    guards = []
+    for x in (k, v):
+        buf = torch.full((2 * pad + L * 64,), float("nan"), dtype=dtype, device=dev)
+        buf[pad:pad + L * 64] = x.reshape(-1).to(dev)
+        guards.append(buf[pad:pad + L * 64].view(1, 1, L, 64))
+    for alpha in (1.0, 0.71, 1.49):
+        say(f"guard rows alpha={alpha} {dtype}")
+        o, lse = fa.fibattn_fwd(q8.to(dev), guards[0], guards[1], alpha, 7, O.FIB_BASE)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+        o_ref, _ = O.forward(q8.double().numpy(), k.double().numpy(), v.double().numpy(), alpha, 7, O.FIB_BASE)
+        check(o.cpu(), o_ref, dtype, what=f"guard a={alpha}")
+
+
+def test_bitwise_determinism_and_side_stream():
+    w = workloads.WORKLOADS["l1024_linear_bf16"]
+    q, k, v = [x.to("cuda:0") for x in workloads.draw(w, 3, B=4, with_grad=False)]
+    alpha = O.alpha_linear(3, 16)
+    say("determinism B=4 L=1024 bf16")
+    o1, l1 = fa.fibattn_fwd(q, k, v, alpha, w.W, O.FIB_BASE)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = fa.fibattn_fwd(q, k, v, alpha, w.W, O.FIB_BASE)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_staged_entry_points_equal_the_combined_call():
+    w = workloads.WORKLOADS["l4096_coprime_bf16"]
+    q, k, v = [x.to("cuda:0") for x in workloads.draw(w, 5, B=1, with_grad=False)]
+    alpha = O.alpha_coprime(5, 16)
+    say("staged entry points B=1 L=4096")
+    o1, l1 = fa.fibattn_fwd(q, k, v, alpha, w.W, O.FIB_BASE)
+    ws = torch.empty(fa.fibattn_fwd_workspace_bytes(1, w.L, 2), dtype=torch.uint8, device="cuda:0")
+    o2 = torch.empty_like(q)
+    l2 = torch.empty_like(l1)
+    fa.fibattn_rope_keys(k, ws)
+    fa.fibattn_fwd_attend(q, v, alpha, w.W, O.FIB_BASE, ws, o2, l2)
+    fa.fibattn_fwd_attend(q, v, alpha, w.W, O.FIB_BASE, ws, o2, None)      # inference: no lse
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
