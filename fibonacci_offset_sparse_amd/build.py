@@ -24,8 +24,7 @@ ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Packed fp32 VALU instructions stay off: kernels use scalar fp32 FMA only.
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-ffp-contract=fast"]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 SOURCES = ["fibattn_api.cpp", "fibattn_fwd.hip", "fibattn_bwd.hip"]
 

@@ -315,8 +315,8 @@ fibattn_status_t fibattn_bwd(const void* q, const void* k, const void* v, const 
     g_error[0] = '\0';
     FIBATTN_TRY(check_dims(B, L, Hq, Hkv, D, W, dtype, rope_theta));
     FIBATTN_TRY(check_offsets(alpha, W, offsets, K));
-    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr || dout == nullptr ||
-        dq == nullptr || dk == nullptr || dv == nullptr)
+    if (q == nullptr || k == nullptr || v == nullptr || lse == nullptr || dout == nullptr || dq == nullptr ||
+        dk == nullptr || dv == nullptr)
         return fail(FIBATTN_ERR_INVALID, "a required pointer is NULL");
     if (!std::isfinite(dalpha_dtheta)) return fail(FIBATTN_ERR_INVALID, "dalpha_dtheta is not finite");
     const size_t need = fibattn_bwd_workspace_bytes(B, L, Hq, Hkv, D, W, K, dtype);

@@ -6,9 +6,11 @@
 //
 // Three kernels, no atomics (results are bitwise reproducible):
 //  * bwd_query: workgroup = (batch, kv head, head chunk, 64 queries), like the forward.
-//      pass V: dP_s = do . val_s, and for interpolated slots g_s = do . (far - near);
-//      pass K: s -> p = exp(s - lse), dS = p (dP - delta) with delta = do . o,
-//              dq_rot += dS key_s / sqrt(D), dt_s = dS (q_rot . (far - near)) / sqrt(D) + p g_s;
+//      pass K1: s -> p = exp(s - lse) for every slot;
+//      pass V:  dP_s = do . val_s, and for interpolated slots g_s = do . (far - near);
+//               delta = sum_s p_s dP_s (equal to do . o, but from the float32 probabilities
+//               rather than from o rounded to its storage type), dS = p (dP - delta);
+//      pass K2: dq_rot += dS key_s / sqrt(D), dt_s = dS (q_rot . (far - near)) / sqrt(D) + p g_s;
 //      writes dq (RoPE transposed), the rotated q, p and dS/sqrt(D) per (query, slot), and one
 //      fixed-order sum of dt per offset per workgroup.
 //  * bwd_key: workgroup = (batch, kv head, 64 key rows). A key row j is read by query j + a of
@@ -95,8 +97,23 @@ __device__ __forceinline__ void axpy_blend(float (&o)[kD], float p, const float*
     }
 }
 
+// Fixed-order sum of v over the workgroup; every thread gets the result. Two barriers.
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) s += red[w];
+    return s;
+}
+
 // ------------------------------------------------------------------------------------------------
-// bwd_query
+// bwd_query. Per-slot values live in the workspace columns p[bh][slot][i] and dS[bh][slot][i]
+// (each thread reads back only what it wrote), so the slot loops need no register arrays.
 // ------------------------------------------------------------------------------------------------
 template <typename T, int HPB>
 __global__ __launch_bounds__(kTile * HPB) void bwd_query_kernel(BwdArgs A) {
@@ -104,7 +121,8 @@ __global__ __launch_bounds__(kTile * HPB) void bwd_query_kernel(BwdArgs A) {
     constexpr float kLog2e = 1.44269504088896340736f;
     __shared__ __attribute__((aligned(16))) float buf[kMaxRows * kPitch];
     __shared__ float2 cs_tab[kTile][kPairs];
-    __shared__ float red[NT / 64][kMaxOff];
+    __shared__ float red[NT / 64];
+    __shared__ float dt_acc[kMaxOff];
 
     const int p = threadIdx.x / HPB;
     const int hh = threadIdx.x % HPB;
@@ -123,65 +141,21 @@ __global__ __launch_bounds__(kTile * HPB) void bwd_query_kernel(BwdArgs A) {
         rope_cos_sin(i0 + pp, A.fr.hi[m], A.fr.lo[m], c, s);
         cs_tab[pp][m] = make_float2(c, s);
     }
+    if (threadIdx.x < kMaxOff) dt_acc[threadIdx.x] = 0.f;
     __syncthreads();
 
     const int64_t bh = static_cast<int64_t>(b) * A.Hq + h;
     const int64_t qrow = (bh * L + i) * kD;
-    float x[kD];   // do during pass V, q_rot during pass K
-    float lse2 = 0.f, delta = 0.f;
-    if (active) {
-        float ov[kD];
-        load_row<T>(static_cast<const T*>(A.o) + qrow, ov);
-        load_row<T>(static_cast<const T*>(A.dout) + qrow, x);
-#pragma unroll
-        for (int e = 0; e < kD; ++e) delta = fmaf(x[e], ov[e], delta);
-        lse2 = A.lse[bh * L + i] * kLog2e;
-    } else {
-#pragma unroll
-        for (int e = 0; e < kD; ++e) x[e] = 0.f;
-    }
-
+    const float lse2 = active ? A.lse[bh * L + i] * kLog2e : 0.f;
+    const float qs2 = A.scale * kLog2e;
     const int64_t kv_base = (static_cast<int64_t>(b) * A.Hkv + g) * L * kD;
     const float* krot = A.krot + kv_base;
     const T* vsrc = static_cast<const T*>(A.v) + kv_base;
+    // this thread's column of the slot tables (only touched when active)
+    float* pcol = A.pbuf + bh * S * L + (active ? i : 0);
+    float* dcol = A.dsbuf + bh * S * L + (active ? i : 0);
 
-    // ---- pass V ----
-    float dpw[kMaxWin], dpo[kMaxOff], gvo[kMaxOff];
-    stage_rows<T, NT>(buf, vsrc, i0 - W, kTile + W, L);
-    __syncthreads();
-#pragma unroll
-    for (int d = 0; d < kMaxWin; ++d) {
-        dpw[d] = 0.f;
-        if (d <= W && active && i >= d) dpw[d] = dot_row(x, buf + (p + W - d) * kPitch);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int n = 0; n < kMaxOff; ++n) {
-        dpo[n] = 0.f;
-        gvo[n] = 0.f;
-        if (n < A.n_off) {
-            const int a = A.off[n].a;
-            const int reach = a + A.off[n].interp;
-            if (i0 + kTile - 1 >= reach) {
-                stage_rows<T, NT>(buf, vsrc, i0 - a - 1, kTile + 1, L);
-                __syncthreads();
-                const float* near = buf + (p + 1) * kPitch;
-                if (active && i >= reach) {
-                    if (A.off[n].interp) {
-                        float dn, dd;
-                        dot_pair(x, near, near - kPitch, dn, dd);
-                        dpo[n] = fmaf(A.off[n].t, dd, dn);
-                        gvo[n] = dd;
-                    } else {
-                        dpo[n] = dot_row(x, near);
-                    }
-                }
-                __syncthreads();
-            }
-        }
-    }
-
-    // ---- q_rot ----
+    float x[kD];   // q_rot in the K passes, do in the V pass
     if (active) {
         load_row<T>(static_cast<const T*>(A.q) + qrow, x);
     } else {
@@ -191,93 +165,140 @@ __global__ __launch_bounds__(kTile * HPB) void bwd_query_kernel(BwdArgs A) {
     rope_apply(x, cs_tab[p]);
     if (active) store_row<float>(A.qrot + qrow, x);
 
-    // ---- pass K ----
-    const float qs2 = A.scale * kLog2e;
+    // ---- pass K1: p = exp(s - lse) for every slot ----
+    stage_rows<float, NT>(buf, krot, i0 - W, kTile + W, L);
+    __syncthreads();
+    for (int d = 0; d <= W; ++d) {
+        float pr = 0.f;
+        if (active && i >= d) pr = exp2f(dot_row(x, buf + (p + W - d) * kPitch) * qs2 - lse2);
+        if (active) pcol[static_cast<int64_t>(d) * L] = pr;
+    }
+    __syncthreads();
+    for (int n = 0; n < A.n_off; ++n) {
+        const int a = A.off[n].a;
+        const int reach = a + A.off[n].interp;
+        float pr = 0.f;
+        if (i0 + kTile - 1 >= reach) {
+            stage_rows<float, NT>(buf, krot, i0 - a - 1, kTile + 1, L);
+            __syncthreads();
+            const float* near = buf + (p + 1) * kPitch;
+            if (active && i >= reach) {
+                float s;
+                if (A.off[n].interp) {
+                    float dn, dd;
+                    dot_pair(x, near, near - kPitch, dn, dd);
+                    s = fmaf(A.off[n].t, dd, dn);
+                } else {
+                    s = dot_row(x, near);
+                }
+                pr = exp2f(s * qs2 - lse2);
+            }
+            __syncthreads();
+        }
+        if (active) pcol[static_cast<int64_t>(W + 1 + n) * L] = pr;
+    }
+
+    // ---- pass V: dP_s (kept in the dS column), delta, and the p g part of dt ----
+    if (active) load_row<T>(static_cast<const T*>(A.dout) + qrow, x);
+    float delta = 0.f;
+    stage_rows<T, NT>(buf, vsrc, i0 - W, kTile + W, L);
+    __syncthreads();
+    for (int d = 0; d <= W; ++d) {
+        if (!active) continue;
+        const float pr = pcol[static_cast<int64_t>(d) * L];
+        float dp = 0.f;
+        if (pr > 0.f) {
+            dp = dot_row(x, buf + (p + W - d) * kPitch);
+            delta = fmaf(pr, dp, delta);
+        }
+        dcol[static_cast<int64_t>(d) * L] = dp;
+    }
+    __syncthreads();
+    for (int n = 0; n < A.n_off; ++n) {
+        const int a = A.off[n].a;
+        const int reach = a + A.off[n].interp;
+        if (i0 + kTile - 1 < reach) {
+            if (active) dcol[static_cast<int64_t>(W + 1 + n) * L] = 0.f;
+            continue;
+        }
+        stage_rows<T, NT>(buf, vsrc, i0 - a - 1, kTile + 1, L);
+        __syncthreads();
+        const float* near = buf + (p + 1) * kPitch;
+        float dp = 0.f, pg = 0.f;
+        const float pr = active ? pcol[static_cast<int64_t>(W + 1 + n) * L] : 0.f;
+        if (pr > 0.f) {
+            if (A.off[n].interp) {
+                float dn, dd;
+                dot_pair(x, near, near - kPitch, dn, dd);
+                dp = fmaf(A.off[n].t, dd, dn);
+                pg = pr * dd;
+            } else {
+                dp = dot_row(x, near);
+            }
+            delta = fmaf(pr, dp, delta);
+        }
+        if (active) dcol[static_cast<int64_t>(W + 1 + n) * L] = dp;
+        if (A.off[n].interp) {
+            const float sum = block_sum<NT>(pg, red);     // barriers also fence the LDS block
+            if (threadIdx.x == 0) dt_acc[n] = sum;
+        } else {
+            __syncthreads();
+        }
+    }
+
+    // ---- dS = p (dP - delta) / sqrt(D) ----
+    if (active) {
+        for (int sl = 0; sl < S; ++sl) {
+            const float pr = pcol[static_cast<int64_t>(sl) * L];
+            const float dp = dcol[static_cast<int64_t>(sl) * L];
+            dcol[static_cast<int64_t>(sl) * L] = pr * (dp - delta) * A.scale;
+        }
+        load_row<T>(static_cast<const T*>(A.q) + qrow, x);
+    }
+    rope_apply(x, cs_tab[p]);
+
+    // ---- pass K2: dq_rot and the dS e part of dt ----
     float dqr[kD];
 #pragma unroll
     for (int e = 0; e < kD; ++e) dqr[e] = 0.f;
-    float dto[kMaxOff];
-    float* pcol = A.pbuf + bh * S * L + i;
-    float* dcol = A.dsbuf + bh * S * L + i;
-
     stage_rows<float, NT>(buf, krot, i0 - W, kTile + W, L);
     __syncthreads();
-#pragma unroll
-    for (int d = 0; d < kMaxWin; ++d) {
-        if (d <= W) {
-            float pr = 0.f, ds = 0.f;
-            if (active && i >= d) {
-                const float* row = buf + (p + W - d) * kPitch;
-                const float s2 = dot_row(x, row) * qs2;
-                pr = exp2f(s2 - lse2);
-                ds = pr * (dpw[d] - delta) * A.scale;
-                axpy_row(dqr, ds, row);
-            }
-            if (active) {
-                pcol[static_cast<int64_t>(d) * L] = pr;
-                dcol[static_cast<int64_t>(d) * L] = ds;
-            }
-        }
+    for (int d = 0; d <= W; ++d) {
+        const float ds = active ? dcol[static_cast<int64_t>(d) * L] : 0.f;
+        if (ds != 0.f) axpy_row(dqr, ds, buf + (p + W - d) * kPitch);
     }
     __syncthreads();
-#pragma unroll
-    for (int n = 0; n < kMaxOff; ++n) {
-        dto[n] = 0.f;
-        if (n < A.n_off) {
-            const int a = A.off[n].a;
-            const int reach = a + A.off[n].interp;
-            const int slot = W + 1 + n;
-            float pr = 0.f, ds = 0.f;
-            if (i0 + kTile - 1 >= reach) {
-                stage_rows<float, NT>(buf, krot, i0 - a - 1, kTile + 1, L);
-                __syncthreads();
-                const float* near = buf + (p + 1) * kPitch;
-                if (active && i >= reach) {
-                    if (A.off[n].interp) {
-                        const float t = A.off[n].t;
-                        float dn, dd;
-                        dot_pair(x, near, near - kPitch, dn, dd);
-                        const float s2 = fmaf(t, dd, dn) * qs2;
-                        pr = exp2f(s2 - lse2);
-                        ds = pr * (dpo[n] - delta) * A.scale;
-                        axpy_blend(dqr, ds, near, near - kPitch, t);
-                        dto[n] = fmaf(ds, dd, pr * gvo[n]);
-                    } else {
-                        const float s2 = dot_row(x, near) * qs2;
-                        pr = exp2f(s2 - lse2);
-                        ds = pr * (dpo[n] - delta) * A.scale;
-                        axpy_row(dqr, ds, near);
-                    }
-                }
-                __syncthreads();
+    for (int n = 0; n < A.n_off; ++n) {
+        const int a = A.off[n].a;
+        const int reach = a + A.off[n].interp;
+        if (i0 + kTile - 1 < reach) continue;
+        stage_rows<float, NT>(buf, krot, i0 - a - 1, kTile + 1, L);
+        __syncthreads();
+        const float* near = buf + (p + 1) * kPitch;
+        const float ds = active ? dcol[static_cast<int64_t>(W + 1 + n) * L] : 0.f;
+        float de = 0.f;
+        if (A.off[n].interp) {
+            if (ds != 0.f) {
+                float dn, dd;
+                dot_pair(x, near, near - kPitch, dn, dd);
+                axpy_blend(dqr, ds, near, near - kPitch, A.off[n].t);
+                de = ds * dd;
             }
-            if (active) {
-                pcol[static_cast<int64_t>(slot) * L] = pr;
-                dcol[static_cast<int64_t>(slot) * L] = ds;
-            }
+            const float sum = block_sum<NT>(de, red);
+            if (threadIdx.x == 0) dt_acc[n] += sum;
+        } else {
+            if (ds != 0.f) axpy_row(dqr, ds, near);
+            __syncthreads();
         }
     }
 
     rope_apply_t(dqr, cs_tab[p]);
     if (active) store_row<T>(static_cast<T*>(A.dq) + qrow, dqr);
 
-    // ---- fixed-order workgroup sums of dt per offset ----
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-#pragma unroll
-    for (int n = 0; n < kMaxOff; ++n) {
-        if (n < A.n_off) {
-            float v = dto[n];
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-            if (lane == 0) red[wave][n] = v;
-        }
-    }
     __syncthreads();
     if (threadIdx.x < A.n_off) {
-        float s = 0.f;
-        for (int w = 0; w < NT / 64; ++w) s += red[w][threadIdx.x];
         const int64_t wg = (static_cast<int64_t>(blockIdx.z) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
-        A.partial[wg * kMaxOff + threadIdx.x] = s;
+        A.partial[wg * kMaxOff + threadIdx.x] = dt_acc[threadIdx.x];
     }
 }
 
@@ -327,13 +348,21 @@ __global__ __launch_bounds__(kTile * HPB) void bwd_key_kernel(BwdArgs A) {
                 const int64_t idx = static_cast<int64_t>(slot) * L + qi;
                 const float ds = db[idx] * w, pr = pb[idx] * w;
                 if (ds == 0.f && pr == 0.f) return;
-                float xr[kD];
-                load_row<float>(qrot + static_cast<int64_t>(qi) * kD, xr);
+                const float* qr = qrot + static_cast<int64_t>(qi) * kD;
+                const T* dr = dout + static_cast<int64_t>(qi) * kD;
 #pragma unroll
-                for (int e = 0; e < kD; ++e) dk[e] = fmaf(ds, xr[e], dk[e]);
-                load_row<T>(dout + static_cast<int64_t>(qi) * kD, xr);
-#pragma unroll
-                for (int e = 0; e < kD; ++e) dv[e] = fmaf(pr, xr[e], dv[e]);
+                for (int c = 0; c < kD / 4; ++c) {
+                    const float4 a = load4<float>(qr + 4 * c);
+                    const float4 u = load4<T>(dr + 4 * c);
+                    dk[4 * c + 0] = fmaf(ds, a.x, dk[4 * c + 0]);
+                    dk[4 * c + 1] = fmaf(ds, a.y, dk[4 * c + 1]);
+                    dk[4 * c + 2] = fmaf(ds, a.z, dk[4 * c + 2]);
+                    dk[4 * c + 3] = fmaf(ds, a.w, dk[4 * c + 3]);
+                    dv[4 * c + 0] = fmaf(pr, u.x, dv[4 * c + 0]);
+                    dv[4 * c + 1] = fmaf(pr, u.y, dv[4 * c + 1]);
+                    dv[4 * c + 2] = fmaf(pr, u.z, dv[4 * c + 2]);
+                    dv[4 * c + 3] = fmaf(pr, u.w, dv[4 * c + 3]);
+                }
             };
             for (int d = 0; d <= W; ++d) term(j + d, d, 1.f);
             for (int n = 0; n < A.n_off; ++n) {

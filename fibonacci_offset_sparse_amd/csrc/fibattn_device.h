@@ -62,14 +62,15 @@ template <typename T> __device__ __forceinline__ void store_row(T* p, const floa
         store4<T>(p + 4 * c, make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]));
 }
 
-// cos and sin of pos * omega_j. The angle is reduced in revolutions with an exact
-// product (fma) against omega_j / (2 pi) held as hi + lo, so the reduction error stays near
-// 2^-25 revolutions for every position below 2^24, then sincosf evaluates the reduced angle.
+// cos and sin of pos * omega_j. The angle is reduced in revolutions against omega_j / (2 pi)
+// held as hi + lo (double accuracy): n is the nearest whole revolution, fma(pos, hi, -n) takes the
+// exact product minus n and rounds once, and pos * lo is added, so the reduced angle is good to
+// about 2^-25 revolutions for every position below 2^24. Only explicit fmas appear, so no
+// contraction can change what is computed.
 __device__ __forceinline__ void rope_cos_sin(int pos, float hi, float lo, float& c, float& s) {
     const float fp = static_cast<float>(pos);
-    const float prod = fp * hi;
-    const float err = fmaf(fp, hi, -prod);
-    const float frac = (prod - rintf(prod)) + fmaf(fp, lo, err);
+    const float n = rintf(fp * hi);
+    const float frac = fmaf(fp, lo, fmaf(fp, hi, -n));
     sincosf(frac * 6.28318530717958647692f, &s, &c);
 }
 

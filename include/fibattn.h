@@ -161,8 +161,11 @@ size_t fibattn_bwd_workspace_bytes(int32_t B, int32_t L, int32_t Hq, int32_t Hkv
 /*
  * Backward pass: gradients of sum(do * o) for the forward above (§2 "Attended set": the
  * interpolation keeps a gradient to alpha; §2 "Per-layer scalar": alpha = 0.5 + sigmoid(theta)).
- * Inputs: q, k, v, o (the forward's output), lse (the forward's float32 lse), dout = do, all
- * device, same shapes and storage type as the forward.
+ * Inputs: q, k, v, lse (the forward's float32 lse), dout = do, all device, same shapes and
+ * storage type as the forward. o (the forward's output) is accepted for the usual attention
+ * backward signature but is not read and may be NULL: the row term delta = do . o is formed as
+ * sum_s p_s (do . val_s) from the recomputed float32 probabilities, which keeps the rounding of o
+ * to its storage type out of the gradients.
  * Outputs (device, overwritten): dq [B, Hq, L, D], dk, dv [B, Hkv, L, D] of `dtype`;
  * dalpha float32[1] or NULL; dtheta float32[1] or NULL, set to dalpha * dalpha_dtheta (pass the
  * factor from fibattn_alpha_from_theta for the learned schedule).
