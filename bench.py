@@ -134,8 +134,8 @@ class Layers:
         self.fa.fibattn_fwd(q, k, v, self.alphas[layer], self.w.W, self.base, o=self.o[layer],
                             lse=self.lse[layer], workspace=self.ws_f)
 
-    def rope(self, layer):
-        self.fa.fibattn_rope_keys(self.inputs[layer][1], self.ws_f)
+    def prep(self, layer):
+        self.fa.fibattn_fwd_prep(self.inputs[layer][1], self.inputs[layer][2], self.ws_f)
 
     def attend(self, layer):
         q, _, v, _ = self.inputs[layer]
@@ -172,19 +172,19 @@ def time_steps(net: Layers, steps: int, warmup: int):
 def time_stages(net: Layers, sweeps: int):
     """Average duration of each stage, from HIP events on the stream the kernels run on."""
     n = net.w.n_layers
-    tot = {"rope_keys": 0.0, "fwd_attend": 0.0, "bwd": 0.0}
+    tot = {"fwd_prep": 0.0, "fwd_attend": 0.0, "bwd": 0.0}
     for _ in range(sweeps):
         for layer in range(n):
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             ev[0].record()
-            net.rope(layer)
+            net.prep(layer)
             ev[1].record()
             net.attend(layer)
             ev[2].record()
             net.bwd(layer)
             ev[3].record()
             torch.cuda.synchronize()
-            tot["rope_keys"] += ev[0].elapsed_time(ev[1])
+            tot["fwd_prep"] += ev[0].elapsed_time(ev[1])
             tot["fwd_attend"] += ev[1].elapsed_time(ev[2])
             tot["bwd"] += ev[2].elapsed_time(ev[3])
     return {k: v / (sweeps * n) for k, v in tot.items()}
@@ -203,7 +203,7 @@ def measure(fa, name: str, steps: int, warmup: int, dev):
     fwd_bytes = (2 * w.Hq + 2 * w.Hkv) * w.B * w.L * w.D * eb + qh * 4           # q, k, v, o, lse
     bwd_bytes = (3 * w.Hq + 2 * w.Hkv) * w.B * w.L * w.D * eb + qh * 4 \
         + (w.Hq + 2 * w.Hkv) * w.B * w.L * w.D * eb                            # + dq, dk, dv
-    fwd_ms = st["rope_keys"] + st["fwd_attend"]
+    fwd_ms = st["fwd_prep"] + st["fwd_attend"]
     res = {
         "ms_per_step": ms_step,
         "wall_s": wall,

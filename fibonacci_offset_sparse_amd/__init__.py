@@ -3,7 +3,7 @@
 Argument marshalling only. Every step of the forward and backward pass runs in the library's
 HIP kernels; PyTorch supplies device memory and the current stream. The functions carry the
 names of the C entry points in include/fibattn.h. Importing this package fails if the library
-has not been built (python -m fibonacci_offset_sparse_amd.build).
+has not been built (python fibonacci_offset_sparse_amd/build.py).
 """
 
 from __future__ import annotations
@@ -30,7 +30,7 @@ _P = ctypes.POINTER
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m fibonacci_offset_sparse_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python fibonacci_offset_sparse_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     sig = {
         "fibattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -44,8 +44,8 @@ def _load() -> ctypes.CDLL:
         "fibattn_fwd": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_f64, _c_i32, _P(_c_i32), _c_i32,
                                         _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f64,
                                         _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
-        "fibattn_rope_keys": (ctypes.c_int, [_c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f64,
-                                              _c_ptr, _c_size, _c_ptr]),
+        "fibattn_fwd_prep": (ctypes.c_int, [_c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                             _c_f64, _c_ptr, _c_size, _c_ptr]),
         "fibattn_fwd_attend": (ctypes.c_int, [_c_ptr, _c_ptr, _c_f64, _c_i32, _P(_c_i32), _c_i32,
                                                _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f64,
                                                _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
@@ -202,20 +202,22 @@ def fibattn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float,
     return o, lse
 
 
-def fibattn_rope_keys(k: torch.Tensor, workspace: torch.Tensor, rope_theta: float = 1e4, stream=None):
-    """First forward stage: rotated keys into `workspace` (for timing the stages apart)."""
+def fibattn_fwd_prep(k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor, rope_theta: float = 1e4,
+                     stream=None):
+    """First forward stage: rotated keys (and fp16 values for bf16) into `workspace`."""
     B, Hkv, L, D = k.shape
     dt = _dtype_code(k)
     _dev(k, "k", (B, Hkv, L, D), k.dtype)
+    _dev(v, "v", (B, Hkv, L, D), k.dtype)
     with torch.cuda.device(k.device):
-        _check(lib.fibattn_rope_keys(k.data_ptr(), B, L, Hkv, D, dt, float(rope_theta),
-                                     workspace.data_ptr(), workspace.numel(), _stream(k.device, stream)))
+        _check(lib.fibattn_fwd_prep(k.data_ptr(), v.data_ptr(), B, L, Hkv, D, dt, float(rope_theta),
+                                    workspace.data_ptr(), workspace.numel(), _stream(k.device, stream)))
 
 
 def fibattn_fwd_attend(q: torch.Tensor, v: torch.Tensor, alpha: float, W: int, offsets: Sequence[int],
                        workspace: torch.Tensor, o: torch.Tensor, lse: Optional[torch.Tensor] = None,
                        rope_theta: float = 1e4, stream=None):
-    """Second forward stage; reads the rotated keys fibattn_rope_keys left in `workspace`."""
+    """Second forward stage; reads what fibattn_fwd_prep left in `workspace`."""
     B, Hq, L, D = q.shape
     Hkv = v.shape[1]
     dt = _dtype_code(q)
@@ -233,12 +235,17 @@ def fibattn_fwd_attend(q: torch.Tensor, v: torch.Tensor, alpha: float, W: int, o
 def fibattn_bwd(q, k, v, o, lse, dout, alpha: float, W: int, offsets: Sequence[int],
                 rope_theta: float = 1e4, dalpha_dtheta: float = 0.0, want_dalpha: bool = False,
                 workspace: Optional[torch.Tensor] = None, stream=None):
-    """(dq, dk, dv, dalpha, dtheta); dalpha and dtheta are float32[1] GPU tensors or None."""
+    """(dq, dk, dv, dalpha, dtheta); dalpha and dtheta are float32[1] GPU tensors or None.
+
+    o and lse may be None (the library does not read them)."""
     B, Hq, L, D, Hkv = _shapes(q, k)
     dt = _dtype_code(q)
+    # o and lse are part of the usual signature; the library recomputes what it needs from them
     ptrs = [_dev(q, "q", (B, Hq, L, D), q.dtype), _dev(k, "k", (B, Hkv, L, D), q.dtype),
-            _dev(v, "v", (B, Hkv, L, D), q.dtype), _dev(o, "o", (B, Hq, L, D), q.dtype),
-            _dev(lse, "lse", (B, Hq, L), torch.float32), _dev(dout, "dout", (B, Hq, L, D), q.dtype)]
+            _dev(v, "v", (B, Hkv, L, D), q.dtype),
+            _dev(o, "o", (B, Hq, L, D), q.dtype) if o is not None else None,
+            _dev(lse, "lse", (B, Hq, L), torch.float32) if lse is not None else None,
+            _dev(dout, "dout", (B, Hq, L, D), q.dtype)]
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     da = torch.empty(1, dtype=torch.float32, device=q.device) if want_dalpha else None
     dth = torch.empty(1, dtype=torch.float32, device=q.device) if want_dalpha else None
@@ -257,6 +264,6 @@ def fibattn_bwd(q, k, v, o, lse, dout, alpha: float, W: int, offsets: Sequence[i
 __all__ = [
     "fibattn_status_string", "fibattn_last_error", "fibattn_base_offsets", "fibattn_alpha_schedule",
     "fibattn_alpha_from_theta", "fibattn_plan", "fibattn_fwd_workspace_bytes", "fibattn_fwd",
-    "fibattn_rope_keys", "fibattn_fwd_attend", "fibattn_bwd_workspace_bytes", "fibattn_bwd",
+    "fibattn_fwd_prep", "fibattn_fwd_attend", "fibattn_bwd_workspace_bytes", "fibattn_bwd",
     "FibAttnError", "lib", "LIB_PATH",
 ]

@@ -1,6 +1,8 @@
 """Builds libfibattn.so in-tree for gfx950 with hipcc (cross-compiles without a GPU).
 
-    python -m fibonacci_offset_sparse_amd.build      (or __graft_entry__.build())
+    python fibonacci_offset_sparse_amd/build.py      (or __graft_entry__.build())
+
+Run it as a script (not with -m): importing the package loads the library being rebuilt.
 
 Objects go to _build/ at the repository root; the library lands next to this file.
 """
@@ -26,7 +28,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Packed fp32 VALU instructions stay off: kernels use scalar fp32 FMA only.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
-SOURCES = ["fibattn_api.cpp", "fibattn_fwd.hip", "fibattn_bwd.hip"]
+SOURCES = ["fibattn_api.cpp", "fibattn_fwd.hip", "fibattn_fwd_quad.hip", "fibattn_bwd.hip"]
 
 
 def hipcc() -> str:

@@ -43,7 +43,7 @@ constexpr int32_t kMaxL = 1 << 20;
 struct Plan {
     int n_keep = 0;          // kept offsets (INT and INTERP)
     bool any_integral = false;
-    OffsetSlot keep[kMaxOff];
+    OffsetSlot keep[kMaxOff] = {};
 };
 
 fibattn_status_t check_offsets(double alpha, int32_t W, const int32_t* offsets, int32_t K) {
@@ -128,8 +128,13 @@ size_t elem_bytes(int32_t dtype) { return dtype == FIBATTN_F32 ? 4 : 2; }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Staged keys (and values) of the forward: float32 rotated keys for float32 storage, or fp16
+// rotated keys followed by fp16 values for bf16 storage; the same bytes either way.
 size_t krot_bytes(int32_t B, int32_t L, int32_t Hkv) {
     return align256(static_cast<size_t>(B) * Hkv * L * kD * sizeof(float));
+}
+size_t half_rows_bytes(int32_t B, int32_t L, int32_t Hkv) {
+    return static_cast<size_t>(B) * Hkv * L * kD * sizeof(uint16_t);
 }
 
 #define FIBATTN_TRY(expr)                        \
@@ -227,22 +232,36 @@ size_t fibattn_fwd_workspace_bytes(int32_t B, int32_t L, int32_t Hkv, int32_t D,
     return krot_bytes(B, L, Hkv);
 }
 
-fibattn_status_t fibattn_rope_keys(const void* k, int32_t B, int32_t L, int32_t Hkv, int32_t D, int32_t dtype,
-                                   double rope_theta, void* workspace, size_t workspace_bytes, void* stream) {
+fibattn_status_t fibattn_fwd_prep(const void* k, const void* v, int32_t B, int32_t L, int32_t Hkv, int32_t D,
+                                  int32_t dtype, double rope_theta, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
     g_error[0] = '\0';
     FIBATTN_TRY(check_dims(B, L, Hkv, Hkv, D, 0, dtype, rope_theta));
-    if (k == nullptr) return fail(FIBATTN_ERR_INVALID, "k is NULL");
+    if (k == nullptr || v == nullptr) return fail(FIBATTN_ERR_INVALID, "k or v is NULL");
     const size_t need = krot_bytes(B, L, Hkv);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(FIBATTN_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
-    RopeKeysArgs a;
-    a.k = k;
-    a.krot = static_cast<float*>(workspace);
-    a.n_bh = B * Hkv;
-    a.L = L;
-    a.fr = make_freq(rope_theta);
-    const hipError_t e = launch_rope_keys(dtype, a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "rope_keys launch");
+    hipError_t e;
+    if (dtype == FIBATTN_F32) {
+        RopeKeysArgs a;
+        a.k = k;
+        a.krot = static_cast<float*>(workspace);
+        a.n_bh = B * Hkv;
+        a.L = L;
+        a.fr = make_freq(rope_theta);
+        e = launch_rope_keys(dtype, a, static_cast<hipStream_t>(stream));
+    } else {
+        PrepArgs a;
+        a.k = k;
+        a.v = v;
+        a.k16 = static_cast<_Float16*>(workspace);
+        a.v16 = reinterpret_cast<_Float16*>(static_cast<char*>(workspace) + half_rows_bytes(B, L, Hkv));
+        a.n_bh = B * Hkv;
+        a.L = L;
+        a.fr = make_freq(rope_theta);
+        e = launch_prep_kv16(a, static_cast<hipStream_t>(stream));
+    }
+    if (e != hipSuccess) return hip_fail(e, "forward prep launch");
     return FIBATTN_OK;
 }
 
@@ -260,8 +279,8 @@ fibattn_status_t fibattn_fwd_attend(const void* q, const void* v, double alpha, 
     const Plan plan = make_plan(alpha, W, offsets, K);
     FwdArgs a;
     a.q = q;
-    a.v = v;
-    a.krot = static_cast<const float*>(workspace);
+    a.kstage = workspace;
+    a.vstage = dtype == FIBATTN_F32 ? v : static_cast<const char*>(workspace) + half_rows_bytes(B, L, Hkv);
     a.o = o;
     a.lse = lse;
     a.B = B;
@@ -289,7 +308,7 @@ fibattn_status_t fibattn_fwd(const void* q, const void* k, const void* v, double
     FIBATTN_TRY(check_offsets(alpha, W, offsets, K));
     if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
         return fail(FIBATTN_ERR_INVALID, "q, k, v or o is NULL");
-    FIBATTN_TRY(fibattn_rope_keys(k, B, L, Hkv, D, dtype, rope_theta, workspace, workspace_bytes, stream));
+    FIBATTN_TRY(fibattn_fwd_prep(k, v, B, L, Hkv, D, dtype, rope_theta, workspace, workspace_bytes, stream));
     return fibattn_fwd_attend(q, v, alpha, W, offsets, K, B, L, Hq, Hkv, D, dtype, rope_theta, o, lse, workspace,
                               workspace_bytes, stream);
 }
@@ -315,8 +334,8 @@ fibattn_status_t fibattn_bwd(const void* q, const void* k, const void* v, const 
     g_error[0] = '\0';
     FIBATTN_TRY(check_dims(B, L, Hq, Hkv, D, W, dtype, rope_theta));
     FIBATTN_TRY(check_offsets(alpha, W, offsets, K));
-    if (q == nullptr || k == nullptr || v == nullptr || lse == nullptr || dout == nullptr || dq == nullptr ||
-        dk == nullptr || dv == nullptr)
+    if (q == nullptr || k == nullptr || v == nullptr || dout == nullptr || dq == nullptr || dk == nullptr ||
+        dv == nullptr)
         return fail(FIBATTN_ERR_INVALID, "a required pointer is NULL");
     if (!std::isfinite(dalpha_dtheta)) return fail(FIBATTN_ERR_INVALID, "dalpha_dtheta is not finite");
     const size_t need = fibattn_bwd_workspace_bytes(B, L, Hq, Hkv, D, W, K, dtype);

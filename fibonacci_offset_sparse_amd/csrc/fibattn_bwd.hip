@@ -6,8 +6,10 @@
 //
 // Three kernels, no atomics (results are bitwise reproducible):
 //  * bwd_query: workgroup = (batch, kv head, head chunk, 64 queries), like the forward.
-//      pass K1: s -> p = exp(s - lse) for every slot;
-//      pass V:  dP_s = do . val_s, and for interpolated slots g_s = do . (far - near);
+//      pass K1: every score s, and lse = log sum exp s (recomputed here in float32, so the
+//               gradients do not inherit the rounding of the forward's lse or o);
+//      pass V:  p = exp(s - lse), dP_s = do . val_s, and for interpolated slots
+//               g_s = do . (far - near);
 //               delta = sum_s p_s dP_s (equal to do . o, but from the float32 probabilities
 //               rather than from o rounded to its storage type), dS = p (dP - delta);
 //      pass K2: dq_rot += dS key_s / sqrt(D), dt_s = dS (q_rot . (far - near)) / sqrt(D) + p g_s;
@@ -146,7 +148,6 @@ __global__ __launch_bounds__(kTile * HPB) void bwd_query_kernel(BwdArgs A) {
 
     const int64_t bh = static_cast<int64_t>(b) * A.Hq + h;
     const int64_t qrow = (bh * L + i) * kD;
-    const float lse2 = active ? A.lse[bh * L + i] * kLog2e : 0.f;
     const float qs2 = A.scale * kLog2e;
     const int64_t kv_base = (static_cast<int64_t>(b) * A.Hkv + g) * L * kD;
     const float* krot = A.krot + kv_base;
@@ -165,47 +166,60 @@ __global__ __launch_bounds__(kTile * HPB) void bwd_query_kernel(BwdArgs A) {
     rope_apply(x, cs_tab[p]);
     if (active) store_row<float>(A.qrot + qrow, x);
 
-    // ---- pass K1: p = exp(s - lse) for every slot ----
+    // ---- pass K1: base-2 scores into the p column, running max and sum for lse ----
+    constexpr float kNegInf = -__builtin_huge_valf();
+    float mx = kNegInf, sm = 0.f;
+    auto keep = [&](int slot, float s2) {
+        if (!active) return;
+        pcol[static_cast<int64_t>(slot) * L] = s2;
+        if (s2 > mx) {
+            sm = sm * exp2f(mx - s2) + 1.f;
+            mx = s2;
+        } else if (s2 != kNegInf) {
+            sm += exp2f(s2 - mx);
+        }
+    };
     stage_rows<float, NT>(buf, krot, i0 - W, kTile + W, L);
     __syncthreads();
     for (int d = 0; d <= W; ++d) {
-        float pr = 0.f;
-        if (active && i >= d) pr = exp2f(dot_row(x, buf + (p + W - d) * kPitch) * qs2 - lse2);
-        if (active) pcol[static_cast<int64_t>(d) * L] = pr;
+        float s2 = kNegInf;
+        if (active && i >= d) s2 = dot_row(x, buf + (p + W - d) * kPitch) * qs2;
+        keep(d, s2);
     }
     __syncthreads();
     for (int n = 0; n < A.n_off; ++n) {
         const int a = A.off[n].a;
         const int reach = a + A.off[n].interp;
-        float pr = 0.f;
+        float s2 = kNegInf;
         if (i0 + kTile - 1 >= reach) {
             stage_rows<float, NT>(buf, krot, i0 - a - 1, kTile + 1, L);
             __syncthreads();
             const float* near = buf + (p + 1) * kPitch;
             if (active && i >= reach) {
-                float s;
                 if (A.off[n].interp) {
                     float dn, dd;
                     dot_pair(x, near, near - kPitch, dn, dd);
-                    s = fmaf(A.off[n].t, dd, dn);
+                    s2 = fmaf(A.off[n].t, dd, dn) * qs2;
                 } else {
-                    s = dot_row(x, near);
+                    s2 = dot_row(x, near) * qs2;
                 }
-                pr = exp2f(s * qs2 - lse2);
             }
             __syncthreads();
         }
-        if (active) pcol[static_cast<int64_t>(W + 1 + n) * L] = pr;
+        keep(W + 1 + n, s2);
     }
+    const float lse2 = active ? mx + log2f(sm) : 0.f;
 
-    // ---- pass V: dP_s (kept in the dS column), delta, and the p g part of dt ----
+    // ---- pass V: p = exp(s - lse) (into the p column), dP_s (kept in the dS column), delta,
+    // and the p g part of dt ----
     if (active) load_row<T>(static_cast<const T*>(A.dout) + qrow, x);
     float delta = 0.f;
     stage_rows<T, NT>(buf, vsrc, i0 - W, kTile + W, L);
     __syncthreads();
     for (int d = 0; d <= W; ++d) {
         if (!active) continue;
-        const float pr = pcol[static_cast<int64_t>(d) * L];
+        const float pr = exp2f(pcol[static_cast<int64_t>(d) * L] - lse2);
+        pcol[static_cast<int64_t>(d) * L] = pr;
         float dp = 0.f;
         if (pr > 0.f) {
             dp = dot_row(x, buf + (p + W - d) * kPitch);
@@ -218,14 +232,18 @@ __global__ __launch_bounds__(kTile * HPB) void bwd_query_kernel(BwdArgs A) {
         const int a = A.off[n].a;
         const int reach = a + A.off[n].interp;
         if (i0 + kTile - 1 < reach) {
-            if (active) dcol[static_cast<int64_t>(W + 1 + n) * L] = 0.f;
+            if (active) {
+                pcol[static_cast<int64_t>(W + 1 + n) * L] = 0.f;
+                dcol[static_cast<int64_t>(W + 1 + n) * L] = 0.f;
+            }
             continue;
         }
         stage_rows<T, NT>(buf, vsrc, i0 - a - 1, kTile + 1, L);
         __syncthreads();
         const float* near = buf + (p + 1) * kPitch;
         float dp = 0.f, pg = 0.f;
-        const float pr = active ? pcol[static_cast<int64_t>(W + 1 + n) * L] : 0.f;
+        const float pr = active ? exp2f(pcol[static_cast<int64_t>(W + 1 + n) * L] - lse2) : 0.f;
+        if (active) pcol[static_cast<int64_t>(W + 1 + n) * L] = pr;
         if (pr > 0.f) {
             if (A.off[n].interp) {
                 float dn, dd;

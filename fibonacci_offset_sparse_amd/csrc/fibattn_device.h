@@ -10,6 +10,8 @@
 namespace fibattn {
 
 using bf16_t = uint16_t;  // bfloat16 storage
+using f16_t = _Float16;   // half storage of the staged keys and values
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -36,12 +38,24 @@ template <> __device__ __forceinline__ float4 load4<bf16_t>(const bf16_t* p) {
     return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
 }
 
+template <> __device__ __forceinline__ float4 load4<f16_t>(const f16_t* p) {
+    uint2 w = *reinterpret_cast<const uint2*>(p);
+    const h2_t a = __builtin_bit_cast(h2_t, w.x), b = __builtin_bit_cast(h2_t, w.y);
+    return make_float4(static_cast<float>(a.x), static_cast<float>(a.y), static_cast<float>(b.x),
+                       static_cast<float>(b.y));
+}
+
 template <typename T> __device__ __forceinline__ void store4(T* p, float4 x);
 template <> __device__ __forceinline__ void store4<float>(float* p, float4 x) {
     *reinterpret_cast<float4*>(p) = x;
 }
 template <> __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float4 x) {
     *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
+}
+template <> __device__ __forceinline__ void store4<f16_t>(f16_t* p, float4 x) {
+    const h2_t a = {static_cast<_Float16>(x.x), static_cast<_Float16>(x.y)};
+    const h2_t b = {static_cast<_Float16>(x.z), static_cast<_Float16>(x.w)};
+    *reinterpret_cast<uint2*>(p) = make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
 }
 
 // A 64-element row into registers.

@@ -5,8 +5,10 @@
 // shifted gather and RoPE before the gather.
 //
 // Two kernels:
-//  * rope_keys: every key row rotated once at its own position, float32, into the workspace.
-//  * fwd_attend: one workgroup per (batch, key-value head, group of query heads, 64 query
+//  * rope_keys: every key row rotated once at its own position, float32, into the workspace
+//    (float32 storage; bf16 storage uses prep_kv16 in fibattn_fwd_quad.hip).
+//  * fwd_attend: the general kernel, used for float32 storage and for shapes outside the fast
+//    bf16 kernel (fwd_quad in fibattn_fwd_quad.hip). One workgroup per (batch, key-value head, group of query heads, 64 query
 //    positions). The offsets are shared by all queries, so the rows one slot needs for the
 //    whole tile form one contiguous block: the window block [i0 - W, i0 + 64) and, per offset,
 //    [i0 - a - 1, i0 + 64 - a). Each block is staged in LDS by coalesced loads and read by the
@@ -23,39 +25,31 @@ constexpr int kPitch = kD + 4;                    // LDS row pitch in floats (16
 constexpr int kMaxRows = kTile + kMaxWin;         // window block rows (64 + W <= 95)
 
 // ------------------------------------------------------------------------------------------------
-// rope_keys: thread = (position j, 4 RoPE pairs), looping over a few (batch, head) rows so that
-// each cos/sin pair is computed once per 8 rows.
+// rope_keys: thread = (row, 4 RoPE pairs), 8 threads per row, all rows in parallel.
 // ------------------------------------------------------------------------------------------------
-constexpr int kRopeRowsPerThread = 8;
-
 template <typename T>
 __global__ __launch_bounds__(256) void rope_keys_kernel(RopeKeysArgs A) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int quad = static_cast<int>(gid & 7);                  // pairs 4*quad .. 4*quad+3
-    const int64_t pos_bh = gid >> 3;
-    const int j = static_cast<int>(pos_bh % A.L);
-    const int bh0 = static_cast<int>(pos_bh / A.L) * kRopeRowsPerThread;
-    if (bh0 >= A.n_bh) return;
-    float2 cs[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-        rope_cos_sin(j, A.fr.hi[4 * quad + u], A.fr.lo[4 * quad + u], cs[u].x, cs[u].y);
+    const int64_t row_id = gid >> 3;
+    if (row_id >= static_cast<int64_t>(A.n_bh) * A.L) return;
+    const int j = static_cast<int>(row_id % A.L);
+    const int64_t row = row_id * kD;
     const T* src = static_cast<const T*>(A.k);
-    for (int bh = bh0; bh < bh0 + kRopeRowsPerThread && bh < A.n_bh; ++bh) {
-        const int64_t row = (static_cast<int64_t>(bh) * A.L + j) * kD;
-        const float4 x1 = load4<T>(src + row + 4 * quad);
-        const float4 x2 = load4<T>(src + row + kPairs + 4 * quad);
-        const float a[4] = {x1.x, x1.y, x1.z, x1.w};
-        const float b[4] = {x2.x, x2.y, x2.z, x2.w};
-        float r1[4], r2[4];
+    const float4 x1 = load4<T>(src + row + 4 * quad);
+    const float4 x2 = load4<T>(src + row + kPairs + 4 * quad);
+    const float a[4] = {x1.x, x1.y, x1.z, x1.w};
+    const float b[4] = {x2.x, x2.y, x2.z, x2.w};
+    float r1[4], r2[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            r1[u] = a[u] * cs[u].x - b[u] * cs[u].y;
-            r2[u] = b[u] * cs[u].x + a[u] * cs[u].y;
-        }
-        store4<float>(A.krot + row + 4 * quad, make_float4(r1[0], r1[1], r1[2], r1[3]));
-        store4<float>(A.krot + row + kPairs + 4 * quad, make_float4(r2[0], r2[1], r2[2], r2[3]));
+    for (int u = 0; u < 4; ++u) {
+        float c, s;
+        rope_cos_sin(j, A.fr.hi[4 * quad + u], A.fr.lo[4 * quad + u], c, s);
+        r1[u] = a[u] * c - b[u] * s;
+        r2[u] = b[u] * c + a[u] * s;
     }
+    store4<float>(A.krot + row + 4 * quad, make_float4(r1[0], r1[1], r1[2], r1[3]));
+    store4<float>(A.krot + row + kPairs + 4 * quad, make_float4(r2[0], r2[1], r2[2], r2[3]));
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -128,10 +122,13 @@ __device__ __forceinline__ void axpy_blend(float (&o)[kD], float p, const float*
     }
 }
 
+// The general kernel: any GQA group, W <= 31, up to 32 offsets, float32 arithmetic on staged
+// rows. T is the storage type of q and o; KT and VT are the element types of the staged keys and
+// values (float32 input for float32 storage, fp16 rows from prep_kv16 for bf16 storage).
 // HPB query heads per workgroup (the heads of one key-value head, or a chunk of them).
 // Thread t: position p = t / HPB of the tile, head h = t % HPB of the chunk, so the HPB heads
 // of one position sit in adjacent lanes and read the same LDS row.
-template <typename T, int HPB>
+template <typename T, typename KT, typename VT, int HPB>
 __global__ __launch_bounds__(kTile * HPB) void fwd_attend_kernel(FwdArgs A) {
     constexpr int NT = kTile * HPB;
     constexpr float kNegInf = -__builtin_huge_valf();
@@ -170,12 +167,12 @@ __global__ __launch_bounds__(kTile * HPB) void fwd_attend_kernel(FwdArgs A) {
     for (int e = 0; e < kD; ++e) q[e] *= A.qscale;
 
     const int64_t kv_base = (static_cast<int64_t>(b) * A.Hkv + g) * L * kD;
-    const float* krot = A.krot + kv_base;
-    const T* vsrc = static_cast<const T*>(A.v) + kv_base;
+    const KT* krot = static_cast<const KT*>(A.kstage) + kv_base;
+    const VT* vsrc = static_cast<const VT*>(A.vstage) + kv_base;
 
     // ---- pass 1: scores (base 2), window then offsets ----
     float sw[kMaxWin], so[kMaxOff];
-    stage_rows<float, NT>(buf, krot, i0 - W, kTile + W, L);
+    stage_rows<KT, NT>(buf, krot, i0 - W, kTile + W, L);
     __syncthreads();
 #pragma unroll
     for (int d = 0; d < kMaxWin; ++d) {
@@ -190,7 +187,7 @@ __global__ __launch_bounds__(kTile * HPB) void fwd_attend_kernel(FwdArgs A) {
             const int a = A.off[n].a;
             const int reach = a + A.off[n].interp;
             if (i0 + kTile - 1 >= reach) {                     // some query of the tile reads it
-                stage_rows<float, NT>(buf, krot, i0 - a - 1, kTile + 1, L);
+                stage_rows<KT, NT>(buf, krot, i0 - a - 1, kTile + 1, L);
                 __syncthreads();
                 const float* near = buf + (p + 1) * kPitch;
                 if (active && i >= reach)
@@ -224,7 +221,7 @@ __global__ __launch_bounds__(kTile * HPB) void fwd_attend_kernel(FwdArgs A) {
     float o[kD];
 #pragma unroll
     for (int e = 0; e < kD; ++e) o[e] = 0.f;
-    stage_rows<T, NT>(buf, vsrc, i0 - W, kTile + W, L);
+    stage_rows<VT, NT>(buf, vsrc, i0 - W, kTile + W, L);
     __syncthreads();
 #pragma unroll
     for (int d = 0; d < kMaxWin; ++d)
@@ -236,7 +233,7 @@ __global__ __launch_bounds__(kTile * HPB) void fwd_attend_kernel(FwdArgs A) {
             const int a = A.off[n].a;
             const int reach = a + A.off[n].interp;
             if (i0 + kTile - 1 >= reach) {
-                stage_rows<T, NT>(buf, vsrc, i0 - a - 1, kTile + 1, L);
+                stage_rows<VT, NT>(buf, vsrc, i0 - a - 1, kTile + 1, L);
                 __syncthreads();
                 const float* near = buf + (p + 1) * kPitch;
                 if (so[n] > 0.f) {
@@ -260,24 +257,23 @@ __global__ __launch_bounds__(kTile * HPB) void fwd_attend_kernel(FwdArgs A) {
     }
 }
 
-template <typename T>
+template <typename T, typename KT, typename VT>
 hipError_t launch_fwd_typed(const FwdArgs& A, hipStream_t s) {
     const int hpb = (A.G % 4 == 0) ? 4 : (A.G % 2 == 0) ? 2 : 1;
     dim3 grid((A.L + kTile - 1) / kTile, A.Hkv * (A.G / hpb), A.B);
     if (hpb == 4)
-        hipLaunchKernelGGL((fwd_attend_kernel<T, 4>), grid, dim3(kTile * 4), 0, s, A);
+        hipLaunchKernelGGL((fwd_attend_kernel<T, KT, VT, 4>), grid, dim3(kTile * 4), 0, s, A);
     else if (hpb == 2)
-        hipLaunchKernelGGL((fwd_attend_kernel<T, 2>), grid, dim3(kTile * 2), 0, s, A);
+        hipLaunchKernelGGL((fwd_attend_kernel<T, KT, VT, 2>), grid, dim3(kTile * 2), 0, s, A);
     else
-        hipLaunchKernelGGL((fwd_attend_kernel<T, 1>), grid, dim3(kTile), 0, s, A);
+        hipLaunchKernelGGL((fwd_attend_kernel<T, KT, VT, 1>), grid, dim3(kTile), 0, s, A);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_rope_keys(int dtype, const RopeKeysArgs& A, hipStream_t s) {
-    const int64_t groups = (static_cast<int64_t>(A.n_bh) + kRopeRowsPerThread - 1) / kRopeRowsPerThread;
-    const int64_t threads = groups * A.L * 8;
+    const int64_t threads = static_cast<int64_t>(A.n_bh) * A.L * 8;
     const unsigned blocks = static_cast<unsigned>((threads + 255) / 256);
     if (dtype == 0)
         hipLaunchKernelGGL((rope_keys_kernel<float>), dim3(blocks), dim3(256), 0, s, A);
@@ -287,7 +283,9 @@ hipError_t launch_rope_keys(int dtype, const RopeKeysArgs& A, hipStream_t s) {
 }
 
 hipError_t launch_fwd_attend(int dtype, const FwdArgs& A, hipStream_t s) {
-    return dtype == 0 ? launch_fwd_typed<float>(A, s) : launch_fwd_typed<bf16_t>(A, s);
+    if (dtype == 0) return launch_fwd_typed<float, float, float>(A, s);
+    if (fwd_quad_supported(A)) return launch_fwd_quad(A, s);
+    return launch_fwd_typed<bf16_t, f16_t, f16_t>(A, s);
 }
 
 }  // namespace fibattn

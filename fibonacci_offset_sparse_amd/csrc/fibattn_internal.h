@@ -35,10 +35,21 @@ struct RopeKeysArgs {
     RopeFreq fr;
 };
 
+// bf16 storage: rotated keys and values as fp16 rows for the forward kernels.
+struct PrepArgs {
+    const void* k;       // [B*Hkv, L, 64] bf16
+    const void* v;       // [B*Hkv, L, 64] bf16
+    _Float16* k16;       // [B*Hkv, L, 64] rotated keys
+    _Float16* v16;       // [B*Hkv, L, 64] values
+    int32_t n_bh;
+    int32_t L;
+    RopeFreq fr;
+};
+
 struct FwdArgs {
-    const void* q;       // [B, Hq, L, 64]
-    const void* v;       // [B, Hkv, L, 64]
-    const float* krot;   // [B, Hkv, L, 64] float32, rotated
+    const void* q;       // [B, Hq, L, 64] storage type
+    const void* kstage;  // [B, Hkv, L, 64] rotated keys: float32 (f32 storage) or fp16 (bf16 storage)
+    const void* vstage;  // [B, Hkv, L, 64] values: the input (f32 storage) or fp16 (bf16 storage)
     void* o;             // [B, Hq, L, 64]
     float* lse;          // [B, Hq, L] or nullptr
     int32_t B, L, Hq, Hkv, G, W, n_off;
@@ -72,7 +83,10 @@ struct BwdArgs {
 };
 
 hipError_t launch_rope_keys(int dtype, const RopeKeysArgs& a, hipStream_t s);
+hipError_t launch_prep_kv16(const PrepArgs& a, hipStream_t s);
 hipError_t launch_fwd_attend(int dtype, const FwdArgs& a, hipStream_t s);
+bool fwd_quad_supported(const FwdArgs& a);
+hipError_t launch_fwd_quad(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd(int dtype, const BwdArgs& a, bool want_dalpha, hipStream_t s);
 int bwd_query_workgroups(int B, int L, int Hkv, int G);
 

@@ -115,7 +115,7 @@ fibattn_status_t fibattn_plan(double alpha, int32_t W, const int32_t* offsets, i
                               uint8_t* kind_out, int32_t* floor_out, float* t_out,
                               int32_t* reach_out);
 
-/* Bytes of device workspace fibattn_fwd needs (rotated keys). */
+/* Bytes of device workspace fibattn_fwd needs (staged rotated keys and values). */
 size_t fibattn_fwd_workspace_bytes(int32_t B, int32_t L, int32_t Hkv, int32_t D, int32_t dtype);
 
 /*
@@ -124,7 +124,11 @@ size_t fibattn_fwd_workspace_bytes(int32_t B, int32_t L, int32_t Hkv, int32_t D,
  * o: device [B, Hq, L, D] of `dtype` (written). lse: device float32 [B, Hq, L] (written) or
  * NULL when no backward pass will follow.
  * workspace: device, >= fibattn_fwd_workspace_bytes(...) bytes, scratch for this call only.
- * Queues two kernels on `stream`: fibattn_rope_keys, then fibattn_fwd_attend.
+ * Queues two kernels on `stream`: fibattn_fwd_prep, then fibattn_fwd_attend.
+ * Arithmetic: float32 for FIBATTN_F32. For FIBATTN_BF16, scores and P.V take products of fp16
+ * operands (rotated q and k, values, softmax weights; each rounded to fp16, relative error
+ * <= 2^-11) accumulated in float32, and interpolated keys are blended in fp16; inputs must stay
+ * below 65504 in magnitude (after rotation) for this to hold.
  * Errors: INVALID (NULL pointers, B/L/Hq/Hkv < 1, Hq % Hkv != 0, W < 0, K outside [0, 32],
  * bad alpha, bad offsets, unknown dtype, rope_theta not finite and > 0), UNSUPPORTED (D != 64,
  * W > 31, L > 2^20), WORKSPACE, HIP.
@@ -136,17 +140,21 @@ fibattn_status_t fibattn_fwd(const void* q, const void* k, const void* v, double
                              void* stream);
 
 /*
- * First stage of fibattn_fwd, exposed so that each kernel can be timed on its own: rotate
- * every key row at its position into the workspace. Same arguments and errors as fibattn_fwd.
+ * First stage of fibattn_fwd, exposed so that each kernel can be timed on its own: rotate every
+ * key row at its position once (RoPE before the gather, §2 "Attended set") into the workspace.
+ * For FIBATTN_F32 the rotated keys are stored as float32; for FIBATTN_BF16 the rotated keys and
+ * the values are stored as fp16 rows (bf16 values of magnitude below 65504 convert exactly).
+ * k, v: device [B, Hkv, L, D] of `dtype`. Errors as fibattn_fwd.
  */
-fibattn_status_t fibattn_rope_keys(const void* k, int32_t B, int32_t L, int32_t Hkv, int32_t D,
-                                   int32_t dtype, double rope_theta, void* workspace,
-                                   size_t workspace_bytes, void* stream);
+fibattn_status_t fibattn_fwd_prep(const void* k, const void* v, int32_t B, int32_t L, int32_t Hkv,
+                                  int32_t D, int32_t dtype, double rope_theta, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
- * Second stage of fibattn_fwd: the attention itself. Reads the rotated keys that
- * fibattn_rope_keys left in `workspace` (same k shape, dtype and rope_theta), so it must follow
- * it on the same stream with the workspace untouched in between.
+ * Second stage of fibattn_fwd: the attention itself. Reads what fibattn_fwd_prep left in
+ * `workspace` (same shapes, dtype and rope_theta), so it must follow it on the same stream with the
+ * workspace untouched in between. v is read directly for FIBATTN_F32 (and ignored for
+ * FIBATTN_BF16, whose values are in the workspace).
  */
 fibattn_status_t fibattn_fwd_attend(const void* q, const void* v, double alpha, int32_t W,
                                     const int32_t* offsets, int32_t K, int32_t B, int32_t L,
@@ -161,11 +169,12 @@ size_t fibattn_bwd_workspace_bytes(int32_t B, int32_t L, int32_t Hq, int32_t Hkv
 /*
  * Backward pass: gradients of sum(do * o) for the forward above (§2 "Attended set": the
  * interpolation keeps a gradient to alpha; §2 "Per-layer scalar": alpha = 0.5 + sigmoid(theta)).
- * Inputs: q, k, v, lse (the forward's float32 lse), dout = do, all device, same shapes and
- * storage type as the forward. o (the forward's output) is accepted for the usual attention
- * backward signature but is not read and may be NULL: the row term delta = do . o is formed as
- * sum_s p_s (do . val_s) from the recomputed float32 probabilities, which keeps the rounding of o
- * to its storage type out of the gradients.
+ * Inputs: q, k, v, dout = do, all device, same shapes and storage type as the forward.
+ * o and lse (the forward's outputs) are accepted for the usual attention backward signature but
+ * are not read and may be NULL: the backward recomputes every score and the log-sum-exp in
+ * float32, and forms the row term delta = do . o as sum_s p_s (do . val_s), which keeps the
+ * rounding of the forward's outputs (and the forward's fp16 products for bf16 storage) out of
+ * the gradients.
  * Outputs (device, overwritten): dq [B, Hq, L, D], dk, dv [B, Hkv, L, D] of `dtype`;
  * dalpha float32[1] or NULL; dtheta float32[1] or NULL, set to dalpha * dalpha_dtheta (pass the
  * factor from fibattn_alpha_from_theta for the learned schedule).

@@ -157,7 +157,6 @@ def bwd_call(alpha=0.73, offsets=O.FIB_BASE, want_dalpha=True, ws_bytes=1 << 40,
 
 def test_bwd_argument_checks():
     assert bwd_call(dq=None) == 1
-    assert bwd_call(lse=None) == 1
     assert bwd_call(D=48) == 2
     assert bwd_call(ws_bytes=100) == 3
     assert bwd_call(dadt=float("nan")) == 1

@@ -14,7 +14,7 @@ import torch
 
 import workloads
 from oracle import fibattn_oracle as O
-from parity import check, check_f32
+from parity import check
 
 pytestmark = pytest.mark.gpu
 
