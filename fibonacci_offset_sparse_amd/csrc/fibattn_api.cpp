@@ -136,6 +136,9 @@ size_t krot_bytes(int32_t B, int32_t L, int32_t Hkv) {
 size_t half_rows_bytes(int32_t B, int32_t L, int32_t Hkv) {
     return static_cast<size_t>(B) * Hkv * L * kD * sizeof(uint16_t);
 }
+// cos/sin table [L, 32, 2] float32 after the staged rows (bf16 storage)
+size_t cs_table_bytes(int32_t L) { return align256(static_cast<size_t>(L) * kPairs * 2 * sizeof(float)); }
+size_t fwd_ws_bytes(int32_t B, int32_t L, int32_t Hkv) { return krot_bytes(B, L, Hkv) + cs_table_bytes(L); }
 
 #define FIBATTN_TRY(expr)                        \
     do {                                         \
@@ -229,7 +232,7 @@ size_t fibattn_fwd_workspace_bytes(int32_t B, int32_t L, int32_t Hkv, int32_t D,
     (void)D;
     (void)dtype;
     if (B < 1 || L < 1 || Hkv < 1) return 0;
-    return krot_bytes(B, L, Hkv);
+    return fwd_ws_bytes(B, L, Hkv);
 }
 
 fibattn_status_t fibattn_fwd_prep(const void* k, const void* v, int32_t B, int32_t L, int32_t Hkv, int32_t D,
@@ -238,7 +241,7 @@ fibattn_status_t fibattn_fwd_prep(const void* k, const void* v, int32_t B, int32
     g_error[0] = '\0';
     FIBATTN_TRY(check_dims(B, L, Hkv, Hkv, D, 0, dtype, rope_theta));
     if (k == nullptr || v == nullptr) return fail(FIBATTN_ERR_INVALID, "k or v is NULL");
-    const size_t need = krot_bytes(B, L, Hkv);
+    const size_t need = fwd_ws_bytes(B, L, Hkv);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(FIBATTN_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
     hipError_t e;
@@ -256,6 +259,7 @@ fibattn_status_t fibattn_fwd_prep(const void* k, const void* v, int32_t B, int32
         a.v = v;
         a.k16 = static_cast<_Float16*>(workspace);
         a.v16 = reinterpret_cast<_Float16*>(static_cast<char*>(workspace) + half_rows_bytes(B, L, Hkv));
+        a.cs = reinterpret_cast<float*>(static_cast<char*>(workspace) + krot_bytes(B, L, Hkv));
         a.n_bh = B * Hkv;
         a.L = L;
         a.fr = make_freq(rope_theta);
@@ -273,7 +277,7 @@ fibattn_status_t fibattn_fwd_attend(const void* q, const void* v, double alpha, 
     FIBATTN_TRY(check_dims(B, L, Hq, Hkv, D, W, dtype, rope_theta));
     FIBATTN_TRY(check_offsets(alpha, W, offsets, K));
     if (q == nullptr || v == nullptr || o == nullptr) return fail(FIBATTN_ERR_INVALID, "q, v or o is NULL");
-    const size_t need = krot_bytes(B, L, Hkv);
+    const size_t need = fwd_ws_bytes(B, L, Hkv);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(FIBATTN_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
     const Plan plan = make_plan(alpha, W, offsets, K);
@@ -281,6 +285,8 @@ fibattn_status_t fibattn_fwd_attend(const void* q, const void* v, double alpha, 
     a.q = q;
     a.kstage = workspace;
     a.vstage = dtype == FIBATTN_F32 ? v : static_cast<const char*>(workspace) + half_rows_bytes(B, L, Hkv);
+    a.cstab = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + krot_bytes(B, L, Hkv));
+    a.xcd_map = 0;
     a.o = o;
     a.lse = lse;
     a.B = B;

@@ -41,6 +41,7 @@ struct PrepArgs {
     const void* v;       // [B*Hkv, L, 64] bf16
     _Float16* k16;       // [B*Hkv, L, 64] rotated keys
     _Float16* v16;       // [B*Hkv, L, 64] values
+    float* cs;           // [L, 32, 2] cos and sin of every position and RoPE pair
     int32_t n_bh;
     int32_t L;
     RopeFreq fr;
@@ -50,9 +51,11 @@ struct FwdArgs {
     const void* q;       // [B, Hq, L, 64] storage type
     const void* kstage;  // [B, Hkv, L, 64] rotated keys: float32 (f32 storage) or fp16 (bf16 storage)
     const void* vstage;  // [B, Hkv, L, 64] values: the input (f32 storage) or fp16 (bf16 storage)
+    const float* cstab;  // [L, 32, 2] cos/sin table (bf16 storage)
     void* o;             // [B, Hq, L, 64]
     float* lse;          // [B, Hq, L] or nullptr
     int32_t B, L, Hq, Hkv, G, W, n_off;
+    int32_t xcd_map;     // fast kernel: keep each (batch, kv head)'s tiles on one XCD
     float qscale;        // log2(e) / sqrt(D): scores kept in base 2
     RopeFreq fr;
     OffsetSlot off[kMaxOff];
