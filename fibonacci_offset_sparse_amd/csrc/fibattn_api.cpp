@@ -281,11 +281,12 @@ fibattn_status_t fibattn_fwd_attend(const void* q, const void* v, double alpha, 
     if (workspace == nullptr || workspace_bytes < need)
         return fail(FIBATTN_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
     const Plan plan = make_plan(alpha, W, offsets, K);
-    FwdArgs a;
+    FwdArgs a{};
     a.q = q;
     a.kstage = workspace;
     a.vstage = dtype == FIBATTN_F32 ? v : static_cast<const char*>(workspace) + half_rows_bytes(B, L, Hkv);
     a.cstab = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + krot_bytes(B, L, Hkv));
+    a.v = v;
     a.xcd_map = 0;
     a.o = o;
     a.lse = lse;

@@ -6,9 +6,9 @@
 //
 // Two kernels:
 //  * rope_keys: every key row rotated once at its own position, float32, into the workspace
-//    (float32 storage; bf16 storage uses prep_kv16 in fibattn_fwd_quad.hip).
+//    (float32 storage; bf16 storage uses prep_kv16 in fibattn_fwd_mfma.hip).
 //  * fwd_attend: the general kernel, used for float32 storage and for shapes outside the fast
-//    bf16 kernel (fwd_quad in fibattn_fwd_quad.hip). One workgroup per (batch, key-value head, group of query heads, 64 query
+//    bf16 kernel (fwd_mfma in fibattn_fwd_mfma.hip). One workgroup per (batch, key-value head, group of query heads, 64 query
 //    positions). The offsets are shared by all queries, so the rows one slot needs for the
 //    whole tile form one contiguous block: the window block [i0 - W, i0 + 64) and, per offset,
 //    [i0 - a - 1, i0 + 64 - a). Each block is staged in LDS by coalesced loads and read by the
@@ -284,8 +284,11 @@ hipError_t launch_rope_keys(int dtype, const RopeKeysArgs& A, hipStream_t s) {
 
 hipError_t launch_fwd_attend(int dtype, const FwdArgs& A, hipStream_t s) {
     if (dtype == 0) return launch_fwd_typed<float, float, float>(A, s);
-    if (fwd_quad_supported(A)) return launch_fwd_quad(A, s);
-    return launch_fwd_typed<bf16_t, f16_t, f16_t>(A, s);
+    if (fwd_mfma_supported(A)) return launch_fwd_mfma(A, s);
+    // the staged fp16 values are laid out for the matrix-core kernel: read the caller's values
+    FwdArgs B = A;
+    B.vstage = A.v;
+    return launch_fwd_typed<bf16_t, f16_t, bf16_t>(B, s);
 }
 
 }  // namespace fibattn

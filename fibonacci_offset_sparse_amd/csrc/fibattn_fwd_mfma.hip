@@ -1,0 +1,513 @@
+// Forward attention for bfloat16 storage on gfx950: the fast kernel, on the matrix cores.
+//
+// Section references are to "Depth-Staggered Fibonacci Spacing for Sparse Attention" (arXiv
+// 2606.28560), §2 "Attended set": window distances 0..W plus one slot per rung at distance
+// d = alpha f, read by linear interpolation between rows i - floor(d) and i - floor(d) - 1, with
+// RoPE applied before the gather. Offsets are shared by all queries, so for a tile of 64 queries
+// each slot reads one contiguous block of rows.
+//
+// Inputs come from prep_kv16: keys rotated at their positions and values, both as fp16 rows of
+// 128 bytes. A workgroup owns (batch b, key-value head g, 4 query heads, 64 positions); wave w
+// takes positions 16w..16w+15 of the tile.
+//
+// Every position is its own small product: its 4 query heads (they share the key-value head)
+// against the rows its slots read. v_mfma_f32_4x4x4_16b_f16 computes 16 independent 4x4x4
+// blocks, one per position of the wave; lane 4p' + x is row x of the A operand and column x of
+// the B operand and of the result, of block p'.
+//
+//  * Virtual slots: a window distance is one row; an interpolated rung is two rows, near (the
+//    nearer row, coefficient 1 - t) and far (coefficient t). Scores and outputs are linear in
+//    the blended row, so q.(blend) = (1 - t) q.near + t q.far, and the value blend spreads its
+//    weight p as p (1 - t), p t. An integral rung keeps t = 0. Groups of 4 virtual slots are
+//    4 window distances, or (near, far) of two consecutive rungs.
+//  * QK: A = the 4 rows of the group (lane x reads virtual slot x's row), B = q of head x,
+//    K = 64 dims in 16 products. The result lane (p', x) holds head x's 4 scores: all of a
+//    lane's scores stay in its registers, the softmax is exact and in-lane (base 2).
+//  * PV: A = head x's 4 weights (the same lane), B = the 4 rows' values at 4 dims (built with
+//    v_perm from 16-byte reads), 16 products cover 64 dims; the result lane (p', x) holds dims
+//    16x..16x+15 of all 4 heads.
+//  * LDS: the window block (64 + W + 4 rows) and a ring of three steps, each holding the blocks
+//    of two rungs (65 rows each). Staging is LDS DMA (buffer_load ... lds): no VGPRs; rows
+//    before 0 or past L fall outside the buffer resource and arrive as zeros, so every row a
+//    lane reads is finite. Blocks are issued two steps ahead, with one barrier per step after a
+//    counted vmcnt wait, and a sparse L2 warm-up (one 16-byte load per row into a sink) runs
+//    further ahead.
+//  * Banks: 16-byte chunk k of slot s sits at chunk k ^ ((s >> 1) & 7), so the same chunk of 16
+//    consecutive slots covers all 64 banks, and the second rung's block sits two slots up. Key
+//    reads (16 lanes per pass) are then free of bank conflicts for window and rung groups, as
+//    are the transposing value reads of window groups; those of rung groups are 2-way.
+//  * The grid is mapped so that all tiles of one (batch, key-value head) run on one XCD, whose L2
+//    then holds that head's keys and values for every tile that re-reads them.
+#include "fibattn_device.h"
+
+namespace fibattn {
+
+namespace {
+
+constexpr int kNT = 256;                 // 4 waves x 16 positions x 4 lanes
+constexpr int kRowBytes = kD * 2;        // one fp16 row
+constexpr int kWinSlots = 96;            // 64 + W + 4 <= 83 rows; 12 DMA groups, 3 per wave
+constexpr int kWinPad = 4;               // window slot of row i0 - W - 4 is 0: pads stay in range
+constexpr int kBlkSlots = 72;            // 65 (+2 for the second rung) rows, 9 DMA groups
+constexpr int kRing = 3;
+constexpr int kBcast0 = 0x00, kBcast1 = 0x55, kBcast2 = 0xAA, kBcast3 = 0xFF;   // quad_perm [r,r,r,r]
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, gfx9 family
+#ifndef FIBATTN_FWD_WGS_PER_CU
+#define FIBATTN_FWD_WGS_PER_CU 2
+#endif
+// Workgroups per CU: LDS is 12 + 6 x 9 KB per workgroup, and the register budget this gives
+// (256 per lane) holds q, the scores and the 64 output accumulators without spilling (a spill
+// reload is a vector-memory load and would wait behind every staging load in flight).
+constexpr int kWgsPerCu = FIBATTN_FWD_WGS_PER_CU;
+
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(h4_t, (u2_t){a0, a1}),
+                                              __builtin_bit_cast(h4_t, (u2_t){b0, b1}), c, 0, 0, 0);
+}
+
+template <int CTRL> __device__ __forceinline__ float quad_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+    const h2_t v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two floats as bfloat16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+    typedef float fl2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((fl2_t){lo, hi}, bf2_t));
+}
+
+__device__ __forceinline__ uint4 lds16(const char* lds, int addr) {
+    return *reinterpret_cast<const uint4*>(lds + addr);
+}
+
+// The chunk swizzle of slot s, as a byte offset to XOR into (logical chunk << 4).
+__device__ __forceinline__ int swz(int s) { return ((s >> 1) & 7) << 4; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// An LDS DMA destination passed through an opaque (uniform) value: the compiler then keeps no
+// record of which LDS array a DMA writes and adds no waits of its own before LDS reads;
+// publish<N> orders every read after the DMA it needs.
+__device__ __forceinline__ lds_ptr_t dma_dst(char* dst) {
+    uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)dst));
+    asm volatile("" : "+s"(a));   // an SGPR: the value is the same for the whole wave
+    return (lds_ptr_t)static_cast<uintptr_t>(a);
+}
+
+// Wait until at most N vector-memory instructions of this wave are in flight (its LDS DMAs up to
+// the block the next step reads have landed) and its LDS reads are done, then the workgroup
+// barrier. __syncthreads would also drain every staging load in flight.
+template <int N> __device__ __forceinline__ void publish() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// QK of one group: lane x supplies the row at slot byte offset base (swizzle F = swz(slot)), q
+// supplies head x; returns the 4 scores of head x. Two accumulators keep two chains.
+__device__ __forceinline__ f4_t qk_group(const uint32_t (&q)[8][4], const char* lds, int base, int F) {
+    f4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint4 k = lds16(lds, base | ((c << 4) ^ F));
+        if (c & 1) {
+            a1 = mfma4(k.x, k.y, q[c][0], q[c][1], a1);
+            a1 = mfma4(k.z, k.w, q[c][2], q[c][3], a1);
+        } else {
+            a0 = mfma4(k.x, k.y, q[c][0], q[c][1], a0);
+            a0 = mfma4(k.z, k.w, q[c][2], q[c][3], a0);
+        }
+    }
+    return a0 + a1;
+}
+
+// PV of one group. The lane reads its assigned (position, slot) row, at slot byte offset base
+// with swizzle F, for dim blocks m = 0..15 (elements 4m..4m+3: byte 8m of the logical row). The
+// transposing read hands every lane the 4 rows at its own dim 16x + m; (w01, w23) are the lane's
+// head's weights, o[m] accumulates dim 16x + m of the 4 heads.
+__device__ __forceinline__ void pv_group(f4_t (&o)[16], uint32_t w01, uint32_t w23, const char* lds, int base, int F) {
+    typedef short s4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4_t* lds_s4_t;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int addr = (base | (((m >> 1) << 4) ^ F)) + 8 * (m & 1);
+        const s4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t)(lds + addr));
+        const u2_t vv = __builtin_bit_cast(u2_t, v);
+        o[m] = mfma4(w01, w23, vv.x, vv.y, o[m]);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// prep_kv16: rotated keys and values as fp16 rows, plus the cos/sin table of every position (for
+// the queries). Thread = (row, u): key pairs 4u..4u+3 and value row elements 8u..8u+7.
+// Value rows are stored with their dims permuted, element 4m + c holding dim 16c + m, so that a
+// transposing LDS read of 4 consecutive elements gives a lane 4 rows of one of its own dims.
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int u = static_cast<int>(gid & 7);
+    const int64_t row_id = gid >> 3;
+    if (row_id >= static_cast<int64_t>(A.n_bh) * A.L) return;
+    const int j = static_cast<int>(row_id % A.L);
+    const int64_t row = row_id * kD;
+    const bf16_t* ks = static_cast<const bf16_t*>(A.k);
+    const bf16_t* vs = static_cast<const bf16_t*>(A.v);
+    const float4 x1 = load4<bf16_t>(ks + row + 4 * u);
+    const float4 x2 = load4<bf16_t>(ks + row + kPairs + 4 * u);
+    // elements 8u..8u+7 are dims 16c + 2u (c = 0..3), then 16c + 2u + 1
+    uint32_t vp[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vp[c] = *reinterpret_cast<const uint32_t*>(vs + row + 16 * c + 2 * u);
+    const float a[4] = {x1.x, x1.y, x1.z, x1.w};
+    const float b[4] = {x2.x, x2.y, x2.z, x2.w};
+    float r1[4], r2[4];
+    float2 cs[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        rope_cos_sin(j, A.fr.hi[4 * u + e], A.fr.lo[4 * u + e], cs[e].x, cs[e].y);
+        r1[e] = a[e] * cs[e].x - b[e] * cs[e].y;
+        r2[e] = b[e] * cs[e].x + a[e] * cs[e].y;
+    }
+    store4<f16_t>(A.k16 + row + 4 * u, make_float4(r1[0], r1[1], r1[2], r1[3]));
+    store4<f16_t>(A.k16 + row + kPairs + 4 * u, make_float4(r2[0], r2[1], r2[2], r2[3]));
+    store4<f16_t>(A.v16 + row + 8 * u, make_float4(bf16_lo(vp[0]), bf16_lo(vp[1]), bf16_lo(vp[2]), bf16_lo(vp[3])));
+    store4<f16_t>(A.v16 + row + 8 * u + 4, make_float4(bf16_hi(vp[0]), bf16_hi(vp[1]), bf16_hi(vp[2]), bf16_hi(vp[3])));
+    if (row_id < A.L) {   // the first (batch, head) writes the table: [L][32] (cos, sin)
+        float4* t = reinterpret_cast<float4*>(A.cs + (static_cast<int64_t>(j) * kPairs + 4 * u) * 2);
+        t[0] = make_float4(cs[0].x, cs[0].y, cs[1].x, cs[1].y);
+        t[1] = make_float4(cs[2].x, cs[2].y, cs[3].x, cs[3].y);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// fwd_mfma: W <= 15 (4 window groups), kept rungs <= 2 MAXS, query heads per key-value head % 4 == 0.
+// ------------------------------------------------------------------------------------------------
+template <int MAXS>
+__global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
+    constexpr float kNegInf = -__builtin_huge_valf();
+    constexpr int kWG = 4;                              // window groups (W <= 15)
+    constexpr int MAXK = 2 * MAXS;
+    constexpr int kBlkBytes = kBlkSlots * kRowBytes;
+    __shared__ __attribute__((aligned(1024))) char ldsW[kWinSlots * kRowBytes];
+    // one array per ring step (the compiler then tells a step's reads from the next steps' DMA):
+    // block A (rung 2k) at slot 0, block B (rung 2k + 1) at slot kBlkSlots
+    __shared__ __attribute__((aligned(1024))) char ldsS0[2 * kBlkBytes];
+    __shared__ __attribute__((aligned(1024))) char ldsS1[2 * kBlkBytes];
+    __shared__ __attribute__((aligned(1024))) char ldsS2[2 * kBlkBytes];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int pq = lane >> 2, x = lane & 3;             // position within the wave, quad lane
+    const int p = 16 * wave + pq;                       // position within the tile
+    const int L = A.L, W = A.W;
+    const int n_tiles = (L + kTile - 1) / kTile;
+    const int n_chunk = A.G >> 2;
+    // workgroup -> (unit, tile); with the XCD map, unit u runs on XCD u % 8 for all its tiles
+    int unit, tile;
+    {
+        const int w = blockIdx.x;
+        if (A.xcd_map) {
+            const int sl = w >> 3;
+            unit = (sl / n_tiles) * 8 + (w & 7);
+            tile = sl % n_tiles;
+        } else {
+            unit = w / n_tiles;
+            tile = w % n_tiles;
+        }
+    }
+    const int chunk = unit % n_chunk;
+    const int bg = unit / n_chunk;                      // b * Hkv + g
+    const int b = bg / A.Hkv;
+    const int h0 = (bg % A.Hkv) * A.G + chunk * 4;
+    const int i0 = tile * kTile;
+    const int i = i0 + p;
+    const bool active = i < L;
+
+    // kept rungs this tile reaches (a prefix: the reach grows with the rung), in steps of two
+    int n_reach = 0;
+    for (int n = 0; n < A.n_off; ++n)
+        if (i0 + kTile - 1 >= A.off[n].a + A.off[n].interp) n_reach = n + 1;
+    const int n_steps = (n_reach + 1) >> 1;
+
+    // ---- staging: LDS DMA of one (batch, kv head). A 16-byte wave instruction fills 1 KB = 8
+    // slots: lane l lands on slot 8g + (l >> 3), physical chunk l & 7, and fetches that slot's row
+    // and the logical chunk the swizzle puts there. A 4-byte instruction fills 2 slots: lane l
+    // lands on slot 2g' + (l >> 5), physical dword l & 31. Every wave issues 3 instructions per
+    // block, so the waits can count them.
+    const int64_t kv_row0 = static_cast<int64_t>(bg) * L;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(A.kstage) + kv_row0 * kRowBytes), 0, L * kRowBytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(A.vstage) + kv_row0 * kRowBytes), 0, L * kRowBytes, kRsrcWord3);
+    // 16-byte part: slot 8g + lrow has swizzle (4 (g & 1) + (lrow >> 1)) & 7, per parity of g
+    const int lrow = lane >> 3;
+    const int voff16[2] = {lrow * kRowBytes + (((lane & 7) ^ (lrow >> 1)) << 4),
+                           lrow * kRowBytes + (((lane & 7) ^ (4 + (lrow >> 1))) << 4)};
+    // 4-byte part: slot 64 + 2 wave + (lane >> 5) (block B: 72 more) has swizzle wave (4 + wave)
+    const int dw = lane & 31;
+    const int voff4[2] = {(lane >> 5) * kRowBytes + (((dw >> 2) ^ wave) << 4) + ((dw & 3) << 2),
+                          (lane >> 5) * kRowBytes + (((dw >> 2) ^ (4 + wave)) << 4) + ((dw & 3) << 2)};
+    const int gpar = wave & 1;                          // parity of this wave's groups in block A
+    auto dma16 = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int row0, int par) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dma_dst(dst), 16, row0 * kRowBytes + voff16[par], 0, 0, 0);
+    };
+    auto dma4 = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int row0, int blk) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dma_dst(dst), 4, row0 * kRowBytes + voff4[blk], 0, 0, 0);
+    };
+    // window block: rows i0 - W - 4 + s at slot s, s < 96 (12 groups, 3 per wave)
+    auto stage_window = [&](const __amdgpu_buffer_rsrc_t& rs) {
+        const int j0 = i0 - W - kWinPad;
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int g = wave + 4 * u;
+            dma16(rs, ldsW + g * 1024, j0 + 8 * g, gpar);
+        }
+    };
+    // block of rung n at slot shift `up` (0 or 2): far row of position p at slot p + up, near row
+    // at p + up + 1; 72 slots: two 16-byte groups and one 4-byte pair per wave. Rungs past the
+    // reach stage rows before 0: zeros.
+    // (block B starts at slot 72 = 9 groups: its groups have the other parity)
+    auto stage_rung = [&](const __amdgpu_buffer_rsrc_t& rs, char* buf, int n, int blk) {
+        const int up = 2 * blk;
+        const int j0 = (n < n_reach) ? i0 - A.off[n].a - 1 - up : -(kTile + kBlkSlots + 8);
+        dma16(rs, buf + wave * 1024, j0 + 8 * wave, gpar ^ blk);
+        dma16(rs, buf + (wave + 4) * 1024, j0 + 8 * (wave + 4), gpar ^ blk);
+        dma4(rs, buf + 64 * kRowBytes + wave * 256, j0 + 64 + 2 * wave, blk);
+    };
+    auto stage_step = [&](const __amdgpu_buffer_rsrc_t& rs, char* buf, int k) {
+        stage_rung(rs, buf, 2 * k, 0);
+        stage_rung(rs, buf + kBlkBytes, 2 * k + 1, 1);
+    };
+    auto ring = [&](int k) -> char* { return k == 0 ? ldsS0 : (k == 1 ? ldsS1 : ldsS2); };
+
+    // ---- q of head h0 + x, raw (RoPE after the staging loads are issued) ----
+    uint4 qraw[8];
+    float4 ctab[16];
+    {
+        const bf16_t* qr = static_cast<const bf16_t*>(A.q) +
+                           ((static_cast<int64_t>(b) * A.Hq + h0 + x) * L + (active ? i : 0)) * kD;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) qraw[c] = *reinterpret_cast<const uint4*>(qr + 8 * c);
+        const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(active ? i : 0) * (kPairs / 2);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) ctab[u] = ct[u];
+    }
+
+    stage_window(krs);
+    stage_step(krs, ldsS0, 0);
+    stage_step(krs, ldsS1, 1);
+
+    uint32_t q[8][4];                                   // dims 8c..8c+7 in chunk c, fp16 pairs
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {                       // RoPE pairs 8c..8c+7: chunks c and c + 4
+        const uint32_t lw[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
+        const uint32_t hw[4] = {qraw[c + 4].x, qraw[c + 4].y, qraw[c + 4].z, qraw[c + 4].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float4 t = ctab[4 * c + m];           // (cos, sin) of pairs 8c + 2m, 8c + 2m + 1
+            const float x0 = bf16_lo(lw[m]), x1 = bf16_hi(lw[m]);
+            const float y0 = bf16_lo(hw[m]), y1 = bf16_hi(hw[m]);
+            q[c][m] = pack_h2((x0 * t.x - y0 * t.y) * A.qscale, (x1 * t.z - y1 * t.w) * A.qscale);
+            q[c + 4][m] = pack_h2((y0 * t.x + x0 * t.y) * A.qscale, (y1 * t.z + x1 * t.w) * A.qscale);
+        }
+    }
+    publish<12>();                                      // the key window has landed
+
+    // ---- phase A: scores of the lane's head x (base 2) ----
+    // Ring schedule: step k's two blocks sit in ring k % 3. The window phase issues step 2; step
+    // k issues step k + 2 (the value window at step 0) into the ring step k - 1 released. A step
+    // is 6 instructions per wave (the value window 3); the wait before each barrier lets exactly
+    // the loads issued after the next step's blocks stay in flight.
+    float s[4 * kWG + MAXK];
+    {
+        stage_step(krs, ldsS2, 2);
+        // lane x reads window distance d = 4g + x: slot p - d + W + 4 (pads d > W read staged rows)
+        const int s0 = p - x + W + kWinPad;
+#pragma unroll
+        for (int g = 0; g < kWG; ++g) {
+            f4_t acc = {0.f, 0.f, 0.f, 0.f};
+            if (4 * g <= W) acc = qk_group(q, ldsW, (s0 - 4 * g) * kRowBytes, swz(s0 - 4 * g));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = 4 * g + r;
+                s[d] = (active && d <= W && i >= d) ? acc[r] : kNegInf;
+            }
+        }
+        if (n_steps == 0) {                             // no rungs: bring in the value window now
+            publish<0>();
+            stage_window(vrs);
+            publish<0>();
+        } else {
+            publish<12>();                              // step 0 (12 loads issued after it) landed
+        }
+    }
+    // lane x of a rung group: rung 2k + (x >> 1), near (x even) or far row
+    const int rslot = p + ((x >> 1) ? kBlkSlots + 2 : 0) + ((x & 1) ? 0 : 1);
+    const int rbase = rslot * kRowBytes, rsw = swz(rslot);
+#pragma unroll
+    for (int k = 0; k < MAXS; ++k) {
+        s[4 * kWG + 2 * k] = kNegInf;
+        s[4 * kWG + 2 * k + 1] = kNegInf;
+        if (k < n_steps) {
+            if (k == 0)
+                stage_window(vrs);
+            else
+                stage_step(krs, ring((k + 2) % kRing), k + 2);
+            const f4_t acc = qk_group(q, ring(k % kRing), rbase, rsw);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int n = 2 * k + e;
+                if (n < n_reach) {
+                    const float sc = fmaf(A.off[n].t, acc[2 * e + 1] - acc[2 * e], acc[2 * e]);
+                    s[4 * kWG + n] = (active && i >= A.off[n].a + A.off[n].interp) ? sc : kNegInf;
+                }
+            }
+            if (k + 1 == n_steps)
+                publish<0>();                           // next: the value window, issued at step 0
+            else if (k == 0)
+                publish<9>();
+            else if (k == 1)
+                publish<9>();
+            else
+                publish<6>();
+        }
+    }
+
+    // ---- exact softmax; weights as fp16 groups of 4 ----
+    float m = kNegInf;
+#pragma unroll
+    for (int y = 0; y < 4 * kWG + MAXK; ++y) m = fmaxf(m, s[y]);
+    if (!active) m = 0.f;
+    float l = 0.f;
+#pragma unroll
+    for (int y = 0; y < 4 * kWG + MAXK; ++y) {
+        s[y] = __builtin_amdgcn_exp2f(s[y] - m);   // v_exp_f32; s - m <= 0
+        l += s[y];
+    }
+    uint32_t pw[kWG][2], po[MAXS][2];
+#pragma unroll
+    for (int g = 0; g < kWG; ++g) {
+        pw[g][0] = pack_h2(s[4 * g], s[4 * g + 1]);
+        pw[g][1] = pack_h2(s[4 * g + 2], s[4 * g + 3]);
+    }
+#pragma unroll
+    for (int k = 0; k < MAXS; ++k) {
+        float w[4];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int n = 2 * k + e;
+            const float ev = s[4 * kWG + n];
+            const float far = (n < n_reach) ? ev * A.off[n].t : 0.f;   // ev is 0 past the reach
+            w[2 * e] = ev - far;
+            w[2 * e + 1] = far;
+        }
+        po[k][0] = pack_h2(w[0], w[1]);
+        po[k][1] = pack_h2(w[2], w[3]);
+    }
+
+    // ---- phase B: P.V ----
+    // The B operand of dim block m for lane (p', x) is (v[row 0][16x + m], .., v[row 3][16x + m]).
+    // ds_read_b64_tr_b16 transposes within each 16 lanes: lane (p', x) receives element x of the
+    // 8 bytes that lane (4 (p' >> 2) + k, p' & 3) read, for k = 0..3. So lane (p', x) reads, for
+    // position pt = 4 (p' >> 2) + x of the wave and slot k = p' & 3 of the group, elements
+    // 4m..4m+3 of that row: dims 16c + m, c = 0..3.
+    const int pt = 16 * wave + 4 * (pq >> 2) + x;       // the position this lane reads for
+    const int kt = pq & 3;                              // the slot of the group this lane reads
+    // value step k sits in ring k % 3; the window phase issues steps 0, 1, 2 (every ring is free
+    // after the last key step), step k >= 1 issues step k + 2
+    f4_t o[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[e] = (f4_t){0.f, 0.f, 0.f, 0.f};
+    stage_step(vrs, ldsS0, 0);
+    stage_step(vrs, ldsS1, 1);
+    stage_step(vrs, ldsS2, 2);
+    {
+        // window group g: slot pt - 4g - kt + W + 4
+        const int sv = pt - kt + W + kWinPad;
+#pragma unroll
+        for (int g = 0; g < kWG; ++g)
+            if (4 * g <= W) pv_group(o, pw[g][0], pw[g][1], ldsW, (sv - 4 * g) * kRowBytes, swz(sv - 4 * g));
+    }
+    if (n_steps > 0) publish<12>();                     // value step 0 has landed
+    {
+        // slot k of a rung group: near and far of rung 2k (block A, slots pt + 1, pt) and of
+        // rung 2k + 1 (block B, slots pt + 3, pt + 2)
+        const int sv = (kt < 2) ? pt + 1 - kt : kBlkSlots + pt + 5 - kt;
+        const int vbase = sv * kRowBytes, vsw = swz(sv);
+#pragma unroll
+        for (int k = 0; k < MAXS; ++k) {
+            if (k < n_steps) {
+                if (k >= 1) stage_step(vrs, ring((k + 2) % kRing), k + 2);
+                pv_group(o, po[k][0], po[k][1], ring(k % kRing), vbase, vsw);
+                if (k + 1 == n_steps) {
+                    // last block: nothing left to publish
+                } else if (k == 0) {
+                    publish<6>();
+                } else {
+                    publish<6>();
+                }
+            }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA may outlive the workgroup
+
+    // ---- normalise and write: lane x holds dims 16x..16x+15 of heads 0..3 ----
+    const float inv = 1.0f / l;
+    float invh[4];
+    invh[0] = quad_f<kBcast0>(inv);
+    invh[1] = quad_f<kBcast1>(inv);
+    invh[2] = quad_f<kBcast2>(inv);
+    invh[3] = quad_f<kBcast3>(inv);
+    if (active) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            bf16_t* orow = static_cast<bf16_t*>(A.o) + ((static_cast<int64_t>(b) * A.Hq + h0 + r) * L + i) * kD + 16 * x;
+            uint4 lo, hi;
+            lo.x = pack_bf2(o[0][r] * invh[r], o[1][r] * invh[r]);
+            lo.y = pack_bf2(o[2][r] * invh[r], o[3][r] * invh[r]);
+            lo.z = pack_bf2(o[4][r] * invh[r], o[5][r] * invh[r]);
+            lo.w = pack_bf2(o[6][r] * invh[r], o[7][r] * invh[r]);
+            hi.x = pack_bf2(o[8][r] * invh[r], o[9][r] * invh[r]);
+            hi.y = pack_bf2(o[10][r] * invh[r], o[11][r] * invh[r]);
+            hi.z = pack_bf2(o[12][r] * invh[r], o[13][r] * invh[r]);
+            hi.w = pack_bf2(o[14][r] * invh[r], o[15][r] * invh[r]);
+            *reinterpret_cast<uint4*>(orow) = lo;
+            *reinterpret_cast<uint4*>(orow + 8) = hi;
+        }
+        if (A.lse != nullptr)
+            A.lse[(static_cast<int64_t>(b) * A.Hq + h0 + x) * L + i] = (m + log2f(l)) * 0.69314718055994530942f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prep_kv16(const PrepArgs& A, hipStream_t s) {
+    const int64_t threads = static_cast<int64_t>(A.n_bh) * A.L * 8;
+    const unsigned blocks = static_cast<unsigned>((threads + 255) / 256);
+    hipLaunchKernelGGL(prep_kv16_kernel, dim3(blocks), dim3(256), 0, s, A);
+    return hipGetLastError();
+}
+
+bool fwd_mfma_supported(const FwdArgs& A) {
+    return A.G % 4 == 0 && A.W <= 15 && A.n_off <= 16;
+}
+
+hipError_t launch_fwd_mfma(const FwdArgs& A0, hipStream_t s) {
+    FwdArgs A = A0;
+    const int64_t n_tiles = (A.L + kTile - 1) / kTile;
+    const int64_t n_units = static_cast<int64_t>(A.B) * A.Hkv * (A.G / 4);
+    A.xcd_map = (n_units % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((fwd_mfma_kernel<8>), dim3(static_cast<unsigned>(n_units * n_tiles)), dim3(kNT), 0, s, A);
+    return hipGetLastError();
+}
+
+}  // namespace fibattn

@@ -40,7 +40,7 @@ struct PrepArgs {
     const void* k;       // [B*Hkv, L, 64] bf16
     const void* v;       // [B*Hkv, L, 64] bf16
     _Float16* k16;       // [B*Hkv, L, 64] rotated keys
-    _Float16* v16;       // [B*Hkv, L, 64] values
+    _Float16* v16;       // [B*Hkv, L, 64] values, element 4m + c of a row holding dim 16c + m
     float* cs;           // [L, 32, 2] cos and sin of every position and RoPE pair
     int32_t n_bh;
     int32_t L;
@@ -50,7 +50,9 @@ struct PrepArgs {
 struct FwdArgs {
     const void* q;       // [B, Hq, L, 64] storage type
     const void* kstage;  // [B, Hkv, L, 64] rotated keys: float32 (f32 storage) or fp16 (bf16 storage)
-    const void* vstage;  // [B, Hkv, L, 64] values: the input (f32 storage) or fp16 (bf16 storage)
+    const void* vstage;  // [B, Hkv, L, 64] values: the input (f32 storage) or fp16 (bf16 storage,
+                         // dims permuted for the matrix-core kernel: element 4m + c is dim 16c + m)
+    const void* v;       // [B, Hkv, L, 64] the caller's values
     const float* cstab;  // [L, 32, 2] cos/sin table (bf16 storage)
     void* o;             // [B, Hq, L, 64]
     float* lse;          // [B, Hq, L] or nullptr
@@ -88,8 +90,8 @@ struct BwdArgs {
 hipError_t launch_rope_keys(int dtype, const RopeKeysArgs& a, hipStream_t s);
 hipError_t launch_prep_kv16(const PrepArgs& a, hipStream_t s);
 hipError_t launch_fwd_attend(int dtype, const FwdArgs& a, hipStream_t s);
-bool fwd_quad_supported(const FwdArgs& a);
-hipError_t launch_fwd_quad(const FwdArgs& a, hipStream_t s);
+bool fwd_mfma_supported(const FwdArgs& a);
+hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd(int dtype, const BwdArgs& a, bool want_dalpha, hipStream_t s);
 int bwd_query_workgroups(int B, int L, int Hkv, int G);
 
