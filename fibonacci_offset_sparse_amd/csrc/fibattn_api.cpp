@@ -97,6 +97,9 @@ Plan make_plan(double alpha, int32_t W, const int32_t* offsets, int32_t K) {
     return p;
 }
 
+// Scores are kept in base 2: q.k * log2(e) / sqrt(D).
+float score_scale() { return static_cast<float>(1.4426950408889634074 / std::sqrt(static_cast<double>(kD))); }
+
 RopeFreq make_freq(double theta) {
     RopeFreq fr;
     for (int j = 0; j < kPairs; ++j) {
@@ -262,6 +265,7 @@ fibattn_status_t fibattn_fwd_prep(const void* k, const void* v, int32_t B, int32
         a.cs = reinterpret_cast<float*>(static_cast<char*>(workspace) + krot_bytes(B, L, Hkv));
         a.n_bh = B * Hkv;
         a.L = L;
+        a.qscale = score_scale();
         a.fr = make_freq(rope_theta);
         e = launch_prep_kv16(a, static_cast<hipStream_t>(stream));
     }
@@ -297,7 +301,7 @@ fibattn_status_t fibattn_fwd_attend(const void* q, const void* v, double alpha, 
     a.G = Hq / Hkv;
     a.W = W;
     a.n_off = plan.n_keep;
-    a.qscale = static_cast<float>(1.4426950408889634074 / std::sqrt(static_cast<double>(kD)));
+    a.qscale = score_scale();
     a.fr = make_freq(rope_theta);
     std::memcpy(a.off, plan.keep, sizeof(plan.keep));
     const hipError_t e = launch_fwd_attend(dtype, a, static_cast<hipStream_t>(stream));

@@ -46,19 +46,15 @@ namespace {
 
 constexpr int kNT = 256;                 // 4 waves x 16 positions x 4 lanes
 constexpr int kRowBytes = kD * 2;        // one fp16 row
-constexpr int kWinSlots = 96;            // 64 + W + 4 <= 83 rows; 12 DMA groups, 3 per wave
 constexpr int kWinPad = 4;               // window slot of row i0 - W - 4 is 0: pads stay in range
 constexpr int kBlkSlots = 72;            // 65 (+2 for the second rung) rows, 9 DMA groups
-constexpr int kRing = 3;
 constexpr int kBcast0 = 0x00, kBcast1 = 0x55, kBcast2 = 0xAA, kBcast3 = 0xFF;   // quad_perm [r,r,r,r]
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, gfx9 family
-#ifndef FIBATTN_FWD_WGS_PER_CU
-#define FIBATTN_FWD_WGS_PER_CU 2
-#endif
-// Workgroups per CU: LDS is 12 + 6 x 9 KB per workgroup, and the register budget this gives
-// (256 per lane) holds q, the scores and the 64 output accumulators without spilling (a spill
-// reload is a vector-memory load and would wait behind every staging load in flight).
-constexpr int kWgsPerCu = FIBATTN_FWD_WGS_PER_CU;
+// Workgroups per CU: LDS is 2 x 18 KB per workgroup, so four fit (1024 workgroups at the paper's
+// shape are one wave of the grid); the register budget this gives (128 per lane) must hold q,
+// the scores and the 64 output accumulators without spilling (a spill reload is a vector-memory
+// load and would wait behind every staging load in flight).
+constexpr int kWgsPerCu = 4;
 
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
@@ -113,21 +109,19 @@ template <int N> __device__ __forceinline__ void publish() {
 }
 
 // QK of one group: lane x supplies the row at slot byte offset base (swizzle F = swz(slot)), q
-// supplies head x; returns the 4 scores of head x. Two accumulators keep two chains.
+// supplies head x; returns the 4 scores of head x. Four accumulators keep the dependent chains
+// short (a 4x4x4 product's result is ready only some 40 cycles after issue).
 __device__ __forceinline__ f4_t qk_group(const uint32_t (&q)[8][4], const char* lds, int base, int F) {
-    f4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+    f4_t a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] = (f4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const uint4 k = lds16(lds, base | ((c << 4) ^ F));
-        if (c & 1) {
-            a1 = mfma4(k.x, k.y, q[c][0], q[c][1], a1);
-            a1 = mfma4(k.z, k.w, q[c][2], q[c][3], a1);
-        } else {
-            a0 = mfma4(k.x, k.y, q[c][0], q[c][1], a0);
-            a0 = mfma4(k.z, k.w, q[c][2], q[c][3], a0);
-        }
+        a[(2 * c) & 3] = mfma4(k.x, k.y, q[c][0], q[c][1], a[(2 * c) & 3]);
+        a[(2 * c + 1) & 3] = mfma4(k.z, k.w, q[c][2], q[c][3], a[(2 * c + 1) & 3]);
     }
-    return a0 + a1;
+    return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
 // PV of one group. The lane reads its assigned (position, slot) row, at slot byte offset base
@@ -181,10 +175,11 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
     store4<f16_t>(A.k16 + row + kPairs + 4 * u, make_float4(r2[0], r2[1], r2[2], r2[3]));
     store4<f16_t>(A.v16 + row + 8 * u, make_float4(bf16_lo(vp[0]), bf16_lo(vp[1]), bf16_lo(vp[2]), bf16_lo(vp[3])));
     store4<f16_t>(A.v16 + row + 8 * u + 4, make_float4(bf16_hi(vp[0]), bf16_hi(vp[1]), bf16_hi(vp[2]), bf16_hi(vp[3])));
-    if (row_id < A.L) {   // the first (batch, head) writes the table: [L][32] (cos, sin)
+    if (row_id < A.L) {   // the first (batch, head) writes the table: [L][32] (cos, sin) x qscale
+        const float sc = A.qscale;
         float4* t = reinterpret_cast<float4*>(A.cs + (static_cast<int64_t>(j) * kPairs + 4 * u) * 2);
-        t[0] = make_float4(cs[0].x, cs[0].y, cs[1].x, cs[1].y);
-        t[1] = make_float4(cs[2].x, cs[2].y, cs[3].x, cs[3].y);
+        t[0] = make_float4(cs[0].x * sc, cs[0].y * sc, cs[1].x * sc, cs[1].y * sc);
+        t[1] = make_float4(cs[2].x * sc, cs[2].y * sc, cs[3].x * sc, cs[3].y * sc);
     }
 }
 
@@ -197,12 +192,14 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     constexpr int kWG = 4;                              // window groups (W <= 15)
     constexpr int MAXK = 2 * MAXS;
     constexpr int kBlkBytes = kBlkSlots * kRowBytes;
-    __shared__ __attribute__((aligned(1024))) char ldsW[kWinSlots * kRowBytes];
-    // one array per ring step (the compiler then tells a step's reads from the next steps' DMA):
-    // block A (rung 2k) at slot 0, block B (rung 2k + 1) at slot kBlkSlots
-    __shared__ __attribute__((aligned(1024))) char ldsS0[2 * kBlkBytes];
-    __shared__ __attribute__((aligned(1024))) char ldsS1[2 * kBlkBytes];
-    __shared__ __attribute__((aligned(1024))) char ldsS2[2 * kBlkBytes];
+    constexpr int kBufBytes = 2 * kBlkBytes;
+    // Two staging buffers used in turn. An item is the key window, a step of two key rungs, the
+    // value window or a step of two value rungs: item j sits in buffer j % 2. A rung step holds
+    // rung 2k at slot 0 (block A) and rung 2k + 1 at slot kBlkSlots (block B); a window holds
+    // rows i0 - W - 4 + s at slot s. Two arrays, always named at compile time where they are
+    // read: the compiler then knows an LDS read does not touch the buffer the DMA in flight fills.
+    __shared__ __attribute__((aligned(1024))) char lds0[kBufBytes];
+    __shared__ __attribute__((aligned(1024))) char lds1[kBufBytes];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -242,7 +239,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     // slots: lane l lands on slot 8g + (l >> 3), physical chunk l & 7, and fetches that slot's row
     // and the logical chunk the swizzle puts there. A 4-byte instruction fills 2 slots: lane l
     // lands on slot 2g' + (l >> 5), physical dword l & 31. Every wave issues 3 instructions per
-    // block, so the waits can count them.
+    // block or window.
     const int64_t kv_row0 = static_cast<int64_t>(bg) * L;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(static_cast<const char*>(A.kstage) + kv_row0 * kRowBytes), 0, L * kRowBytes, kRsrcWord3);
@@ -263,33 +260,33 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     auto dma4 = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int row0, int blk) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dma_dst(dst), 4, row0 * kRowBytes + voff4[blk], 0, 0, 0);
     };
-    // window block: rows i0 - W - 4 + s at slot s, s < 96 (12 groups, 3 per wave)
-    auto stage_window = [&](const __amdgpu_buffer_rsrc_t& rs) {
+    auto buf = [&](int j) -> char* { return (j & 1) ? lds1 : lds0; };
+    // window: rows i0 - W - 4 + s at slot s, s < 96 (12 groups, 3 per wave)
+    auto stage_window = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst) {
         const int j0 = i0 - W - kWinPad;
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
             const int g = wave + 4 * u;
-            dma16(rs, ldsW + g * 1024, j0 + 8 * g, gpar);
+            dma16(rs, dst + g * 1024, j0 + 8 * g, gpar);
         }
     };
-    // block of rung n at slot shift `up` (0 or 2): far row of position p at slot p + up, near row
-    // at p + up + 1; 72 slots: two 16-byte groups and one 4-byte pair per wave. Rungs past the
-    // reach stage rows before 0: zeros.
-    // (block B starts at slot 72 = 9 groups: its groups have the other parity)
-    auto stage_rung = [&](const __amdgpu_buffer_rsrc_t& rs, char* buf, int n, int blk) {
-        const int up = 2 * blk;
-        const int j0 = (n < n_reach) ? i0 - A.off[n].a - 1 - up : -(kTile + kBlkSlots + 8);
-        dma16(rs, buf + wave * 1024, j0 + 8 * wave, gpar ^ blk);
-        dma16(rs, buf + (wave + 4) * 1024, j0 + 8 * (wave + 4), gpar ^ blk);
-        dma4(rs, buf + 64 * kRowBytes + wave * 256, j0 + 64 + 2 * wave, blk);
+    // block of rung n (blk 0: A, 1: B two slots up): far row of position p at slot p + 2 blk, near
+    // row at p + 2 blk + 1; 72 slots: two 16-byte groups and one 4-byte pair per wave (block B
+    // starts at slot 72 = 9 groups: its groups have the other parity). Rungs past the reach
+    // stage rows before 0: zeros.
+    auto stage_rung = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int n, int blk) {
+        const int j0 = (n < n_reach) ? i0 - A.off[n].a - 1 - 2 * blk : -(kTile + kBlkSlots + 8);
+        dma16(rs, dst + wave * 1024, j0 + 8 * wave, gpar ^ blk);
+        dma16(rs, dst + (wave + 4) * 1024, j0 + 8 * (wave + 4), gpar ^ blk);
+        dma4(rs, dst + 64 * kRowBytes + wave * 256, j0 + 64 + 2 * wave, blk);
     };
-    auto stage_step = [&](const __amdgpu_buffer_rsrc_t& rs, char* buf, int k) {
-        stage_rung(rs, buf, 2 * k, 0);
-        stage_rung(rs, buf + kBlkBytes, 2 * k + 1, 1);
+    auto stage_step = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int k) {
+        stage_rung(rs, dst, 2 * k, 0);
+        stage_rung(rs, dst + kBlkBytes, 2 * k + 1, 1);
     };
-    auto ring = [&](int k) -> char* { return k == 0 ? ldsS0 : (k == 1 ? ldsS1 : ldsS2); };
 
-    // ---- q of head h0 + x, raw (RoPE after the staging loads are issued) ----
+    // ---- prologue: key window (item 0), q, item 1 (key step 0, or the value window) ----
+    stage_window(krs, buf(0));
     uint4 qraw[8];
     float4 ctab[16];
     {
@@ -301,14 +298,13 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) ctab[u] = ct[u];
     }
+    stage_step(krs, buf(1), 0);                         // (zero rows when no rung is reached)
 
-    stage_window(krs);
-    stage_step(krs, ldsS0, 0);
-    stage_step(krs, ldsS1, 1);
-
-    uint32_t q[8][4];                                   // dims 8c..8c+7 in chunk c, fp16 pairs
+    // q of head h0 + x, rotated at its position and scaled (the table carries qscale), fp16:
+    // register chunk c holds dims 8c..8c+7; RoPE pairs 8c..8c+7 are chunks c and c + 4
+    uint32_t q[8][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {                       // RoPE pairs 8c..8c+7: chunks c and c + 4
+    for (int c = 0; c < 4; ++c) {
         const uint32_t lw[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
         const uint32_t hw[4] = {qraw[c + 4].x, qraw[c + 4].y, qraw[c + 4].z, qraw[c + 4].w};
 #pragma unroll
@@ -316,39 +312,32 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
             const float4 t = ctab[4 * c + m];           // (cos, sin) of pairs 8c + 2m, 8c + 2m + 1
             const float x0 = bf16_lo(lw[m]), x1 = bf16_hi(lw[m]);
             const float y0 = bf16_lo(hw[m]), y1 = bf16_hi(hw[m]);
-            q[c][m] = pack_h2((x0 * t.x - y0 * t.y) * A.qscale, (x1 * t.z - y1 * t.w) * A.qscale);
-            q[c + 4][m] = pack_h2((y0 * t.x + x0 * t.y) * A.qscale, (y1 * t.z + x1 * t.w) * A.qscale);
+            q[c][m] = pack_h2(x0 * t.x - y0 * t.y, x1 * t.z - y1 * t.w);
+            q[c + 4][m] = pack_h2(y0 * t.x + x0 * t.y, y1 * t.z + x1 * t.w);
         }
     }
-    publish<12>();                                      // the key window has landed
+    publish<6>();                                       // the key window has landed
 
     // ---- phase A: scores of the lane's head x (base 2) ----
-    // Ring schedule: step k's two blocks sit in ring k % 3. The window phase issues step 2; step
-    // k issues step k + 2 (the value window at step 0) into the ring step k - 1 released. A step
-    // is 6 instructions per wave (the value window 3); the wait before each barrier lets exactly
-    // the loads issued after the next step's blocks stay in flight.
+    // Key step k computes from buffer (k + 1) % 2 after issuing step k + 1 into the other buffer
+    // (the barrier that ended step k - 1 released it); the wait before each barrier is for step
+    // k + 1, the only load in flight.
     float s[4 * kWG + MAXK];
     {
-        stage_step(krs, ldsS2, 2);
-        // lane x reads window distance d = 4g + x: slot p - d + W + 4 (pads d > W read staged rows)
+        // item 0: lane x reads window distance d = 4g + x, slot p - d + W + 4 (pads d > W read
+        // staged rows)
         const int s0 = p - x + W + kWinPad;
 #pragma unroll
         for (int g = 0; g < kWG; ++g) {
             f4_t acc = {0.f, 0.f, 0.f, 0.f};
-            if (4 * g <= W) acc = qk_group(q, ldsW, (s0 - 4 * g) * kRowBytes, swz(s0 - 4 * g));
+            if (4 * g <= W) acc = qk_group(q, buf(0), (s0 - 4 * g) * kRowBytes, swz(s0 - 4 * g));
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int d = 4 * g + r;
                 s[d] = (active && d <= W && i >= d) ? acc[r] : kNegInf;
             }
         }
-        if (n_steps == 0) {                             // no rungs: bring in the value window now
-            publish<0>();
-            stage_window(vrs);
-            publish<0>();
-        } else {
-            publish<12>();                              // step 0 (12 loads issued after it) landed
-        }
+        publish<0>();                                   // item 1 has landed, buffer 0 is free
     }
     // lane x of a rung group: rung 2k + (x >> 1), near (x even) or far row
     const int rslot = p + ((x >> 1) ? kBlkSlots + 2 : 0) + ((x & 1) ? 0 : 1);
@@ -357,12 +346,9 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     for (int k = 0; k < MAXS; ++k) {
         s[4 * kWG + 2 * k] = kNegInf;
         s[4 * kWG + 2 * k + 1] = kNegInf;
-        if (k < n_steps) {
-            if (k == 0)
-                stage_window(vrs);
-            else
-                stage_step(krs, ring((k + 2) % kRing), k + 2);
-            const f4_t acc = qk_group(q, ring(k % kRing), rbase, rsw);
+        if (k < n_steps) {                              // item k + 1, in buffer (k + 1) % 2
+            if (k + 1 < n_steps) stage_step(krs, buf(k + 2), k + 1);
+            const f4_t acc = qk_group(q, buf(k + 1), rbase, rsw);
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int n = 2 * k + e;
@@ -371,16 +357,14 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
                     s[4 * kWG + n] = (active && i >= A.off[n].a + A.off[n].interp) ? sc : kNegInf;
                 }
             }
-            if (k + 1 == n_steps)
-                publish<0>();                           // next: the value window, issued at step 0
-            else if (k == 0)
-                publish<9>();
-            else if (k == 1)
-                publish<9>();
-            else
-                publish<6>();
+            publish<0>();
         }
     }
+
+    // ---- value window into buffer 0 and value step 0 into buffer 1 (both free after the last
+    // barrier), under the softmax ----
+    stage_window(vrs, lds0);
+    stage_step(vrs, lds1, 0);
 
     // ---- exact softmax; weights as fp16 groups of 4 ----
     float m = kNegInf;
@@ -422,43 +406,32 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     // 4m..4m+3 of that row: dims 16c + m, c = 0..3.
     const int pt = 16 * wave + 4 * (pq >> 2) + x;       // the position this lane reads for
     const int kt = pq & 3;                              // the slot of the group this lane reads
-    // value step k sits in ring k % 3; the window phase issues steps 0, 1, 2 (every ring is free
-    // after the last key step), step k >= 1 issues step k + 2
     f4_t o[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[e] = (f4_t){0.f, 0.f, 0.f, 0.f};
-    stage_step(vrs, ldsS0, 0);
-    stage_step(vrs, ldsS1, 1);
-    stage_step(vrs, ldsS2, 2);
     {
+        publish<6>();                                   // the value window has landed
         // window group g: slot pt - 4g - kt + W + 4
         const int sv = pt - kt + W + kWinPad;
 #pragma unroll
         for (int g = 0; g < kWG; ++g)
-            if (4 * g <= W) pv_group(o, pw[g][0], pw[g][1], ldsW, (sv - 4 * g) * kRowBytes, swz(sv - 4 * g));
+            if (4 * g <= W) pv_group(o, pw[g][0], pw[g][1], lds0, (sv - 4 * g) * kRowBytes, swz(sv - 4 * g));
+        if (n_steps > 0) publish<0>();                  // value step 0 has landed, buffer 0 is free
     }
-    if (n_steps > 0) publish<12>();                     // value step 0 has landed
     {
         // slot k of a rung group: near and far of rung 2k (block A, slots pt + 1, pt) and of
-        // rung 2k + 1 (block B, slots pt + 3, pt + 2)
+        // rung 2k + 1 (block B, slots pt + 3, pt + 2); value step k sits in buffer (k + 1) % 2
         const int sv = (kt < 2) ? pt + 1 - kt : kBlkSlots + pt + 5 - kt;
         const int vbase = sv * kRowBytes, vsw = swz(sv);
 #pragma unroll
         for (int k = 0; k < MAXS; ++k) {
             if (k < n_steps) {
-                if (k >= 1) stage_step(vrs, ring((k + 2) % kRing), k + 2);
-                pv_group(o, po[k][0], po[k][1], ring(k % kRing), vbase, vsw);
-                if (k + 1 == n_steps) {
-                    // last block: nothing left to publish
-                } else if (k == 0) {
-                    publish<6>();
-                } else {
-                    publish<6>();
-                }
+                if (k + 1 < n_steps) stage_step(vrs, buf(k + 2), k + 1);
+                pv_group(o, po[k][0], po[k][1], buf(k + 1), vbase, vsw);
+                if (k + 1 < n_steps) publish<0>();
             }
         }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA may outlive the workgroup
 
     // ---- normalise and write: lane x holds dims 16x..16x+15 of heads 0..3 ----
     const float inv = 1.0f / l;

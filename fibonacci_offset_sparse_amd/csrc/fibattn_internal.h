@@ -41,9 +41,10 @@ struct PrepArgs {
     const void* v;       // [B*Hkv, L, 64] bf16
     _Float16* k16;       // [B*Hkv, L, 64] rotated keys
     _Float16* v16;       // [B*Hkv, L, 64] values, element 4m + c of a row holding dim 16c + m
-    float* cs;           // [L, 32, 2] cos and sin of every position and RoPE pair
+    float* cs;           // [L, 32, 2] cos and sin of every position and RoPE pair, times qscale
     int32_t n_bh;
     int32_t L;
+    float qscale;        // the score scale folded into the table (log2(e) / sqrt(D))
     RopeFreq fr;
 };
 
@@ -53,7 +54,7 @@ struct FwdArgs {
     const void* vstage;  // [B, Hkv, L, 64] values: the input (f32 storage) or fp16 (bf16 storage,
                          // dims permuted for the matrix-core kernel: element 4m + c is dim 16c + m)
     const void* v;       // [B, Hkv, L, 64] the caller's values
-    const float* cstab;  // [L, 32, 2] cos/sin table (bf16 storage)
+    const float* cstab;  // [L, 32, 2] cos/sin table times qscale (bf16 storage)
     void* o;             // [B, Hq, L, 64]
     float* lse;          // [B, Hq, L] or nullptr
     int32_t B, L, Hq, Hkv, G, W, n_off;
