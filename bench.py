@@ -170,24 +170,26 @@ def time_steps(net: Layers, steps: int, warmup: int):
 
 
 def time_stages(net: Layers, sweeps: int):
-    """Average duration of each stage, from HIP events on the stream the kernels run on."""
+    """Average duration of each stage, from HIP events on the stream the kernels run on.
+
+    Each stage is launched for all layers back to back behind a short GPU spin, so the launches
+    are queued before the GPU reaches them and the events see kernel time, not host gaps. The
+    forward stages run on whichever layer's keys the shared workspace holds last (same work)."""
     n = net.w.n_layers
-    tot = {"fwd_prep": 0.0, "fwd_attend": 0.0, "bwd": 0.0}
+    stages = {"fwd_prep": net.prep, "fwd_attend": net.attend, "bwd": net.bwd}
+    tot = {k: 0.0 for k in stages}
     for _ in range(sweeps):
-        for layer in range(n):
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            ev[0].record()
-            net.prep(layer)
-            ev[1].record()
-            net.attend(layer)
-            ev[2].record()
-            net.bwd(layer)
-            ev[3].record()
+        for name, fn in stages.items():
             torch.cuda.synchronize()
-            tot["fwd_prep"] += ev[0].elapsed_time(ev[1])
-            tot["fwd_attend"] += ev[1].elapsed_time(ev[2])
-            tot["bwd"] += ev[2].elapsed_time(ev[3])
-    return {k: v / (sweeps * n) for k, v in tot.items()}
+            torch.cuda._sleep(20_000_000)               # keeps the GPU busy while the launches queue
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for layer in range(n):
+                fn(layer)
+            e1.record()
+            torch.cuda.synchronize()
+            tot[name] += e0.elapsed_time(e1) / n
+    return {k: v / sweeps for k, v in tot.items()}
 
 
 def measure(fa, name: str, steps: int, warmup: int, dev):

@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -143,6 +144,23 @@ size_t half_rows_bytes(int32_t B, int32_t L, int32_t Hkv) {
 size_t cs_table_bytes(int32_t L) { return align256(static_cast<size_t>(L) * kPairs * 2 * sizeof(float)); }
 size_t fwd_ws_bytes(int32_t B, int32_t L, int32_t Hkv) { return krot_bytes(B, L, Hkv) + cs_table_bytes(L); }
 
+// Workspace of the matrix-core backward (bfloat16 storage): staged fp16 keys and values and the
+// cos/sin table (the forward's layout of the same sizes), the rotated queries (fp16), the per key
+// row term weights, and the per-workgroup d(loss)/dt partials.
+struct BwdFastLayout {
+    size_t qrot, do16, wts, part, total;
+};
+BwdFastLayout bwd_fast_layout(int32_t B, int32_t L, int32_t Hq, int32_t Hkv) {
+    BwdFastLayout f;
+    f.qrot = fwd_ws_bytes(B, L, Hkv);
+    f.do16 = f.qrot + align256(static_cast<size_t>(B) * Hq * L * kD * sizeof(uint16_t));
+    f.wts = f.do16 + align256(static_cast<size_t>(B) * Hq * L * kD * sizeof(uint16_t));
+    f.part = f.wts + align256(static_cast<size_t>(B) * Hq * L * kNV * sizeof(uint32_t));
+    const size_t n_wg = static_cast<size_t>(bwd_query_workgroups(B, L, Hkv, Hq / Hkv));
+    f.total = f.part + align256(n_wg * kMaxOff * sizeof(float));
+    return f;
+}
+
 #define FIBATTN_TRY(expr)                        \
     do {                                         \
         const fibattn_status_t st_ = (expr);     \
@@ -267,7 +285,7 @@ fibattn_status_t fibattn_fwd_prep(const void* k, const void* v, int32_t B, int32
         a.L = L;
         a.qscale = score_scale();
         a.fr = make_freq(rope_theta);
-        e = launch_prep_kv16(a, static_cast<hipStream_t>(stream));
+        e = launch_prep_kv16(a, false, static_cast<hipStream_t>(stream));
     }
     if (e != hipSuccess) return hip_fail(e, "forward prep launch");
     return FIBATTN_OK;
@@ -334,7 +352,8 @@ size_t fibattn_bwd_workspace_bytes(int32_t B, int32_t L, int32_t Hq, int32_t Hkv
     const size_t slots = align256(static_cast<size_t>(B) * Hq * S * L * sizeof(float));
     const size_t n_wg = static_cast<size_t>(bwd_query_workgroups(B, L, Hkv, Hq / Hkv));
     const size_t part = align256(n_wg * kMaxOff * sizeof(float));
-    return krot_bytes(B, L, Hkv) + qrot + 2 * slots + part;
+    const size_t general = krot_bytes(B, L, Hkv) + qrot + 2 * slots + part;
+    return std::max(general, bwd_fast_layout(B, L, Hq, Hkv).total);
 }
 
 fibattn_status_t fibattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -359,7 +378,7 @@ fibattn_status_t fibattn_bwd(const void* q, const void* k, const void* v, const 
                     "d(alpha) requested but some alpha * f_k is integral (no two-sided slope there)");
 
     char* ws = static_cast<char*>(workspace);
-    BwdArgs a;
+    BwdArgs a{};
     a.krot = reinterpret_cast<float*>(ws);
     ws += krot_bytes(B, L, Hkv);
     a.qrot = reinterpret_cast<float*>(ws);
@@ -395,14 +414,47 @@ fibattn_status_t fibattn_bwd(const void* q, const void* k, const void* v, const 
     a.fr = make_freq(rope_theta);
     std::memcpy(a.off, plan.keep, sizeof(plan.keep));
 
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dtype == FIBATTN_BF16) {
+        // matrix-core path: staged fp16 rows in the backward layout
+        a.qscale = score_scale();
+        a.xcd_map = 0;
+        if (bwd_mfma_supported(a)) {
+            const BwdFastLayout f = bwd_fast_layout(B, L, Hq, Hkv);
+            char* w0 = static_cast<char*>(workspace);
+            PrepArgs pa;
+            pa.k = k;
+            pa.v = v;
+            pa.k16 = reinterpret_cast<_Float16*>(w0);
+            pa.v16 = reinterpret_cast<_Float16*>(w0 + half_rows_bytes(B, L, Hkv));
+            pa.cs = reinterpret_cast<float*>(w0 + krot_bytes(B, L, Hkv));
+            pa.n_bh = B * Hkv;
+            pa.L = L;
+            pa.qscale = 1.0f;
+            pa.fr = a.fr;
+            a.kstage = pa.k16;
+            a.vstage = pa.v16;
+            a.cstab = pa.cs;
+            a.qrot16 = w0 + f.qrot;
+            a.do16 = w0 + f.do16;
+            a.wts = reinterpret_cast<uint32_t*>(w0 + f.wts);
+            a.partial = reinterpret_cast<float*>(w0 + f.part);
+            e = launch_prep_kv16(pa, true, s);
+            if (e != hipSuccess) return hip_fail(e, "backward prep launch");
+            e = launch_bwd_mfma(a, want_dalpha, s);
+            if (e != hipSuccess) return hip_fail(e, "bwd launch");
+            return FIBATTN_OK;
+        }
+    }
+
     RopeKeysArgs r;
     r.k = k;
     r.krot = const_cast<float*>(a.krot);
     r.n_bh = B * Hkv;
     r.L = L;
     r.fr = a.fr;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_rope_keys(dtype, r, s);
+    e = launch_rope_keys(dtype, r, s);
     if (e != hipSuccess) return hip_fail(e, "rope_keys launch");
     e = launch_bwd(dtype, a, want_dalpha, s);
     if (e != hipSuccess) return hip_fail(e, "bwd launch");

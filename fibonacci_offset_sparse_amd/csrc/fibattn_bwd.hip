@@ -472,6 +472,15 @@ hipError_t launch_bwd_typed(const BwdArgs& A, bool want_dalpha, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_dalpha(const BwdArgs& A, hipStream_t s) {
+    hipLaunchKernelGGL(dalpha_kernel, dim3(1), dim3(256), 0, s, A);
+    return hipGetLastError();
+}
+
+namespace {
+
+}  // namespace
+
 int bwd_query_workgroups(int B, int L, int Hkv, int G) {
     const int hpb = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
     return ((L + kTile - 1) / kTile) * Hkv * (G / hpb) * B;

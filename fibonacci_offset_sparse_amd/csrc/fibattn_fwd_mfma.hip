@@ -38,114 +38,32 @@
 //    are the transposing value reads of window groups; those of rung groups are 2-way.
 //  * The grid is mapped so that all tiles of one (batch, key-value head) run on one XCD, whose L2
 //    then holds that head's keys and values for every tile that re-reads them.
-#include "fibattn_device.h"
+#include "fibattn_mfma.h"
 
 namespace fibattn {
 
 namespace {
 
-constexpr int kNT = 256;                 // 4 waves x 16 positions x 4 lanes
-constexpr int kRowBytes = kD * 2;        // one fp16 row
-constexpr int kWinPad = 4;               // window slot of row i0 - W - 4 is 0: pads stay in range
-constexpr int kBlkSlots = 72;            // 65 (+2 for the second rung) rows, 9 DMA groups
-constexpr int kBcast0 = 0x00, kBcast1 = 0x55, kBcast2 = 0xAA, kBcast3 = 0xFF;   // quad_perm [r,r,r,r]
-constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, gfx9 family
+using namespace mx;
+
 // Workgroups per CU: LDS is 2 x 18 KB per workgroup, so four fit (1024 workgroups at the paper's
 // shape are one wave of the grid); the register budget this gives (128 per lane) must hold q,
 // the scores and the 64 output accumulators without spilling (a spill reload is a vector-memory
 // load and would wait behind every staging load in flight).
 constexpr int kWgsPerCu = 4;
 
-typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
-typedef float f4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f4_t c) {
-    return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(h4_t, (u2_t){a0, a1}),
-                                              __builtin_bit_cast(h4_t, (u2_t){b0, b1}), c, 0, 0, 0);
-}
-
-template <int CTRL> __device__ __forceinline__ float quad_f(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
-}
-
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-    const h2_t v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-// Two floats as bfloat16, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-    typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
-    typedef float fl2_t __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((fl2_t){lo, hi}, bf2_t));
-}
-
-__device__ __forceinline__ uint4 lds16(const char* lds, int addr) {
-    return *reinterpret_cast<const uint4*>(lds + addr);
-}
-
-// The chunk swizzle of slot s, as a byte offset to XOR into (logical chunk << 4).
-__device__ __forceinline__ int swz(int s) { return ((s >> 1) & 7) << 4; }
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// An LDS DMA destination passed through an opaque (uniform) value: the compiler then keeps no
-// record of which LDS array a DMA writes and adds no waits of its own before LDS reads;
-// publish<N> orders every read after the DMA it needs.
-__device__ __forceinline__ lds_ptr_t dma_dst(char* dst) {
-    uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)dst));
-    asm volatile("" : "+s"(a));   // an SGPR: the value is the same for the whole wave
-    return (lds_ptr_t)static_cast<uintptr_t>(a);
-}
-
-// Wait until at most N vector-memory instructions of this wave are in flight (its LDS DMAs up to
-// the block the next step reads have landed) and its LDS reads are done, then the workgroup
-// barrier. __syncthreads would also drain every staging load in flight.
-template <int N> __device__ __forceinline__ void publish() {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// QK of one group: lane x supplies the row at slot byte offset base (swizzle F = swz(slot)), q
-// supplies head x; returns the 4 scores of head x. Four accumulators keep the dependent chains
-// short (a 4x4x4 product's result is ready only some 40 cycles after issue).
-__device__ __forceinline__ f4_t qk_group(const uint32_t (&q)[8][4], const char* lds, int base, int F) {
-    f4_t a[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) a[u] = (f4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const uint4 k = lds16(lds, base | ((c << 4) ^ F));
-        a[(2 * c) & 3] = mfma4(k.x, k.y, q[c][0], q[c][1], a[(2 * c) & 3]);
-        a[(2 * c + 1) & 3] = mfma4(k.z, k.w, q[c][2], q[c][3], a[(2 * c + 1) & 3]);
-    }
-    return (a[0] + a[1]) + (a[2] + a[3]);
-}
-
-// PV of one group. The lane reads its assigned (position, slot) row, at slot byte offset base
-// with swizzle F, for dim blocks m = 0..15 (elements 4m..4m+3: byte 8m of the logical row). The
-// transposing read hands every lane the 4 rows at its own dim 16x + m; (w01, w23) are the lane's
-// head's weights, o[m] accumulates dim 16x + m of the 4 heads.
-__device__ __forceinline__ void pv_group(f4_t (&o)[16], uint32_t w01, uint32_t w23, const char* lds, int base, int F) {
-    typedef short s4_t __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s4_t* lds_s4_t;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int addr = (base | (((m >> 1) << 4) ^ F)) + 8 * (m & 1);
-        const s4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t)(lds + addr));
-        const u2_t vv = __builtin_bit_cast(u2_t, v);
-        o[m] = mfma4(w01, w23, vv.x, vv.y, o[m]);
-    }
-}
-
 // ------------------------------------------------------------------------------------------------
-// prep_kv16: rotated keys and values as fp16 rows, plus the cos/sin table of every position (for
-// the queries). Thread = (row, u): key pairs 4u..4u+3 and value row elements 8u..8u+7.
-// Value rows are stored with their dims permuted, element 4m + c holding dim 16c + m, so that a
-// transposing LDS read of 4 consecutive elements gives a lane 4 rows of one of its own dims.
+// prep_kv16: rotated keys and values as fp16 rows, plus the cos/sin table of every position. Thread
+// = (row, u). Two layouts, each the one its kernels read:
+//  * forward (KS = false): keys in dim order (thread u: RoPE pairs 4u..4u+3); values with their
+//    dims permuted, element 4m + c holding dim 16c + m (thread u: elements 8u..8u+7), so that a
+//    transposing LDS read of 4 consecutive elements gives a lane 4 rows of its own dims; the
+//    table times qscale.
+//  * backward (KS = true): keys permuted the same way (thread u: elements 8u..8u+7, dims
+//    16c + 2u and 16c + 2u + 1, which hold RoPE pairs 2u, 2u + 1, 16 + 2u, 17 + 2u whole); values
+//    in dim order; the table as is.
 // ------------------------------------------------------------------------------------------------
+template <bool KS>
 __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int u = static_cast<int>(gid & 7);
@@ -155,31 +73,63 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
     const int64_t row = row_id * kD;
     const bf16_t* ks = static_cast<const bf16_t*>(A.k);
     const bf16_t* vs = static_cast<const bf16_t*>(A.v);
-    const float4 x1 = load4<bf16_t>(ks + row + 4 * u);
-    const float4 x2 = load4<bf16_t>(ks + row + kPairs + 4 * u);
-    // elements 8u..8u+7 are dims 16c + 2u (c = 0..3), then 16c + 2u + 1
-    uint32_t vp[4];
+    const float sc = A.qscale;
+    if (!KS) {
+        const float4 x1 = load4<bf16_t>(ks + row + 4 * u);
+        const float4 x2 = load4<bf16_t>(ks + row + kPairs + 4 * u);
+        // elements 8u..8u+7 are dims 16c + 2u (c = 0..3), then 16c + 2u + 1
+        uint32_t vp[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) vp[c] = *reinterpret_cast<const uint32_t*>(vs + row + 16 * c + 2 * u);
-    const float a[4] = {x1.x, x1.y, x1.z, x1.w};
-    const float b[4] = {x2.x, x2.y, x2.z, x2.w};
-    float r1[4], r2[4];
-    float2 cs[4];
+        for (int c = 0; c < 4; ++c) vp[c] = *reinterpret_cast<const uint32_t*>(vs + row + 16 * c + 2 * u);
+        const float a[4] = {x1.x, x1.y, x1.z, x1.w};
+        const float b[4] = {x2.x, x2.y, x2.z, x2.w};
+        float r1[4], r2[4];
+        float2 cs[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        rope_cos_sin(j, A.fr.hi[4 * u + e], A.fr.lo[4 * u + e], cs[e].x, cs[e].y);
-        r1[e] = a[e] * cs[e].x - b[e] * cs[e].y;
-        r2[e] = b[e] * cs[e].x + a[e] * cs[e].y;
-    }
-    store4<f16_t>(A.k16 + row + 4 * u, make_float4(r1[0], r1[1], r1[2], r1[3]));
-    store4<f16_t>(A.k16 + row + kPairs + 4 * u, make_float4(r2[0], r2[1], r2[2], r2[3]));
-    store4<f16_t>(A.v16 + row + 8 * u, make_float4(bf16_lo(vp[0]), bf16_lo(vp[1]), bf16_lo(vp[2]), bf16_lo(vp[3])));
-    store4<f16_t>(A.v16 + row + 8 * u + 4, make_float4(bf16_hi(vp[0]), bf16_hi(vp[1]), bf16_hi(vp[2]), bf16_hi(vp[3])));
-    if (row_id < A.L) {   // the first (batch, head) writes the table: [L][32] (cos, sin) x qscale
-        const float sc = A.qscale;
-        float4* t = reinterpret_cast<float4*>(A.cs + (static_cast<int64_t>(j) * kPairs + 4 * u) * 2);
-        t[0] = make_float4(cs[0].x * sc, cs[0].y * sc, cs[1].x * sc, cs[1].y * sc);
-        t[1] = make_float4(cs[2].x * sc, cs[2].y * sc, cs[3].x * sc, cs[3].y * sc);
+        for (int e = 0; e < 4; ++e) {
+            rope_cos_sin(j, A.fr.hi[4 * u + e], A.fr.lo[4 * u + e], cs[e].x, cs[e].y);
+            r1[e] = a[e] * cs[e].x - b[e] * cs[e].y;
+            r2[e] = b[e] * cs[e].x + a[e] * cs[e].y;
+        }
+        store4<f16_t>(A.k16 + row + 4 * u, make_float4(r1[0], r1[1], r1[2], r1[3]));
+        store4<f16_t>(A.k16 + row + kPairs + 4 * u, make_float4(r2[0], r2[1], r2[2], r2[3]));
+        store4<f16_t>(A.v16 + row + 8 * u, make_float4(bf16_lo(vp[0]), bf16_lo(vp[1]), bf16_lo(vp[2]), bf16_lo(vp[3])));
+        store4<f16_t>(A.v16 + row + 8 * u + 4, make_float4(bf16_hi(vp[0]), bf16_hi(vp[1]), bf16_hi(vp[2]), bf16_hi(vp[3])));
+        if (row_id < A.L) {   // the first (batch, head) writes the table: [L][32] (cos, sin) x qscale
+            float4* t = reinterpret_cast<float4*>(A.cs + (static_cast<int64_t>(j) * kPairs + 4 * u) * 2);
+            t[0] = make_float4(cs[0].x * sc, cs[0].y * sc, cs[1].x * sc, cs[1].y * sc);
+            t[1] = make_float4(cs[2].x * sc, cs[2].y * sc, cs[3].x * sc, cs[3].y * sc);
+        }
+    } else {
+        // key dims 16c + 2u, 16c + 2u + 1 for c = 0..3: pairs p0 = 2u, p0 + 1 (x: c = 0, y: c = 2)
+        // and p1 = 16 + 2u, p1 + 1 (x: c = 1, y: c = 3)
+        uint32_t kp[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kp[c] = *reinterpret_cast<const uint32_t*>(ks + row + 16 * c + 2 * u);
+        const int pr[4] = {2 * u, 2 * u + 1, 16 + 2 * u, 17 + 2 * u};
+        float2 cs[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rope_cos_sin(j, A.fr.hi[pr[e]], A.fr.lo[pr[e]], cs[e].x, cs[e].y);
+        // x, y of each pair
+        const float x[4] = {bf16_lo(kp[0]), bf16_hi(kp[0]), bf16_lo(kp[1]), bf16_hi(kp[1])};
+        const float y[4] = {bf16_lo(kp[2]), bf16_hi(kp[2]), bf16_lo(kp[3]), bf16_hi(kp[3])};
+        float rx[4], ry[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            rx[e] = x[e] * cs[e].x - y[e] * cs[e].y;
+            ry[e] = y[e] * cs[e].x + x[e] * cs[e].y;
+        }
+        // element 8u + e: e < 4 is dim 16e + 2u, e >= 4 is dim 16(e - 4) + 2u + 1
+        store4<f16_t>(A.k16 + row + 8 * u, make_float4(rx[0], rx[2], ry[0], ry[2]));
+        store4<f16_t>(A.k16 + row + 8 * u + 4, make_float4(rx[1], rx[3], ry[1], ry[3]));
+        const uint4 vw = *reinterpret_cast<const uint4*>(vs + row + 8 * u);
+        store4<f16_t>(A.v16 + row + 8 * u, make_float4(bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y)));
+        store4<f16_t>(A.v16 + row + 8 * u + 4, make_float4(bf16_lo(vw.z), bf16_hi(vw.z), bf16_lo(vw.w), bf16_hi(vw.w)));
+        if (row_id < A.L) {   // the table: pairs 2u, 2u + 1 and 16 + 2u, 17 + 2u
+            float4* t = reinterpret_cast<float4*>(A.cs + static_cast<int64_t>(j) * kPairs * 2);
+            t[u] = make_float4(cs[0].x * sc, cs[0].y * sc, cs[1].x * sc, cs[1].y * sc);
+            t[8 + u] = make_float4(cs[2].x * sc, cs[2].y * sc, cs[3].x * sc, cs[3].y * sc);
+        }
     }
 }
 
@@ -189,10 +139,7 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
 template <int MAXS>
 __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     constexpr float kNegInf = -__builtin_huge_valf();
-    constexpr int kWG = 4;                              // window groups (W <= 15)
     constexpr int MAXK = 2 * MAXS;
-    constexpr int kBlkBytes = kBlkSlots * kRowBytes;
-    constexpr int kBufBytes = 2 * kBlkBytes;
     // Two staging buffers used in turn. An item is the key window, a step of two key rungs, the
     // value window or a step of two value rungs: item j sits in buffer j % 2. A rung step holds
     // rung 2k at slot 0 (block A) and rung 2k + 1 at slot kBlkSlots (block B); a window holds
@@ -208,19 +155,8 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     const int L = A.L, W = A.W;
     const int n_tiles = (L + kTile - 1) / kTile;
     const int n_chunk = A.G >> 2;
-    // workgroup -> (unit, tile); with the XCD map, unit u runs on XCD u % 8 for all its tiles
     int unit, tile;
-    {
-        const int w = blockIdx.x;
-        if (A.xcd_map) {
-            const int sl = w >> 3;
-            unit = (sl / n_tiles) * 8 + (w & 7);
-            tile = sl % n_tiles;
-        } else {
-            unit = w / n_tiles;
-            tile = w % n_tiles;
-        }
-    }
+    unit_tile(blockIdx.x, n_tiles, A.xcd_map, unit, tile);
     const int chunk = unit % n_chunk;
     const int bg = unit / n_chunk;                      // b * Hkv + g
     const int b = bg / A.Hkv;
@@ -235,58 +171,21 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
         if (i0 + kTile - 1 >= A.off[n].a + A.off[n].interp) n_reach = n + 1;
     const int n_steps = (n_reach + 1) >> 1;
 
-    // ---- staging: LDS DMA of one (batch, kv head). A 16-byte wave instruction fills 1 KB = 8
-    // slots: lane l lands on slot 8g + (l >> 3), physical chunk l & 7, and fetches that slot's row
-    // and the logical chunk the swizzle puts there. A 4-byte instruction fills 2 slots: lane l
-    // lands on slot 2g' + (l >> 5), physical dword l & 31. Every wave issues 3 instructions per
-    // block or window.
     const int64_t kv_row0 = static_cast<int64_t>(bg) * L;
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(static_cast<const char*>(A.kstage) + kv_row0 * kRowBytes), 0, L * kRowBytes, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(static_cast<const char*>(A.vstage) + kv_row0 * kRowBytes), 0, L * kRowBytes, kRsrcWord3);
-    // 16-byte part: slot 8g + lrow has swizzle (4 (g & 1) + (lrow >> 1)) & 7, per parity of g
-    const int lrow = lane >> 3;
-    const int voff16[2] = {lrow * kRowBytes + (((lane & 7) ^ (lrow >> 1)) << 4),
-                           lrow * kRowBytes + (((lane & 7) ^ (4 + (lrow >> 1))) << 4)};
-    // 4-byte part: slot 64 + 2 wave + (lane >> 5) (block B: 72 more) has swizzle wave (4 + wave)
-    const int dw = lane & 31;
-    const int voff4[2] = {(lane >> 5) * kRowBytes + (((dw >> 2) ^ wave) << 4) + ((dw & 3) << 2),
-                          (lane >> 5) * kRowBytes + (((dw >> 2) ^ (4 + wave)) << 4) + ((dw & 3) << 2)};
-    const int gpar = wave & 1;                          // parity of this wave's groups in block A
-    auto dma16 = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int row0, int par) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dma_dst(dst), 16, row0 * kRowBytes + voff16[par], 0, 0, 0);
+    const __amdgpu_buffer_rsrc_t krs = rows_rsrc(A.kstage, kv_row0, L);
+    const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(A.vstage, kv_row0, L);
+    Stager st;
+    st.init(lane, wave);
+    // rung step k: rungs 2k and 2k + 1 (zeros past the reach); the far row of position p sits at
+    // slot p (block A) or 72 + p + 2 (block B), the near row one slot up
+    auto step = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int k) {
+        st.step(rs, dst, 2 * k < n_reach, i0 - A.off[2 * k].a - 1, 2 * k + 1 < n_reach, i0 - A.off[2 * k + 1].a - 3);
     };
-    auto dma4 = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int row0, int blk) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dma_dst(dst), 4, row0 * kRowBytes + voff4[blk], 0, 0, 0);
-    };
+    const int jw = i0 - W - kWinPad;                    // the window's row at slot 0
     auto buf = [&](int j) -> char* { return (j & 1) ? lds1 : lds0; };
-    // window: rows i0 - W - 4 + s at slot s, s < 96 (12 groups, 3 per wave)
-    auto stage_window = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst) {
-        const int j0 = i0 - W - kWinPad;
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            const int g = wave + 4 * u;
-            dma16(rs, dst + g * 1024, j0 + 8 * g, gpar);
-        }
-    };
-    // block of rung n (blk 0: A, 1: B two slots up): far row of position p at slot p + 2 blk, near
-    // row at p + 2 blk + 1; 72 slots: two 16-byte groups and one 4-byte pair per wave (block B
-    // starts at slot 72 = 9 groups: its groups have the other parity). Rungs past the reach
-    // stage rows before 0: zeros.
-    auto stage_rung = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int n, int blk) {
-        const int j0 = (n < n_reach) ? i0 - A.off[n].a - 1 - 2 * blk : -(kTile + kBlkSlots + 8);
-        dma16(rs, dst + wave * 1024, j0 + 8 * wave, gpar ^ blk);
-        dma16(rs, dst + (wave + 4) * 1024, j0 + 8 * (wave + 4), gpar ^ blk);
-        dma4(rs, dst + 64 * kRowBytes + wave * 256, j0 + 64 + 2 * wave, blk);
-    };
-    auto stage_step = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int k) {
-        stage_rung(rs, dst, 2 * k, 0);
-        stage_rung(rs, dst + kBlkBytes, 2 * k + 1, 1);
-    };
 
     // ---- prologue: key window (item 0), q, item 1 (key step 0, or the value window) ----
-    stage_window(krs, buf(0));
+    st.window(krs, buf(0), jw);
     uint4 qraw[8];
     float4 ctab[16];
     {
@@ -298,7 +197,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) ctab[u] = ct[u];
     }
-    stage_step(krs, buf(1), 0);                         // (zero rows when no rung is reached)
+    step(krs, buf(1), 0);                         // (zero rows when no rung is reached)
 
     // q of head h0 + x, rotated at its position and scaled (the table carries qscale), fp16:
     // register chunk c holds dims 8c..8c+7; RoPE pairs 8c..8c+7 are chunks c and c + 4
@@ -330,7 +229,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
 #pragma unroll
         for (int g = 0; g < kWG; ++g) {
             f4_t acc = {0.f, 0.f, 0.f, 0.f};
-            if (4 * g <= W) acc = qk_group(q, buf(0), (s0 - 4 * g) * kRowBytes, swz(s0 - 4 * g));
+            if (4 * g <= W) acc = row_dot_group(q, buf(0), (s0 - 4 * g) * kRowBytes, swz(s0 - 4 * g));
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int d = 4 * g + r;
@@ -347,8 +246,8 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
         s[4 * kWG + 2 * k] = kNegInf;
         s[4 * kWG + 2 * k + 1] = kNegInf;
         if (k < n_steps) {                              // item k + 1, in buffer (k + 1) % 2
-            if (k + 1 < n_steps) stage_step(krs, buf(k + 2), k + 1);
-            const f4_t acc = qk_group(q, buf(k + 1), rbase, rsw);
+            if (k + 1 < n_steps) step(krs, buf(k + 2), k + 1);
+            const f4_t acc = row_dot_group(q, buf(k + 1), rbase, rsw);
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int n = 2 * k + e;
@@ -363,8 +262,8 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
 
     // ---- value window into buffer 0 and value step 0 into buffer 1 (both free after the last
     // barrier), under the softmax ----
-    stage_window(vrs, lds0);
-    stage_step(vrs, lds1, 0);
+    st.window(vrs, lds0, jw);
+    step(vrs, lds1, 0);
 
     // ---- exact softmax; weights as fp16 groups of 4 ----
     float m = kNegInf;
@@ -415,7 +314,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
         const int sv = pt - kt + W + kWinPad;
 #pragma unroll
         for (int g = 0; g < kWG; ++g)
-            if (4 * g <= W) pv_group(o, pw[g][0], pw[g][1], lds0, (sv - 4 * g) * kRowBytes, swz(sv - 4 * g));
+            if (4 * g <= W) row_sum_group(o, pw[g][0], pw[g][1], lds0, (sv - 4 * g) * kRowBytes, swz(sv - 4 * g));
         if (n_steps > 0) publish<0>();                  // value step 0 has landed, buffer 0 is free
     }
     {
@@ -426,8 +325,8 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
 #pragma unroll
         for (int k = 0; k < MAXS; ++k) {
             if (k < n_steps) {
-                if (k + 1 < n_steps) stage_step(vrs, buf(k + 2), k + 1);
-                pv_group(o, po[k][0], po[k][1], buf(k + 1), vbase, vsw);
+                if (k + 1 < n_steps) step(vrs, buf(k + 2), k + 1);
+                row_sum_group(o, po[k][0], po[k][1], buf(k + 1), vbase, vsw);
                 if (k + 1 < n_steps) publish<0>();
             }
         }
@@ -463,10 +362,13 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
 
 }  // namespace
 
-hipError_t launch_prep_kv16(const PrepArgs& A, hipStream_t s) {
+hipError_t launch_prep_kv16(const PrepArgs& A, bool backward_layout, hipStream_t s) {
     const int64_t threads = static_cast<int64_t>(A.n_bh) * A.L * 8;
     const unsigned blocks = static_cast<unsigned>((threads + 255) / 256);
-    hipLaunchKernelGGL(prep_kv16_kernel, dim3(blocks), dim3(256), 0, s, A);
+    if (backward_layout)
+        hipLaunchKernelGGL(prep_kv16_kernel<true>, dim3(blocks), dim3(256), 0, s, A);
+    else
+        hipLaunchKernelGGL(prep_kv16_kernel<false>, dim3(blocks), dim3(256), 0, s, A);
     return hipGetLastError();
 }
 

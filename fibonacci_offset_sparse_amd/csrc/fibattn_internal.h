@@ -40,7 +40,7 @@ struct PrepArgs {
     const void* k;       // [B*Hkv, L, 64] bf16
     const void* v;       // [B*Hkv, L, 64] bf16
     _Float16* k16;       // [B*Hkv, L, 64] rotated keys
-    _Float16* v16;       // [B*Hkv, L, 64] values, element 4m + c of a row holding dim 16c + m
+    _Float16* v16;       // [B*Hkv, L, 64] values
     float* cs;           // [L, 32, 2] cos and sin of every position and RoPE pair, times qscale
     int32_t n_bh;
     int32_t L;
@@ -86,14 +86,33 @@ struct BwdArgs {
     float dalpha_dtheta;
     RopeFreq fr;
     OffsetSlot off[kMaxOff];
+    // matrix-core path (bfloat16 storage): staged rows from prep_kv16's backward layout, and what
+    // the query-side kernel hands the key-side kernel
+    const void* kstage;  // [B*Hkv, L, 64] fp16 rotated keys, dims permuted
+    const void* vstage;  // [B*Hkv, L, 64] fp16 values
+    const float* cstab;  // [L, 32, 2] cos, sin
+    void* qrot16;        // [B, Hq, L, 64] fp16 rotated queries, dims permuted
+    void* do16;          // [B, Hq, L, 64] fp16 copy of dout (dim order)
+    uint32_t* wts;       // [B, Hq, L, kNV] per key row and term: fp16 p (low), fp16 dS/sqrt(D) (high)
+    float qscale;        // log2(e)/sqrt(D)
+    int32_t xcd_map;
 };
 
+// Terms per key row in the weight table of the matrix-core backward: 16 window distances, then
+// (near, far) of 16 rungs.
+constexpr int kNV = 48;
+
 hipError_t launch_rope_keys(int dtype, const RopeKeysArgs& a, hipStream_t s);
-hipError_t launch_prep_kv16(const PrepArgs& a, hipStream_t s);
+// forward layout: keys in dim order, values permuted, table x qscale; backward layout: keys
+// permuted, values in dim order (element 4m + c of a permuted row holds dim 16c + m)
+hipError_t launch_prep_kv16(const PrepArgs& a, bool backward_layout, hipStream_t s);
 hipError_t launch_fwd_attend(int dtype, const FwdArgs& a, hipStream_t s);
 bool fwd_mfma_supported(const FwdArgs& a);
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd(int dtype, const BwdArgs& a, bool want_dalpha, hipStream_t s);
+bool bwd_mfma_supported(const BwdArgs& a);
+hipError_t launch_bwd_mfma(const BwdArgs& a, bool want_dalpha, hipStream_t s);
+hipError_t launch_dalpha(const BwdArgs& a, hipStream_t s);
 int bwd_query_workgroups(int B, int L, int Hkv, int G);
 
 }  // namespace fibattn

@@ -1,0 +1,204 @@
+// Matrix-core building blocks shared by the gfx950 forward and backward kernels for bfloat16
+// storage: 4x4x4 fp16 MFMA groups, the LDS slot swizzle, the transposing LDS read, LDS DMA staging
+// of shifted row blocks with counted waits. Included by the .hip files only.
+//
+// Layout conventions (section references: "Depth-Staggered Fibonacci Spacing for Sparse
+// Attention", §2 "Attended set"):
+//  * A workgroup owns 64 consecutive positions of one (batch, key-value head) and 4 query heads;
+//    wave w takes positions 16w..16w+15, lane 4p' + x is position p' of the wave and head (or
+//    slot, or dim column) x. v_mfma_f32_4x4x4_16b_f16 computes one 4x4x4 block per position:
+//    lane 4p' + x is row x of A and column x of B and of the result, of block p'.
+//  * A group is 4 virtual slots: 4 window distances, or (near, far) of two consecutive rungs. An
+//    interpolated rung reads two rows, nearer (coefficient 1 - t) and farther (t); scores and
+//    outputs are linear in the blended row.
+//  * LDS slots are 128-byte fp16 rows; 16-byte chunk k of slot s sits at chunk k ^ ((s >> 1) & 7).
+//    A rung step holds rung 2k at slot 0 (block A) and rung 2k + 1 at slot kBlkSlots (block B,
+//    two slots up); a window holds rows i0 - W - 4 + s at slot s.
+#pragma once
+
+#include "fibattn_device.h"
+
+namespace fibattn {
+namespace mx {
+
+constexpr int kNT = 256;                 // 4 waves x 16 positions x 4 lanes
+constexpr int kRowBytes = kD * 2;        // one fp16 row
+constexpr int kWinPad = 4;               // window slot of row i0 - W - 4 is 0: pads stay in range
+constexpr int kBlkSlots = 72;            // 65 (+2 for the second rung) rows, 9 DMA groups
+constexpr int kBlkBytes = kBlkSlots * kRowBytes;
+constexpr int kBufBytes = 2 * kBlkBytes; // one staging buffer: a window or a rung step
+constexpr int kWG = 4;                   // window groups (W <= 15)
+constexpr int kBcast0 = 0x00, kBcast1 = 0x55, kBcast2 = 0xAA, kBcast3 = 0xFF;   // quad_perm [r,r,r,r]
+constexpr int kXor2 = 0x4E;              // quad_perm [2,3,0,1]: lane x ^ 2
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, gfx9 family
+
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ f4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(h4_t, (u2_t){a0, a1}),
+                                              __builtin_bit_cast(h4_t, (u2_t){b0, b1}), c, 0, 0, 0);
+}
+
+template <int CTRL> __device__ __forceinline__ float quad_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+    const h2_t v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two floats as bfloat16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+    typedef float fl2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((fl2_t){lo, hi}, bf2_t));
+}
+
+__device__ __forceinline__ uint4 lds16(const char* lds, int addr) {
+    return *reinterpret_cast<const uint4*>(lds + addr);
+}
+
+// The chunk swizzle of slot s, as a byte offset to XOR into (logical chunk << 4).
+__device__ __forceinline__ int swz(int s) { return ((s >> 1) & 7) << 4; }
+
+// An LDS DMA destination passed through an opaque (uniform) value: the compiler then keeps no
+// record of which LDS array a DMA writes and adds no waits of its own before LDS reads;
+// publish<N> orders every read after the DMA it needs.
+__device__ __forceinline__ lds_ptr_t dma_dst(char* dst) {
+    uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)dst));
+    asm volatile("" : "+s"(a));   // an SGPR: the value is the same for the whole wave
+    return (lds_ptr_t)static_cast<uintptr_t>(a);
+}
+
+// Wait until at most N vector-memory instructions of this wave are in flight (its LDS DMAs up to
+// the block the next step reads have landed) and its LDS reads are done, then the workgroup
+// barrier. __syncthreads would also drain every staging load in flight.
+template <int N> __device__ __forceinline__ void publish() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Product of one group with a per-head operand x held in registers (register chunk c = elements
+// 8c..8c+7 of the staged row order): lane x supplies the row at slot byte offset base (swizzle
+// F = swz(slot)), x supplies head x; returns head x's 4 products. Four accumulators keep the
+// dependent chains short.
+__device__ __forceinline__ f4_t row_dot_group(const uint32_t (&x)[8][4], const char* lds, int base, int F) {
+    f4_t a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] = (f4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint4 k = lds16(lds, base | ((c << 4) ^ F));
+        a[(2 * c) & 3] = mfma4(k.x, k.y, x[c][0], x[c][1], a[(2 * c) & 3]);
+        a[(2 * c + 1) & 3] = mfma4(k.z, k.w, x[c][2], x[c][3], a[(2 * c + 1) & 3]);
+    }
+    return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
+// ds_read_b64_tr_b16 at lds + addr: 4 fp16 (or bf16) elements, as a whole. (Splitting the result
+// into its two dwords is left to the callers that need it: an optimisation has been seen to fold
+// the second dword of this builtin's result onto the first.)
+__device__ __forceinline__ h4_t tr_read_h4(const char* lds, int addr) {
+    typedef short s4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4_t* lds_s4_t;
+    return __builtin_bit_cast(h4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_t)(lds + addr)));
+}
+
+// Weighted sum of one group's rows. The lane reads its assigned (position, slot) row, at slot
+// byte offset base with swizzle F, for element blocks m = 0..15 (elements 4m..4m+3: byte 8m of
+// the staged row). ds_read_b64_tr_b16 transposes within each 16 lanes and hands every lane the 4
+// rows' element 4m + x; (w01, w23) are the lane's head's weights, o[m] accumulates element
+// 4m + x of the 4 heads.
+__device__ __forceinline__ void row_sum_group(f4_t (&o)[16], uint32_t w01, uint32_t w23, const char* lds, int base,
+                                              int F) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int addr = (base | (((m >> 1) << 4) ^ F)) + 8 * (m & 1);
+        o[m] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(h4_t, (u2_t){w01, w23}), tr_read_h4(lds, addr), o[m],
+                                                  0, 0, 0);
+    }
+}
+
+// LDS DMA staging of one (batch, kv head)'s fp16 rows. A 16-byte wave instruction fills 1 KB = 8
+// slots: lane l lands on slot 8g + (l >> 3), physical chunk l & 7, and fetches that slot's row and
+// the logical chunk the swizzle puts there. A 4-byte instruction fills 2 slots: lane l lands on
+// slot 2g' + (l >> 5), physical dword l & 31. Every wave issues 3 instructions per window or rung
+// block, so the waits can count them. Rows before 0 or past L fall outside the buffer resource
+// and arrive as zeros.
+// Blocks are given by the row that lands at slot 0. (Rows are passed by value: taking the address
+// of the kernel's argument struct would make the compiler copy it to scratch memory.)
+struct Stager {
+    int wave, gpar;
+    int voff16_0, voff16_1, voff4_0, voff4_1;   // per swizzle parity / block (no indexed arrays:
+                                                // those would put the struct in scratch memory)
+
+    __device__ __forceinline__ void init(int lane, int wave_) {
+        wave = wave_;
+        gpar = wave & 1;                                // parity of this wave's groups in block A
+        // 16-byte part: slot 8g + lrow has swizzle (4 (g & 1) + (lrow >> 1)) & 7, per parity of g
+        const int lrow = lane >> 3;
+        voff16_0 = lrow * kRowBytes + (((lane & 7) ^ (lrow >> 1)) << 4);
+        voff16_1 = lrow * kRowBytes + (((lane & 7) ^ (4 + (lrow >> 1))) << 4);
+        // 4-byte part: slot 64 + 2 wave + (lane >> 5) (block B: 72 more) has swizzle wave (4 + wave)
+        const int dw = lane & 31;
+        voff4_0 = (lane >> 5) * kRowBytes + (((dw >> 2) ^ wave) << 4) + ((dw & 3) << 2);
+        voff4_1 = (lane >> 5) * kRowBytes + (((dw >> 2) ^ (4 + wave)) << 4) + ((dw & 3) << 2);
+    }
+    __device__ __forceinline__ void dma16(const __amdgpu_buffer_rsrc_t& rs, char* dst, int row0, int par) const {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dma_dst(dst), 16, row0 * kRowBytes + (par ? voff16_1 : voff16_0), 0, 0, 0);
+    }
+    __device__ __forceinline__ void dma4(const __amdgpu_buffer_rsrc_t& rs, char* dst, int row0, int blk) const {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dma_dst(dst), 4, row0 * kRowBytes + (blk ? voff4_1 : voff4_0), 0, 0, 0);
+    }
+    // window: rows j0 + s at slot s, s < 96 (12 groups, 3 per wave)
+    __device__ __forceinline__ void window(const __amdgpu_buffer_rsrc_t& rs, char* dst, int j0) const {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int g = wave + 4 * u;
+            dma16(rs, dst + g * 1024, j0 + 8 * g, gpar);
+        }
+    }
+    // rung block blk (0: A, 1: B at slot 72): rows j0 + s at slot s < 72; two 16-byte groups and
+    // one 4-byte pair per wave (block B starts at slot 72 = 9 groups: its groups have the other
+    // parity). A block that is not real stages rows before 0: zeros.
+    __device__ __forceinline__ void rung(const __amdgpu_buffer_rsrc_t& rs, char* dst, bool real, int j0_real,
+                                         int blk) const {
+        const int j0 = real ? j0_real : -(kTile + kBlkSlots + 8);
+        dma16(rs, dst + wave * 1024, j0 + 8 * wave, gpar ^ blk);
+        dma16(rs, dst + (wave + 4) * 1024, j0 + 8 * (wave + 4), gpar ^ blk);
+        dma4(rs, dst + 64 * kRowBytes + wave * 256, j0 + 64 + 2 * wave, blk);
+    }
+    // a rung step: block A from row j0a, block B from row j0b
+    __device__ __forceinline__ void step(const __amdgpu_buffer_rsrc_t& rs, char* dst, bool r0, int j0a, bool r1,
+                                         int j0b) const {
+        rung(rs, dst, r0, j0a, 0);
+        rung(rs, dst + kBlkBytes, r1, j0b, 1);
+    }
+};
+
+// Buffer resource over rows [row0, row0 + L) of 128-byte rows.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int64_t row0, int L) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base) + row0 * kRowBytes), 0,
+                                             L * kRowBytes, kRsrcWord3);
+}
+
+// Workgroup -> (unit, tile): with the XCD map, unit u runs on XCD u % 8 for all its tiles, whose
+// L2 then holds that unit's keys and values for every tile that re-reads them.
+__device__ __forceinline__ void unit_tile(int w, int n_tiles, int xcd_map, int& unit, int& tile) {
+    if (xcd_map) {
+        const int sl = w >> 3;
+        unit = (sl / n_tiles) * 8 + (w & 7);
+        tile = sl % n_tiles;
+    } else {
+        unit = w / n_tiles;
+        tile = w % n_tiles;
+    }
+}
+
+}  // namespace mx
+}  // namespace fibattn

