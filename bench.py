@@ -31,6 +31,10 @@ import torch  # noqa: E402
 import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, 8 TB/s
+# HBM bytes per launch measured with FETCH_SIZE / WRITE_SIZE (calibrated on a plain copy), with the
+# hash of the sources each kernel was built from: a figure is used only while the sources match
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_bytes_l1024_linear.json")
+TRAFFIC_WORKLOAD = "l1024_linear_bf16"
 FP32_VALU_PEAK_TFLOPS = 78.6    # 256 CU x 2.4 GHz x 64 lanes x 2 (FMA), scalar fp32 (no packed ops)
 
 
@@ -41,6 +45,13 @@ def log(*a):
 # ------------------------------------------------------------------------------------------------
 # CPU baseline: the float64 oracle as it stands, on the host's cores, on a bounded sample.
 # ------------------------------------------------------------------------------------------------
+
+def _one_thread():
+    # one thread per worker process: the pool's size is the core count
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+    torch.set_num_threads(1)
+
 
 def _oracle_unit(args):
     name, layer, b = args
@@ -66,7 +77,7 @@ def cpu_baseline(name: str, budget_s: float = 15.0):
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
     done = 0
-    with ctx.Pool(workers) as pool:
+    with ctx.Pool(workers, initializer=_one_thread) as pool:
         it = pool.imap_unordered(_oracle_unit, units)
         for _ in it:
             done += 1
@@ -86,8 +97,26 @@ def cpu_baseline(name: str, budget_s: float = 15.0):
     return {
         "value": qh / wall, "unit": "queries*heads/s (fwd+bwd)", "cores": workers, "kind": "oracle",
         "sample": f"{done} (layer, batch element 0) units of {name}, each a float64 forward + backward at "
-                  f"B=1, L={w.L}, {wall:.1f} s wall on {workers} worker processes ({cpu}, {platform.machine()})",
+                  f"B=1, L={w.L}, {wall:.1f} s wall on {workers} single-threaded worker processes ({cpu}, "
+                  f"{platform.machine()})",
     }
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when it was taken
+    on another workload or the kernel's sources have changed since."""
+    import hashlib
+    if workload != TRAFFIC_WORKLOAD or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        entry = json.load(f)["kernels"].get(kernel)
+    if entry is None:
+        return None
+    h = hashlib.sha256()
+    for fn in entry["sources"]:
+        with open(os.path.join(ROOT, "fibonacci_offset_sparse_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return entry["bytes_per_launch"] if h.hexdigest() == entry["sources_sha256"] else None
 
 
 # ------------------------------------------------------------------------------------------------
@@ -97,8 +126,9 @@ def cpu_baseline(name: str, budget_s: float = 15.0):
 class Layers:
     """Per-layer inputs, outputs and shared workspaces for one workload, resident on the GPU."""
 
-    def __init__(self, fa, w, dev):
+    def __init__(self, fa, w, dev, n_sets=None):
         self.fa, self.w, self.dev = fa, w, dev
+        self.n_sets = w.n_layers if n_sets is None else n_sets
         base = fa.fibattn_base_offsets(fa.BASE_FIB if w.base == "fib" else fa.BASE_POW2, 1024)
         self.base = base
         code = {"fixed": fa.SCHEDULE_FIXED, "linear": fa.SCHEDULE_LINEAR, "coprime": fa.SCHEDULE_COPRIME}
@@ -118,13 +148,18 @@ class Layers:
             kind = fa.fibattn_plan(a, w.W, base)[0]
             self.want_dalpha.append(w.schedule == "learned" and bool((kind == fa.INTERP).all()))
         self.inputs = []
-        for layer in range(w.n_layers):
+        for layer in range(self.n_sets):
             q, k, v, do = workloads.draw(w, layer, with_grad=True)
             self.inputs.append(tuple(x.to(dev) for x in (q, k, v, do)))
             log(f"  inputs of layer {layer} resident")
         B, L, Hq, Hkv, D = w.B, w.L, w.Hq, w.Hkv, w.D
-        self.o = [torch.empty(B, Hq, L, D, dtype=w.torch_dtype, device=dev) for _ in range(w.n_layers)]
-        self.lse = [torch.empty(B, Hq, L, dtype=torch.float32, device=dev) for _ in range(w.n_layers)]
+        self.o = [torch.empty(B, Hq, L, D, dtype=w.torch_dtype, device=dev) for _ in range(self.n_sets)]
+        self.lse = [torch.empty(B, Hq, L, dtype=torch.float32, device=dev) for _ in range(self.n_sets)]
+        self.dq = [torch.empty(B, Hq, L, D, dtype=w.torch_dtype, device=dev) for _ in range(self.n_sets)]
+        self.dk = [torch.empty(B, Hkv, L, D, dtype=w.torch_dtype, device=dev) for _ in range(self.n_sets)]
+        self.dv = [torch.empty(B, Hkv, L, D, dtype=w.torch_dtype, device=dev) for _ in range(self.n_sets)]
+        self.dalpha = torch.empty(1, dtype=torch.float32, device=dev)
+        self.dtheta = torch.empty(1, dtype=torch.float32, device=dev)
         self.ws_f = torch.empty(fa.fibattn_fwd_workspace_bytes(B, L, Hkv), dtype=torch.uint8, device=dev)
         self.ws_b = torch.empty(fa.fibattn_bwd_workspace_bytes(B, L, Hq, Hkv, D, w.W, len(base)),
                                 dtype=torch.uint8, device=dev)
@@ -142,16 +177,45 @@ class Layers:
         self.fa.fibattn_fwd_attend(q, v, self.alphas[layer], self.w.W, self.base, self.ws_f, self.o[layer],
                                    self.lse[layer])
 
-    def bwd(self, layer):
+    def bwd_stages(self, layer, stages):
         q, k, v, do = self.inputs[layer]
-        return self.fa.fibattn_bwd(q, k, v, self.o[layer], self.lse[layer], do, self.alphas[layer], self.w.W,
-                                   self.base, dalpha_dtheta=self.dadt[layer],
-                                   want_dalpha=self.want_dalpha[layer], workspace=self.ws_b)
+        wd = self.want_dalpha[layer]
+        self.fa.fibattn_bwd_stages(stages, q, k, v, do, self.alphas[layer], self.w.W, self.base, self.dq[layer],
+                                   self.dk[layer], self.dv[layer], self.ws_b, dalpha_dtheta=self.dadt[layer],
+                                   dalpha=self.dalpha if wd else None, dtheta=self.dtheta if wd else None)
+
+    def bwd(self, layer):
+        self.bwd_stages(layer, self.fa.STAGE_ALL)
+
+    def bwd_prep(self, layer):
+        self.bwd_stages(layer, self.fa.STAGE_PREP)
+
+    def bwd_query(self, layer):
+        self.bwd_stages(layer, self.fa.STAGE_QUERY)
+
+    def bwd_key(self, layer):
+        self.bwd_stages(layer, self.fa.STAGE_KEY)
 
     def step(self):
-        for layer in range(self.w.n_layers):
+        for layer in range(self.n_sets):
             self.fwd(layer)
             self.bwd(layer)
+
+
+def profile_pass(fa, name: str, dev):
+    """A short program for hardware-counter runs: two layers of the workload, two forward + backward
+    passes over them, then a plain 256 MiB device-to-device copy (torch's copy kernel) whose byte
+    counters calibrate the kernels' (it reads and writes exactly 2^28 bytes)."""
+    w = workloads.WORKLOADS[name]
+    net = Layers(fa, w, dev, n_sets=2)
+    for _ in range(2):
+        net.step()
+    src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[{name}] profile pass done")
 
 
 def time_steps(net: Layers, steps: int, warmup: int):
@@ -173,10 +237,12 @@ def time_stages(net: Layers, sweeps: int):
     """Average duration of each stage, from HIP events on the stream the kernels run on.
 
     Each stage is launched for all layers back to back behind a short GPU spin, so the launches
-    are queued before the GPU reaches them and the events see kernel time, not host gaps. The
-    forward stages run on whichever layer's keys the shared workspace holds last (same work)."""
+    are queued before the GPU reaches them and the events see kernel time, not host gaps. A later
+    stage reads what the earlier one left in the shared workspace, from the last layer it ran on
+    (the same work: the workspace holds values only, its layout does not depend on the layer)."""
     n = net.w.n_layers
-    stages = {"fwd_prep": net.prep, "fwd_attend": net.attend, "bwd": net.bwd}
+    stages = {"fwd_prep": net.prep, "fwd_attend": net.attend, "bwd": net.bwd, "bwd_prep": net.bwd_prep,
+              "bwd_query": net.bwd_query, "bwd_key": net.bwd_key}
     tot = {k: 0.0 for k in stages}
     for _ in range(sweeps):
         for name, fn in stages.items():
@@ -202,9 +268,16 @@ def measure(fa, name: str, steps: int, warmup: int, dev):
     st = time_stages(net, 3)
     qh = w.B * w.L * w.Hq
     eb = 2 if w.dtype == "bf16" else 4
-    fwd_bytes = (2 * w.Hq + 2 * w.Hkv) * w.B * w.L * w.D * eb + qh * 4           # q, k, v, o, lse
-    bwd_bytes = (3 * w.Hq + 2 * w.Hkv) * w.B * w.L * w.D * eb + qh * 4 \
-        + (w.Hq + 2 * w.Hkv) * w.B * w.L * w.D * eb                            # + dq, dk, dv
+    rows = w.B * w.L * w.D * eb                                                # one head's rows
+    fwd_bytes = (2 * w.Hq + 2 * w.Hkv) * rows + qh * 4                          # q, k, v, o, lse
+    bwd_bytes = (3 * w.Hq + 2 * w.Hkv) * rows + qh * 4 \
+        + (w.Hq + 2 * w.Hkv) * rows                                            # + dq, dk, dv
+    # per kernel: the caller's tensors each one reads or writes (workspace hand-offs excluded)
+    kernel_bytes = {
+        "fwd_attend": fwd_bytes,                                                # q, k, v (staged), o, lse
+        "bwd_query": (3 * w.Hq + 2 * w.Hkv) * rows,                             # q, dout, k, v; dq
+        "bwd_key": (2 * w.Hq + 2 * w.Hkv) * rows,                               # q, dout; dk, dv
+    }
     fwd_ms = st["fwd_prep"] + st["fwd_attend"]
     res = {
         "ms_per_step": ms_step,
@@ -219,7 +292,7 @@ def measure(fa, name: str, steps: int, warmup: int, dev):
                 "frac_hbm_peak": bwd_bytes / (st["bwd"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 "algorithmic_bytes": bwd_bytes},
         "kernels_ms": st,
-        "attend_bytes": fwd_bytes,
+        "kernel_bytes": kernel_bytes,
     }
     del net
     torch.cuda.empty_cache()
@@ -235,11 +308,18 @@ def main():
     ap.add_argument("--long-workload", default="l4096_coprime_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="run the short counter-collection program instead of the timed bench")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU mode)", file=sys.stderr)
         sys.exit(2)
+
+    if args.profile_pass:
+        import fibonacci_offset_sparse_amd as fa
+        profile_pass(fa, args.workload, torch.device("cuda:0"))
+        return
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -253,8 +333,17 @@ def main():
     long_res = None if args.no_long else measure(fa, args.long_workload, max(3, args.steps // 4), 1, dev)
 
     w = workloads.WORKLOADS[args.workload]
-    att_ms = main_res["kernels_ms"]["fwd_attend"]
-    achieved = main_res["attend_bytes"] / (att_ms * 1e-3) / 1e9
+    kms = main_res["kernels_ms"]
+
+    def roofline(stage, kernel):
+        ms, nbytes = kms[stage], main_res["kernel_bytes"][stage]
+        achieved = nbytes / (ms * 1e-3) / 1e9
+        return {"kernel": kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(kernel, args.workload),
+                "traffic_unit": "bytes per launch", "avg_launch_ms": ms, "algorithmic_bytes_per_launch": nbytes}
+    kernel_names = {"fwd_attend": "fwd_mfma_kernel", "bwd_query": "bwd_q_mfma_kernel",
+                    "bwd_key": "bwd_k_dot_kernel"}
+    dominant = max(kernel_names, key=lambda s: kms[s])
     line = {
         "metric": "fwd+bwd queries*heads/sec (and fwd HBM GB/s, % of peak)",
         "value": main_res["qh_per_s"],
@@ -266,16 +355,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16/f32acc",
         "io_dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": args.workload, "B": w.B, "L": w.L, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
                    "W": w.W, "base": w.base, "schedule": w.schedule, "layers": w.n_layers,
                    "pass": "fwd+bwd", "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": "fwd_attend_kernel", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "avg_launch_ms": att_ms,
-                     "algorithmic_bytes_per_launch": main_res["attend_bytes"]},
+        "roofline": roofline(dominant, kernel_names[dominant]),
+        "roofline_fwd_attend": roofline("fwd_attend", kernel_names["fwd_attend"]),
         "fwd": main_res["fwd"],
         "bwd": main_res["bwd"],
         "kernels_ms": main_res["kernels_ms"],

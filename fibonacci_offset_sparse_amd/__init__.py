@@ -22,6 +22,7 @@ DUP, INT, INTERP = 0, 1, 2
 BASE_FIB, BASE_POW2 = 0, 1
 SCHEDULE_FIXED, SCHEDULE_LINEAR, SCHEDULE_COPRIME = 0, 1, 2
 MAX_W, MAX_K = 31, 32
+STAGE_PREP, STAGE_QUERY, STAGE_KEY, STAGE_ALL = 1, 2, 4, 7
 
 _c_i32, _c_u8, _c_f32, _c_f64 = ctypes.c_int32, ctypes.c_uint8, ctypes.c_float, ctypes.c_double
 _c_ptr, _c_size = ctypes.c_void_p, ctypes.c_size_t
@@ -54,6 +55,10 @@ def _load() -> ctypes.CDLL:
                                         _P(_c_i32), _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                         _c_i32, _c_f64, _c_f64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                         _c_ptr, _c_ptr, _c_size, _c_ptr]),
+        "fibattn_bwd_stages": (ctypes.c_int, [_c_i32, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_f64, _c_i32,
+                                               _P(_c_i32), _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                               _c_i32, _c_f64, _c_f64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                               _c_ptr, _c_ptr, _c_size, _c_ptr]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -232,12 +237,38 @@ def fibattn_fwd_attend(q: torch.Tensor, v: torch.Tensor, alpha: float, W: int, o
                                       workspace.data_ptr(), workspace.numel(), _stream(q.device, stream)))
 
 
+def fibattn_bwd_stages(stages: int, q, k, v, dout, alpha: float, W: int, offsets: Sequence[int],
+                       dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, workspace: torch.Tensor,
+                       rope_theta: float = 1e4, dalpha_dtheta: float = 0.0,
+                       dalpha: Optional[torch.Tensor] = None, dtheta: Optional[torch.Tensor] = None,
+                       stream=None):
+    """Backward stages selected by the mask `stages` (STAGE_PREP | STAGE_QUERY | STAGE_KEY) into
+    the given outputs; a subset must follow the calls that ran the earlier stages on the same
+    workspace and stream."""
+    B, Hq, L, D, Hkv = _shapes(q, k)
+    dt = _dtype_code(q)
+    ptrs = [_dev(q, "q", (B, Hq, L, D), q.dtype), _dev(k, "k", (B, Hkv, L, D), q.dtype),
+            _dev(v, "v", (B, Hkv, L, D), q.dtype), _dev(dout, "dout", (B, Hq, L, D), q.dtype)]
+    outs = [_dev(dq, "dq", (B, Hq, L, D), q.dtype), _dev(dk, "dk", (B, Hkv, L, D), q.dtype),
+            _dev(dv, "dv", (B, Hkv, L, D), q.dtype),
+            _dev(dalpha, "dalpha", (1,), torch.float32) if dalpha is not None else None,
+            _dev(dtheta, "dtheta", (1,), torch.float32) if dtheta is not None else None]
+    offs, K = _i32_array(offsets)
+    nbytes = fibattn_bwd_workspace_bytes(B, L, Hq, Hkv, D, W, K, dt)
+    ws = _workspace(workspace, nbytes, q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.fibattn_bwd_stages(int(stages), *ptrs, float(alpha), int(W), offs, K, B, L, Hq, Hkv, D, dt,
+                                      float(rope_theta), float(dalpha_dtheta), *outs, ws.data_ptr(), ws.numel(),
+                                      _stream(q.device, stream)))
+
+
 def fibattn_bwd(q, k, v, o, lse, dout, alpha: float, W: int, offsets: Sequence[int],
                 rope_theta: float = 1e4, dalpha_dtheta: float = 0.0, want_dalpha: bool = False,
-                workspace: Optional[torch.Tensor] = None, stream=None):
+                workspace: Optional[torch.Tensor] = None, stream=None, dq: Optional[torch.Tensor] = None,
+                dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None):
     """(dq, dk, dv, dalpha, dtheta); dalpha and dtheta are float32[1] GPU tensors or None.
 
-    o and lse may be None (the library does not read them)."""
+    o and lse may be None (the library does not read them). dq, dk, dv are allocated unless given."""
     B, Hq, L, D, Hkv = _shapes(q, k)
     dt = _dtype_code(q)
     # o and lse are part of the usual signature; the library recomputes what it needs from them
@@ -246,7 +277,11 @@ def fibattn_bwd(q, k, v, o, lse, dout, alpha: float, W: int, offsets: Sequence[i
             _dev(o, "o", (B, Hq, L, D), q.dtype) if o is not None else None,
             _dev(lse, "lse", (B, Hq, L), torch.float32) if lse is not None else None,
             _dev(dout, "dout", (B, Hq, L, D), q.dtype)]
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    outs = [_dev(dq, "dq", (B, Hq, L, D), q.dtype), _dev(dk, "dk", (B, Hkv, L, D), q.dtype),
+            _dev(dv, "dv", (B, Hkv, L, D), q.dtype)]
     da = torch.empty(1, dtype=torch.float32, device=q.device) if want_dalpha else None
     dth = torch.empty(1, dtype=torch.float32, device=q.device) if want_dalpha else None
     offs, K = _i32_array(offsets)
@@ -254,8 +289,8 @@ def fibattn_bwd(q, k, v, o, lse, dout, alpha: float, W: int, offsets: Sequence[i
     ws = _workspace(workspace, nbytes, q.device)
     with torch.cuda.device(q.device):
         _check(lib.fibattn_bwd(*ptrs, float(alpha), int(W), offs, K, B, L, Hq, Hkv, D, dt,
-                               float(rope_theta), float(dalpha_dtheta), dq.data_ptr(), dk.data_ptr(),
-                               dv.data_ptr(), da.data_ptr() if da is not None else None,
+                               float(rope_theta), float(dalpha_dtheta), *outs,
+                               da.data_ptr() if da is not None else None,
                                dth.data_ptr() if dth is not None else None, ws.data_ptr(), ws.numel(),
                                _stream(q.device, stream)))
     return dq, dk, dv, da, dth
@@ -265,5 +300,6 @@ __all__ = [
     "fibattn_status_string", "fibattn_last_error", "fibattn_base_offsets", "fibattn_alpha_schedule",
     "fibattn_alpha_from_theta", "fibattn_plan", "fibattn_fwd_workspace_bytes", "fibattn_fwd",
     "fibattn_fwd_prep", "fibattn_fwd_attend", "fibattn_bwd_workspace_bytes", "fibattn_bwd",
+    "fibattn_bwd_stages", "STAGE_PREP", "STAGE_QUERY", "STAGE_KEY", "STAGE_ALL",
     "FibAttnError", "lib", "LIB_PATH",
 ]

@@ -356,12 +356,15 @@ size_t fibattn_bwd_workspace_bytes(int32_t B, int32_t L, int32_t Hq, int32_t Hkv
     return std::max(general, bwd_fast_layout(B, L, Hq, Hkv).total);
 }
 
-fibattn_status_t fibattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                             const void* dout, double alpha, int32_t W, const int32_t* offsets, int32_t K,
-                             int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
-                             double rope_theta, double dalpha_dtheta, void* dq, void* dk, void* dv, float* dalpha,
-                             float* dtheta, void* workspace, size_t workspace_bytes, void* stream) {
+fibattn_status_t fibattn_bwd_stages(int32_t stages, const void* q, const void* k, const void* v,
+                                    const void* dout, double alpha, int32_t W, const int32_t* offsets, int32_t K,
+                                    int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
+                                    double rope_theta, double dalpha_dtheta, void* dq, void* dk, void* dv,
+                                    float* dalpha, float* dtheta, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
     g_error[0] = '\0';
+    if (stages < 1 || stages > FIBATTN_STAGE_ALL)
+        return fail(FIBATTN_ERR_INVALID, "stage mask %d outside [1, %d]", stages, FIBATTN_STAGE_ALL);
     FIBATTN_TRY(check_dims(B, L, Hq, Hkv, D, W, dtype, rope_theta));
     FIBATTN_TRY(check_offsets(alpha, W, offsets, K));
     if (q == nullptr || k == nullptr || v == nullptr || dout == nullptr || dq == nullptr || dk == nullptr ||
@@ -392,8 +395,8 @@ fibattn_status_t fibattn_bwd(const void* q, const void* k, const void* v, const 
     a.partial = reinterpret_cast<float*>(ws);
     a.q = q;
     a.v = v;
-    a.o = o;
-    a.lse = lse;
+    a.o = nullptr;
+    a.lse = nullptr;
     a.dout = dout;
     a.dq = dq;
     a.dk = dk;
@@ -440,10 +443,14 @@ fibattn_status_t fibattn_bwd(const void* q, const void* k, const void* v, const 
             a.do16 = w0 + f.do16;
             a.wts = reinterpret_cast<uint32_t*>(w0 + f.wts);
             a.partial = reinterpret_cast<float*>(w0 + f.part);
-            e = launch_prep_kv16(pa, true, s);
-            if (e != hipSuccess) return hip_fail(e, "backward prep launch");
-            e = launch_bwd_mfma(a, want_dalpha, s);
-            if (e != hipSuccess) return hip_fail(e, "bwd launch");
+            if (stages & FIBATTN_STAGE_PREP) {
+                e = launch_prep_kv16(pa, true, s);
+                if (e != hipSuccess) return hip_fail(e, "backward prep launch");
+            }
+            if (stages & (FIBATTN_STAGE_QUERY | FIBATTN_STAGE_KEY)) {
+                e = launch_bwd_mfma(a, want_dalpha, stages, s);
+                if (e != hipSuccess) return hip_fail(e, "bwd launch");
+            }
             return FIBATTN_OK;
         }
     }
@@ -454,11 +461,27 @@ fibattn_status_t fibattn_bwd(const void* q, const void* k, const void* v, const 
     r.n_bh = B * Hkv;
     r.L = L;
     r.fr = a.fr;
-    e = launch_rope_keys(dtype, r, s);
-    if (e != hipSuccess) return hip_fail(e, "rope_keys launch");
-    e = launch_bwd(dtype, a, want_dalpha, s);
-    if (e != hipSuccess) return hip_fail(e, "bwd launch");
+    if (stages & FIBATTN_STAGE_PREP) {
+        e = launch_rope_keys(dtype, r, s);
+        if (e != hipSuccess) return hip_fail(e, "rope_keys launch");
+    }
+    if (stages & (FIBATTN_STAGE_QUERY | FIBATTN_STAGE_KEY)) {
+        e = launch_bwd(dtype, a, want_dalpha, stages, s);
+        if (e != hipSuccess) return hip_fail(e, "bwd launch");
+    }
     return FIBATTN_OK;
+}
+
+fibattn_status_t fibattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, double alpha, int32_t W, const int32_t* offsets, int32_t K,
+                             int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
+                             double rope_theta, double dalpha_dtheta, void* dq, void* dk, void* dv, float* dalpha,
+                             float* dtheta, void* workspace, size_t workspace_bytes, void* stream) {
+    (void)o;
+    (void)lse;
+    return fibattn_bwd_stages(FIBATTN_STAGE_ALL, q, k, v, dout, alpha, W, offsets, K, B, L, Hq, Hkv, D, dtype,
+                              rope_theta, dalpha_dtheta, dq, dk, dv, dalpha, dtheta, workspace, workspace_bytes,
+                              stream);
 }
 
 }  // extern "C"

@@ -450,23 +450,24 @@ __global__ __launch_bounds__(256) void dalpha_kernel(BwdArgs A) {
     }
 }
 
-template <typename T>
-hipError_t launch_bwd_typed(const BwdArgs& A, bool want_dalpha, hipStream_t s) {
-    const int hpb = (A.G % 4 == 0) ? 4 : (A.G % 2 == 0) ? 2 : 1;
+template <typename T, int HPB>
+void launch_bwd_heads(const BwdArgs& A, bool want_dalpha, int stages, hipStream_t s) {
     const int tiles = (A.L + kTile - 1) / kTile;
-    dim3 gq(tiles, A.Hkv * (A.G / hpb), A.B);
-    dim3 gk(tiles, A.Hkv, A.B);
-    if (hpb == 4) {
-        hipLaunchKernelGGL((bwd_query_kernel<T, 4>), gq, dim3(kTile * 4), 0, s, A);
-        hipLaunchKernelGGL((bwd_key_kernel<T, 4>), gk, dim3(kTile * 4), 0, s, A);
-    } else if (hpb == 2) {
-        hipLaunchKernelGGL((bwd_query_kernel<T, 2>), gq, dim3(kTile * 2), 0, s, A);
-        hipLaunchKernelGGL((bwd_key_kernel<T, 2>), gk, dim3(kTile * 2), 0, s, A);
-    } else {
-        hipLaunchKernelGGL((bwd_query_kernel<T, 1>), gq, dim3(kTile), 0, s, A);
-        hipLaunchKernelGGL((bwd_key_kernel<T, 1>), gk, dim3(kTile), 0, s, A);
+    if (stages & kStageQuery)
+        hipLaunchKernelGGL((bwd_query_kernel<T, HPB>), dim3(tiles, A.Hkv * (A.G / HPB), A.B), dim3(kTile * HPB), 0,
+                           s, A);
+    if (stages & kStageKey) {
+        hipLaunchKernelGGL((bwd_key_kernel<T, HPB>), dim3(tiles, A.Hkv, A.B), dim3(kTile * HPB), 0, s, A);
+        if (want_dalpha) hipLaunchKernelGGL(dalpha_kernel, dim3(1), dim3(256), 0, s, A);
     }
-    if (want_dalpha) hipLaunchKernelGGL(dalpha_kernel, dim3(1), dim3(256), 0, s, A);
+}
+
+template <typename T>
+hipError_t launch_bwd_typed(const BwdArgs& A, bool want_dalpha, int stages, hipStream_t s) {
+    const int hpb = (A.G % 4 == 0) ? 4 : (A.G % 2 == 0) ? 2 : 1;
+    if (hpb == 4) launch_bwd_heads<T, 4>(A, want_dalpha, stages, s);
+    else if (hpb == 2) launch_bwd_heads<T, 2>(A, want_dalpha, stages, s);
+    else launch_bwd_heads<T, 1>(A, want_dalpha, stages, s);
     return hipGetLastError();
 }
 
@@ -486,9 +487,9 @@ int bwd_query_workgroups(int B, int L, int Hkv, int G) {
     return ((L + kTile - 1) / kTile) * Hkv * (G / hpb) * B;
 }
 
-hipError_t launch_bwd(int dtype, const BwdArgs& A, bool want_dalpha, hipStream_t s) {
-    return dtype == 0 ? launch_bwd_typed<float>(A, want_dalpha, s)
-                      : launch_bwd_typed<bf16_t>(A, want_dalpha, s);
+hipError_t launch_bwd(int dtype, const BwdArgs& A, bool want_dalpha, int stages, hipStream_t s) {
+    return dtype == 0 ? launch_bwd_typed<float>(A, want_dalpha, stages, s)
+                      : launch_bwd_typed<bf16_t>(A, want_dalpha, stages, s);
 }
 
 }  // namespace fibattn

@@ -566,21 +566,28 @@ bool bwd_mfma_supported(const BwdArgs& A) {
     return A.G % 4 == 0 && A.W <= 15 && A.n_off <= 16;
 }
 
-hipError_t launch_bwd_mfma(const BwdArgs& A0, bool want_dalpha, hipStream_t s) {
+hipError_t launch_bwd_mfma(const BwdArgs& A0, bool want_dalpha, int stages, hipStream_t s) {
     BwdArgs A = A0;
     const int64_t n_tiles = (A.L + kTile - 1) / kTile;
     const int64_t q_units = static_cast<int64_t>(A.B) * A.Hkv * (A.G / 4);
     const int64_t k_units = static_cast<int64_t>(A.B) * A.Hkv;
-    A.xcd_map = (q_units % 8 == 0) ? 1 : 0;
     A.n_wg = static_cast<int32_t>(q_units * n_tiles);
-    hipLaunchKernelGGL((bwd_q_mfma_kernel<8>), dim3(static_cast<unsigned>(q_units * n_tiles)), dim3(kNT), 0, s, A);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    A.xcd_map = (k_units % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((bwd_k_dot_kernel<8>), dim3(static_cast<unsigned>(k_units * n_tiles)), dim3(kNT), 0, s, A);
-    e = hipGetLastError();
-    if (e != hipSuccess || !want_dalpha) return e;
-    return launch_dalpha(A, s);
+    if (stages & kStageQuery) {
+        A.xcd_map = (q_units % 8 == 0) ? 1 : 0;
+        hipLaunchKernelGGL((bwd_q_mfma_kernel<8>), dim3(static_cast<unsigned>(q_units * n_tiles)), dim3(kNT), 0, s,
+                           A);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (stages & kStageKey) {
+        A.xcd_map = (k_units % 8 == 0) ? 1 : 0;
+        hipLaunchKernelGGL((bwd_k_dot_kernel<8>), dim3(static_cast<unsigned>(k_units * n_tiles)), dim3(kNT), 0, s,
+                           A);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess || !want_dalpha) return e;
+        return launch_dalpha(A, s);
+    }
+    return hipSuccess;
 }
 
 }  // namespace fibattn

@@ -12,6 +12,8 @@ constexpr int kPairs = 32;    // RoPE pairs (j, j + 32)
 constexpr int kTile = 64;     // query (or key) positions per workgroup
 constexpr int kMaxWin = 32;   // window slots 0..W with W <= 31
 constexpr int kMaxOff = 32;   // base rungs
+// backward stages (the bit values of the public stage mask)
+constexpr int kStagePrep = 1, kStageQuery = 2, kStageKey = 4;
 
 // One kept offset of the plan (DUP rungs are removed before launch).
 struct OffsetSlot {
@@ -109,9 +111,9 @@ hipError_t launch_prep_kv16(const PrepArgs& a, bool backward_layout, hipStream_t
 hipError_t launch_fwd_attend(int dtype, const FwdArgs& a, hipStream_t s);
 bool fwd_mfma_supported(const FwdArgs& a);
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s);
-hipError_t launch_bwd(int dtype, const BwdArgs& a, bool want_dalpha, hipStream_t s);
+hipError_t launch_bwd(int dtype, const BwdArgs& a, bool want_dalpha, int stages, hipStream_t s);
 bool bwd_mfma_supported(const BwdArgs& a);
-hipError_t launch_bwd_mfma(const BwdArgs& a, bool want_dalpha, hipStream_t s);
+hipError_t launch_bwd_mfma(const BwdArgs& a, bool want_dalpha, int stages, hipStream_t s);
 hipError_t launch_dalpha(const BwdArgs& a, hipStream_t s);
 int bwd_query_workgroups(int B, int L, int Hkv, int G);
 

@@ -192,6 +192,32 @@ fibattn_status_t fibattn_bwd(const void* q, const void* k, const void* v, const 
                              float* dtheta, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Stages of the backward pass, for fibattn_bwd_stages (bit mask). */
+typedef enum {
+    FIBATTN_STAGE_PREP = 1,   /* keys rotated at their positions (and fp16 values) into the workspace */
+    FIBATTN_STAGE_QUERY = 2,  /* dq, plus what the key stage reads from the workspace */
+    FIBATTN_STAGE_KEY = 4,    /* dk, dv, and dalpha / dtheta when requested */
+    FIBATTN_STAGE_ALL = 7
+} fibattn_bwd_stage_t;
+
+/*
+ * fibattn_bwd split into its stages, so that each kernel can be timed (or overlapped) on its own.
+ * stages: a nonzero mask of fibattn_bwd_stage_t bits; the selected stages are queued in the order
+ * PREP, QUERY, KEY. A stage reads what the earlier stages left in `workspace`: a call with a subset
+ * of the bits must follow the calls that ran the earlier stages, on the same stream, with the same
+ * arguments and the workspace untouched in between. dq is written by the QUERY stage, dk, dv,
+ * dalpha and dtheta by the KEY stage; pointers a selected stage does not write are not read.
+ * FIBATTN_STAGE_ALL is fibattn_bwd (which forwards here). Arguments and errors as fibattn_bwd,
+ * plus INVALID for a mask outside [1, 7]; every argument is checked whatever the mask.
+ */
+fibattn_status_t fibattn_bwd_stages(int32_t stages, const void* q, const void* k, const void* v,
+                                    const void* dout, double alpha, int32_t W,
+                                    const int32_t* offsets, int32_t K, int32_t B, int32_t L,
+                                    int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
+                                    double rope_theta, double dalpha_dtheta, void* dq, void* dk,
+                                    void* dv, float* dalpha, float* dtheta, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

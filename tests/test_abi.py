@@ -165,6 +165,19 @@ def test_bwd_argument_checks():
     assert "integral" in fa.fibattn_last_error()
 
 
+def test_bwd_stage_mask_checks():
+    offs, n = fa._i32_array(O.FIB_BASE)
+
+    def staged(mask, dq=FAKE):
+        return fa.lib.fibattn_bwd_stages(mask, FAKE, FAKE, FAKE, FAKE, 0.73, 6, offs, n, 1, 64, 8, 2, 64, 1, 1e4,
+                                         0.0, dq, FAKE, FAKE, None, None, FAKE, 1 << 40, None)
+    for bad in (0, 8, -1):
+        assert staged(bad) == 1
+        assert "stage mask" in fa.fibattn_last_error()
+    # every argument is checked whatever the mask
+    assert staged(fa.STAGE_PREP, dq=None) == 1
+
+
 def test_host_helpers_argument_checks():
     out = (ctypes.c_int32 * 4)()
     n = ctypes.c_int32()

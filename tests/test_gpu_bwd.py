@@ -144,6 +144,25 @@ def test_integral_offsets_with_pow2_base_and_window_extremes():
     compare(q, k, v, do, 1.0, 5, [], "no offsets", want_dalpha=False)
 
 
+def test_staged_calls_equal_the_combined_call():
+    w = workloads.WORKLOADS["l1024_learned_bf16"]
+    q, k, v, do = [x.to("cuda:0") for x in workloads.draw(w, 3, B=2)]
+    th = float(workloads.draw_theta(16)[3])
+    alpha, dadt = O.alpha_from_theta(th), O.dalpha_dtheta(th)
+    say("bwd staged calls B=2 L=1024")
+    ref = fa.fibattn_bwd(q, k, v, None, None, do, alpha, w.W, O.FIB_BASE, dalpha_dtheta=dadt, want_dalpha=True)
+    ws = torch.empty(fa.fibattn_bwd_workspace_bytes(2, w.L, 8, 2, 64, w.W, len(O.FIB_BASE)), dtype=torch.uint8,
+                     device="cuda:0")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    da, dth = torch.empty(1, device="cuda:0"), torch.empty(1, device="cuda:0")
+    for st in (fa.STAGE_PREP, fa.STAGE_QUERY, fa.STAGE_KEY):
+        fa.fibattn_bwd_stages(st, q, k, v, do, alpha, w.W, O.FIB_BASE, dq, dk, dv, ws, dalpha_dtheta=dadt,
+                              dalpha=da, dtheta=dth)
+    torch.cuda.synchronize()
+    for x, y in zip(ref, (dq, dk, dv, da, dth)):
+        assert torch.equal(x, y)
+
+
 def test_bitwise_determinism():
     w = workloads.WORKLOADS["l1024_learned_bf16"]
     q, k, v, do = workloads.draw(w, 2, B=4)
