@@ -26,12 +26,12 @@
 //  * PV: A = head x's 4 weights (the same lane), B = the 4 rows' values at 4 dims (built with
 //    v_perm from 16-byte reads), 16 products cover 64 dims; the result lane (p', x) holds dims
 //    16x..16x+15 of all 4 heads.
-//  * LDS: the window block (64 + W + 4 rows) and a ring of three steps, each holding the blocks
-//    of two rungs (65 rows each). Staging is LDS DMA (buffer_load ... lds): no VGPRs; rows
+//  * LDS: two staging buffers of 18 KB (four workgroups per CU), used in turn by a sequence of
+//    items: the key window (64 + W + 4 rows), the key rung steps (two rungs of 65 rows each), the
+//    value window, the value rung steps. Staging is LDS DMA (buffer_load ... lds): no VGPRs; rows
 //    before 0 or past L fall outside the buffer resource and arrive as zeros, so every row a
-//    lane reads is finite. Blocks are issued two steps ahead, with one barrier per step after a
-//    counted vmcnt wait, and a sparse L2 warm-up (one 16-byte load per row into a sink) runs
-//    further ahead.
+//    lane reads is finite. Each item is issued while the one before it is being computed on,
+//    with one barrier per item after a counted vmcnt wait.
 //  * Banks: 16-byte chunk k of slot s sits at chunk k ^ ((s >> 1) & 7), so the same chunk of 16
 //    consecutive slots covers all 64 banks, and the second rung's block sits two slots up. Key
 //    reads (16 lanes per pass) are then free of bank conflicts for window and rung groups, as
