@@ -148,14 +148,15 @@ size_t fwd_ws_bytes(int32_t B, int32_t L, int32_t Hkv) { return krot_bytes(B, L,
 // cos/sin table (the forward's layout of the same sizes), the rotated queries (fp16), the per key
 // row term weights, and the per-workgroup d(loss)/dt partials.
 struct BwdFastLayout {
-    size_t qrot, do16, wts, part, total;
+    size_t qrot, do16, wwin, wrung, part, total;
 };
 BwdFastLayout bwd_fast_layout(int32_t B, int32_t L, int32_t Hq, int32_t Hkv) {
     BwdFastLayout f;
     f.qrot = fwd_ws_bytes(B, L, Hkv);
     f.do16 = f.qrot + align256(static_cast<size_t>(B) * Hq * L * kD * sizeof(uint16_t));
-    f.wts = f.do16 + align256(static_cast<size_t>(B) * Hq * L * kD * sizeof(uint16_t));
-    f.part = f.wts + align256(static_cast<size_t>(B) * Hq * L * kNV * sizeof(uint32_t));
+    f.wwin = f.do16 + align256(static_cast<size_t>(B) * Hq * L * kD * sizeof(uint16_t));
+    f.wrung = f.wwin + align256(static_cast<size_t>(B) * Hq * L * kNW * sizeof(uint32_t));
+    f.part = f.wrung + align256(static_cast<size_t>(B) * Hq * L * kNR * sizeof(uint32_t));
     const size_t n_wg = static_cast<size_t>(bwd_query_workgroups(B, L, Hkv, Hq / Hkv));
     f.total = f.part + align256(n_wg * kMaxOff * sizeof(float));
     return f;
@@ -441,7 +442,8 @@ fibattn_status_t fibattn_bwd_stages(int32_t stages, const void* q, const void* k
             a.cstab = pa.cs;
             a.qrot16 = w0 + f.qrot;
             a.do16 = w0 + f.do16;
-            a.wts = reinterpret_cast<uint32_t*>(w0 + f.wts);
+            a.wwin = reinterpret_cast<uint32_t*>(w0 + f.wwin);
+            a.wrung = reinterpret_cast<uint32_t*>(w0 + f.wrung);
             a.partial = reinterpret_cast<float*>(w0 + f.part);
             if (stages & FIBATTN_STAGE_PREP) {
                 e = launch_prep_kv16(pa, true, s);

@@ -50,8 +50,11 @@ __device__ __forceinline__ uint32_t pack_p_ds(float p, float ds) { return pack_h
 template <int MAXS>
 __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     constexpr int MAXK = 2 * MAXS;
-    __shared__ __attribute__((aligned(1024))) char lds0[kBufBytes];
-    __shared__ __attribute__((aligned(1024))) char lds1[kBufBytes];
+    // Two item buffers used in turn, each a key part and a value part. Items: the key and value
+    // windows, then the key and value rung steps (pass AB); then the key window and key steps
+    // again (pass C, key parts only).
+    __shared__ __attribute__((aligned(1024))) char lds0[2 * kBufBytes];
+    __shared__ __attribute__((aligned(1024))) char lds1[2 * kBufBytes];
     __shared__ float red[4][MAXK];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -84,11 +87,16 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     auto step = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int k) {
         st.step(rs, dst, 2 * k < n_reach, i0 - A.off[2 * k].a - 1, 2 * k + 1 < n_reach, i0 - A.off[2 * k + 1].a - 3);
     };
+    auto kv_step = [&](char* dst, int k) {         // 12 DMA instructions per wave
+        step(krs, dst, k);
+        step(vrs, dst + kBufBytes, k);
+    };
     auto buf = [&](int j) -> char* { return (j & 1) ? lds1 : lds0; };
     const int jw = i0 - W - kWinPad;
 
-    // ---- prologue: key window, q and do of head h0 + x, key step 0 ----
+    // ---- prologue: key and value windows, q and do of head h0 + x, key and value step 0 ----
     st.window(krs, lds0, jw);
+    st.window(vrs, lds0 + kBufBytes, jw);
     const int64_t qrow = (static_cast<int64_t>(b) * A.Hq + h0 + x) * L + (active ? i : 0);
     uint4 qraw[8], draw[8];
     float4 ctab[16];
@@ -103,7 +111,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) ctab[u] = ct[u];
     }
-    step(krs, lds1, 0);
+    kv_step(lds1, 0);
 
     // q rotated at its position (unscaled), fp16, in the keys' permuted order: word 2m holds dims
     // (m, 16 + m), word 2m + 1 dims (32 + m, 48 + m); register chunk c = words 4c..4c+3
@@ -140,21 +148,26 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) dov[c][u] = pack_h2(bf16_lo(w4[u]), bf16_hi(w4[u]));
     }
-    publish<6>();                                       // the key window has landed
+    publish<12>();                                      // the key and value windows have landed
 
-    // ---- pass A: scores (base 2) and far - near of the rung products ----
-    float s[4 * kWG + MAXK], sd[MAXK];
+    // ---- pass AB: scores s (base 2) with the keys, dP = do . value row with the values, and for
+    // each rung far - near of both products ----
+    float s[4 * kWG + MAXK], sd[MAXK], dp[4 * kWG + MAXK], dpd[MAXK];
     const int s0 = p - x + W + kWinPad;                 // window: lane x reads distance 4g + x
     const int rslot = p + ((x >> 1) ? kBlkSlots + 2 : 0) + ((x & 1) ? 0 : 1);   // rung rows
     const int rbase = rslot * kRowBytes, rsw = swz(rslot);
 #pragma unroll
     for (int g = 0; g < kWG; ++g) {
-        f4_t acc = {0.f, 0.f, 0.f, 0.f};
-        if (4 * g <= W) acc = row_dot_group(q, lds0, (s0 - 4 * g) * kRowBytes, swz(s0 - 4 * g));
+        f4_t acc = {0.f, 0.f, 0.f, 0.f}, accv = {0.f, 0.f, 0.f, 0.f};
+        if (4 * g <= W) {
+            acc = row_dot_group(q, lds0, (s0 - 4 * g) * kRowBytes, swz(s0 - 4 * g));
+            accv = row_dot_group(dov, lds0 + kBufBytes, (s0 - 4 * g) * kRowBytes, swz(s0 - 4 * g));
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int d = 4 * g + r;
             s[d] = (active && d <= W && i >= d) ? acc[r] * A.qscale : kNegInf;
+            dp[d] = accv[r];
         }
     }
     // (stores count in vmcnt too: issued where the next wait drains everything anyway)
@@ -166,35 +179,43 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) dq16[c] = make_uint4(dov[c][0], dov[c][1], dov[c][2], dov[c][3]);
     }
-    publish<0>();
+    publish<0>();                                       // step 0 has landed, buffer 0 is free
 #pragma unroll
     for (int k = 0; k < MAXS; ++k) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             s[4 * kWG + 2 * k + e] = kNegInf;
             sd[2 * k + e] = 0.f;
+            dp[4 * kWG + 2 * k + e] = 0.f;
+            dpd[2 * k + e] = 0.f;
         }
         if (k < n_steps) {
-            if (k + 1 < n_steps) step(krs, buf(k + 2), k + 1);
+            if (k + 1 < n_steps) kv_step(buf(k + 2), k + 1);
             const f4_t acc = row_dot_group(q, buf(k + 1), rbase, rsw);
+            const f4_t accv = row_dot_group(dov, buf(k + 1) + kBufBytes, rbase, rsw);
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int n = 2 * k + e;
                 if (n < n_reach) {
+                    const float t = A.off[n].t;
                     const float dd = (acc[2 * e + 1] - acc[2 * e]) * A.qscale;
-                    const float sc = fmaf(A.off[n].t, dd, acc[2 * e] * A.qscale);
+                    const float sc = fmaf(t, dd, acc[2 * e] * A.qscale);
                     const bool ok = active && i >= A.off[n].a + A.off[n].interp;
                     s[4 * kWG + n] = ok ? sc : kNegInf;
                     sd[n] = ok ? dd : 0.f;
+                    const float dv = accv[2 * e + 1] - accv[2 * e];
+                    dp[4 * kWG + n] = fmaf(t, dv, accv[2 * e]);
+                    dpd[n] = dv;
                 }
             }
             publish<0>();
         }
     }
 
-    // ---- value window and value step 0 under the softmax ----
-    st.window(vrs, lds0, jw);
-    step(vrs, lds1, 0);
+    // ---- key window and key step 0 again (pass C), under the softmax ----
+    st.window(krs, lds0, jw);
+    step(krs, lds1, 0);
+
     float mx = kNegInf;
 #pragma unroll
     for (int y = 0; y < 4 * kWG + MAXK; ++y) mx = fmaxf(mx, s[y]);
@@ -208,42 +229,8 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     const float inv = active ? 1.0f / l : 0.f;
 #pragma unroll
     for (int y = 0; y < 4 * kWG + MAXK; ++y) s[y] *= inv;   // s now holds p
-    publish<6>();
 
-    // ---- pass B: dP = do . value row; far - near for rungs ----
-    float dp[4 * kWG + MAXK], dpd[MAXK];
-#pragma unroll
-    for (int g = 0; g < kWG; ++g) {
-        f4_t acc = {0.f, 0.f, 0.f, 0.f};
-        if (4 * g <= W) acc = row_dot_group(dov, lds0, (s0 - 4 * g) * kRowBytes, swz(s0 - 4 * g));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dp[4 * g + r] = acc[r];
-    }
-    publish<0>();
-#pragma unroll
-    for (int k = 0; k < MAXS; ++k) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            dp[4 * kWG + 2 * k + e] = 0.f;
-            dpd[2 * k + e] = 0.f;
-        }
-        if (k < n_steps) {
-            if (k + 1 < n_steps) step(vrs, buf(k + 2), k + 1);
-            const f4_t acc = row_dot_group(dov, buf(k + 1), rbase, rsw);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int n = 2 * k + e;
-                if (n < n_reach) {
-                    const float dd = acc[2 * e + 1] - acc[2 * e];
-                    dp[4 * kWG + n] = fmaf(A.off[n].t, dd, acc[2 * e]);
-                    dpd[n] = dd;
-                }
-            }
-            publish<0>();
-        }
-    }
-
-    // ---- softmax gradient; then key window and key step 0 again ----
+    // ---- softmax gradient ----
     float delta = 0.f;
 #pragma unroll
     for (int y = 0; y < 4 * kWG + MAXK; ++y) delta = fmaf(s[y], dp[y], delta);
@@ -253,31 +240,15 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     for (int y = 0; y < 4 * kWG + MAXK; ++y) dp[y] = s[y] * (dp[y] - delta) * A.scale;
 #pragma unroll
     for (int n = 0; n < MAXK; ++n) {
-        // dS (q . (k_far - k_near)) / sqrt(D) = (dS / sqrt(D)) sd ln2 sqrt(D) / ... in base 2:
-        // sd = (q . dk) log2(e) / sqrt(D), so dS sd ln2 = dS (q . dk) / sqrt(D)
+        // dS (q . (k_far - k_near)) / sqrt(D) in base 2: sd = (q . dk) log2(e) / sqrt(D), so
+        // (dS / sqrt(D)) sd ln2 sqrt(D) = dS (q . dk) / sqrt(D)
         dt[n] = fmaf(dp[4 * kWG + n] * (kLn2 / A.scale), sd[n], s[4 * kWG + n] * dpd[n]);
     }
-    // weights for the key side: term v of key row j = i - delta_v
-    if (active) {
-        uint32_t* wrow = A.wts + (static_cast<int64_t>(b) * A.Hq + h0 + x) * L * kNV;
+    // the key side's weights of this query: (p, dS/sqrt(D)) per window distance and per rung
+    // (without the rung's coefficients), fp16 pairs; stored at the end
+    uint32_t wq[4 * kWG + MAXK];
 #pragma unroll
-        for (int d = 0; d < 4 * kWG; ++d)
-            if (i - d >= 0) wrow[static_cast<int64_t>(i - d) * kNV + d] = pack_p_ds(s[d], dp[d]);
-#pragma unroll
-        for (int n = 0; n < MAXK; ++n) {
-            if (n < n_reach) {
-                const float t = A.off[n].t;
-                const int jn = i - A.off[n].a;
-                const float pn = s[4 * kWG + n], dn = dp[4 * kWG + n];
-                if (jn >= 0) wrow[static_cast<int64_t>(jn) * kNV + 16 + 2 * n] = pack_p_ds(pn - pn * t, dn - dn * t);
-                if (jn - 1 >= 0) wrow[static_cast<int64_t>(jn - 1) * kNV + 17 + 2 * n] = pack_p_ds(pn * t, dn * t);
-            }
-        }
-    }
-    // (the stores above count in vmcnt: the key blocks are issued after them, so the wait below
-    // leaves key step 0 in flight)
-    st.window(krs, lds0, jw);
-    step(krs, lds1, 0);
+    for (int y = 0; y < 4 * kWG + MAXK; ++y) wq[y] = pack_p_ds(s[y], dp[y]);
     // pass C weights: dS/sqrt(D) times the coefficients, fp16, groups of 4
     uint32_t ww[kWG][2], wo[MAXS][2];
 #pragma unroll
@@ -299,7 +270,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         wo[k][0] = pack_h2(w[0], w[1]);
         wo[k][1] = pack_h2(w[2], w[3]);
     }
-    publish<6>();
+    publish<6>();                                       // the key window has landed
 
     // ---- pass C: dq_rot = sum of weighted key rows (transposing reads of the permuted keys:
     // lane x gets element 4m + x, which is dim 16x + m) ----
@@ -329,9 +300,18 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // ---- dq: RoPE transposed at position i. Lane x holds dims 16x + m of heads 0..3; the other
-    // half of pair (16x + m) mod 32 is in lane x ^ 2 ----
     if (active) {
+        // ---- the key side's weights: the window row of this query (64 bytes) and one entry of
+        // each rung's row (rung-major, so a wave's stores of one rung are contiguous) ----
+        uint4* wr = reinterpret_cast<uint4*>(A.wwin + qrow * kNW);
+#pragma unroll
+        for (int c = 0; c < kNW / 4; ++c) wr[c] = make_uint4(wq[4 * c], wq[4 * c + 1], wq[4 * c + 2], wq[4 * c + 3]);
+        uint32_t* rr = A.wrung + (static_cast<int64_t>(b) * A.Hq + h0 + x) * kNR * L + i;
+#pragma unroll
+        for (int n = 0; n < kNR; ++n) rr[static_cast<int64_t>(n) * L] = (n < MAXK) ? wq[4 * kWG + n] : 0u;
+
+        // ---- dq: RoPE transposed at position i. Lane x holds dims 16x + m of heads 0..3; the
+        // other half of pair (16x + m) mod 32 is in lane x ^ 2 ----
         const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(i) * (kPairs / 2) + 8 * (x & 1);
         float2 cs[16];
 #pragma unroll
@@ -378,185 +358,268 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         float v = 0.f;
         if (threadIdx.x < MAXK) v = ((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) + red[3][threadIdx.x];
         A.partial[static_cast<int64_t>(blockIdx.x) * kMaxOff + threadIdx.x] = v;
+
     }
 }
 
 // ------------------------------------------------------------------------------------------------
 // bwd_k_dot
 // ------------------------------------------------------------------------------------------------
+// The window weight block of wave w: the window rows (64 bytes) of the 32 queries its 16 key rows
+// read in the window, staged in the free space after the two row windows of a window item.
+__device__ __forceinline__ int win_wregion(int wave) {
+    return (wave < 2 ? 0 : kBufBytes) + kWinBytes + (wave & 1) * 2048;
+}
+
 template <int MAXS>
 __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
-    __shared__ __attribute__((aligned(1024))) char lds0[kBufBytes];   // rotated-query blocks
-    __shared__ __attribute__((aligned(1024))) char lds1[kBufBytes];   // do blocks
+    // Two item buffers used in turn, each a rotated-query part and a do part (kBufBytes each).
+    // Items of a query head: its window (the rotated-query and do windows and the window weights),
+    // then its rung steps, padded to an odd count so that every head's window sits in lds0.
+    __shared__ __attribute__((aligned(1024))) char lds0[2 * kBufBytes];
+    __shared__ __attribute__((aligned(1024))) char lds1[2 * kBufBytes];
+    // a rung step's weights per key row: (dS near, dS far) of its two rungs, then (p near, p far)
+    __shared__ uint4 wst[2][kTile];
+    // the (p, dS) entries of a step's two rungs for queries j0 + a + 0..127 (step s: buffer s % 2),
+    // staged by the item before the step's own
+    __shared__ uint32_t went[2][2][128];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int pq = lane >> 2, x = lane & 3;
-    const int r = 16 * wave + pq;                       // key row of this lane within the tile
-    const int L = A.L, W = A.W;
+    const int L = A.L;
     const int n_tiles = (L + kTile - 1) / kTile;
     int unit, tile;
     unit_tile(blockIdx.x, n_tiles, A.xcd_map, unit, tile);
     const int bg = unit;                                // b * Hkv + g
     const int b = bg / A.Hkv, g = bg % A.Hkv;
     const int j0 = tile * kTile;
-    const int j = j0 + r;
 
     // rungs some key row of the tile receives (query j + a < L): a prefix
     int n_reach = 0;
     for (int n = 0; n < A.n_off; ++n)
         if (j0 + A.off[n].a < L) n_reach = n + 1;
     const int n_steps = (n_reach + 1) >> 1;
+    const int n_items = n_steps | 1;                    // rung items per head (odd)
+
+    // Lanes follow v_mfma_f32_16x16x16f16: lane l = 16 lg + lr holds A[lr][4 lg + 0..3],
+    // B[4 lg + 0..3][lr] and D[4 lg + 0..3][lr]. Its outputs (window and rungs alike) are key rows
+    // 16w + 4 lg + q (q = 0..3) at element E(nb, lr) of block nb = 0..3, where column t = 4b' + c
+    // is element 8 ch + 4 (b' & 1) + c with chunk ch = nb + 4 (b' >> 1) (elements of the permuted
+    // rotated-query rows for dk, dims of do for dv). With the slot swizzle, the transposing reads
+    // of a pass of 32 lanes then fall on distinct banks.
+    const int lr = lane & 15, lg = lane >> 4;
+    const int tb = lr & 3, te = lr >> 2;                // as a source of a transposing read: block tb, row te
+    f4_t dk[4], dv[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+        dk[nb] = (f4_t){0.f, 0.f, 0.f, 0.f};
+        dv[nb] = (f4_t){0.f, 0.f, 0.f, 0.f};
+    }
+    // byte offset of element block tb of block nb inside slot s
+    auto blk_addr = [&](int s, int nb) { return (s * kRowBytes | (((nb + 4 * (tb >> 1)) << 4) ^ swz(s))) + 8 * (tb & 1); };
 
     Stager st;
     st.init(lane, wave);
-    // key row r's terms: window distance d at slot r + d; rung 2k near at slot r, far at r + 1
-    // (block A), rung 2k + 1 near at 72 + r + 2, far at 72 + r + 3 (block B)
+    // rung step k: rung 2k rows j0 + a + s at slot s (near of key row r at r, far at r + 1), rung
+    // 2k + 1 rows j0 + a' - 2 + s at slot 72 + s (near at 72 + r + 2, far at 72 + r + 3); steps past
+    // n_steps stage zeros
     auto step = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int k) {
         st.step(rs, dst, 2 * k < n_reach, j0 + A.off[2 * k].a, 2 * k + 1 < n_reach, j0 + A.off[2 * k + 1].a - 2);
     };
-    // transposing reads: lane (p', x) reads for key row rt = 16w + 4 (p' >> 2) + x, term kt = p' & 3
-    const int rt = 16 * wave + 4 * (pq >> 2) + x;
-    const int kt = pq & 3;
-    const int swin = rt + kt;                           // window group g: slot swin + 4g
-    const int srung = (kt < 2) ? rt + kt : kBlkSlots + rt + 2 + (kt - 2);
-    const int rgbase = srung * kRowBytes, rgsw = swz(srung);
-
-    // validity of a term for key row j: its query q_i = j + delta must exist and read this row
-    auto term_ok = [&](int delta, bool interp_near) { return j + delta < L && !(interp_near && j == 0); };
-
-    float dk[16], dv[16];
+    auto buf = [&](int it) -> char* { return (it & 1) ? lds1 : lds0; };
+    // the rung entries of step k of head h into went[k % 2]: one 4-byte DMA per wave (rung
+    // 2k + (w & 1), queries j0 + a + 64 (w >> 1) + lane; zeros past L or past the reach)
+    auto entries = [&](int h, int k) {
+        const int n = 2 * k + (wave & 1);
+        const bool real = n < n_reach;
+        const uint32_t* wrn = A.wrung + ((static_cast<int64_t>(b) * A.Hq + h) * kNR + (real ? n : 0)) * L;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(wrn), 0, L * 4, kRsrcWord3);
+        const int q0 = real ? j0 + A.off[n].a + 64 * (wave >> 1) : -(1 << 24);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dma_dst(reinterpret_cast<char*>(&went[k & 1][wave & 1][64 * (wave >> 1)])),
+                                                 4, (q0 + lane) * 4, 0, 0, 0);
+    };
+    // the window item of head h: rotated-query and do rows j0 + s at slot s (3 + 3 instructions
+    // per wave), the wave's window weights (2) and the entries of step 0 (1)
+    auto window_item = [&](int h) {
+        const int64_t hrow0 = (static_cast<int64_t>(b) * A.Hq + h) * L;
+        st.window(rows_rsrc(A.qrot16, hrow0, L), lds0, j0);
+        st.window(rows_rsrc(A.do16, hrow0, L), lds0 + kBufBytes, j0);
+        const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<char*>(A.wwin + hrow0 * kNW), 0, L * kNW * 4, kRsrcWord3);
+        const int vrow = (j0 + 16 * wave + (lane >> 2)) * (kNW * 4) + (lane & 3) * 16;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        dk[m] = 0.f;
-        dv[m] = 0.f;
-    }
+        for (int u = 0; u < 2; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ws, dma_dst(lds0 + win_wregion(wave) + u * 1024), 16,
+                                                     vrow + u * 16 * (kNW * 4), 0, 0, 0);
+        entries(h, 0);
+    };
+    // rung step weights: thread (row wrow, part wv) builds one word of wst for key row j0 + wrow:
+    // rung 2k + (wv & 1), dS halves (wv < 2) or p halves, (near, far) times (1 - t, t)
+    const int wrow = threadIdx.x >> 2, wv = threadIdx.x & 3;
+    auto put_w = [&](int k) {
+        const int n = 2 * k + (wv & 1);
+        const float t = A.off[n].t;
+        const uint32_t en = went[k & 1][wv & 1][wrow], ef = went[k & 1][wv & 1][wrow + 1];
+        const uint32_t pr = __builtin_amdgcn_perm(ef, en, (wv >> 1) ? 0x05040100u : 0x07060302u);
+        const h2_t c = {static_cast<_Float16>(1.f - t), static_cast<_Float16>(t)};
+        reinterpret_cast<uint32_t*>(&wst[k & 1][wrow])[wv] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, pr) * c);
+    };
 
+    // 4 terms of key rows 16w + 4 lg + q at block nb: the lane reads (as a source) term te's row
+    // at element block tb and receives the 4 terms' element E(nb, lr); two v_dot2 per element.
+    // The reads are issued first; each result then passes an empty asm as a 64-bit value before it
+    // is split into its two dwords (an optimisation has been seen to fold the second dword of the
+    // read onto the first).
+    const int rbase16 = 16 * wave + 4 * lg;
+    // term te of key row r: near / far of rung 2k at slots r, r + 1, of rung 2k + 1 at 74 + r,
+    // 75 + r; element block nb of it is at radr[q] ^ (nb << 4)
+    int radr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) radr[q] = blk_addr(rbase16 + q + (te & 1) + (te >> 1) * (kBlkSlots + 2), 0);
+    auto sum_rungs = [&](f4_t (&acc)[4], const uint4 (&w)[4], bool use_p, const char* lds) {
+#pragma unroll
+        for (int q0 = 0; q0 < 4; q0 += 2) {
+            unsigned long long rv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int q = q0 + (u >> 2), nb = u & 3;
+                rv[u] = __builtin_bit_cast(unsigned long long, tr_read_h4(lds, radr[q] ^ (nb << 4)));
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int q = q0 + (u >> 2), nb = u & 3;
+                asm volatile("" : "+v"(rv[u]));
+                const uint32_t lo = static_cast<uint32_t>(rv[u]), hi = static_cast<uint32_t>(rv[u] >> 32);
+                const uint32_t w01 = use_p ? w[q].z : w[q].x, w23 = use_p ? w[q].w : w[q].y;
+                acc[nb][q] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, w01), __builtin_bit_cast(h2_t, lo), acc[nb][q], false);
+                acc[nb][q] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, w23), __builtin_bit_cast(h2_t, hi), acc[nb][q], false);
+            }
+        }
+    };
+
+    window_item(g * A.G);
     for (int hh = 0; hh < A.G; ++hh) {
         const int h = g * A.G + hh;
         const int64_t hrow0 = (static_cast<int64_t>(b) * A.Hq + h) * L;
         const __amdgpu_buffer_rsrc_t qrs = rows_rsrc(A.qrot16, hrow0, L);
         const __amdgpu_buffer_rsrc_t drs = rows_rsrc(A.do16, hrow0, L);
-        const uint4* wrow = reinterpret_cast<const uint4*>(A.wts + (hrow0 + (j < L ? j : 0)) * kNV);
+        step(qrs, lds1, 0);
+        step(drs, lds1 + kBufBytes, 0);
+        entries(h, 1);
+        publish<13>();                                  // this head's window item has landed
 
-        // all of this head's weights for key row j (16-byte loads, issued before the head's first
-        // DMA: loads count in vmcnt with the DMAs, in issue order)
-        uint4 wl[(4 * kWG + 2 * MAXS * 2) / 4];
+        // ---- window terms on the matrix cores: for the wave's key rows 16w + rr and queries
+        // 16w + c (c < 32), dk_rot[rr] += sum_c A[rr][c] qrot[c], A[rr][c] = dS of query c at
+        // distance c - rr (zero outside 0..15); dv likewise with p and do ----
+        {
+            const char* wreg = lds0 + win_wregion(wave);
 #pragma unroll
-        for (int u = 0; u < (4 * kWG + 2 * MAXS * 2) / 4; ++u) wl[u] = wrow[u];
-        // 4 terms' weights: fp16 ds pairs and fp16 p pairs (masked terms are 0)
-        auto weights = [&](int v0, const bool (&ok)[4], uint32_t& ds01, uint32_t& ds23, uint32_t& p01, uint32_t& p23) {
-            const uint4 e = wl[v0 >> 2];
-            uint32_t w[4] = {e.x, e.y, e.z, e.w};
+            for (int kb = 0; kb < 2; ++kb) {
+                uint32_t e4[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) w[t] &= (ok[t] && j < L) ? 0xffffffffu : 0u;
-            p01 = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
-            p23 = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
-            ds01 = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
-            ds23 = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
-        };
-        // accumulate 4 terms: acc[m] += dot(w01, rows01[4m + x]) + dot(w23, rows23[4m + x]). The 16
-        // transposing reads are issued first; each result then passes an empty asm as a 64-bit
-        // value before it is split into its two dwords (an optimisation has been seen to fold the
-        // second dword of the read onto the first).
-        auto sum_terms = [&](float (&acc)[16], uint32_t w01, uint32_t w23, const char* lds, int base, int F) {
-            unsigned long long rv[16];
-#pragma unroll
-            for (int m = 0; m < 16; ++m)
-                rv[m] = __builtin_bit_cast(unsigned long long,
-                                           tr_read_h4(lds, (base | (((m >> 1) << 4) ^ F)) + 8 * (m & 1)));
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                asm volatile("" : "+v"(rv[m]));
-                const uint32_t lo = static_cast<uint32_t>(rv[m]), hi = static_cast<uint32_t>(rv[m] >> 32);
-                acc[m] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, w01), __builtin_bit_cast(h2_t, lo), acc[m], false);
-                acc[m] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, w23), __builtin_bit_cast(h2_t, hi), acc[m], false);
-            }
-        };
-
-        // items of this head: window (rotated q, then do), steps (rotated q, then do); an item
-        // sits in lds0 (rotated q) or lds1 (do); the next item is issued before each is summed
-        // (global loads count in vmcnt with the DMAs, in issue order: weights are loaded before the
-        // DMA that must stay in flight while they are used)
-        uint32_t wq[kWG][4];                            // window weights (ds01, ds23, p01, p23)
-#pragma unroll
-        for (int gg = 0; gg < kWG; ++gg) {
-            const bool ok[4] = {term_ok(4 * gg, false), term_ok(4 * gg + 1, false), term_ok(4 * gg + 2, false),
-                                term_ok(4 * gg + 3, false)};
-            weights(4 * gg, ok, wq[gg][0], wq[gg][1], wq[gg][2], wq[gg][3]);
-        }
-        if (hh == 0) st.window(qrs, lds0, j0);          // later heads: issued at the end of the previous head
-        st.window(drs, lds1, j0);
-        publish<3>();                                   // the rotated-q window has landed
-#pragma unroll
-        for (int gg = 0; gg < kWG; ++gg)
-            if (4 * gg <= W) sum_terms(dk, wq[gg][0], wq[gg][1], lds0, (swin + 4 * gg) * kRowBytes, swz(swin + 4 * gg));
-        publish<0>();                                   // do window landed, lds0 free
-        if (n_steps > 0) step(qrs, lds0, 0);
-        else if (hh + 1 < A.G) st.window(rows_rsrc(A.qrot16, hrow0 + L, L), lds0, j0);
-#pragma unroll
-        for (int gg = 0; gg < kWG; ++gg)
-            if (4 * gg <= W) sum_terms(dv, wq[gg][2], wq[gg][3], lds1, (swin + 4 * gg) * kRowBytes, swz(swin + 4 * gg));
-        publish<0>();
-#pragma unroll
-        for (int k = 0; k < MAXS; ++k) {
-            if (k < n_steps) {
-                // rotated-q step k in lds0; its weights, then issue do step k
-                uint32_t w4[4];
-                {
-                    const int n0 = 2 * k, n1 = 2 * k + 1;
-                    const bool i0n = n0 < A.n_off && A.off[n0].interp, i1n = n1 < A.n_off && A.off[n1].interp;
-                    const int a0 = A.off[n0].a, a1 = A.off[n1].a;
-                    const bool ok[4] = {n0 < A.n_off && term_ok(a0, i0n), n0 < A.n_off && term_ok(a0 + 1, false),
-                                        n1 < A.n_off && term_ok(a1, i1n), n1 < A.n_off && term_ok(a1 + 1, false)};
-                    weights(16 + 4 * k, ok, w4[0], w4[1], w4[2], w4[3]);
+                for (int ee = 0; ee < 4; ++ee) {
+                    const int c = 16 * kb + 4 * lg + ee;
+                    const int d = c - lr;
+                    const uint32_t v = *reinterpret_cast<const uint32_t*>(wreg + 64 * c + 4 * (d & 15));
+                    e4[ee] = (d >= 0 && d < kNW) ? v : 0u;
                 }
-                step(drs, lds1, k);
-                sum_terms(dk, w4[0], w4[1], lds0, rgbase, rgsw);
-                publish<0>();                           // do step k landed, lds0 free
-                if (k + 1 < n_steps) step(qrs, lds0, k + 1);
-                else if (hh + 1 < A.G) st.window(rows_rsrc(A.qrot16, hrow0 + L, L), lds0, j0);
-                sum_terms(dv, w4[2], w4[3], lds1, rgbase, rgsw);
+                // (p, dS) pairs: dS in the high halves (dk), p in the low halves (dv)
+                const u2_t a_dk = {__builtin_amdgcn_perm(e4[1], e4[0], 0x07060302u),
+                                   __builtin_amdgcn_perm(e4[3], e4[2], 0x07060302u)};
+                const u2_t a_dv = {__builtin_amdgcn_perm(e4[1], e4[0], 0x05040100u),
+                                   __builtin_amdgcn_perm(e4[3], e4[2], 0x05040100u)};
+                const int slot = 16 * wave + 16 * kb + 4 * lg + te;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    const h4_t bq = tr_read_h4(lds0, blk_addr(slot, nb));
+                    const h4_t bd = tr_read_h4(lds0 + kBufBytes, blk_addr(slot, nb));
+                    dk[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4_t, a_dk), bq, dk[nb], 0, 0, 0);
+                    dv[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4_t, a_dv), bd, dv[nb], 0, 0, 0);
+                }
+            }
+        }
+        put_w(0);
+        publish<0>();                                   // step 0 and its weights are in place, lds0 is free
+
+        // ---- rung steps: step k is item k + 1, in lds(k + 1) % 2 ----
+#pragma unroll
+        for (int k = 0; k < MAXS + 1; ++k) {
+            if (k < n_items) {
+                if (k + 1 < n_items) {
+                    step(qrs, buf(k + 2), k + 1);
+                    step(drs, buf(k + 2) + kBufBytes, k + 1);
+                    entries(h, k + 2);
+                } else if (hh + 1 < A.G) {
+                    window_item(h + 1);                 // the last item sits in lds1
+                }
+                if (k < n_steps) {
+                    uint4 w[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) w[q] = wst[k & 1][rbase16 + q];
+                    sum_rungs(dk, w, false, buf(k + 1));
+                    sum_rungs(dv, w, true, buf(k + 1) + kBufBytes);
+                }
+                if (k + 1 < n_steps) put_w(k + 1);
                 publish<0>();
             }
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    if (j < L) {
-        // dk: lane x holds dims 16x + m of dk_rot; RoPE transposed at key position j, the other
-        // half of pair (16x + m) mod 32 in lane x ^ 2
-        const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(j) * (kPairs / 2) + 8 * (x & 1);
-        const float sg = (x < 2) ? 1.f : -1.f;
-        float v[16];
+    // ---- dk: RoPE transposed at each key position. Element 4m + c of the permuted rows is dim
+    // 16c + m; the lane's element E = 8 ch + 4 (b' & 1) + c is dim 16c + 2 ch + (b' & 1); its
+    // pair partner (dim +- 32) is element E ^ 2, in lane lr ^ 2 ----
+    {
+        const int bq_ = lr >> 2, c = lr & 3;
+        const float sg = (c < 2) ? 1.f : -1.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float4 t = ct[u];
-            const float o0 = quad_f<kXor2>(dk[2 * u]), o1 = quad_f<kXor2>(dk[2 * u + 1]);
-            v[2 * u] = fmaf(sg * o0, t.y, dk[2 * u] * t.x);
-            v[2 * u + 1] = fmaf(sg * o1, t.w, dk[2 * u + 1] * t.z);
+        for (int q = 0; q < 4; ++q) {
+            const int jr = j0 + rbase16 + q;
+            const float2* cs = reinterpret_cast<const float2*>(A.cstab) + static_cast<int64_t>(jr < L ? jr : 0) * kPairs;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                const int ch = nb + 4 * (bq_ >> 1);
+                const int pair = (16 * c + 2 * ch + (bq_ & 1)) & 31;
+                const float2 t = cs[pair];
+                const float other = quad_f<kXor2>(dk[nb][q]);
+                dk[nb][q] = fmaf(sg * other, t.y, dk[nb][q] * t.x);
+            }
         }
-        const int64_t orow = (static_cast<int64_t>(bg) * L + j) * kD;
-        bf16_t* dkr = static_cast<bf16_t*>(A.dk) + orow + 16 * x;
-        *reinterpret_cast<uint4*>(dkr) = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
-                                                    pack_bf2(v[6], v[7]));
-        *reinterpret_cast<uint4*>(dkr + 8) = make_uint4(pack_bf2(v[8], v[9]), pack_bf2(v[10], v[11]),
-                                                        pack_bf2(v[12], v[13]), pack_bf2(v[14], v[15]));
     }
-    // dv: lane x holds dims 4m + x; regroup through LDS (lds1 is free) so that lane x writes dims
-    // 16x..16x+15
+    // ---- regroup through LDS into rows of 64 dims (bf16), then 16-byte stores ----
+    {
+        bf16_t* tk = reinterpret_cast<bf16_t*>(lds0);
+        bf16_t* tv = reinterpret_cast<bf16_t*>(lds1);
+        const int bq_ = lr >> 2, c = lr & 3;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int ch = nb + 4 * (bq_ >> 1);
+            const int ek = 16 * c + 2 * ch + (bq_ & 1);                 // dim of dk's element
+            const int ev = 8 * ch + 4 * (bq_ & 1) + c;                  // dim of dv's element
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = rbase16 + q;
+                tk[row * kD + ek] = static_cast<bf16_t>(pack_bf2(dk[nb][q], 0.f) & 0xffffu);
+                tv[row * kD + ev] = static_cast<bf16_t>(pack_bf2(dv[nb][q], 0.f) & 0xffffu);
+            }
+        }
+    }
     __syncthreads();
     {
-        bf16_t* t = reinterpret_cast<bf16_t*>(lds1) + r * kD;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) t[4 * m + x] = static_cast<bf16_t>(pack_bf2(dv[m], 0.f) & 0xffffu);
-    }
-    __syncthreads();
-    if (j < L) {
-        const uint4* t = reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(lds1) + r * kD + 16 * x);
-        uint4* dvr = reinterpret_cast<uint4*>(static_cast<bf16_t*>(A.dv) + (static_cast<int64_t>(bg) * L + j) * kD + 16 * x);
-        dvr[0] = t[0];
-        dvr[1] = t[1];
+        const int row = threadIdx.x >> 2, part = threadIdx.x & 3;      // 16 dims of one row
+        const int j = j0 + row;
+        if (j < L) {
+            const int64_t orow = (static_cast<int64_t>(bg) * L + j) * kD + 16 * part;
+            const uint4* sk = reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(lds0) + row * kD + 16 * part);
+            const uint4* sv = reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(lds1) + row * kD + 16 * part);
+            uint4* gk = reinterpret_cast<uint4*>(static_cast<bf16_t*>(A.dk) + orow);
+            uint4* gv = reinterpret_cast<uint4*>(static_cast<bf16_t*>(A.dv) + orow);
+            gk[0] = sk[0];
+            gk[1] = sk[1];
+            gv[0] = sv[0];
+            gv[1] = sv[1];
+        }
     }
 }
 

@@ -95,14 +95,17 @@ struct BwdArgs {
     const float* cstab;  // [L, 32, 2] cos, sin
     void* qrot16;        // [B, Hq, L, 64] fp16 rotated queries, dims permuted
     void* do16;          // [B, Hq, L, 64] fp16 copy of dout (dim order)
-    uint32_t* wts;       // [B, Hq, L, kNV] per key row and term: fp16 p (low), fp16 dS/sqrt(D) (high)
+    // per query and head, fp16 pairs (p low, dS/sqrt(D) high): the window distances 0..15 of each
+    // query ([B, Hq, L, kNW]), and each rung's entry without its coefficients, rung-major
+    // ([B, Hq, kNR, L])
+    uint32_t* wwin;
+    uint32_t* wrung;
     float qscale;        // log2(e)/sqrt(D)
     int32_t xcd_map;
 };
 
-// Terms per key row in the weight table of the matrix-core backward: 16 window distances, then
-// (near, far) of 16 rungs.
-constexpr int kNV = 48;
+// Entries per query in the weight tables of the matrix-core backward: 16 window distances, 16 rungs.
+constexpr int kNW = 16, kNR = 16;
 
 hipError_t launch_rope_keys(int dtype, const RopeKeysArgs& a, hipStream_t s);
 // forward layout: keys in dim order, values permuted, table x qscale; backward layout: keys

@@ -27,6 +27,7 @@ constexpr int kWinPad = 4;               // window slot of row i0 - W - 4 is 0: 
 constexpr int kBlkSlots = 72;            // 65 (+2 for the second rung) rows, 9 DMA groups
 constexpr int kBlkBytes = kBlkSlots * kRowBytes;
 constexpr int kBufBytes = 2 * kBlkBytes; // one staging buffer: a window or a rung step
+constexpr int kWinBytes = 96 * kRowBytes; // a window (rows j0 + s at slot s < 96)
 constexpr int kWG = 4;                   // window groups (W <= 15)
 constexpr int kBcast0 = 0x00, kBcast1 = 0x55, kBcast2 = 0xAA, kBcast3 = 0xFF;   // quad_perm [r,r,r,r]
 constexpr int kXor2 = 0x4E;              // quad_perm [2,3,0,1]: lane x ^ 2
