@@ -94,22 +94,42 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     auto buf = [&](int j) -> char* { return (j & 1) ? lds1 : lds0; };
     const int jw = i0 - W - kWinPad;
 
-    // ---- prologue: key and value windows, q and do of head h0 + x, key and value step 0 ----
+    // ---- prologue: key and value windows; q and do of the wave's 16 positions and 4 heads (1 KB
+    // contiguous loads, turned into one row per lane through the wave's part of lds1); key and
+    // value step 0 ----
     st.window(krs, lds0, jw);
     st.window(vrs, lds0 + kBufBytes, jw);
-    const int64_t qrow = (static_cast<int64_t>(b) * A.Hq + h0 + x) * L + (active ? i : 0);
+    // row of linear-view slot s (head h0 + (s >> 4), position i0 + 16w + (s & 15)), or -1 past L
+    auto lin_row = [&](int s) -> int64_t {
+        const int pos = i0 + 16 * wave + (s & 15);
+        return pos < L ? (static_cast<int64_t>(b) * A.Hq + h0 + (s >> 4)) * L + pos : -1;
+    };
     uint4 qraw[8], draw[8];
     float4 ctab[16];
     {
-        const bf16_t* qr = static_cast<const bf16_t*>(A.q) + qrow * kD;
-        const bf16_t* dr = static_cast<const bf16_t*>(A.dout) + qrow * kD;
+        uint4 ql[8], dl[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) qraw[c] = *reinterpret_cast<const uint4*>(qr + 8 * c);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) draw[c] = *reinterpret_cast<const uint4*>(dr + 8 * c);
+        for (int u = 0; u < 8; ++u) {
+            const int64_t row = lin_row(lin_slot(lane, u));
+            const int64_t off = (row < 0 ? 0 : row) * kD + (lane & 7) * 8;
+            ql[u] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(A.q) + off);
+            dl[u] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(A.dout) + off);
+        }
         const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(active ? i : 0) * (kPairs / 2);
 #pragma unroll
         for (int u = 0; u < 16; ++u) ctab[u] = ct[u];
+        char* reg = lds1 + wave * 8192;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) *reinterpret_cast<uint4*>(reg + lin_view_addr(lane, u)) = ql[u];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) qraw[c] = *reinterpret_cast<const uint4*>(reg + row_view_addr(pq, x, c));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) *reinterpret_cast<uint4*>(reg + lin_view_addr(lane, u)) = dl[u];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) draw[c] = *reinterpret_cast<const uint4*>(reg + row_view_addr(pq, x, c));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();                   // every wave is done with lds1
+        asm volatile("" ::: "memory");
     }
     kv_step(lds1, 0);
 
@@ -170,15 +190,6 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             dp[d] = accv[r];
         }
     }
-    // (stores count in vmcnt too: issued where the next wait drains everything anyway)
-    if (active) {
-        uint4* qo = reinterpret_cast<uint4*>(static_cast<f16_t*>(A.qrot16) + qrow * kD);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) qo[c] = make_uint4(q[c][0], q[c][1], q[c][2], q[c][3]);
-        uint4* dq16 = reinterpret_cast<uint4*>(static_cast<f16_t*>(A.do16) + qrow * kD);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) dq16[c] = make_uint4(dov[c][0], dov[c][1], dov[c][2], dov[c][3]);
-    }
     publish<0>();                                       // step 0 has landed, buffer 0 is free
 #pragma unroll
     for (int k = 0; k < MAXS; ++k) {
@@ -215,6 +226,24 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     // ---- key window and key step 0 again (pass C), under the softmax ----
     st.window(krs, lds0, jw);
     step(krs, lds1, 0);
+    // from here on the value halves of both buffers are free: 8 KB per wave
+    char* const treg = (wave < 2 ? lds0 : lds1) + kBufBytes + (wave & 1) * 8192;
+    // rotated q and do (fp16) for the key side, through treg: 1 KB contiguous stores (they count
+    // in vmcnt after the key DMAs; the wait before pass C counts them conservatively)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            *reinterpret_cast<uint4*>(treg + row_view_addr(pq, x, c)) =
+                t ? make_uint4(dov[c][0], dov[c][1], dov[c][2], dov[c][3]) : make_uint4(q[c][0], q[c][1], q[c][2], q[c][3]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint4 v = *reinterpret_cast<const uint4*>(treg + lin_view_addr(lane, u));
+            const int64_t row = lin_row(lin_slot(lane, u));
+            if (row >= 0)
+                *reinterpret_cast<uint4*>(static_cast<f16_t*>(t ? A.do16 : A.qrot16) + row * kD + (lane & 7) * 8) = v;
+        }
+    }
 
     float mx = kNegInf;
 #pragma unroll
@@ -300,19 +329,31 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    if (active) {
-        // ---- the key side's weights: the window row of this query (64 bytes) and one entry of
-        // each rung's row (rung-major, so a wave's stores of one rung are contiguous) ----
-        uint4* wr = reinterpret_cast<uint4*>(A.wwin + qrow * kNW);
+    // (pass C read only the key halves: treg is still the wave's own)
+    // ---- the key side's weights: the window row of this query (64 bytes; through treg as 16
+    // rows per head, chunk c at c ^ x, 1 KB contiguous stores) and one entry of each rung's row
+    // (rung-major, so a wave's stores of one rung are contiguous) ----
 #pragma unroll
-        for (int c = 0; c < kNW / 4; ++c) wr[c] = make_uint4(wq[4 * c], wq[4 * c + 1], wq[4 * c + 2], wq[4 * c + 3]);
+    for (int c = 0; c < kNW / 4; ++c)
+        *reinterpret_cast<uint4*>(treg + (16 * x + pq) * (kNW * 4) + ((c ^ x) << 4)) =
+            make_uint4(wq[4 * c], wq[4 * c + 1], wq[4 * c + 2], wq[4 * c + 3]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int sl = 16 * u + (lane >> 2), c = lane & 3;
+        const uint4 v = *reinterpret_cast<const uint4*>(treg + sl * (kNW * 4) + ((c ^ u) << 4));
+        const int64_t row = lin_row(sl);
+        if (row >= 0) *reinterpret_cast<uint4*>(A.wwin + row * kNW + 4 * c) = v;
+    }
+    if (active) {
         uint32_t* rr = A.wrung + (static_cast<int64_t>(b) * A.Hq + h0 + x) * kNR * L + i;
 #pragma unroll
         for (int n = 0; n < kNR; ++n) rr[static_cast<int64_t>(n) * L] = (n < MAXK) ? wq[4 * kWG + n] : 0u;
-
+    }
+    {
         // ---- dq: RoPE transposed at position i. Lane x holds dims 16x + m of heads 0..3; the
-        // other half of pair (16x + m) mod 32 is in lane x ^ 2 ----
-        const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(i) * (kPairs / 2) + 8 * (x & 1);
+        // other half of pair (16x + m) mod 32 is in lane x ^ 2. Rows go through treg: 1 KB
+        // contiguous stores ----
+        const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(active ? i : 0) * (kPairs / 2) + 8 * (x & 1);
         float2 cs[16];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -329,8 +370,6 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
                 const float other = quad_f<kXor2>(o[m][r]);
                 v[m] = fmaf(sg * other, cs[m].y, o[m][r] * cs[m].x);
             }
-            bf16_t* drow = static_cast<bf16_t*>(A.dq) + (static_cast<int64_t>(b) * A.Hq + h0 + r) * L * kD +
-                           static_cast<int64_t>(i) * kD + 16 * x;
             uint4 lo, hi;
             lo.x = pack_bf2(v[0], v[1]);
             lo.y = pack_bf2(v[2], v[3]);
@@ -340,8 +379,14 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             hi.y = pack_bf2(v[10], v[11]);
             hi.z = pack_bf2(v[12], v[13]);
             hi.w = pack_bf2(v[14], v[15]);
-            *reinterpret_cast<uint4*>(drow) = lo;
-            *reinterpret_cast<uint4*>(drow + 8) = hi;
+            *reinterpret_cast<uint4*>(treg + row_view_addr(pq, r, 2 * x)) = lo;
+            *reinterpret_cast<uint4*>(treg + row_view_addr(pq, r, 2 * x + 1)) = hi;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const uint4 v = *reinterpret_cast<const uint4*>(treg + lin_view_addr(lane, u));
+            const int64_t row = lin_row(lin_slot(lane, u));
+            if (row >= 0) *reinterpret_cast<uint4*>(static_cast<bf16_t*>(A.dq) + row * kD + (lane & 7) * 8) = v;
         }
     }
 

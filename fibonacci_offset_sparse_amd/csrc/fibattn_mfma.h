@@ -182,6 +182,25 @@ struct Stager {
     }
 };
 
+// Wave-private LDS transposes between the lanes' rows and contiguous memory. In the row view lane
+// (p', x) holds the 128-byte row of head x at position p' of the wave as 8 chunks; the row's slot
+// in the wave's 8 KB region is s = 16 x + p' (head-major: a head's 16 positions are 2 KB of
+// contiguous memory). In the linear view, instruction u (0..7) covers slots 8u..8u+7: lane l
+// holds chunk l & 7 of slot 8u + (l >> 3), so a wave's global access is 1 KB of contiguous rows.
+// Chunk c of slot s sits at chunk c ^ tr_f(s); a pass of 16 lanes then touches 16 distinct banks
+// in both views.
+__device__ __forceinline__ int tr_f(int s) { return ((s >> 1) & 1) | ((s >> 4) << 1); }
+__device__ __forceinline__ int row_view_addr(int pq, int x, int c) {
+    const int s = 16 * x + pq;
+    return s * kRowBytes + ((c ^ tr_f(s)) << 4);
+}
+__device__ __forceinline__ int lin_view_addr(int lane, int u) {
+    const int s = 8 * u + (lane >> 3);
+    return s * kRowBytes + (((lane & 7) ^ tr_f(s)) << 4);
+}
+// the slot (head-major) of linear-view instruction u for this lane
+__device__ __forceinline__ int lin_slot(int lane, int u) { return 8 * u + (lane >> 3); }
+
 // Buffer resource over rows [row0, row0 + L) of 128-byte rows.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int64_t row0, int L) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base) + row0 * kRowBytes), 0,
