@@ -63,72 +63,94 @@ constexpr int kWgsPerCu = 4;
 //    16c + 2u and 16c + 2u + 1, which hold RoPE pairs 2u, 2u + 1, 16 + 2u, 17 + 2u whole); values
 //    in dim order; the table as is.
 // ------------------------------------------------------------------------------------------------
+// A thread takes one position j and kPrepRows (batch, head) rows of it: the cos/sin of its 4
+// RoPE pairs are computed once for all of them, and every row's loads are issued before any is
+// used.
+constexpr int kPrepRows = 4;
+
 template <bool KS>
 __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int u = static_cast<int>(gid & 7);
-    const int64_t row_id = gid >> 3;
-    if (row_id >= static_cast<int64_t>(A.n_bh) * A.L) return;
-    const int j = static_cast<int>(row_id % A.L);
-    const int64_t row = row_id * kD;
+    const int64_t pj = gid >> 3;                        // (row group, position)
+    const int j = static_cast<int>(pj % A.L);
+    const int grp = static_cast<int>(pj / A.L);
+    if (grp * kPrepRows >= A.n_bh) return;
     const bf16_t* ks = static_cast<const bf16_t*>(A.k);
     const bf16_t* vs = static_cast<const bf16_t*>(A.v);
     const float sc = A.qscale;
-    if (!KS) {
-        const float4 x1 = load4<bf16_t>(ks + row + 4 * u);
-        const float4 x2 = load4<bf16_t>(ks + row + kPairs + 4 * u);
-        // elements 8u..8u+7 are dims 16c + 2u (c = 0..3), then 16c + 2u + 1
-        uint32_t vp[4];
+    // the thread's pairs: 4u..4u+3 (forward: keys in dim order), or 2u, 2u + 1, 16 + 2u, 17 + 2u
+    // (backward: keys permuted, element 8u + e holding dim 16e + 2u (e < 4) or 16(e - 4) + 2u + 1)
+    int pr[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) vp[c] = *reinterpret_cast<const uint32_t*>(vs + row + 16 * c + 2 * u);
-        const float a[4] = {x1.x, x1.y, x1.z, x1.w};
-        const float b[4] = {x2.x, x2.y, x2.z, x2.w};
-        float r1[4], r2[4];
-        float2 cs[4];
+    for (int e = 0; e < 4; ++e) pr[e] = KS ? ((e >> 1) * 16 + 2 * u + (e & 1)) : 4 * u + e;
+    float2 cs[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            rope_cos_sin(j, A.fr.hi[4 * u + e], A.fr.lo[4 * u + e], cs[e].x, cs[e].y);
-            r1[e] = a[e] * cs[e].x - b[e] * cs[e].y;
-            r2[e] = b[e] * cs[e].x + a[e] * cs[e].y;
+    for (int e = 0; e < 4; ++e) rope_cos_sin(j, A.fr.hi[pr[e]], A.fr.lo[pr[e]], cs[e].x, cs[e].y);
+    if (grp == 0) {   // the table: [L][32] (cos, sin) x qscale
+        float2* t = reinterpret_cast<float2*>(A.cs) + static_cast<int64_t>(j) * kPairs;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[pr[e]] = make_float2(cs[e].x * sc, cs[e].y * sc);
+    }
+    // loads of every row first
+    uint32_t kw[kPrepRows][4], vw[kPrepRows][4];
+#pragma unroll
+    for (int r = 0; r < kPrepRows; ++r) {
+        const int bh = grp * kPrepRows + r;
+        const int64_t row = (static_cast<int64_t>(bh < A.n_bh ? bh : 0) * A.L + j) * kD;
+        if (!KS) {
+            // keys: pairs 4u..4u+3 (x at dims 4u.., y at 32 + 4u..); values: dims 16c + 2u, + 1
+            const uint2 a = *reinterpret_cast<const uint2*>(ks + row + 4 * u);
+            const uint2 b2 = *reinterpret_cast<const uint2*>(ks + row + kPairs + 4 * u);
+            kw[r][0] = a.x; kw[r][1] = a.y; kw[r][2] = b2.x; kw[r][3] = b2.y;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) vw[r][c] = *reinterpret_cast<const uint32_t*>(vs + row + 16 * c + 2 * u);
+        } else {
+            // keys: dims 16c + 2u, 16c + 2u + 1; values: elements 8u..8u+7 in dim order
+#pragma unroll
+            for (int c = 0; c < 4; ++c) kw[r][c] = *reinterpret_cast<const uint32_t*>(ks + row + 16 * c + 2 * u);
+            const uint4 v4 = *reinterpret_cast<const uint4*>(vs + row + 8 * u);
+            vw[r][0] = v4.x; vw[r][1] = v4.y; vw[r][2] = v4.z; vw[r][3] = v4.w;
         }
-        store4<f16_t>(A.k16 + row + 4 * u, make_float4(r1[0], r1[1], r1[2], r1[3]));
-        store4<f16_t>(A.k16 + row + kPairs + 4 * u, make_float4(r2[0], r2[1], r2[2], r2[3]));
-        store4<f16_t>(A.v16 + row + 8 * u, make_float4(bf16_lo(vp[0]), bf16_lo(vp[1]), bf16_lo(vp[2]), bf16_lo(vp[3])));
-        store4<f16_t>(A.v16 + row + 8 * u + 4, make_float4(bf16_hi(vp[0]), bf16_hi(vp[1]), bf16_hi(vp[2]), bf16_hi(vp[3])));
-        if (row_id < A.L) {   // the first (batch, head) writes the table: [L][32] (cos, sin) x qscale
-            float4* t = reinterpret_cast<float4*>(A.cs + (static_cast<int64_t>(j) * kPairs + 4 * u) * 2);
-            t[0] = make_float4(cs[0].x * sc, cs[0].y * sc, cs[1].x * sc, cs[1].y * sc);
-            t[1] = make_float4(cs[2].x * sc, cs[2].y * sc, cs[3].x * sc, cs[3].y * sc);
-        }
-    } else {
-        // key dims 16c + 2u, 16c + 2u + 1 for c = 0..3: pairs p0 = 2u, p0 + 1 (x: c = 0, y: c = 2)
-        // and p1 = 16 + 2u, p1 + 1 (x: c = 1, y: c = 3)
-        uint32_t kp[4];
+    }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kp[c] = *reinterpret_cast<const uint32_t*>(ks + row + 16 * c + 2 * u);
-        const int pr[4] = {2 * u, 2 * u + 1, 16 + 2 * u, 17 + 2 * u};
-        float2 cs[4];
+    for (int r = 0; r < kPrepRows; ++r) {
+        const int bh = grp * kPrepRows + r;
+        if (bh >= A.n_bh) break;
+        const int64_t row = (static_cast<int64_t>(bh) * A.L + j) * kD;
+        if (!KS) {
+            const float a[4] = {bf16_lo(kw[r][0]), bf16_hi(kw[r][0]), bf16_lo(kw[r][1]), bf16_hi(kw[r][1])};
+            const float b[4] = {bf16_lo(kw[r][2]), bf16_hi(kw[r][2]), bf16_lo(kw[r][3]), bf16_hi(kw[r][3])};
+            float r1[4], r2[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rope_cos_sin(j, A.fr.hi[pr[e]], A.fr.lo[pr[e]], cs[e].x, cs[e].y);
-        // x, y of each pair
-        const float x[4] = {bf16_lo(kp[0]), bf16_hi(kp[0]), bf16_lo(kp[1]), bf16_hi(kp[1])};
-        const float y[4] = {bf16_lo(kp[2]), bf16_hi(kp[2]), bf16_lo(kp[3]), bf16_hi(kp[3])};
-        float rx[4], ry[4];
+            for (int e = 0; e < 4; ++e) {
+                r1[e] = a[e] * cs[e].x - b[e] * cs[e].y;
+                r2[e] = b[e] * cs[e].x + a[e] * cs[e].y;
+            }
+            store4<f16_t>(A.k16 + row + 4 * u, make_float4(r1[0], r1[1], r1[2], r1[3]));
+            store4<f16_t>(A.k16 + row + kPairs + 4 * u, make_float4(r2[0], r2[1], r2[2], r2[3]));
+            // values permuted: elements 8u..8u+7 are dims 16c + 2u (c = 0..3), then 16c + 2u + 1
+            store4<f16_t>(A.v16 + row + 8 * u,
+                          make_float4(bf16_lo(vw[r][0]), bf16_lo(vw[r][1]), bf16_lo(vw[r][2]), bf16_lo(vw[r][3])));
+            store4<f16_t>(A.v16 + row + 8 * u + 4,
+                          make_float4(bf16_hi(vw[r][0]), bf16_hi(vw[r][1]), bf16_hi(vw[r][2]), bf16_hi(vw[r][3])));
+        } else {
+            // x, y of pairs 2u, 2u + 1 (dims 2u, 2u + 1 and 32 + ..) and 16 + 2u, 17 + 2u
+            const float x[4] = {bf16_lo(kw[r][0]), bf16_hi(kw[r][0]), bf16_lo(kw[r][1]), bf16_hi(kw[r][1])};
+            const float y[4] = {bf16_lo(kw[r][2]), bf16_hi(kw[r][2]), bf16_lo(kw[r][3]), bf16_hi(kw[r][3])};
+            float rx[4], ry[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            rx[e] = x[e] * cs[e].x - y[e] * cs[e].y;
-            ry[e] = y[e] * cs[e].x + x[e] * cs[e].y;
-        }
-        // element 8u + e: e < 4 is dim 16e + 2u, e >= 4 is dim 16(e - 4) + 2u + 1
-        store4<f16_t>(A.k16 + row + 8 * u, make_float4(rx[0], rx[2], ry[0], ry[2]));
-        store4<f16_t>(A.k16 + row + 8 * u + 4, make_float4(rx[1], rx[3], ry[1], ry[3]));
-        const uint4 vw = *reinterpret_cast<const uint4*>(vs + row + 8 * u);
-        store4<f16_t>(A.v16 + row + 8 * u, make_float4(bf16_lo(vw.x), bf16_hi(vw.x), bf16_lo(vw.y), bf16_hi(vw.y)));
-        store4<f16_t>(A.v16 + row + 8 * u + 4, make_float4(bf16_lo(vw.z), bf16_hi(vw.z), bf16_lo(vw.w), bf16_hi(vw.w)));
-        if (row_id < A.L) {   // the table: pairs 2u, 2u + 1 and 16 + 2u, 17 + 2u
-            float4* t = reinterpret_cast<float4*>(A.cs + static_cast<int64_t>(j) * kPairs * 2);
-            t[u] = make_float4(cs[0].x * sc, cs[0].y * sc, cs[1].x * sc, cs[1].y * sc);
-            t[8 + u] = make_float4(cs[2].x * sc, cs[2].y * sc, cs[3].x * sc, cs[3].y * sc);
+            for (int e = 0; e < 4; ++e) {
+                rx[e] = x[e] * cs[e].x - y[e] * cs[e].y;
+                ry[e] = y[e] * cs[e].x + x[e] * cs[e].y;
+            }
+            // element 8u + e: e < 4 is dim 16e + 2u, e >= 4 is dim 16(e - 4) + 2u + 1
+            store4<f16_t>(A.k16 + row + 8 * u, make_float4(rx[0], rx[2], ry[0], ry[2]));
+            store4<f16_t>(A.k16 + row + 8 * u + 4, make_float4(rx[1], rx[3], ry[1], ry[3]));
+            store4<f16_t>(A.v16 + row + 8 * u,
+                          make_float4(bf16_lo(vw[r][0]), bf16_hi(vw[r][0]), bf16_lo(vw[r][1]), bf16_hi(vw[r][1])));
+            store4<f16_t>(A.v16 + row + 8 * u + 4,
+                          make_float4(bf16_lo(vw[r][2]), bf16_hi(vw[r][2]), bf16_lo(vw[r][3]), bf16_hi(vw[r][3])));
         }
     }
 }
@@ -363,7 +385,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
 }  // namespace
 
 hipError_t launch_prep_kv16(const PrepArgs& A, bool backward_layout, hipStream_t s) {
-    const int64_t threads = static_cast<int64_t>(A.n_bh) * A.L * 8;
+    const int64_t threads = static_cast<int64_t>((A.n_bh + kPrepRows - 1) / kPrepRows) * A.L * 8;
     const unsigned blocks = static_cast<unsigned>((threads + 255) / 256);
     if (backward_layout)
         hipLaunchKernelGGL(prep_kv16_kernel<true>, dim3(blocks), dim3(256), 0, s, A);
