@@ -162,11 +162,12 @@ template <int MAXS>
 __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     constexpr float kNegInf = -__builtin_huge_valf();
     constexpr int MAXK = 2 * MAXS;
-    // Two staging buffers used in turn. An item is the key window, a step of two key rungs, the
-    // value window or a step of two value rungs: item j sits in buffer j % 2. A rung step holds
-    // rung 2k at slot 0 (block A) and rung 2k + 1 at slot kBlkSlots (block B); a window holds
-    // rows i0 - W - 4 + s at slot s. Two arrays, always named at compile time where they are
-    // read: the compiler then knows an LDS read does not touch the buffer the DMA in flight fills.
+    // Two staging buffers used in turn. An item is the key near block (the window and the rungs
+    // with a <= 63), a far step of two key rungs, the value near block or a far step of two value
+    // rungs. The near block holds rows i0 - 64 + s at slot s; a far step holds rung 2k at slot 0
+    // (block A) and rung 2k + 1 at slot kBlkSlots (block B). Two arrays, always named at compile
+    // time where they are read: the compiler then knows an LDS read does not touch the buffer the
+    // DMA in flight fills.
     __shared__ __attribute__((aligned(1024))) char lds0[kBufBytes];
     __shared__ __attribute__((aligned(1024))) char lds1[kBufBytes];
 
@@ -192,6 +193,13 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     for (int n = 0; n < A.n_off; ++n)
         if (i0 + kTile - 1 >= A.off[n].a + A.off[n].interp) n_reach = n + 1;
     const int n_steps = (n_reach + 1) >> 1;
+    // near rungs: the prefix with a <= 63 (near and far rows inside the near block). Rung pairs
+    // k < kn come from the near block, kn even; pairs kn .. n_steps - 1 are far steps, pair k in
+    // buffer (k + 1) % 2.
+    int n_near = 0;
+    for (int n = 0; n < n_reach; ++n)
+        if (A.off[n].a <= kNear - 1) n_near = n + 1;
+    const int kn = (n_near >> 1) & ~1;
 
     const int64_t kv_row0 = static_cast<int64_t>(bg) * L;
     const __amdgpu_buffer_rsrc_t krs = rows_rsrc(A.kstage, kv_row0, L);
@@ -203,11 +211,11 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     auto step = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int k) {
         st.step(rs, dst, 2 * k < n_reach, i0 - A.off[2 * k].a - 1, 2 * k + 1 < n_reach, i0 - A.off[2 * k + 1].a - 3);
     };
-    const int jw = i0 - W - kWinPad;                    // the window's row at slot 0
+    const int jn = i0 - kNear;                          // the near block's row at slot 0
     auto buf = [&](int j) -> char* { return (j & 1) ? lds1 : lds0; };
 
-    // ---- prologue: key window (item 0), q, item 1 (key step 0, or the value window) ----
-    st.window(krs, buf(0), jw);
+    // ---- prologue: key near block (item 0), q, item 1 (key far step kn) ----
+    st.near(krs, buf(0), jn);
     uint4 qraw[8];
     float4 ctab[16];
     {
@@ -219,7 +227,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) ctab[u] = ct[u];
     }
-    step(krs, buf(1), 0);                         // (zero rows when no rung is reached)
+    step(krs, buf(1), kn);                        // (zero rows when no far rung is reached)
 
     // q of head h0 + x, rotated at its position and scaled (the table carries qscale), fp16:
     // register chunk c holds dims 8c..8c+7; RoPE pairs 8c..8c+7 are chunks c and c + 4
@@ -237,17 +245,29 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
             q[c + 4][m] = pack_h2(y0 * t.x + x0 * t.y, y1 * t.z + x1 * t.w);
         }
     }
-    publish<6>();                                       // the key window has landed
+    publish<6>();                                       // the key near block has landed
 
     // ---- phase A: scores of the lane's head x (base 2) ----
-    // Key step k computes from buffer (k + 1) % 2 after issuing step k + 1 into the other buffer
-    // (the barrier that ended step k - 1 released it); the wait before each barrier is for step
-    // k + 1, the only load in flight.
+    // Far step k computes from buffer (k + 1) % 2 after issuing step k + 1 into the other buffer
+    // (the barrier that ended the item before released it); the wait before each barrier is for
+    // step k + 1, the only load in flight.
     float s[4 * kWG + MAXK];
+    // lane x of a rung group: rung 2k + (x >> 1), near (x even) or far row
+    auto score = [&](const f4_t& acc, int k) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int n = 2 * k + e;
+            if (n < n_reach) {
+                const float sc = fmaf(A.off[n].t, acc[2 * e + 1] - acc[2 * e], acc[2 * e]);
+                s[4 * kWG + n] = (active && i >= A.off[n].a + A.off[n].interp) ? sc : kNegInf;
+            }
+        }
+    };
     {
-        // item 0: lane x reads window distance d = 4g + x, slot p - d + W + 4 (pads d > W read
-        // staged rows)
-        const int s0 = p - x + W + kWinPad;
+        // item 0: lane x reads window distance d = 4g + x, slot p - d + 64 (pads d > W read
+        // staged rows); then the near rung pairs: rung 2k + (x >> 1), near row i - a at slot
+        // p + 64 - a (x even) or far row one slot down
+        const int s0 = p - x + kNear;
 #pragma unroll
         for (int g = 0; g < kWG; ++g) {
             f4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -258,34 +278,33 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
                 s[d] = (active && d <= W && i >= d) ? acc[r] : kNegInf;
             }
         }
+#pragma unroll
+        for (int k = 0; k < MAXS; ++k) {
+            s[4 * kWG + 2 * k] = kNegInf;
+            s[4 * kWG + 2 * k + 1] = kNegInf;
+            if (k < kn) {
+                const int sl = p + kNear - ((x >> 1) ? A.off[2 * k + 1].a : A.off[2 * k].a) - (x & 1);
+                score(row_dot_group(q, buf(0), sl * kRowBytes, swz(sl)), k);
+            }
+        }
         publish<0>();                                   // item 1 has landed, buffer 0 is free
     }
-    // lane x of a rung group: rung 2k + (x >> 1), near (x even) or far row
+    // far steps: lane x reads rung 2k + (x >> 1), near (x even) or far row
     const int rslot = p + ((x >> 1) ? kBlkSlots + 2 : 0) + ((x & 1) ? 0 : 1);
     const int rbase = rslot * kRowBytes, rsw = swz(rslot);
 #pragma unroll
     for (int k = 0; k < MAXS; ++k) {
-        s[4 * kWG + 2 * k] = kNegInf;
-        s[4 * kWG + 2 * k + 1] = kNegInf;
-        if (k < n_steps) {                              // item k + 1, in buffer (k + 1) % 2
+        if (k >= kn && k < n_steps) {                   // buffer (k + 1) % 2
             if (k + 1 < n_steps) step(krs, buf(k + 2), k + 1);
-            const f4_t acc = row_dot_group(q, buf(k + 1), rbase, rsw);
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int n = 2 * k + e;
-                if (n < n_reach) {
-                    const float sc = fmaf(A.off[n].t, acc[2 * e + 1] - acc[2 * e], acc[2 * e]);
-                    s[4 * kWG + n] = (active && i >= A.off[n].a + A.off[n].interp) ? sc : kNegInf;
-                }
-            }
+            score(row_dot_group(q, buf(k + 1), rbase, rsw), k);
             publish<0>();
         }
     }
 
-    // ---- value window into buffer 0 and value step 0 into buffer 1 (both free after the last
-    // barrier), under the softmax ----
-    st.window(vrs, lds0, jw);
-    step(vrs, lds1, 0);
+    // ---- value near block into buffer 0 and value far step kn into buffer 1 (both free after
+    // the last barrier), under the softmax ----
+    st.near(vrs, lds0, jn);
+    step(vrs, lds1, kn);
 
     // ---- exact softmax; weights as fp16 groups of 4 ----
     float m = kNegInf;
@@ -298,6 +317,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
         s[y] = __builtin_amdgcn_exp2f(s[y] - m);   // v_exp_f32; s - m <= 0
         l += s[y];
     }
+    asm volatile("" : "+v"(l));                     // the sum now: the exponentials die with the packing
     uint32_t pw[kWG][2], po[MAXS][2];
 #pragma unroll
     for (int g = 0; g < kWG; ++g) {
@@ -331,22 +351,31 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[e] = (f4_t){0.f, 0.f, 0.f, 0.f};
     {
-        publish<6>();                                   // the value window has landed
-        // window group g: slot pt - 4g - kt + W + 4
-        const int sv = pt - kt + W + kWinPad;
+        publish<6>();                                   // the value near block has landed
+        // window group g: slot pt - 4g - kt + 64
+        const int sv = pt - kt + kNear;
 #pragma unroll
         for (int g = 0; g < kWG; ++g)
             if (4 * g <= W) row_sum_group(o, pw[g][0], pw[g][1], lds0, (sv - 4 * g) * kRowBytes, swz(sv - 4 * g));
-        if (n_steps > 0) publish<0>();                  // value step 0 has landed, buffer 0 is free
+        // near rung pairs: slot kt of the group is rung 2k + (kt >> 1), near row pt - a at slot
+        // pt + 64 - a (kt even) or far row one slot down
+#pragma unroll
+        for (int k = 0; k < MAXS; ++k) {
+            if (k < kn) {
+                const int sl = pt + kNear - ((kt >> 1) ? A.off[2 * k + 1].a : A.off[2 * k].a) - (kt & 1);
+                row_sum_group(o, po[k][0], po[k][1], lds0, sl * kRowBytes, swz(sl));
+            }
+        }
+        if (n_steps > kn) publish<0>();                 // value far step kn has landed, buffer 0 is free
     }
     {
-        // slot k of a rung group: near and far of rung 2k (block A, slots pt + 1, pt) and of
-        // rung 2k + 1 (block B, slots pt + 3, pt + 2); value step k sits in buffer (k + 1) % 2
+        // slot k of a far step's group: near and far of rung 2k (block A, slots pt + 1, pt) and
+        // of rung 2k + 1 (block B, slots pt + 3, pt + 2); value step k sits in buffer (k + 1) % 2
         const int sv = (kt < 2) ? pt + 1 - kt : kBlkSlots + pt + 5 - kt;
         const int vbase = sv * kRowBytes, vsw = swz(sv);
 #pragma unroll
         for (int k = 0; k < MAXS; ++k) {
-            if (k < n_steps) {
+            if (k >= kn && k < n_steps) {
                 if (k + 1 < n_steps) step(vrs, buf(k + 2), k + 1);
                 row_sum_group(o, po[k][0], po[k][1], buf(k + 1), vbase, vsw);
                 if (k + 1 < n_steps) publish<0>();

@@ -28,6 +28,9 @@ constexpr int kBlkSlots = 72;            // 65 (+2 for the second rung) rows, 9 
 constexpr int kBlkBytes = kBlkSlots * kRowBytes;
 constexpr int kBufBytes = 2 * kBlkBytes; // one staging buffer: a window or a rung step
 constexpr int kWinBytes = 96 * kRowBytes; // a window (rows j0 + s at slot s < 96)
+// The near block of a tile of 64 positions i0..i0+63: key rows i0 - 64 .. i0 + 63 (slot s holds
+// row i0 - kNear + s). It holds the window (W <= 15) and both rows of every rung with a <= 63.
+constexpr int kNear = 64;
 constexpr int kWG = 4;                   // window groups (W <= 15)
 constexpr int kBcast0 = 0x00, kBcast1 = 0x55, kBcast2 = 0xAA, kBcast3 = 0xFF;   // quad_perm [r,r,r,r]
 constexpr int kXor2 = 0x4E;              // quad_perm [2,3,0,1]: lane x ^ 2
@@ -160,6 +163,14 @@ struct Stager {
     __device__ __forceinline__ void window(const __amdgpu_buffer_rsrc_t& rs, char* dst, int j0) const {
 #pragma unroll
         for (int u = 0; u < 3; ++u) {
+            const int g = wave + 4 * u;
+            dma16(rs, dst + g * 1024, j0 + 8 * g, gpar);
+        }
+    }
+    // near block: rows j0 + s at slot s, s < 128 (16 groups, 4 per wave)
+    __device__ __forceinline__ void near(const __amdgpu_buffer_rsrc_t& rs, char* dst, int j0) const {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
             const int g = wave + 4 * u;
             dma16(rs, dst + g * 1024, j0 + 8 * g, gpar);
         }
