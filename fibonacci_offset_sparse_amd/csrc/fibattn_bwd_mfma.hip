@@ -78,6 +78,13 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     for (int n = 0; n < A.n_off; ++n)
         if (i0 + kTile - 1 >= A.off[n].a + A.off[n].interp) n_reach = n + 1;
     const int n_steps = (n_reach + 1) >> 1;
+    // near rungs: the prefix with a <= 63 (near and far rows inside the near block, key rows
+    // i0 - 64 .. i0 + 63). Rung pairs k < kn come from the near block, kn even; pairs
+    // kn .. n_steps - 1 are far steps, pair k in buffer (k + 1) % 2.
+    int n_near = 0;
+    for (int n = 0; n < n_reach; ++n)
+        if (A.off[n].a <= kNear - 1) n_near = n + 1;
+    const int kn = (n_near >> 1) & ~1;
 
     const int64_t kv_row0 = static_cast<int64_t>(bg) * L;
     const __amdgpu_buffer_rsrc_t krs = rows_rsrc(A.kstage, kv_row0, L);
@@ -92,13 +99,13 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         step(vrs, dst + kBufBytes, k);
     };
     auto buf = [&](int j) -> char* { return (j & 1) ? lds1 : lds0; };
-    const int jw = i0 - W - kWinPad;
+    const int jn = i0 - kNear;                          // the near block's row at slot 0
 
-    // ---- prologue: key and value windows; q and do of the wave's 16 positions and 4 heads (1 KB
-    // contiguous loads, turned into one row per lane through the wave's part of lds1); key and
-    // value step 0 ----
-    st.window(krs, lds0, jw);
-    st.window(vrs, lds0 + kBufBytes, jw);
+    // ---- prologue: key and value near blocks; q and do of the wave's 16 positions and 4 heads
+    // (1 KB contiguous loads, turned into one row per lane through the wave's part of lds1); key
+    // and value far step kn ----
+    st.near(krs, lds0, jn);
+    st.near(vrs, lds0 + kBufBytes, jn);
     // row of linear-view slot s (head h0 + (s >> 4), position i0 + 16w + (s & 15)), or -1 past L
     auto lin_row = [&](int s) -> int64_t {
         const int pos = i0 + 16 * wave + (s & 15);
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         __builtin_amdgcn_s_barrier();                   // every wave is done with lds1
         asm volatile("" ::: "memory");
     }
-    kv_step(lds1, 0);
+    kv_step(lds1, kn);
 
     // q rotated at its position (unscaled), fp16, in the keys' permuted order: word 2m holds dims
     // (m, 16 + m), word 2m + 1 dims (32 + m, 48 + m); register chunk c = words 4c..4c+3
@@ -168,14 +175,39 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) dov[c][u] = pack_h2(bf16_lo(w4[u]), bf16_hi(w4[u]));
     }
-    publish<12>();                                      // the key and value windows have landed
+    publish<12>();                                      // the key and value near blocks have landed
 
     // ---- pass AB: scores s (base 2) with the keys, dP = do . value row with the values, and for
     // each rung far - near of both products ----
     float s[4 * kWG + MAXK], sd[MAXK], dp[4 * kWG + MAXK], dpd[MAXK];
-    const int s0 = p - x + W + kWinPad;                 // window: lane x reads distance 4g + x
-    const int rslot = p + ((x >> 1) ? kBlkSlots + 2 : 0) + ((x & 1) ? 0 : 1);   // rung rows
+    const int s0 = p - x + kNear;                       // window: lane x reads distance 4g + x
+    const int rslot = p + ((x >> 1) ? kBlkSlots + 2 : 0) + ((x & 1) ? 0 : 1);   // far-step rung rows
     const int rbase = rslot * kRowBytes, rsw = swz(rslot);
+    // a rung pair's products (lane x: rung 2k + (x >> 1), near row for x even, far row for x odd)
+    auto pair_terms = [&](const f4_t& acc, const f4_t& accv, int k) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int n = 2 * k + e;
+            if (n < n_reach) {
+                const float t = A.off[n].t;
+                const float dd = (acc[2 * e + 1] - acc[2 * e]) * A.qscale;
+                const float sc = fmaf(t, dd, acc[2 * e] * A.qscale);
+                const bool ok = active && i >= A.off[n].a + A.off[n].interp;
+                s[4 * kWG + n] = ok ? sc : kNegInf;
+                sd[n] = ok ? dd : 0.f;
+                const float dv = accv[2 * e + 1] - accv[2 * e];
+                dp[4 * kWG + n] = fmaf(t, dv, accv[2 * e]);
+                dpd[n] = dv;
+            }
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k) {
+        s[4 * kWG + k] = kNegInf;
+        sd[k] = 0.f;
+        dp[4 * kWG + k] = 0.f;
+        dpd[k] = 0.f;
+    }
 #pragma unroll
     for (int g = 0; g < kWG; ++g) {
         f4_t acc = {0.f, 0.f, 0.f, 0.f}, accv = {0.f, 0.f, 0.f, 0.f};
@@ -190,42 +222,28 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             dp[d] = accv[r];
         }
     }
-    publish<0>();                                       // step 0 has landed, buffer 0 is free
+    // near rung pairs: near row i - a at slot p + 64 - a, far row one slot down
 #pragma unroll
     for (int k = 0; k < MAXS; ++k) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            s[4 * kWG + 2 * k + e] = kNegInf;
-            sd[2 * k + e] = 0.f;
-            dp[4 * kWG + 2 * k + e] = 0.f;
-            dpd[2 * k + e] = 0.f;
+        if (k < kn) {
+            const int sl = p + kNear - ((x >> 1) ? A.off[2 * k + 1].a : A.off[2 * k].a) - (x & 1);
+            pair_terms(row_dot_group(q, lds0, sl * kRowBytes, swz(sl)),
+                       row_dot_group(dov, lds0 + kBufBytes, sl * kRowBytes, swz(sl)), k);
         }
-        if (k < n_steps) {
-            if (k + 1 < n_steps) kv_step(buf(k + 2), k + 1);
-            const f4_t acc = row_dot_group(q, buf(k + 1), rbase, rsw);
-            const f4_t accv = row_dot_group(dov, buf(k + 1) + kBufBytes, rbase, rsw);
+    }
+    publish<0>();                                       // far step kn has landed, buffer 0 is free
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int n = 2 * k + e;
-                if (n < n_reach) {
-                    const float t = A.off[n].t;
-                    const float dd = (acc[2 * e + 1] - acc[2 * e]) * A.qscale;
-                    const float sc = fmaf(t, dd, acc[2 * e] * A.qscale);
-                    const bool ok = active && i >= A.off[n].a + A.off[n].interp;
-                    s[4 * kWG + n] = ok ? sc : kNegInf;
-                    sd[n] = ok ? dd : 0.f;
-                    const float dv = accv[2 * e + 1] - accv[2 * e];
-                    dp[4 * kWG + n] = fmaf(t, dv, accv[2 * e]);
-                    dpd[n] = dv;
-                }
-            }
+    for (int k = 0; k < MAXS; ++k) {
+        if (k >= kn && k < n_steps) {
+            if (k + 1 < n_steps) kv_step(buf(k + 2), k + 1);
+            pair_terms(row_dot_group(q, buf(k + 1), rbase, rsw), row_dot_group(dov, buf(k + 1) + kBufBytes, rbase, rsw), k);
             publish<0>();
         }
     }
 
-    // ---- key window and key step 0 again (pass C), under the softmax ----
-    st.window(krs, lds0, jw);
-    step(krs, lds1, 0);
+    // ---- key near block and key far step kn again (pass C), under the softmax ----
+    st.near(krs, lds0, jn);
+    step(krs, lds1, kn);
     // from here on the value halves of both buffers are free: 8 KB per wave
     char* const treg = (wave < 2 ? lds0 : lds1) + kBufBytes + (wave & 1) * 8192;
     // rotated q and do (fp16) for the key side, through treg: 1 KB contiguous stores (they count
@@ -299,7 +317,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         wo[k][0] = pack_h2(w[0], w[1]);
         wo[k][1] = pack_h2(w[2], w[3]);
     }
-    publish<6>();                                       // the key window has landed
+    publish<6>();                                       // the key near block has landed
 
     // ---- pass C: dq_rot = sum of weighted key rows (transposing reads of the permuted keys:
     // lane x gets element 4m + x, which is dim 16x + m) ----
@@ -309,10 +327,19 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[e] = (f4_t){0.f, 0.f, 0.f, 0.f};
     {
-        const int sv = pt - kt + W + kWinPad;
+        const int sv = pt - kt + kNear;
 #pragma unroll
         for (int g = 0; g < kWG; ++g)
             if (4 * g <= W) row_sum_group(o, ww[g][0], ww[g][1], lds0, (sv - 4 * g) * kRowBytes, swz(sv - 4 * g));
+        // near rung pairs: slot kt of the group is rung 2k + (kt >> 1), near row (kt even) at
+        // pt + 64 - a, far row one slot down
+#pragma unroll
+        for (int k = 0; k < MAXS; ++k) {
+            if (k < kn) {
+                const int sl = pt + kNear - ((kt >> 1) ? A.off[2 * k + 1].a : A.off[2 * k].a) - (kt & 1);
+                row_sum_group(o, wo[k][0], wo[k][1], lds0, sl * kRowBytes, swz(sl));
+            }
+        }
         publish<0>();
     }
     {
@@ -320,7 +347,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         const int vbase = sv * kRowBytes, vsw = swz(sv);
 #pragma unroll
         for (int k = 0; k < MAXS; ++k) {
-            if (k < n_steps) {
+            if (k >= kn && k < n_steps) {
                 if (k + 1 < n_steps) step(krs, buf(k + 2), k + 1);
                 row_sum_group(o, wo[k][0], wo[k][1], buf(k + 1), vbase, vsw);
                 if (k + 1 < n_steps) publish<0>();
