@@ -437,17 +437,13 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
 // ------------------------------------------------------------------------------------------------
 // bwd_k_dot
 // ------------------------------------------------------------------------------------------------
-// The window weight block of wave w: the window rows (64 bytes) of the 32 queries its 16 key rows
-// read in the window, staged in the free space after the two row windows of a window item.
-__device__ __forceinline__ int win_wregion(int wave) {
-    return (wave < 2 ? 0 : kBufBytes) + kWinBytes + (wave & 1) * 2048;
-}
-
 template <int MAXS>
 __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     // Two item buffers used in turn, each a rotated-query part and a do part (kBufBytes each).
-    // Items of a query head: its window (the rotated-query and do windows and the window weights),
-    // then its rung steps, padded to an odd count so that every head's window sits in lds0.
+    // Items of a query head: its near block (query rows j0 .. j0 + 127 of the rotated queries and
+    // of do: the window and every rung pair with a <= 63), then its far steps (two larger rungs
+    // each), padded to an odd count so that every head's near block sits in lds0. The near
+    // block's buffer also holds the weights of the near rung pairs (2 KB after each part).
     __shared__ __attribute__((aligned(1024))) char lds0[2 * kBufBytes];
     __shared__ __attribute__((aligned(1024))) char lds1[2 * kBufBytes];
     // a rung step's weights per key row: (dS near, dS far) of its two rungs, then (p near, p far)
@@ -471,7 +467,15 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     for (int n = 0; n < A.n_off; ++n)
         if (j0 + A.off[n].a < L) n_reach = n + 1;
     const int n_steps = (n_reach + 1) >> 1;
-    const int n_items = n_steps | 1;                    // rung items per head (odd)
+    // near rungs: the prefix with a <= 63 (both query rows of every key row of the tile inside the
+    // near block). Pairs k < kn come from the near block (kn even, at most 4); pairs
+    // kn .. n_far - 1 are far steps, pair k in buffer (k + 1) % 2, n_far odd so that the last one
+    // sits in lds1.
+    int n_near = 0;
+    for (int n = 0; n < n_reach; ++n)
+        if (A.off[n].a <= kNear - 1) n_near = n + 1;
+    const int kn = min((n_near >> 1) & ~1, 4);
+    const int n_far = max(n_steps, kn + 1) | 1;
 
     // Lanes follow v_mfma_f32_16x16x16f16: lane l = 16 lg + lr holds A[lr][4 lg + 0..3],
     // B[4 lg + 0..3][lr] and D[4 lg + 0..3][lr]. Its outputs (window and rungs alike) are key rows
@@ -511,20 +515,17 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dma_dst(reinterpret_cast<char*>(&went[k & 1][wave & 1][64 * (wave >> 1)])),
                                                  4, (q0 + lane) * 4, 0, 0, 0);
     };
-    // the window item of head h: rotated-query and do rows j0 + s at slot s (3 + 3 instructions
-    // per wave), the wave's window weights (2) and the entries of step 0 (1)
-    auto window_item = [&](int h) {
+    // the near item of head h: rotated-query and do rows j0 + s at slot s < 128 (4 + 4
+    // instructions per wave) and the entries of far pair kn (1)
+    auto near_item = [&](int h) {
         const int64_t hrow0 = (static_cast<int64_t>(b) * A.Hq + h) * L;
-        st.window(rows_rsrc(A.qrot16, hrow0, L), lds0, j0);
-        st.window(rows_rsrc(A.do16, hrow0, L), lds0 + kBufBytes, j0);
-        const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(
-            reinterpret_cast<char*>(A.wwin + hrow0 * kNW), 0, L * kNW * 4, kRsrcWord3);
-        const int vrow = (j0 + 16 * wave + (lane >> 2)) * (kNW * 4) + (lane & 3) * 16;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ws, dma_dst(lds0 + win_wregion(wave) + u * 1024), 16,
-                                                     vrow + u * 16 * (kNW * 4), 0, 0, 0);
-        entries(h, 0);
+        st.near(rows_rsrc(A.qrot16, hrow0, L), lds0, j0);
+        st.near(rows_rsrc(A.do16, hrow0, L), lds0 + kBufBytes, j0);
+        entries(h, kn);
+    };
+    // the weights of near pair k (< 4) in lds0: 64 rows of 16 bytes after the near block's rows
+    auto wnear = [&](int k) -> uint4* {
+        return reinterpret_cast<uint4*>(lds0 + (k < 2 ? 0 : kBufBytes) + kNear * 2 * kRowBytes + (k & 1) * 1024);
     };
     // rung step weights: thread (row wrow, part wv) builds one word of wst for key row j0 + wrow:
     // rung 2k + (wv & 1), dS halves (wv < 2) or p halves, (near, far) times (1 - t, t)
@@ -544,12 +545,12 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     // is split into its two dwords (an optimisation has been seen to fold the second dword of the
     // read onto the first).
     const int rbase16 = 16 * wave + 4 * lg;
-    // term te of key row r: near / far of rung 2k at slots r, r + 1, of rung 2k + 1 at 74 + r,
-    // 75 + r; element block nb of it is at radr[q] ^ (nb << 4)
+    // far steps: term te of key row r: near / far of rung 2k at slots r, r + 1, of rung 2k + 1 at
+    // 74 + r, 75 + r; element block nb of it is at radr[q] ^ (nb << 4)
     int radr[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) radr[q] = blk_addr(rbase16 + q + (te & 1) + (te >> 1) * (kBlkSlots + 2), 0);
-    auto sum_rungs = [&](f4_t (&acc)[4], const uint4 (&w)[4], bool use_p, const char* lds) {
+    auto sum_rungs = [&](f4_t (&acc)[4], const uint4 (&w)[4], bool use_p, const char* lds, const int (&radr)[4]) {
 #pragma unroll
         for (int q0 = 0; q0 < 4; q0 += 2) {
             unsigned long long rv[8];
@@ -570,32 +571,66 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
         }
     };
 
-    window_item(g * A.G);
+    near_item(g * A.G);
     for (int hh = 0; hh < A.G; ++hh) {
         const int h = g * A.G + hh;
         const int64_t hrow0 = (static_cast<int64_t>(b) * A.Hq + h) * L;
         const __amdgpu_buffer_rsrc_t qrs = rows_rsrc(A.qrot16, hrow0, L);
         const __amdgpu_buffer_rsrc_t drs = rows_rsrc(A.do16, hrow0, L);
-        step(qrs, lds1, 0);
-        step(drs, lds1 + kBufBytes, 0);
-        entries(h, 1);
-        publish<13>();                                  // this head's window item has landed
+        // window weights of the wave's key rows 16w + lr and queries 16w + c (c = 16 kb + 4 lg +
+        // ee), distance c - lr (zero outside 0..15 or past L), and the (p, dS) entries of the near
+        // pairs for the weight table below: loaded before this head's first DMA (loads count in
+        // vmcnt with the DMAs, in issue order)
+        uint32_t e4w[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int ee = 0; ee < 4; ++ee) {
+                const int c = 16 * kb + 4 * lg + ee;
+                const int d = c - lr;
+                const int qr = j0 + 16 * wave + c;
+                const bool ok = d >= 0 && d < kNW && qr < L;
+                const uint32_t v = A.wwin[(hrow0 + (ok ? qr : 0)) * kNW + (d & 15)];
+                e4w[kb][ee] = ok ? v : 0u;
+            }
+        }
+        uint32_t enr[4], efr[4];
+        {
+            const uint32_t* wr = A.wrung + hrow0 * kNR;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int n = 2 * k + (wv & 1);
+                const int qn = j0 + wrow + A.off[n].a;
+                const bool okn = k < kn && qn < L, okf = k < kn && qn + 1 < L;
+                const uint32_t vn = wr[static_cast<int64_t>(n) * L + (okn ? qn : 0)];
+                const uint32_t vf = wr[static_cast<int64_t>(n) * L + (okf ? qn + 1 : 0)];
+                enr[k] = okn ? vn : 0u;
+                efr[k] = okf ? vf : 0u;
+            }
+        }
+        step(qrs, lds1, kn);
+        step(drs, lds1 + kBufBytes, kn);
+        entries(h, kn + 1);
+        // the near pairs' weights (same words as the far steps' table)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (k < kn) {
+                const int n = 2 * k + (wv & 1);
+                const float t = A.off[n].t;
+                const uint32_t pr = __builtin_amdgcn_perm(efr[k], enr[k], (wv >> 1) ? 0x05040100u : 0x07060302u);
+                const h2_t c = {static_cast<_Float16>(1.f - t), static_cast<_Float16>(t)};
+                reinterpret_cast<uint32_t*>(&wnear(k)[wrow])[wv] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, pr) * c);
+            }
+        }
+        publish<13>();                                  // this head's near item and weights are in place
 
         // ---- window terms on the matrix cores: for the wave's key rows 16w + rr and queries
         // 16w + c (c < 32), dk_rot[rr] += sum_c A[rr][c] qrot[c], A[rr][c] = dS of query c at
         // distance c - rr (zero outside 0..15); dv likewise with p and do ----
         {
-            const char* wreg = lds0 + win_wregion(wave);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                uint32_t e4[4];
-#pragma unroll
-                for (int ee = 0; ee < 4; ++ee) {
-                    const int c = 16 * kb + 4 * lg + ee;
-                    const int d = c - lr;
-                    const uint32_t v = *reinterpret_cast<const uint32_t*>(wreg + 64 * c + 4 * (d & 15));
-                    e4[ee] = (d >= 0 && d < kNW) ? v : 0u;
-                }
+                const uint32_t (&e4)[4] = e4w[kb];
                 // (p, dS) pairs: dS in the high halves (dk), p in the low halves (dv)
                 const u2_t a_dk = {__builtin_amdgcn_perm(e4[1], e4[0], 0x07060302u),
                                    __builtin_amdgcn_perm(e4[3], e4[2], 0x07060302u)};
@@ -611,26 +646,42 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
                 }
             }
         }
-        put_w(0);
-        publish<0>();                                   // step 0 and its weights are in place, lds0 is free
+        // ---- near rung pairs: term te of key row r is rung 2k + (te >> 1), near row j + a at
+        // slot r + a (te even) or far row one slot up ----
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (k < kn) {
+                const int ak = (te >> 1) ? A.off[2 * k + 1].a : A.off[2 * k].a;
+                int nadr[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) nadr[q] = blk_addr(rbase16 + q + ak + (te & 1), 0);
+                uint4 w[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w[q] = wnear(k)[rbase16 + q];
+                sum_rungs(dk, w, false, lds0, nadr);
+                sum_rungs(dv, w, true, lds0 + kBufBytes, nadr);
+            }
+        }
+        put_w(kn);
+        publish<0>();                                   // far pair kn and its weights are in place, lds0 is free
 
-        // ---- rung steps: step k is item k + 1, in lds(k + 1) % 2 ----
+        // ---- far steps: pair k (kn <= k < n_far) in lds(k + 1) % 2 ----
 #pragma unroll
         for (int k = 0; k < MAXS + 1; ++k) {
-            if (k < n_items) {
-                if (k + 1 < n_items) {
+            if (k >= kn && k < n_far) {
+                if (k + 1 < n_far) {
                     step(qrs, buf(k + 2), k + 1);
                     step(drs, buf(k + 2) + kBufBytes, k + 1);
                     entries(h, k + 2);
                 } else if (hh + 1 < A.G) {
-                    window_item(h + 1);                 // the last item sits in lds1
+                    near_item(h + 1);                   // the last item sits in lds1
                 }
                 if (k < n_steps) {
                     uint4 w[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) w[q] = wst[k & 1][rbase16 + q];
-                    sum_rungs(dk, w, false, buf(k + 1));
-                    sum_rungs(dv, w, true, buf(k + 1) + kBufBytes);
+                    sum_rungs(dk, w, false, buf(k + 1), radr);
+                    sum_rungs(dv, w, true, buf(k + 1) + kBufBytes, radr);
                 }
                 if (k + 1 < n_steps) put_w(k + 1);
                 publish<0>();
