@@ -5,7 +5,9 @@
 A step is one pass of the whole path over one batch: for each of the 16 layers of the paper's
 model shape (B = 32, L = 1024, 8 query / 2 key-value heads, head dim 64, bfloat16 storage, W = 12,
 Fibonacci base, linear stagger alpha_l = 0.5 + l/15), the forward call (RoPE'd keys, attention,
-lse) and the backward call (dq, dk, dv). Each layer has its own input set in HBM (16 sets, more
+lse) and the backward call (dq, dk, dv). Both use one workspace: the backward reads the rotated
+keys and the values the forward staged there and skips its own prep wherever the library reports
+that this prep would write the same arrays. Each layer has its own input set in HBM (16 sets, more
 than the 256 MB Infinity Cache holds), resident before timing starts. The same protocol is then
 run once more at the 4x extrapolation shape (B = 8, L = 4096, coprime stagger) and reported under
 "l4096".
@@ -160,32 +162,37 @@ class Layers:
         self.dv = [torch.empty(B, Hkv, L, D, dtype=w.torch_dtype, device=dev) for _ in range(self.n_sets)]
         self.dalpha = torch.empty(1, dtype=torch.float32, device=dev)
         self.dtheta = torch.empty(1, dtype=torch.float32, device=dev)
-        self.ws_f = torch.empty(fa.fibattn_fwd_workspace_bytes(B, L, Hkv), dtype=torch.uint8, device=dev)
-        self.ws_b = torch.empty(fa.fibattn_bwd_workspace_bytes(B, L, Hq, Hkv, D, w.W, len(base)),
-                                dtype=torch.uint8, device=dev)
+        # one workspace for the forward and the backward: the forward's prep (rotated keys, fp16
+        # keys and values, the cos/sin table) is a prefix of it, and where the backward's own prep
+        # would write the same arrays the backward runs its query and key stages only
+        nbytes = max(fa.fibattn_fwd_workspace_bytes(B, L, Hkv), fa.fibattn_bwd_workspace_bytes(B, L, Hq, Hkv, D, w.W, len(base)))
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.reuse = [fa.fibattn_bwd_reuses_fwd_prep(a, w.W, base, B, L, Hq, Hkv, D) for a in self.alphas]
 
     def fwd(self, layer):
         q, k, v, _ = self.inputs[layer]
         self.fa.fibattn_fwd(q, k, v, self.alphas[layer], self.w.W, self.base, o=self.o[layer],
-                            lse=self.lse[layer], workspace=self.ws_f)
+                            lse=self.lse[layer], workspace=self.ws)
 
     def prep(self, layer):
-        self.fa.fibattn_fwd_prep(self.inputs[layer][1], self.inputs[layer][2], self.ws_f)
+        self.fa.fibattn_fwd_prep(self.inputs[layer][1], self.inputs[layer][2], self.ws)
 
     def attend(self, layer):
         q, _, v, _ = self.inputs[layer]
-        self.fa.fibattn_fwd_attend(q, v, self.alphas[layer], self.w.W, self.base, self.ws_f, self.o[layer],
+        self.fa.fibattn_fwd_attend(q, v, self.alphas[layer], self.w.W, self.base, self.ws, self.o[layer],
                                    self.lse[layer])
 
     def bwd_stages(self, layer, stages):
         q, k, v, do = self.inputs[layer]
         wd = self.want_dalpha[layer]
         self.fa.fibattn_bwd_stages(stages, q, k, v, do, self.alphas[layer], self.w.W, self.base, self.dq[layer],
-                                   self.dk[layer], self.dv[layer], self.ws_b, dalpha_dtheta=self.dadt[layer],
+                                   self.dk[layer], self.dv[layer], self.ws, dalpha_dtheta=self.dadt[layer],
                                    dalpha=self.dalpha if wd else None, dtheta=self.dtheta if wd else None)
 
     def bwd(self, layer):
-        self.bwd_stages(layer, self.fa.STAGE_ALL)
+        """The backward as a training step runs it, after this layer's forward on the same workspace."""
+        fa = self.fa
+        self.bwd_stages(layer, fa.STAGE_QUERY | fa.STAGE_KEY if self.reuse[layer] else fa.STAGE_ALL)
 
     def bwd_prep(self, layer):
         self.bwd_stages(layer, self.fa.STAGE_PREP)

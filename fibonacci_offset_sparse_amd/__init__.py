@@ -55,6 +55,8 @@ def _load() -> ctypes.CDLL:
                                         _P(_c_i32), _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                         _c_i32, _c_f64, _c_f64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                         _c_ptr, _c_ptr, _c_size, _c_ptr]),
+        "fibattn_bwd_reuses_fwd_prep": (_c_i32, [_c_f64, _c_i32, _P(_c_i32), _c_i32, _c_i32, _c_i32, _c_i32,
+                                                 _c_i32, _c_i32, _c_i32]),
         "fibattn_bwd_stages": (ctypes.c_int, [_c_i32, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_f64, _c_i32,
                                                _P(_c_i32), _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                                _c_i32, _c_f64, _c_f64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
@@ -237,6 +239,14 @@ def fibattn_fwd_attend(q: torch.Tensor, v: torch.Tensor, alpha: float, W: int, o
                                       workspace.data_ptr(), workspace.numel(), _stream(q.device, stream)))
 
 
+def fibattn_bwd_reuses_fwd_prep(alpha: float, W: int, offsets: Sequence[int], B: int, L: int, Hq: int,
+                                Hkv: int, D: int = 64, dtype: int = BF16) -> bool:
+    """Whether the backward's STAGE_PREP writes what fibattn_fwd_prep writes (then a backward whose
+    workspace holds the forward's prep of the same k, v may run STAGE_QUERY | STAGE_KEY only)."""
+    offs, K = _i32_array(offsets)
+    return bool(lib.fibattn_bwd_reuses_fwd_prep(float(alpha), int(W), offs, K, B, L, Hq, Hkv, D, dtype))
+
+
 def fibattn_bwd_stages(stages: int, q, k, v, dout, alpha: float, W: int, offsets: Sequence[int],
                        dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, workspace: torch.Tensor,
                        rope_theta: float = 1e4, dalpha_dtheta: float = 0.0,
@@ -300,6 +310,6 @@ __all__ = [
     "fibattn_status_string", "fibattn_last_error", "fibattn_base_offsets", "fibattn_alpha_schedule",
     "fibattn_alpha_from_theta", "fibattn_plan", "fibattn_fwd_workspace_bytes", "fibattn_fwd",
     "fibattn_fwd_prep", "fibattn_fwd_attend", "fibattn_bwd_workspace_bytes", "fibattn_bwd",
-    "fibattn_bwd_stages", "STAGE_PREP", "STAGE_QUERY", "STAGE_KEY", "STAGE_ALL",
+    "fibattn_bwd_stages", "fibattn_bwd_reuses_fwd_prep", "STAGE_PREP", "STAGE_QUERY", "STAGE_KEY", "STAGE_ALL",
     "FibAttnError", "lib", "LIB_PATH",
 ]

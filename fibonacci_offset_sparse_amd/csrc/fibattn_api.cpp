@@ -284,9 +284,8 @@ fibattn_status_t fibattn_fwd_prep(const void* k, const void* v, int32_t B, int32
         a.cs = reinterpret_cast<float*>(static_cast<char*>(workspace) + krot_bytes(B, L, Hkv));
         a.n_bh = B * Hkv;
         a.L = L;
-        a.qscale = score_scale();
         a.fr = make_freq(rope_theta);
-        e = launch_prep_kv16(a, false, static_cast<hipStream_t>(stream));
+        e = launch_prep_kv16(a, static_cast<hipStream_t>(stream));
     }
     if (e != hipSuccess) return hip_fail(e, "forward prep launch");
     return FIBATTN_OK;
@@ -357,6 +356,20 @@ size_t fibattn_bwd_workspace_bytes(int32_t B, int32_t L, int32_t Hq, int32_t Hkv
     return std::max(general, bwd_fast_layout(B, L, Hq, Hkv).total);
 }
 
+int32_t fibattn_bwd_reuses_fwd_prep(double alpha, int32_t W, const int32_t* offsets, int32_t K, int32_t B,
+                                    int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype) {
+    g_error[0] = '\0';
+    if (check_dims(B, L, Hq, Hkv, D, W, dtype, 1e4) != FIBATTN_OK) return 0;
+    if (check_offsets(alpha, W, offsets, K) != FIBATTN_OK) return 0;
+    if (dtype == FIBATTN_F32) return 1;   // both run rope_keys into the workspace's first array
+    const Plan plan = make_plan(alpha, W, offsets, K);
+    BwdArgs a{};
+    a.G = Hq / Hkv;
+    a.W = W;
+    a.n_off = plan.n_keep;
+    return bwd_mfma_supported(a) ? 1 : 0;   // else the backward rotates float32 keys of its own
+}
+
 fibattn_status_t fibattn_bwd_stages(int32_t stages, const void* q, const void* k, const void* v,
                                     const void* dout, double alpha, int32_t W, const int32_t* offsets, int32_t K,
                                     int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
@@ -421,7 +434,7 @@ fibattn_status_t fibattn_bwd_stages(int32_t stages, const void* q, const void* k
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (dtype == FIBATTN_BF16) {
-        // matrix-core path: staged fp16 rows in the backward layout
+        // matrix-core path: staged fp16 rows (the forward's layout)
         a.qscale = score_scale();
         a.xcd_map = 0;
         if (bwd_mfma_supported(a)) {
@@ -435,7 +448,6 @@ fibattn_status_t fibattn_bwd_stages(int32_t stages, const void* q, const void* k
             pa.cs = reinterpret_cast<float*>(w0 + krot_bytes(B, L, Hkv));
             pa.n_bh = B * Hkv;
             pa.L = L;
-            pa.qscale = 1.0f;
             pa.fr = a.fr;
             a.kstage = pa.k16;
             a.vstage = pa.v16;
@@ -446,7 +458,7 @@ fibattn_status_t fibattn_bwd_stages(int32_t stages, const void* q, const void* k
             a.wrung = reinterpret_cast<uint32_t*>(w0 + f.wrung);
             a.partial = reinterpret_cast<float*>(w0 + f.part);
             if (stages & FIBATTN_STAGE_PREP) {
-                e = launch_prep_kv16(pa, true, s);
+                e = launch_prep_kv16(pa, s);
                 if (e != hipSuccess) return hip_fail(e, "backward prep launch");
             }
             if (stages & (FIBATTN_STAGE_QUERY | FIBATTN_STAGE_KEY)) {

@@ -7,8 +7,9 @@
 // gather) and §2 "Per-layer scalar" (alpha = 0.5 + sigmoid(theta): the interpolation weight t is
 // what carries a gradient to alpha). Gradients are of sum(do * o).
 //
-// Inputs come from prep_kv16's backward layout: rotated keys with dims permuted (element 4m + c of
-// a row holds dim 16c + m) and values in dim order, fp16, plus the cos/sin table.
+// Inputs come from prep_kv16 (the layout the forward reads too): rotated keys and values with dims
+// permuted (element 4m + c of a row holds dim 16c + m), fp16, plus the cos/sin table. Contractions
+// over dims (scores, dP) read them against q and do permuted the same way.
 //
 //  * bwd_q_mfma: workgroup = (batch, kv head, 4 query heads, 64 positions), lanes as in the forward
 //    (fibattn_mfma.h). Three passes over the staged blocks:
@@ -167,13 +168,21 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             q[w >> 2][w & 3] = (w & 1) ? pack_h2(r[32 + m], r[48 + m]) : pack_h2(r[m], r[16 + m]);
         }
     }
-    // do as fp16 in dim order (the values are staged in dim order)
+    // do as fp16 in the values' permuted order (word 2m: dims (m, 16 + m), word 2m + 1: dims
+    // (32 + m, 48 + m))
     uint32_t dov[8][4];
+    {
+        auto dim = [&](int d) -> float {               // bf16 dim d of the raw row
+            const uint4& r = draw[d >> 3];
+            const int w = (d >> 1) & 3;
+            const uint32_t v = w == 0 ? r.x : w == 1 ? r.y : w == 2 ? r.z : r.w;
+            return (d & 1) ? bf16_hi(v) : bf16_lo(v);
+        };
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const uint32_t w4[4] = {draw[c].x, draw[c].y, draw[c].z, draw[c].w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) dov[c][u] = pack_h2(bf16_lo(w4[u]), bf16_hi(w4[u]));
+        for (int m = 0; m < 16; ++m) {
+            dov[m >> 1][2 * (m & 1)] = pack_h2(dim(m), dim(16 + m));
+            dov[m >> 1][2 * (m & 1) + 1] = pack_h2(dim(32 + m), dim(48 + m));
+        }
     }
     publish<12>();                                      // the key and value near blocks have landed
 
@@ -480,9 +489,9 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     // Lanes follow v_mfma_f32_16x16x16f16: lane l = 16 lg + lr holds A[lr][4 lg + 0..3],
     // B[4 lg + 0..3][lr] and D[4 lg + 0..3][lr]. Its outputs (window and rungs alike) are key rows
     // 16w + 4 lg + q (q = 0..3) at element E(nb, lr) of block nb = 0..3, where column t = 4b' + c
-    // is element 8 ch + 4 (b' & 1) + c with chunk ch = nb + 4 (b' >> 1) (elements of the permuted
-    // rotated-query rows for dk, dims of do for dv). With the slot swizzle, the transposing reads
-    // of a pass of 32 lanes then fall on distinct banks.
+    // is element 8 ch + 4 (b' & 1) + c with chunk ch = nb + 4 (b' >> 1) (of the permuted rows of
+    // the rotated queries for dk, of do for dv). With the slot swizzle, the transposing reads of
+    // a pass of 32 lanes then fall on distinct banks.
     const int lr = lane & 15, lg = lane >> 4;
     const int tb = lr & 3, te = lr >> 2;                // as a source of a transposing read: block tb, row te
     f4_t dk[4], dv[4];
@@ -718,13 +727,12 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
             const int ch = nb + 4 * (bq_ >> 1);
-            const int ek = 16 * c + 2 * ch + (bq_ & 1);                 // dim of dk's element
-            const int ev = 8 * ch + 4 * (bq_ & 1) + c;                  // dim of dv's element
+            const int ek = 16 * c + 2 * ch + (bq_ & 1);                 // dim of the element (dk and dv)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int row = rbase16 + q;
                 tk[row * kD + ek] = static_cast<bf16_t>(pack_bf2(dk[nb][q], 0.f) & 0xffffu);
-                tv[row * kD + ev] = static_cast<bf16_t>(pack_bf2(dv[nb][q], 0.f) & 0xffffu);
+                tv[row * kD + ek] = static_cast<bf16_t>(pack_bf2(dv[nb][q], 0.f) & 0xffffu);
             }
         }
     }

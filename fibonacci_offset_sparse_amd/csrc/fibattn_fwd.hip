@@ -15,6 +15,8 @@
 //    4 query heads of the key-value head (GQA). Pass 1 stages key blocks and keeps every score
 //    in registers; the softmax is then exact (no running rescale); pass 2 stages the value
 //    blocks and accumulates P.V.
+#include <type_traits>
+
 #include "fibattn_device.h"
 
 namespace fibattn {
@@ -165,6 +167,15 @@ __global__ __launch_bounds__(kTile * HPB) void fwd_attend_kernel(FwdArgs A) {
     rope_apply(q, cs_tab[p]);
 #pragma unroll
     for (int e = 0; e < kD; ++e) q[e] *= A.qscale;
+    if constexpr (std::is_same<KT, f16_t>::value) {
+        // the staged fp16 keys have their dims permuted (element 4m + c holds dim 16c + m): the
+        // scores take q in the same order
+        float t[kD];
+#pragma unroll
+        for (int e = 0; e < kD; ++e) t[e] = q[e];
+#pragma unroll
+        for (int e = 0; e < kD; ++e) q[e] = t[16 * (e & 3) + (e >> 2)];
+    }
 
     const int64_t kv_base = (static_cast<int64_t>(b) * A.Hkv + g) * L * kD;
     const KT* krot = static_cast<const KT*>(A.kstage) + kv_base;

@@ -7,8 +7,9 @@
 // each slot reads one contiguous block of rows.
 //
 // Inputs come from prep_kv16: keys rotated at their positions and values, both as fp16 rows of
-// 128 bytes. A workgroup owns (batch b, key-value head g, 4 query heads, 64 positions); wave w
-// takes positions 16w..16w+15 of the tile.
+// 128 bytes with dims permuted (element 4m + c holds dim 16c + m), and the cos/sin table. A
+// workgroup owns (batch b, key-value head g, 4 query heads, 64 positions); wave w takes positions
+// 16w..16w+15 of the tile.
 //
 // Every position is its own small product: its 4 query heads (they share the key-value head)
 // against the rows its slots read. v_mfma_f32_4x4x4_16b_f16 computes 16 independent 4x4x4
@@ -20,18 +21,20 @@
 //    the blended row, so q.(blend) = (1 - t) q.near + t q.far, and the value blend spreads its
 //    weight p as p (1 - t), p t. An integral rung keeps t = 0. Groups of 4 virtual slots are
 //    4 window distances, or (near, far) of two consecutive rungs.
-//  * QK: A = the 4 rows of the group (lane x reads virtual slot x's row), B = q of head x,
-//    K = 64 dims in 16 products. The result lane (p', x) holds head x's 4 scores: all of a
-//    lane's scores stay in its registers, the softmax is exact and in-lane (base 2).
-//  * PV: A = head x's 4 weights (the same lane), B = the 4 rows' values at 4 dims (built with
-//    v_perm from 16-byte reads), 16 products cover 64 dims; the result lane (p', x) holds dims
-//    16x..16x+15 of all 4 heads.
+//  * QK: A = the 4 rows of the group (lane x reads virtual slot x's row), B = q of head x in the
+//    keys' permuted order, K = 64 dims in 16 products. The result lane (p', x) holds head x's 4
+//    scores: all of a lane's scores stay in its registers, the softmax is exact and in-lane
+//    (base 2).
+//  * PV: A = head x's 4 weights (the same lane), B = the 4 rows' element 4m + x, read with the
+//    transposing ds_read_b64_tr_b16 from the permuted values (dim 16x + m), 16 products cover 64
+//    dims; the result lane (p', x) holds dims 16x..16x+15 of all 4 heads.
 //  * LDS: two staging buffers of 18 KB (four workgroups per CU), used in turn by a sequence of
-//    items: the key window (64 + W + 4 rows), the key rung steps (two rungs of 65 rows each), the
-//    value window, the value rung steps. Staging is LDS DMA (buffer_load ... lds): no VGPRs; rows
-//    before 0 or past L fall outside the buffer resource and arrive as zeros, so every row a
-//    lane reads is finite. Each item is issued while the one before it is being computed on,
-//    with one barrier per item after a counted vmcnt wait.
+//    items: the key near block (rows i0 - 64 .. i0 + 63: the window and both rows of every rung
+//    with floor(d) <= 63), the key far steps (two larger rungs of 65 rows each), the value near
+//    block, the value far steps. Staging is LDS DMA (buffer_load ... lds): no VGPRs; rows before
+//    0 or past L fall outside the buffer resource and arrive as zeros, so every row a lane reads
+//    is finite. Each item is issued while the one before it is being computed on, with one
+//    barrier per item after a counted vmcnt wait.
 //  * Banks: 16-byte chunk k of slot s sits at chunk k ^ ((s >> 1) & 7), so the same chunk of 16
 //    consecutive slots covers all 64 banks, and the second rung's block sits two slots up. Key
 //    reads (16 lanes per pass) are then free of bank conflicts for window and rung groups, as
@@ -53,22 +56,19 @@ using namespace mx;
 constexpr int kWgsPerCu = 4;
 
 // ------------------------------------------------------------------------------------------------
-// prep_kv16: rotated keys and values as fp16 rows, plus the cos/sin table of every position. Thread
-// = (row, u). Two layouts, each the one its kernels read:
-//  * forward (KS = false): keys in dim order (thread u: RoPE pairs 4u..4u+3); values with their
-//    dims permuted, element 4m + c holding dim 16c + m (thread u: elements 8u..8u+7), so that a
-//    transposing LDS read of 4 consecutive elements gives a lane 4 rows of its own dims; the
-//    table times qscale.
-//  * backward (KS = true): keys permuted the same way (thread u: elements 8u..8u+7, dims
-//    16c + 2u and 16c + 2u + 1, which hold RoPE pairs 2u, 2u + 1, 16 + 2u, 17 + 2u whole); values
-//    in dim order; the table as is.
+// prep_kv16: rotated keys and values as fp16 rows, plus the cos/sin table of every position. One
+// layout, read by the forward and the backward alike: both keys and values have their dims
+// permuted, element 4m + c holding dim 16c + m, so that a transposing LDS read of 4 consecutive
+// elements gives a lane 4 rows of its own 16 dims (a contraction over dims, as in the scores, reads
+// the permuted rows against a query permuted the same way). Thread u of a row writes elements
+// 8u..8u+7: dims 16e + 2u (e < 4) and 16(e - 4) + 2u + 1, which hold RoPE pairs 2u, 2u + 1,
+// 16 + 2u, 17 + 2u whole (pair m: dims m and m + 32). The table is cos and sin as they are.
 // ------------------------------------------------------------------------------------------------
 // A thread takes one position j and kPrepRows (batch, head) rows of it: the cos/sin of its 4
 // RoPE pairs are computed once for all of them, and every row's loads are issued before any is
 // used.
 constexpr int kPrepRows = 4;
 
-template <bool KS>
 __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int u = static_cast<int>(gid & 7);
@@ -78,39 +78,28 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
     if (grp * kPrepRows >= A.n_bh) return;
     const bf16_t* ks = static_cast<const bf16_t*>(A.k);
     const bf16_t* vs = static_cast<const bf16_t*>(A.v);
-    const float sc = A.qscale;
-    // the thread's pairs: 4u..4u+3 (forward: keys in dim order), or 2u, 2u + 1, 16 + 2u, 17 + 2u
-    // (backward: keys permuted, element 8u + e holding dim 16e + 2u (e < 4) or 16(e - 4) + 2u + 1)
+    // the thread's pairs 2u, 2u + 1, 16 + 2u, 17 + 2u
     int pr[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pr[e] = KS ? ((e >> 1) * 16 + 2 * u + (e & 1)) : 4 * u + e;
+    for (int e = 0; e < 4; ++e) pr[e] = (e >> 1) * 16 + 2 * u + (e & 1);
     float2 cs[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) rope_cos_sin(j, A.fr.hi[pr[e]], A.fr.lo[pr[e]], cs[e].x, cs[e].y);
-    if (grp == 0) {   // the table: [L][32] (cos, sin) x qscale
+    if (grp == 0) {   // the table: [L][32] (cos, sin)
         float2* t = reinterpret_cast<float2*>(A.cs) + static_cast<int64_t>(j) * kPairs;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t[pr[e]] = make_float2(cs[e].x * sc, cs[e].y * sc);
+        for (int e = 0; e < 4; ++e) t[pr[e]] = cs[e];
     }
-    // loads of every row first
+    // loads of every row first: dims 16c + 2u, 16c + 2u + 1 (c = 0..3) of the key and the value
     uint32_t kw[kPrepRows][4], vw[kPrepRows][4];
 #pragma unroll
     for (int r = 0; r < kPrepRows; ++r) {
         const int bh = grp * kPrepRows + r;
         const int64_t row = (static_cast<int64_t>(bh < A.n_bh ? bh : 0) * A.L + j) * kD;
-        if (!KS) {
-            // keys: pairs 4u..4u+3 (x at dims 4u.., y at 32 + 4u..); values: dims 16c + 2u, + 1
-            const uint2 a = *reinterpret_cast<const uint2*>(ks + row + 4 * u);
-            const uint2 b2 = *reinterpret_cast<const uint2*>(ks + row + kPairs + 4 * u);
-            kw[r][0] = a.x; kw[r][1] = a.y; kw[r][2] = b2.x; kw[r][3] = b2.y;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) vw[r][c] = *reinterpret_cast<const uint32_t*>(vs + row + 16 * c + 2 * u);
-        } else {
-            // keys: dims 16c + 2u, 16c + 2u + 1; values: elements 8u..8u+7 in dim order
-#pragma unroll
-            for (int c = 0; c < 4; ++c) kw[r][c] = *reinterpret_cast<const uint32_t*>(ks + row + 16 * c + 2 * u);
-            const uint4 v4 = *reinterpret_cast<const uint4*>(vs + row + 8 * u);
-            vw[r][0] = v4.x; vw[r][1] = v4.y; vw[r][2] = v4.z; vw[r][3] = v4.w;
+        for (int c = 0; c < 4; ++c) {
+            kw[r][c] = *reinterpret_cast<const uint32_t*>(ks + row + 16 * c + 2 * u);
+            vw[r][c] = *reinterpret_cast<const uint32_t*>(vs + row + 16 * c + 2 * u);
         }
     }
 #pragma unroll
@@ -118,40 +107,22 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
         const int bh = grp * kPrepRows + r;
         if (bh >= A.n_bh) break;
         const int64_t row = (static_cast<int64_t>(bh) * A.L + j) * kD;
-        if (!KS) {
-            const float a[4] = {bf16_lo(kw[r][0]), bf16_hi(kw[r][0]), bf16_lo(kw[r][1]), bf16_hi(kw[r][1])};
-            const float b[4] = {bf16_lo(kw[r][2]), bf16_hi(kw[r][2]), bf16_lo(kw[r][3]), bf16_hi(kw[r][3])};
-            float r1[4], r2[4];
+        // x, y of pairs 2u, 2u + 1 (dims 2u, 2u + 1 and 32 + ..) and 16 + 2u, 17 + 2u
+        const float x[4] = {bf16_lo(kw[r][0]), bf16_hi(kw[r][0]), bf16_lo(kw[r][1]), bf16_hi(kw[r][1])};
+        const float y[4] = {bf16_lo(kw[r][2]), bf16_hi(kw[r][2]), bf16_lo(kw[r][3]), bf16_hi(kw[r][3])};
+        float rx[4], ry[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                r1[e] = a[e] * cs[e].x - b[e] * cs[e].y;
-                r2[e] = b[e] * cs[e].x + a[e] * cs[e].y;
-            }
-            store4<f16_t>(A.k16 + row + 4 * u, make_float4(r1[0], r1[1], r1[2], r1[3]));
-            store4<f16_t>(A.k16 + row + kPairs + 4 * u, make_float4(r2[0], r2[1], r2[2], r2[3]));
-            // values permuted: elements 8u..8u+7 are dims 16c + 2u (c = 0..3), then 16c + 2u + 1
-            store4<f16_t>(A.v16 + row + 8 * u,
-                          make_float4(bf16_lo(vw[r][0]), bf16_lo(vw[r][1]), bf16_lo(vw[r][2]), bf16_lo(vw[r][3])));
-            store4<f16_t>(A.v16 + row + 8 * u + 4,
-                          make_float4(bf16_hi(vw[r][0]), bf16_hi(vw[r][1]), bf16_hi(vw[r][2]), bf16_hi(vw[r][3])));
-        } else {
-            // x, y of pairs 2u, 2u + 1 (dims 2u, 2u + 1 and 32 + ..) and 16 + 2u, 17 + 2u
-            const float x[4] = {bf16_lo(kw[r][0]), bf16_hi(kw[r][0]), bf16_lo(kw[r][1]), bf16_hi(kw[r][1])};
-            const float y[4] = {bf16_lo(kw[r][2]), bf16_hi(kw[r][2]), bf16_lo(kw[r][3]), bf16_hi(kw[r][3])};
-            float rx[4], ry[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                rx[e] = x[e] * cs[e].x - y[e] * cs[e].y;
-                ry[e] = y[e] * cs[e].x + x[e] * cs[e].y;
-            }
-            // element 8u + e: e < 4 is dim 16e + 2u, e >= 4 is dim 16(e - 4) + 2u + 1
-            store4<f16_t>(A.k16 + row + 8 * u, make_float4(rx[0], rx[2], ry[0], ry[2]));
-            store4<f16_t>(A.k16 + row + 8 * u + 4, make_float4(rx[1], rx[3], ry[1], ry[3]));
-            store4<f16_t>(A.v16 + row + 8 * u,
-                          make_float4(bf16_lo(vw[r][0]), bf16_hi(vw[r][0]), bf16_lo(vw[r][1]), bf16_hi(vw[r][1])));
-            store4<f16_t>(A.v16 + row + 8 * u + 4,
-                          make_float4(bf16_lo(vw[r][2]), bf16_hi(vw[r][2]), bf16_lo(vw[r][3]), bf16_hi(vw[r][3])));
+        for (int e = 0; e < 4; ++e) {
+            rx[e] = x[e] * cs[e].x - y[e] * cs[e].y;
+            ry[e] = y[e] * cs[e].x + x[e] * cs[e].y;
         }
+        // element 8u + e: e < 4 is dim 16e + 2u, e >= 4 is dim 16(e - 4) + 2u + 1
+        store4<f16_t>(A.k16 + row + 8 * u, make_float4(rx[0], rx[2], ry[0], ry[2]));
+        store4<f16_t>(A.k16 + row + 8 * u + 4, make_float4(rx[1], rx[3], ry[1], ry[3]));
+        store4<f16_t>(A.v16 + row + 8 * u,
+                      make_float4(bf16_lo(vw[r][0]), bf16_lo(vw[r][1]), bf16_lo(vw[r][2]), bf16_lo(vw[r][3])));
+        store4<f16_t>(A.v16 + row + 8 * u + 4,
+                      make_float4(bf16_hi(vw[r][0]), bf16_hi(vw[r][1]), bf16_hi(vw[r][2]), bf16_hi(vw[r][3])));
     }
 }
 
@@ -229,20 +200,28 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     }
     step(krs, buf(1), kn);                        // (zero rows when no far rung is reached)
 
-    // q of head h0 + x, rotated at its position and scaled (the table carries qscale), fp16:
-    // register chunk c holds dims 8c..8c+7; RoPE pairs 8c..8c+7 are chunks c and c + 4
+    // q of head h0 + x, rotated at its position and scaled by qscale, fp16, in the keys' permuted
+    // order: word 2m holds dims (m, 16 + m), word 2m + 1 dims (32 + m, 48 + m), i.e. the x and y
+    // halves of RoPE pairs m and 16 + m; register chunk c = words 4c..4c+3
     uint32_t q[8][4];
+    {
+        auto dim = [&](int d) -> float {               // bf16 dim d of the raw row
+            const uint4& r = qraw[d >> 3];
+            const int w = (d >> 1) & 3;
+            const uint32_t v = w == 0 ? r.x : w == 1 ? r.y : w == 2 ? r.z : r.w;
+            return (d & 1) ? bf16_hi(v) : bf16_lo(v);
+        };
+        auto cos_sin = [&](int pair) -> float2 {
+            const float4& t = ctab[pair >> 1];
+            return (pair & 1) ? make_float2(t.z, t.w) : make_float2(t.x, t.y);
+        };
+        const float qs = A.qscale;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const uint32_t lw[4] = {qraw[c].x, qraw[c].y, qraw[c].z, qraw[c].w};
-        const uint32_t hw[4] = {qraw[c + 4].x, qraw[c + 4].y, qraw[c + 4].z, qraw[c + 4].w};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const float4 t = ctab[4 * c + m];           // (cos, sin) of pairs 8c + 2m, 8c + 2m + 1
-            const float x0 = bf16_lo(lw[m]), x1 = bf16_hi(lw[m]);
-            const float y0 = bf16_lo(hw[m]), y1 = bf16_hi(hw[m]);
-            q[c][m] = pack_h2(x0 * t.x - y0 * t.y, x1 * t.z - y1 * t.w);
-            q[c + 4][m] = pack_h2(y0 * t.x + x0 * t.y, y1 * t.z + x1 * t.w);
+        for (int m = 0; m < 16; ++m) {
+            const float2 t0 = cos_sin(m), t1 = cos_sin(16 + m);
+            const float x0 = dim(m), y0 = dim(32 + m), x1 = dim(16 + m), y1 = dim(48 + m);
+            q[m >> 1][2 * (m & 1)] = pack_h2((x0 * t0.x - y0 * t0.y) * qs, (x1 * t1.x - y1 * t1.y) * qs);
+            q[m >> 1][2 * (m & 1) + 1] = pack_h2((y0 * t0.x + x0 * t0.y) * qs, (y1 * t1.x + x1 * t1.y) * qs);
         }
     }
     publish<6>();                                       // the key near block has landed
@@ -413,13 +392,10 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
 
 }  // namespace
 
-hipError_t launch_prep_kv16(const PrepArgs& A, bool backward_layout, hipStream_t s) {
+hipError_t launch_prep_kv16(const PrepArgs& A, hipStream_t s) {
     const int64_t threads = static_cast<int64_t>((A.n_bh + kPrepRows - 1) / kPrepRows) * A.L * 8;
     const unsigned blocks = static_cast<unsigned>((threads + 255) / 256);
-    if (backward_layout)
-        hipLaunchKernelGGL(prep_kv16_kernel<true>, dim3(blocks), dim3(256), 0, s, A);
-    else
-        hipLaunchKernelGGL(prep_kv16_kernel<false>, dim3(blocks), dim3(256), 0, s, A);
+    hipLaunchKernelGGL(prep_kv16_kernel, dim3(blocks), dim3(256), 0, s, A);
     return hipGetLastError();
 }
 

@@ -37,26 +37,26 @@ struct RopeKeysArgs {
     RopeFreq fr;
 };
 
-// bf16 storage: rotated keys and values as fp16 rows for the forward kernels.
+// bf16 storage: rotated keys and values as fp16 rows for the matrix-core forward and backward
+// (one layout for both: element 4m + c of a row holds dim 16c + m).
 struct PrepArgs {
     const void* k;       // [B*Hkv, L, 64] bf16
     const void* v;       // [B*Hkv, L, 64] bf16
-    _Float16* k16;       // [B*Hkv, L, 64] rotated keys
-    _Float16* v16;       // [B*Hkv, L, 64] values
-    float* cs;           // [L, 32, 2] cos and sin of every position and RoPE pair, times qscale
+    _Float16* k16;       // [B*Hkv, L, 64] rotated keys, dims permuted
+    _Float16* v16;       // [B*Hkv, L, 64] values, dims permuted
+    float* cs;           // [L, 32, 2] cos and sin of every position and RoPE pair
     int32_t n_bh;
     int32_t L;
-    float qscale;        // the score scale folded into the table (log2(e) / sqrt(D))
     RopeFreq fr;
 };
 
 struct FwdArgs {
     const void* q;       // [B, Hq, L, 64] storage type
-    const void* kstage;  // [B, Hkv, L, 64] rotated keys: float32 (f32 storage) or fp16 (bf16 storage)
-    const void* vstage;  // [B, Hkv, L, 64] values: the input (f32 storage) or fp16 (bf16 storage,
-                         // dims permuted for the matrix-core kernel: element 4m + c is dim 16c + m)
+    const void* kstage;  // [B, Hkv, L, 64] rotated keys: float32 in dim order (f32 storage) or fp16
+                         // with dims permuted, element 4m + c holding dim 16c + m (bf16 storage)
+    const void* vstage;  // [B, Hkv, L, 64] values: the input (f32 storage) or fp16, dims permuted
     const void* v;       // [B, Hkv, L, 64] the caller's values
-    const float* cstab;  // [L, 32, 2] cos/sin table times qscale (bf16 storage)
+    const float* cstab;  // [L, 32, 2] cos/sin table (bf16 storage)
     void* o;             // [B, Hq, L, 64]
     float* lse;          // [B, Hq, L] or nullptr
     int32_t B, L, Hq, Hkv, G, W, n_off;
@@ -88,13 +88,14 @@ struct BwdArgs {
     float dalpha_dtheta;
     RopeFreq fr;
     OffsetSlot off[kMaxOff];
-    // matrix-core path (bfloat16 storage): staged rows from prep_kv16's backward layout, and what
-    // the query-side kernel hands the key-side kernel
+    // matrix-core path (bfloat16 storage): staged rows from prep_kv16 (the forward's own), and
+    // what the query-side kernel hands the key-side kernel; rows with dims permuted have element
+    // 4m + c holding dim 16c + m
     const void* kstage;  // [B*Hkv, L, 64] fp16 rotated keys, dims permuted
-    const void* vstage;  // [B*Hkv, L, 64] fp16 values
+    const void* vstage;  // [B*Hkv, L, 64] fp16 values, dims permuted
     const float* cstab;  // [L, 32, 2] cos, sin
     void* qrot16;        // [B, Hq, L, 64] fp16 rotated queries, dims permuted
-    void* do16;          // [B, Hq, L, 64] fp16 copy of dout (dim order)
+    void* do16;          // [B, Hq, L, 64] fp16 copy of dout, dims permuted
     // per query and head, fp16 pairs (p low, dS/sqrt(D) high): the window distances 0..15 of each
     // query ([B, Hq, L, kNW]), and each rung's entry without its coefficients, rung-major
     // ([B, Hq, kNR, L])
@@ -108,9 +109,8 @@ struct BwdArgs {
 constexpr int kNW = 16, kNR = 16;
 
 hipError_t launch_rope_keys(int dtype, const RopeKeysArgs& a, hipStream_t s);
-// forward layout: keys in dim order, values permuted, table x qscale; backward layout: keys
-// permuted, values in dim order (element 4m + c of a permuted row holds dim 16c + m)
-hipError_t launch_prep_kv16(const PrepArgs& a, bool backward_layout, hipStream_t s);
+// keys and values with dims permuted (element 4m + c of a row holds dim 16c + m), and the table
+hipError_t launch_prep_kv16(const PrepArgs& a, hipStream_t s);
 hipError_t launch_fwd_attend(int dtype, const FwdArgs& a, hipStream_t s);
 bool fwd_mfma_supported(const FwdArgs& a);
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s);

@@ -143,7 +143,9 @@ fibattn_status_t fibattn_fwd(const void* q, const void* k, const void* v, double
  * First stage of fibattn_fwd, exposed so that each kernel can be timed on its own: rotate every
  * key row at its position once (RoPE before the gather, §2 "Attended set") into the workspace.
  * For FIBATTN_F32 the rotated keys are stored as float32; for FIBATTN_BF16 the rotated keys and
- * the values are stored as fp16 rows (bf16 values of magnitude below 65504 convert exactly).
+ * the values are stored as fp16 rows (bf16 values of magnitude below 65504 convert exactly), with
+ * the cos/sin table of every position. The backward's FIBATTN_STAGE_PREP writes the same arrays
+ * at the same places of its (larger) workspace where fibattn_bwd_reuses_fwd_prep says so.
  * k, v: device [B, Hkv, L, D] of `dtype`. Errors as fibattn_fwd.
  */
 fibattn_status_t fibattn_fwd_prep(const void* k, const void* v, int32_t B, int32_t L, int32_t Hkv,
@@ -194,7 +196,9 @@ fibattn_status_t fibattn_bwd(const void* q, const void* k, const void* v, const 
 
 /* Stages of the backward pass, for fibattn_bwd_stages (bit mask). */
 typedef enum {
-    FIBATTN_STAGE_PREP = 1,   /* keys rotated at their positions (and fp16 values) into the workspace */
+    FIBATTN_STAGE_PREP = 1,   /* keys rotated at their positions (and fp16 values) into the workspace;
+                                 the same arrays as fibattn_fwd_prep where
+                                 fibattn_bwd_reuses_fwd_prep returns 1 */
     FIBATTN_STAGE_QUERY = 2,  /* dq, plus what the key stage reads from the workspace */
     FIBATTN_STAGE_KEY = 4,    /* dk, dv, and dalpha / dtheta when requested */
     FIBATTN_STAGE_ALL = 7
@@ -209,7 +213,22 @@ typedef enum {
  * dalpha and dtheta by the KEY stage; pointers a selected stage does not write are not read.
  * FIBATTN_STAGE_ALL is fibattn_bwd (which forwards here). Arguments and errors as fibattn_bwd,
  * plus INVALID for a mask outside [1, 7]; every argument is checked whatever the mask.
+ * A training step can leave out PREP where fibattn_bwd_reuses_fwd_prep returns 1 and the
+ * backward's workspace is the one the forward (fibattn_fwd or fibattn_fwd_prep) ran with, on the
+ * same k, v, shapes, dtype and rope_theta, untouched since: that workspace then already holds what
+ * PREP would write.
  */
+/*
+ * 1 when the backward's FIBATTN_STAGE_PREP writes exactly what fibattn_fwd_prep writes for the same
+ * k, v, shapes, dtype and rope_theta (the forward's arrays are a prefix of the backward's
+ * workspace), so that a training step may prep once per layer; 0 otherwise (bfloat16 shapes that
+ * the backward serves with its general kernels, which rotate float32 keys of their own) and for
+ * arguments fibattn_bwd would reject. Host-only: it queues nothing and reads no device memory.
+ */
+int32_t fibattn_bwd_reuses_fwd_prep(double alpha, int32_t W, const int32_t* offsets, int32_t K,
+                                    int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t dtype);
+
 fibattn_status_t fibattn_bwd_stages(int32_t stages, const void* q, const void* k, const void* v,
                                     const void* dout, double alpha, int32_t W,
                                     const int32_t* offsets, int32_t K, int32_t B, int32_t L,

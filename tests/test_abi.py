@@ -178,6 +178,21 @@ def test_bwd_stage_mask_checks():
     assert staged(fa.STAGE_PREP, dq=None) == 1
 
 
+def test_bwd_reuses_fwd_prep():
+    # bf16 on the matrix-core backward (query heads per kv head a multiple of 4, W <= 15, at most
+    # 16 kept rungs) reads the forward's staged arrays; float32 runs the same key rotation in both
+    assert fa.fibattn_bwd_reuses_fwd_prep(0.5 + 3 / 15, 12, O.FIB_BASE, 32, 1024, 8, 2)
+    assert fa.fibattn_bwd_reuses_fwd_prep(1.0, 12, O.FIB_BASE, 1, 64, 8, 2, dtype=fa.F32)
+    assert fa.fibattn_bwd_reuses_fwd_prep(1.0, 31, O.FIB_BASE, 1, 64, 6, 2, dtype=fa.F32)
+    # general bf16 backward (float32 keys of its own): GQA group of 2, a window past 15
+    assert not fa.fibattn_bwd_reuses_fwd_prep(0.7, 12, O.FIB_BASE, 1, 64, 4, 2)
+    assert not fa.fibattn_bwd_reuses_fwd_prep(0.7, 20, O.FIB_BASE, 1, 64, 8, 2)
+    # arguments the backward rejects
+    assert not fa.fibattn_bwd_reuses_fwd_prep(0.7, 12, O.FIB_BASE, 1, 64, 8, 3)
+    assert not fa.fibattn_bwd_reuses_fwd_prep(-1.0, 12, O.FIB_BASE, 1, 64, 8, 2)
+    assert not fa.fibattn_bwd_reuses_fwd_prep(0.7, 12, O.FIB_BASE, 1, 64, 8, 2, D=48)
+
+
 def test_host_helpers_argument_checks():
     out = (ctypes.c_int32 * 4)()
     n = ctypes.c_int32()

@@ -163,6 +163,32 @@ def test_staged_calls_equal_the_combined_call():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_backward_after_forward_skips_its_prep(dtype):
+    # the forward's prep in the shared workspace stands in for the backward's own: same bits
+    w = workloads.WORKLOADS["l1024_learned_bf16"]
+    q, k, v, do = [x.to("cuda:0", dtype) for x in workloads.draw(w, 5, B=2)]
+    th = float(workloads.draw_theta(16)[5])
+    alpha, dadt = O.alpha_from_theta(th), O.dalpha_dtheta(th)
+    B, Hq, L, D = q.shape
+    Hkv = k.shape[1]
+    dt = fa.BF16 if dtype == torch.bfloat16 else fa.F32
+    assert fa.fibattn_bwd_reuses_fwd_prep(alpha, w.W, O.FIB_BASE, B, L, Hq, Hkv, D, dt)
+    say(f"bwd after fwd without prep {dtype} B=2 L=1024")
+    ref = fa.fibattn_bwd(q, k, v, None, None, do, alpha, w.W, O.FIB_BASE, dalpha_dtheta=dadt, want_dalpha=True)
+    nbytes = max(fa.fibattn_fwd_workspace_bytes(B, L, Hkv, D, dt),
+                 fa.fibattn_bwd_workspace_bytes(B, L, Hq, Hkv, D, w.W, len(O.FIB_BASE), dt))
+    ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda:0")
+    fa.fibattn_fwd(q, k, v, alpha, w.W, O.FIB_BASE, workspace=ws)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    da, dth = torch.empty(1, device="cuda:0"), torch.empty(1, device="cuda:0")
+    fa.fibattn_bwd_stages(fa.STAGE_QUERY | fa.STAGE_KEY, q, k, v, do, alpha, w.W, O.FIB_BASE, dq, dk, dv, ws,
+                          dalpha_dtheta=dadt, dalpha=da, dtheta=dth)
+    torch.cuda.synchronize()
+    for x, y in zip(ref, (dq, dk, dv, da, dth)):
+        assert torch.equal(x, y)
+
+
 def test_bitwise_determinism():
     w = workloads.WORKLOADS["l1024_learned_bf16"]
     q, k, v, do = workloads.draw(w, 2, B=4)
