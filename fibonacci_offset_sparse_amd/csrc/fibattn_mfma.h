@@ -78,6 +78,15 @@ __device__ __forceinline__ lds_ptr_t dma_dst(char* dst) {
     return (lds_ptr_t)static_cast<uintptr_t>(a);
 }
 
+// A uniform value made opaque in a scalar register. A per-lane choice between two such values
+// selects values; a choice between two entries of the kernel's offset table would otherwise
+// become one vector load from a per-lane address, which the compiler follows with a full vmcnt
+// wait, behind every staging load in flight.
+template <typename T> __device__ __forceinline__ T in_sgpr(T v) {
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
 // Wait until at most N vector-memory instructions of this wave are in flight (its LDS DMAs up to
 // the block the next step reads have landed) and its LDS reads are done, then the workgroup
 // barrier. __syncthreads would also drain every staging load in flight.
