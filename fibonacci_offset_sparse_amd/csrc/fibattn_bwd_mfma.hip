@@ -102,43 +102,48 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     auto buf = [&](int j) -> char* { return (j & 1) ? lds1 : lds0; };
     const int jn = i0 - kNear;                          // the near block's row at slot 0
 
-    // ---- prologue: key and value near blocks; q and do of the wave's 16 positions and 4 heads
-    // (1 KB contiguous loads, turned into one row per lane through the wave's part of lds1); key
-    // and value far step kn ----
-    st.near(krs, lds0, jn);
-    st.near(vrs, lds0 + kBufBytes, jn);
+    // ---- prologue: q and do of the wave's 16 positions and 4 heads by LDS DMA into the wave's
+    // 8 KB of lds0 (q) and of lds1 (do), 1 KB contiguous per instruction (lane l lands on slot
+    // 8u + (l >> 3), physical chunk l & 7, and fetches the logical chunk the swizzle puts there),
+    // read back one row per lane; then the key and value near blocks and far step kn ----
     // row of linear-view slot s (head h0 + (s >> 4), position i0 + 16w + (s & 15)), or -1 past L
     auto lin_row = [&](int s) -> int64_t {
         const int pos = i0 + 16 * wave + (s & 15);
         return pos < L ? (static_cast<int64_t>(b) * A.Hq + h0 + (s >> 4)) * L + pos : -1;
     };
     uint4 qraw[8], draw[8];
-    float4 ctab[16];
+    float4 ctq[4];                                      // cos/sin of pairs 8x..8x+7 at position i
     {
-        uint4 ql[8], dl[8];
+        // the 4 heads' rows (4 L rows of 128 bytes: within 32 bits for L <= 2^20); positions past
+        // L read row L - 1 (finite, never used)
+        const int64_t hrow = (static_cast<int64_t>(b) * A.Hq + h0) * L;
+        const __amdgpu_buffer_rsrc_t qrs4 = rows_rsrc(A.q, hrow, 4 * L);
+        const __amdgpu_buffer_rsrc_t drs4 = rows_rsrc(A.dout, hrow, 4 * L);
+        char* const rq = lds0 + wave * 8192;
+        char* const rd = lds1 + wave * 8192;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int64_t row = lin_row(lin_slot(lane, u));
-            const int64_t off = (row < 0 ? 0 : row) * kD + (lane & 7) * 8;
-            ql[u] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(A.q) + off);
-            dl[u] = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(A.dout) + off);
+            const int sl = lin_slot(lane, u);
+            const int pos = min(i0 + 16 * wave + (sl & 15), L - 1);
+            const int voff = ((sl >> 4) * L + pos) * kRowBytes + (((lane & 7) ^ tr_f(sl)) << 4);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs4, dma_dst(rq + u * 1024), 16, voff, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(drs4, dma_dst(rd + u * 1024), 16, voff, 0, 0, 0);
         }
-        const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(active ? i : 0) * (kPairs / 2);
+        const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(active ? i : 0) * (kPairs / 2) + 4 * x;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) ctab[u] = ct[u];
-        char* reg = lds1 + wave * 8192;
+        for (int u = 0; u < 4; ++u) ctq[u] = ct[u];
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int u = 0; u < 8; ++u) *reinterpret_cast<uint4*>(reg + lin_view_addr(lane, u)) = ql[u];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) qraw[c] = *reinterpret_cast<const uint4*>(reg + row_view_addr(pq, x, c));
-#pragma unroll
-        for (int u = 0; u < 8; ++u) *reinterpret_cast<uint4*>(reg + lin_view_addr(lane, u)) = dl[u];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) draw[c] = *reinterpret_cast<const uint4*>(reg + row_view_addr(pq, x, c));
+        for (int c = 0; c < 8; ++c) {
+            qraw[c] = *reinterpret_cast<const uint4*>(rq + row_view_addr(pq, x, c));
+            draw[c] = *reinterpret_cast<const uint4*>(rd + row_view_addr(pq, x, c));
+        }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();                   // every wave is done with lds1
+        __builtin_amdgcn_s_barrier();                   // every wave is done with its rows
         asm volatile("" ::: "memory");
     }
+    st.near(krs, lds0, jn);
+    st.near(vrs, lds0 + kBufBytes, jn);
     kv_step(lds1, kn);
 
     // q rotated at its position (unscaled), fp16, in the keys' permuted order: word 2m holds dims
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             const uint32_t hw[4] = {qraw[c + 4].x, qraw[c + 4].y, qraw[c + 4].z, qraw[c + 4].w};
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const float4 t = ctab[4 * c + m];      // pairs 8c + 2m, 8c + 2m + 1
+                const float4 t = quad_bcast(c, ctq[m]);  // pairs 8c + 2m, 8c + 2m + 1 (from lane c)
                 const float x0 = bf16_lo(lw[m]), x1 = bf16_hi(lw[m]);
                 const float y0 = bf16_lo(hw[m]), y1 = bf16_hi(hw[m]);
                 const int j = 8 * c + 2 * m;
@@ -389,13 +394,19 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         // ---- dq: RoPE transposed at position i. Lane x holds dims 16x + m of heads 0..3; the
         // other half of pair (16x + m) mod 32 is in lane x ^ 2. Rows go through treg: 1 KB
         // contiguous stores ----
-        const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(active ? i : 0) * (kPairs / 2) + 8 * (x & 1);
+        // pair 16 (x & 1) + m: lane 2 (x & 1) + (m >> 3) holds it (each lane loads pairs
+        // 8x..8x+7), at entry (m & 7) >> 1 of its quarter
+        const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(active ? i : 0) * (kPairs / 2) + 4 * x;
+        float4 cq[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cq[u] = ct[u];
         float2 cs[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float4 t = ct[u];
-            cs[2 * u] = make_float2(t.x, t.y);
-            cs[2 * u + 1] = make_float2(t.z, t.w);
+        for (int m = 0; m < 16; ++m) {
+            const float4& t = cq[(m & 7) >> 1];
+            const float c = (m & 1) ? t.z : t.x, sn = (m & 1) ? t.w : t.y;
+            cs[m] = (m < 8) ? make_float2(quad_f<kPerm0202>(c), quad_f<kPerm0202>(sn))
+                            : make_float2(quad_f<kPerm1313>(c), quad_f<kPerm1313>(sn));
         }
         const float sg = (x < 2) ? 1.f : -1.f;         // x' = x c + y s;  y' = y c - x s
 #pragma unroll
@@ -434,7 +445,11 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
         if (lane == 0) red[wave][n] = v;
     }
-    __syncthreads();
+    // an LDS-only barrier: the stores above need not have landed (__syncthreads would wait for
+    // every one of them)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     if (threadIdx.x < static_cast<unsigned>(A.n_off)) {
         float v = 0.f;
         if (threadIdx.x < MAXK) v = ((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) + red[3][threadIdx.x];

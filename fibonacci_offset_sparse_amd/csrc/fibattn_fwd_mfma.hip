@@ -185,20 +185,38 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     const int jn = i0 - kNear;                          // the near block's row at slot 0
     auto buf = [&](int j) -> char* { return (j & 1) ? lds1 : lds0; };
 
-    // ---- prologue: key near block (item 0), q, item 1 (key far step kn) ----
-    st.near(krs, buf(0), jn);
+    // ---- prologue: q of the wave's 16 positions and 4 heads by LDS DMA into the wave's 8 KB
+    // (1 KB contiguous per instruction; lane l lands on slot 8u + (l >> 3), physical chunk l & 7,
+    // and fetches the logical chunk the swizzle puts there), read back one row per lane; then the
+    // key near block (item 0) and item 1 (key far step kn) ----
     uint4 qraw[8];
-    float4 ctab[16];
+    float4 ctab[4];
     {
-        const bf16_t* qr = static_cast<const bf16_t*>(A.q) +
-                           ((static_cast<int64_t>(b) * A.Hq + h0 + x) * L + (active ? i : 0)) * kD;
+        char* const reg = (wave < 2 ? lds0 : lds1) + (wave & 1) * 8192;
+        // the 4 heads' rows (4 L rows of 128 bytes: within 32 bits for L <= 2^20); positions
+        // past L read row L - 1 (finite, never used)
+        const __amdgpu_buffer_rsrc_t qrs4 = rows_rsrc(A.q, (static_cast<int64_t>(b) * A.Hq + h0) * L, 4 * L);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) qraw[c] = *reinterpret_cast<const uint4*>(qr + 8 * c);
-        const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(active ? i : 0) * (kPairs / 2);
+        for (int u = 0; u < 8; ++u) {
+            const int sl = lin_slot(lane, u);
+            const int pos = min(i0 + 16 * wave + (sl & 15), L - 1);
+            const int voff = ((sl >> 4) * L + pos) * kRowBytes + (((lane & 7) ^ tr_f(sl)) << 4);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs4, dma_dst(reg + u * 1024), 16, voff, 0, 0, 0);
+        }
+        // the cos/sin of the position: lane x loads pairs 8x..8x+7; the rotation takes the others
+        // from the quad's lanes
+        const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(active ? i : 0) * (kPairs / 2) + 4 * x;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) ctab[u] = ct[u];
+        for (int u = 0; u < 4; ++u) ctab[u] = ct[u];
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int c = 0; c < 8; ++c) qraw[c] = *reinterpret_cast<const uint4*>(reg + row_view_addr(pq, x, c));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();                   // every wave is done with its rows
+        asm volatile("" ::: "memory");
     }
-    step(krs, buf(1), kn);                        // (zero rows when no far rung is reached)
+    st.near(krs, lds0, jn);
+    step(krs, lds1, kn);                                // (zero rows when no far rung is reached)
 
     // q of head h0 + x, rotated at its position and scaled by qscale, fp16, in the keys' permuted
     // order: word 2m holds dims (m, 16 + m), word 2m + 1 dims (32 + m, 48 + m), i.e. the x and y
@@ -211,9 +229,15 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
             const uint32_t v = w == 0 ? r.x : w == 1 ? r.y : w == 2 ? r.z : r.w;
             return (d & 1) ? bf16_hi(v) : bf16_lo(v);
         };
-        auto cos_sin = [&](int pair) -> float2 {
-            const float4& t = ctab[pair >> 1];
-            return (pair & 1) ? make_float2(t.z, t.w) : make_float2(t.x, t.y);
+        auto cos_sin = [&](int pair) -> float2 {         // pair: compile-time; from lane pair >> 3
+            const float4& t = ctab[(pair & 7) >> 1];
+            const float c = (pair & 1) ? t.z : t.x, sn = (pair & 1) ? t.w : t.y;
+            switch (pair >> 3) {
+                case 0: return make_float2(quad_f<kBcast0>(c), quad_f<kBcast0>(sn));
+                case 1: return make_float2(quad_f<kBcast1>(c), quad_f<kBcast1>(sn));
+                case 2: return make_float2(quad_f<kBcast2>(c), quad_f<kBcast2>(sn));
+                default: return make_float2(quad_f<kBcast3>(c), quad_f<kBcast3>(sn));
+            }
         };
         const float qs = A.qscale;
 #pragma unroll

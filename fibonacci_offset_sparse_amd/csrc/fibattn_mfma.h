@@ -34,6 +34,8 @@ constexpr int kNear = 64;
 constexpr int kWG = 4;                   // window groups (W <= 15)
 constexpr int kBcast0 = 0x00, kBcast1 = 0x55, kBcast2 = 0xAA, kBcast3 = 0xFF;   // quad_perm [r,r,r,r]
 constexpr int kXor2 = 0x4E;              // quad_perm [2,3,0,1]: lane x ^ 2
+constexpr int kPerm0202 = 0x88;          // quad_perm [0,2,0,2]: lane 2 (x & 1)
+constexpr int kPerm1313 = 0xDD;          // quad_perm [1,3,1,3]: lane 2 (x & 1) + 1
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, gfx9 family
 
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
@@ -48,6 +50,16 @@ __device__ __forceinline__ f4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uin
 
 template <int CTRL> __device__ __forceinline__ float quad_f(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// The 4 floats of lane c (compile-time) of the quad, in every lane of the quad.
+__device__ __forceinline__ float4 quad_bcast(int c, const float4& v) {
+    switch (c) {
+        case 0: return make_float4(quad_f<kBcast0>(v.x), quad_f<kBcast0>(v.y), quad_f<kBcast0>(v.z), quad_f<kBcast0>(v.w));
+        case 1: return make_float4(quad_f<kBcast1>(v.x), quad_f<kBcast1>(v.y), quad_f<kBcast1>(v.z), quad_f<kBcast1>(v.w));
+        case 2: return make_float4(quad_f<kBcast2>(v.x), quad_f<kBcast2>(v.y), quad_f<kBcast2>(v.z), quad_f<kBcast2>(v.w));
+        default: return make_float4(quad_f<kBcast3>(v.x), quad_f<kBcast3>(v.y), quad_f<kBcast3>(v.z), quad_f<kBcast3>(v.w));
+    }
 }
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
