@@ -74,8 +74,9 @@ def cpu_baseline(name: str, budget_s: float = 15.0):
     w = workloads.WORKLOADS[name]
     workers = min(16, len(os.sched_getaffinity(0)))
     # (layer, repeat) units, each on batch element 0 of that layer's inputs: the oracle's cost does
-    # not depend on the values, and a B = 1 draw keeps input generation out of the way
-    units = [(name, layer, 0) for _ in range(w.B) for layer in range(w.n_layers)]
+    # not depend on the values, and a B = 1 draw keeps input generation out of the way; more units
+    # than the budget lets finish, so that the budget sets the sample
+    units = [(name, layer, 0) for _ in range(8 * w.B) for layer in range(w.n_layers)]
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
     done = 0
