@@ -13,8 +13,8 @@ Dilation and Extrapolate Where Dense Attention Fails" (C. A. Capps, arXiv 2606.2
   gather: §2 "Attended set";
 * alpha = 0.5 + sigmoid(theta) and the four per-layer schedules: §2 "Per-layer scalar";
 * the power-of-two control base: §2 "Control base";
-* integer offsets through a boolean mask are numerically identical to the gather: §2
-  "Implementation note";
+* integer offsets through a boolean mask are numerically identical to the gather, and the fixed
+  and staggered variants have integer offsets: §2 "Implementation note";
 * GQA 8 query / 2 key-value heads, head dim 64, RoPE theta 1e4: §3 "Models and training".
 
 Readings taken where the paper is silent (each one is a definition choice, shared on paper with
@@ -33,6 +33,11 @@ the HIP path but not in code):
 6. Tensors are [B, H, L, D].
 7. The slope of the read position in d is one-sided at an integral d; integer and dropped offsets
    contribute nothing to d(alpha).
+8. The rounded-integer stagger (integer offsets for the static schedules) takes d_k = alpha f_k
+   rounded to the nearest integer, ties to even, after snapping 2 d_k to an integer within the
+   tolerance of reading 3 (so that a ramp value like 0.5 + 5/15 times 3 is the tie 2.5). Its
+   attended set is the window and the distinct rounded distances >= 1 (a union: rungs that round
+   to one distance are one slot); it is read with alpha = 1 through the plan of reading 3.
 """
 
 from __future__ import annotations
@@ -119,6 +124,21 @@ def plan_offsets(alpha: float, W: int, offsets: Sequence[int]) -> List[Offset]:
         else:
             plan.append(Offset(INTERP, int(f), d, int(a), d - a, int(a) + 1))
     return plan
+
+
+def rounded_offsets(alpha: float, offsets: Sequence[int]) -> Tuple[int, ...]:
+    """Reading 8 (§2 "Implementation note": the static variants have integer offsets): the
+    distinct values >= 1 of round-half-even(alpha f_k), increasing."""
+    out = set()
+    for f in offsets:
+        d2 = 2.0 * alpha * float(f)
+        r2 = float(round(d2))
+        if abs(d2 - r2) <= SNAP_TOL:
+            d2 = r2                      # an exact integer or half-integer distance
+        n = int(round(d2 / 2.0))         # Python rounds an exact half to the even integer
+        if n >= 1:
+            out.add(n)
+    return tuple(sorted(out))
 
 
 # ----------------------------------------------------------------------------------------------

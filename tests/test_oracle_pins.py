@@ -411,3 +411,85 @@ def test_no_learned_offset_lands_on_an_integer():
         for f in O.FIB_BASE:
             d = alpha * f
             assert abs(d - round(d)) > 1e-6
+
+
+# ------------------------------------------------------------------------------------------------
+# Rounded-integer stagger (§2 "Implementation note": the fixed and staggered variants have integer
+# offsets and can run through a fused boolean-mask path, numerically identical to the gather)
+# ------------------------------------------------------------------------------------------------
+
+# Worked by hand from the definition: alpha f_k rounded to the nearest integer, ties to even, the
+# distinct values >= 1. alpha = 1/2: 0.5, 1, 1.5, 2.5, 4, 6.5, 10.5, 17, 27.5, 44.5, 72, 116.5,
+# 188.5, 305, 493.5 (0 is the window's self slot; 1.5 and 2.5 both round to 2).
+ROUNDED_FIB = {
+    Fraction(1, 2): (1, 2, 4, 6, 10, 17, 28, 44, 72, 116, 188, 305, 494),
+    Fraction(3, 2): (2, 3, 4, 8, 12, 20, 32, 51, 82, 134, 216, 350, 566, 915, 1480),
+    Fraction(5, 6): (1, 2, 4, 7, 11, 18, 28, 46, 74, 120, 194, 314, 508, 822),   # ramp layer 5
+    Fraction(1): (1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 233, 377, 610, 987),
+}
+
+
+def exact_rounded(alpha_frac, base):
+    """Round half to even on exact rationals; the distinct values >= 1."""
+    out = set()
+    for f in base:
+        d = alpha_frac * f
+        n = d.numerator // d.denominator
+        rem = d - n
+        if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+            n += 1
+        if n >= 1:
+            out.add(n)
+    return tuple(sorted(out))
+
+
+@pytest.mark.parametrize("alpha_frac", list(ROUNDED_FIB))
+def test_rounded_offsets_worked_examples(alpha_frac):
+    assert exact_rounded(alpha_frac, O.FIB_BASE) == ROUNDED_FIB[alpha_frac]
+    assert O.rounded_offsets(float(alpha_frac), O.FIB_BASE) == ROUNDED_FIB[alpha_frac]
+
+
+def test_rounded_offsets_match_exact_rationals_on_every_static_schedule():
+    # the float64 ramp values carry rounding error; ties such as (0.5 + 5/15) * 3 = 2.5 must still
+    # be recognised
+    for layer in range(16):
+        lin = Fraction(15 + 2 * layer, 30)                       # 0.5 + l / 15
+        cop = Fraction(15 + 2 * O.coprime_index(layer, 16), 30)
+        for base in (O.FIB_BASE, O.POW2_BASE_1024):
+            assert O.rounded_offsets(O.alpha_linear(layer, 16), base) == exact_rounded(lin, base)
+            assert O.rounded_offsets(O.alpha_coprime(layer, 16), base) == exact_rounded(cop, base)
+    assert O.rounded_offsets(O.alpha_fixed(0, 16), O.FIB_BASE) == O.FIB_BASE
+
+
+@pytest.mark.parametrize("alpha_frac,W,L", [
+    (Fraction(1, 2), 3, 40),      # rungs 1, 2 inside the window; 4, 6, 10, 17, 28 beyond it
+    (Fraction(5, 6), 6, 48),      # ties 2.5 -> 2 and 17.5 -> 18
+    (Fraction(3, 2), 8, 64),      # 4.5 -> 4, 7.5 -> 8 (a window distance), 19.5 -> 20, ...
+    (Fraction(23, 30), 12, 72),   # ramp layer 4
+])
+def test_rounded_forward_equals_masked_dense_attention(alpha_frac, W, L):
+    dists = O.rounded_offsets(float(alpha_frac), O.FIB_BASE)
+    q, k, v = randn(1, 4, L, 16), randn(1, 2, L, 16), randn(1, 2, L, 16)
+    ref = sdpa_masked(q, k, v, integer_mask(L, W, dists))
+    o, _ = O.forward(q, k, v, 1.0, W, dists)
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def test_rounded_backward_matches_central_differences():
+    L, D, W = 16, 8, 2
+    dists = O.rounded_offsets(0.5, O.FIB_BASE)                # 1, 2 dropped; 4, 6, 10 read
+    q, k, v, do = randn(1, 4, L, D), randn(1, 2, L, D), randn(1, 2, L, D), randn(1, 4, L, D)
+    dq, dk, dv, da = O.backward(q, k, v, do, 1.0, W, dists)
+    assert da == 0.0
+    h = 1e-6
+    for x, g in [(q, dq), (k, dk), (v, dv)]:
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = _loss(q, k, v, do, 1.0, W, dists)
+            x[idx] = old - h
+            lm = _loss(q, k, v, do, 1.0, W, dists)
+            x[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        assert np.max(np.abs(fd - g)) <= 1e-6 * max(1.0, np.max(np.abs(g)))
