@@ -169,11 +169,26 @@ class Layers:
         nbytes = max(fa.fibattn_fwd_workspace_bytes(B, L, Hkv), fa.fibattn_bwd_workspace_bytes(B, L, Hq, Hkv, D, w.W, len(base)))
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.reuse = [fa.fibattn_bwd_reuses_fwd_prep(a, w.W, base, B, L, Hq, Hkv, D) for a in self.alphas]
+        # the rounded-integer variant of the same schedule (integer offsets, read at alpha = 1)
+        self.rounded = [fa.fibattn_round_offsets(a, base) for a in self.alphas]
+        self.reuse_rounded = [fa.fibattn_bwd_reuses_fwd_prep(1.0, w.W, r, B, L, Hq, Hkv, D) for r in self.rounded]
 
     def fwd(self, layer):
         q, k, v, _ = self.inputs[layer]
         self.fa.fibattn_fwd(q, k, v, self.alphas[layer], self.w.W, self.base, o=self.o[layer],
                             lse=self.lse[layer], workspace=self.ws)
+
+    def fwd_rounded(self, layer):
+        q, k, v, _ = self.inputs[layer]
+        self.fa.fibattn_fwd(q, k, v, 1.0, self.w.W, self.rounded[layer], o=self.o[layer], lse=self.lse[layer],
+                            workspace=self.ws)
+
+    def bwd_rounded(self, layer):
+        q, k, v, do = self.inputs[layer]
+        fa = self.fa
+        st = fa.STAGE_QUERY | fa.STAGE_KEY if self.reuse_rounded[layer] else fa.STAGE_ALL
+        fa.fibattn_bwd_stages(st, q, k, v, do, 1.0, self.w.W, self.rounded[layer], self.dq[layer], self.dk[layer],
+                              self.dv[layer], self.ws)
 
     def prep(self, layer):
         self.fa.fibattn_fwd_prep(self.inputs[layer][1], self.inputs[layer][2], self.ws)
@@ -241,7 +256,7 @@ def time_steps(net: Layers, steps: int, warmup: int):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def time_stages(net: Layers, sweeps: int):
+def time_stages(net: Layers, sweeps: int, stages=None):
     """Average duration of each stage, from HIP events on the stream the kernels run on.
 
     Each stage is launched for all layers back to back behind a short GPU spin, so the launches
@@ -249,8 +264,9 @@ def time_stages(net: Layers, sweeps: int):
     stage reads what the earlier one left in the shared workspace, from the last layer it ran on
     (the same work: the workspace holds values only, its layout does not depend on the layer)."""
     n = net.w.n_layers
-    stages = {"fwd_prep": net.prep, "fwd_attend": net.attend, "bwd": net.bwd, "bwd_prep": net.bwd_prep,
-              "bwd_query": net.bwd_query, "bwd_key": net.bwd_key}
+    if stages is None:
+        stages = {"fwd_prep": net.prep, "fwd_attend": net.attend, "bwd": net.bwd, "bwd_prep": net.bwd_prep,
+                  "bwd_query": net.bwd_query, "bwd_key": net.bwd_key}
     tot = {k: 0.0 for k in stages}
     for _ in range(sweeps):
         for name, fn in stages.items():
@@ -274,6 +290,21 @@ def measure(fa, name: str, steps: int, warmup: int, dev):
     ms_step, wall = time_steps(net, steps, warmup)
     log(f"[{name}] {ms_step:.3f} ms per step; timing stages")
     st = time_stages(net, 3)
+    integer_path = None
+    if w.schedule in ("linear", "coprime"):
+        # the same schedule with rounded offsets on the integer path, against the interpolated
+        # gather, per layer call on the same inputs
+        log(f"[{name}] timing the rounded-integer variant")
+        it = time_stages(net, 3, {"fwd_interp": net.fwd, "fwd_int": net.fwd_rounded, "bwd_interp": net.bwd,
+                                  "bwd_int": net.bwd_rounded})
+        integer_path = {
+            "what": "rounded-integer stagger (offsets round-half-even(alpha_l f_k), read at alpha = 1) against "
+                    "the interpolated stagger, same inputs, ms per layer call",
+            "fwd_ms_interp": it["fwd_interp"], "fwd_ms_int": it["fwd_int"], "fwd_ratio": it["fwd_interp"] / it["fwd_int"],
+            "bwd_ms_interp": it["bwd_interp"], "bwd_ms_int": it["bwd_int"], "bwd_ratio": it["bwd_interp"] / it["bwd_int"],
+            "paper": "about 5x inference latency for the learned (interpolated, unfused gather) variant against the "
+                     "fused boolean-mask path of the integer variants (other hardware; context only)",
+        }
     qh = w.B * w.L * w.Hq
     eb = 2 if w.dtype == "bf16" else 4
     rows = w.B * w.L * w.D * eb                                                # one head's rows
@@ -301,6 +332,7 @@ def measure(fa, name: str, steps: int, warmup: int, dev):
                 "algorithmic_bytes": bwd_bytes},
         "kernels_ms": st,
         "kernel_bytes": kernel_bytes,
+        "integer_path": integer_path,
     }
     del net
     torch.cuda.empty_cache()
@@ -374,13 +406,14 @@ def main():
         "fwd": main_res["fwd"],
         "bwd": main_res["bwd"],
         "kernels_ms": main_res["kernels_ms"],
+        "integer_path": main_res["integer_path"],
         "cpu_baseline": cpu,
     }
     if long_res is not None:
         lw = workloads.WORKLOADS[args.long_workload]
         line["l4096"] = {"workload": args.long_workload, "B": lw.B, "L": lw.L, "ms_per_step": long_res["ms_per_step"],
                          "qh_per_s": long_res["qh_per_s"], "fwd": long_res["fwd"], "bwd": long_res["bwd"],
-                         "kernels_ms": long_res["kernels_ms"]}
+                         "kernels_ms": long_res["kernels_ms"], "integer_path": long_res["integer_path"]}
     print(json.dumps(line), flush=True)
 
 

@@ -39,6 +39,7 @@ def _load() -> ctypes.CDLL:
         "fibattn_base_offsets": (ctypes.c_int, [_c_i32, _c_i32, _P(_c_i32), _c_i32, _P(_c_i32)]),
         "fibattn_alpha_schedule": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, _P(_c_f64)]),
         "fibattn_alpha_from_theta": (ctypes.c_int, [_c_f64, _P(_c_f64), _P(_c_f64)]),
+        "fibattn_round_offsets": (ctypes.c_int, [_c_f64, _P(_c_i32), _c_i32, _P(_c_i32), _c_i32, _P(_c_i32)]),
         "fibattn_plan": (ctypes.c_int, [_c_f64, _c_i32, _P(_c_i32), _c_i32, _P(_c_u8), _P(_c_i32),
                                          _P(_c_f32), _P(_c_i32)]),
         "fibattn_fwd_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
@@ -117,6 +118,16 @@ def fibattn_alpha_from_theta(theta: float) -> Tuple[float, float]:
     a, d = _c_f64(), _c_f64()
     _check(lib.fibattn_alpha_from_theta(float(theta), ctypes.byref(a), ctypes.byref(d)))
     return a.value, d.value
+
+
+def fibattn_round_offsets(alpha: float, offsets: Sequence[int]) -> Tuple[int, ...]:
+    """Rounded-integer stagger: the distinct round-half-even(alpha f_k) >= 1, increasing; run them with
+    alpha = 1."""
+    offs, K = _i32_array(offsets)
+    out = (_c_i32 * max(K, 1))()
+    n = _c_i32()
+    _check(lib.fibattn_round_offsets(float(alpha), offs, K, out, max(K, 1), ctypes.byref(n)))
+    return tuple(int(out[i]) for i in range(n.value))
 
 
 def fibattn_plan(alpha: float, W: int, offsets: Sequence[int]):
@@ -308,7 +319,7 @@ def fibattn_bwd(q, k, v, o, lse, dout, alpha: float, W: int, offsets: Sequence[i
 
 __all__ = [
     "fibattn_status_string", "fibattn_last_error", "fibattn_base_offsets", "fibattn_alpha_schedule",
-    "fibattn_alpha_from_theta", "fibattn_plan", "fibattn_fwd_workspace_bytes", "fibattn_fwd",
+    "fibattn_alpha_from_theta", "fibattn_round_offsets", "fibattn_plan", "fibattn_fwd_workspace_bytes", "fibattn_fwd",
     "fibattn_fwd_prep", "fibattn_fwd_attend", "fibattn_bwd_workspace_bytes", "fibattn_bwd",
     "fibattn_bwd_stages", "fibattn_bwd_reuses_fwd_prep", "STAGE_PREP", "STAGE_QUERY", "STAGE_KEY", "STAGE_ALL",
     "FibAttnError", "lib", "LIB_PATH",

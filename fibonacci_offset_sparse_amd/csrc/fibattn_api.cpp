@@ -205,6 +205,30 @@ fibattn_status_t fibattn_base_offsets(int32_t base, int32_t pow2_max, int32_t* o
     return FIBATTN_OK;
 }
 
+fibattn_status_t fibattn_round_offsets(double alpha, const int32_t* offsets, int32_t K, int32_t* out,
+                                       int32_t capacity, int32_t* count) {
+    g_error[0] = '\0';
+    if (out == nullptr || count == nullptr) return fail(FIBATTN_ERR_INVALID, "NULL output");
+    FIBATTN_TRY(check_offsets(alpha, 0, offsets, K));
+    // d = alpha f with 2d snapped to an integer within kSnapTol (an exact integer or half-integer
+    // distance), then rounded to the nearest integer, ties to even (nearbyint in the default
+    // rounding mode); rungs are increasing, so equal distances are adjacent
+    int32_t tmp[FIBATTN_MAX_K];
+    int32_t n = 0;
+    for (int32_t k = 0; k < K; ++k) {
+        double d2 = 2.0 * alpha * static_cast<double>(offsets[k]);
+        const double r2 = std::nearbyint(d2);
+        if (std::fabs(d2 - r2) <= kSnapTol) d2 = r2;
+        const int32_t d = static_cast<int32_t>(std::nearbyint(0.5 * d2));
+        if (d < 1 || (n > 0 && d == tmp[n - 1])) continue;
+        tmp[n++] = d;
+    }
+    if (capacity < n) return fail(FIBATTN_ERR_INVALID, "capacity %d < %d distances", capacity, n);
+    if (n > 0) std::memcpy(out, tmp, sizeof(int32_t) * n);
+    *count = n;
+    return FIBATTN_OK;
+}
+
 fibattn_status_t fibattn_alpha_schedule(int32_t schedule, int32_t layer, int32_t n_layers, double* alpha) {
     g_error[0] = '\0';
     if (alpha == nullptr) return fail(FIBATTN_ERR_INVALID, "NULL alpha");

@@ -104,6 +104,19 @@ fibattn_status_t fibattn_alpha_schedule(int32_t schedule, int32_t layer, int32_t
 fibattn_status_t fibattn_alpha_from_theta(double theta, double* alpha, double* dalpha_dtheta);
 
 /*
+ * Rounded-integer stagger (§2 "Implementation note": the fixed and staggered variants have integer
+ * offsets and can run on the integer path, numerically the same as a boolean-mask attention):
+ * d_k = alpha * offsets[k] rounded to the nearest integer, ties to even, after snapping 2 d_k to an
+ * integer within 1e-9 (so that a ramp value such as 0.5 + 5/15 times 3 is the tie 2.5). Writes the
+ * distinct d_k >= 1, increasing, to out (host, capacity entries) and their number to count; pass
+ * them as the offsets of fibattn_fwd / fibattn_bwd with alpha = 1 (d(alpha) is then UNSUPPORTED:
+ * the offsets are integral). Errors: INVALID for NULL pointers, bad alpha or offsets (as
+ * fibattn_plan) or a capacity below the count; UNSUPPORTED if some alpha * f_k exceeds 2^30.
+ */
+fibattn_status_t fibattn_round_offsets(double alpha, const int32_t* offsets, int32_t K, int32_t* out,
+                                       int32_t capacity, int32_t* count);
+
+/*
  * Offset plan: the slot table the kernels use, host-only and GPU-free (§2 "Attended set").
  * For each rung k: kind_out[k] (fibattn_offset_kind_t), floor_out[k] = a, t_out[k] = t rounded
  * to float32 (0 for INT and DUP), reach_out[k] = first query index at which the slot is valid.

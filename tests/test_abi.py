@@ -193,6 +193,31 @@ def test_bwd_reuses_fwd_prep():
     assert not fa.fibattn_bwd_reuses_fwd_prep(0.7, 12, O.FIB_BASE, 1, 64, 8, 2, D=48)
 
 
+def test_round_offsets_match_the_oracle():
+    # every linear and coprime ramp value, both bases, and a few hand-picked alphas with ties
+    alphas = [O.alpha_linear(l, 16) for l in range(16)] + [O.alpha_coprime(l, 16) for l in range(16)]
+    alphas += [1.0, 0.5, 1.5, 2.5, 0.37, 0.5 + 5 / 15]
+    for base in (O.FIB_BASE, O.POW2_BASE_1024):
+        for a in alphas:
+            assert fa.fibattn_round_offsets(a, base) == O.rounded_offsets(a, base), (a, base)
+    # the integer path reads them at alpha = 1: every kept rung integral
+    kind, fl, t, _ = fa.fibattn_plan(1.0, 12, fa.fibattn_round_offsets(0.5 + 7 / 15, O.FIB_BASE))
+    assert set(kind.tolist()) <= {fa.INT, fa.DUP} and not t.any()
+
+
+def test_round_offsets_argument_checks():
+    offs, n = fa._i32_array(O.FIB_BASE)
+    out = (ctypes.c_int32 * 15)()
+    cnt = ctypes.c_int32()
+    assert fa.lib.fibattn_round_offsets(-1.0, offs, n, out, 15, ctypes.byref(cnt)) == 1
+    assert fa.lib.fibattn_round_offsets(1.0, offs, n, None, 15, ctypes.byref(cnt)) == 1
+    assert fa.lib.fibattn_round_offsets(1.0, offs, n, out, 14, ctypes.byref(cnt)) == 1     # 15 distinct at alpha = 1
+    bad, m = fa._i32_array([1, 3, 2])
+    assert fa.lib.fibattn_round_offsets(1.0, bad, m, out, 15, ctypes.byref(cnt)) == 1
+    assert fa.lib.fibattn_round_offsets(2e9, offs, n, out, 15, ctypes.byref(cnt)) == 2
+    assert fa.lib.fibattn_round_offsets(0.5, offs, 0, out, 0, ctypes.byref(cnt)) == 0 and cnt.value == 0
+
+
 def test_host_helpers_argument_checks():
     out = (ctypes.c_int32 * 4)()
     n = ctypes.c_int32()

@@ -144,6 +144,20 @@ def test_integral_offsets_with_pow2_base_and_window_extremes():
     compare(q, k, v, do, 1.0, 5, [], "no offsets", want_dalpha=False)
 
 
+@pytest.mark.parametrize("name", ["l1024_linear_bf16", "l4096_coprime_bf16"])
+def test_rounded_stagger(name):
+    # the integer path at alpha = 1 with the rounded offsets of §2 "Implementation note"; d(alpha)
+    # is not defined there (integral offsets)
+    w = workloads.WORKLOADS[name]
+    fn = {"linear": O.alpha_linear, "coprime": O.alpha_coprime}[w.schedule]
+    for layer in (0, 7, 15):
+        dists = fa.fibattn_round_offsets(fn(layer, 16), O.FIB_BASE)
+        B, L = (2, 300) if layer != 7 else (1, 1500)
+        q, k, v, do = workloads.draw(w, layer, B=B, L=L, with_grad=True)
+        say(f"bwd rounded {name} layer {layer} B={B} L={L} offsets={dists}")
+        compare(q, k, v, do, 1.0, w.W, dists, f"rounded {name}/{layer}", want_dalpha=False)
+
+
 def test_staged_calls_equal_the_combined_call():
     w = workloads.WORKLOADS["l1024_learned_bf16"]
     q, k, v, do = [x.to("cuda:0") for x in workloads.draw(w, 3, B=2)]

@@ -92,6 +92,32 @@ def test_full_size_sampled_batches(name):
         compare(q, k, v, alphas[layer], w.W, base, f"{name}/{layer}", bsel=bsel)
 
 
+@pytest.mark.parametrize("name", ["l1024_linear_bf16", "l4096_coprime_bf16", "l1024_pow2_linear_bf16"])
+def test_rounded_stagger(name):
+    # §2 "Implementation note": the static schedules with integer offsets (alpha f_k rounded, the
+    # library's rounding checked against the oracle's), on the integer path at alpha = 1
+    w = workloads.WORKLOADS[name]
+    base = base_of(w)
+    for layer, alpha in enumerate(alphas_of(w)):
+        if layer % 3:
+            continue
+        dists = O.rounded_offsets(alpha, base)
+        assert fa.fibattn_round_offsets(alpha, base) == dists
+        B, L = (2, 300) if layer % 2 == 0 else (1, 1500)
+        q, k, v = workloads.draw(w, layer, B=B, L=L, with_grad=False)
+        say(f"rounded {name} layer {layer} alpha={alpha!r} B={B} L={L} offsets={dists}")
+        compare(q, k, v, 1.0, w.W, dists, f"rounded {name}/{layer}")
+
+
+def test_rounded_stagger_full_size_sampled_batches():
+    w = workloads.WORKLOADS["l1024_linear_bf16"]
+    alpha = alphas_of(w)[7]
+    dists = fa.fibattn_round_offsets(alpha, base_of(w))
+    q, k, v = workloads.draw(w, 7, with_grad=False)
+    say(f"rounded l1024_linear_bf16 layer 7 full size, offsets {dists}")
+    compare(q, k, v, 1.0, w.W, dists, "rounded full size", bsel=[0, 15, 31])
+
+
 def randn(shape, seed, dtype=torch.float32):
     return workloads.randn_like_seeded(shape, seed, dtype)
 
