@@ -190,6 +190,24 @@ class Layers:
         fa.fibattn_bwd_stages(st, q, k, v, do, 1.0, self.w.W, self.rounded[layer], self.dq[layer], self.dk[layer],
                               self.dv[layer], self.ws)
 
+    def decode_setup(self):
+        """Each sequence's last row as its new token; the layer's k and v as the cache."""
+        if getattr(self, "dq_last", None) is None:
+            L = self.w.L
+            self.dq_last = [inp[0][:, :, L - 1].contiguous() for inp in self.inputs]
+            self.dpos = torch.full((self.w.B,), L - 1, dtype=torch.int32, device=self.dev)
+            self.do_last = [torch.empty_like(x) for x in self.dq_last]
+
+    def decode(self, layer):
+        _, k, v, _ = self.inputs[layer]
+        self.fa.fibattn_decode(self.dq_last[layer], k, v, self.dpos, self.alphas[layer], self.w.W, self.base,
+                               o=self.do_last[layer], need_lse=False)
+
+    def decode_rounded(self, layer):
+        _, k, v, _ = self.inputs[layer]
+        self.fa.fibattn_decode(self.dq_last[layer], k, v, self.dpos, 1.0, self.w.W, self.rounded[layer],
+                               o=self.do_last[layer], need_lse=False)
+
     def prep(self, layer):
         self.fa.fibattn_fwd_prep(self.inputs[layer][1], self.inputs[layer][2], self.ws)
 
@@ -297,9 +315,14 @@ def measure(fa, name: str, steps: int, warmup: int, dev):
         log(f"[{name}] timing the rounded-integer variant")
         it = time_stages(net, 3, {"fwd_interp": net.fwd, "fwd_int": net.fwd_rounded, "bwd_interp": net.bwd,
                                   "bwd_int": net.bwd_rounded})
+        net.decode_setup()
+        dt = time_stages(net, 3, {"decode_interp": net.decode, "decode_int": net.decode_rounded})
         integer_path = {
             "what": "rounded-integer stagger (offsets round-half-even(alpha_l f_k), read at alpha = 1) against "
                     "the interpolated stagger, same inputs, ms per layer call",
+            "decode_us_interp": dt["decode_interp"] * 1e3, "decode_us_int": dt["decode_int"] * 1e3,
+            "decode_ratio": dt["decode_interp"] / dt["decode_int"],
+            "decode_what": f"single-token decode, {w.B} sequences each at position {w.L - 1} of a {w.L}-row cache",
             "fwd_ms_interp": it["fwd_interp"], "fwd_ms_int": it["fwd_int"], "fwd_ratio": it["fwd_interp"] / it["fwd_int"],
             "bwd_ms_interp": it["bwd_interp"], "bwd_ms_int": it["bwd_int"], "bwd_ratio": it["bwd_interp"] / it["bwd_int"],
             "paper": "about 5x inference latency for the learned (interpolated, unfused gather) variant against the "

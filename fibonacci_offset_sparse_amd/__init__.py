@@ -51,6 +51,9 @@ def _load() -> ctypes.CDLL:
         "fibattn_fwd_attend": (ctypes.c_int, [_c_ptr, _c_ptr, _c_f64, _c_i32, _P(_c_i32), _c_i32,
                                                _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f64,
                                                _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
+        "fibattn_decode": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_f64, _c_i32, _P(_c_i32), _c_i32,
+                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f64, _c_ptr,
+                                           _c_ptr, _c_ptr]),
         "fibattn_bwd_workspace_bytes": (_c_size, [_c_i32] * 8),
         "fibattn_bwd": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_f64, _c_i32,
                                         _P(_c_i32), _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -250,6 +253,31 @@ def fibattn_fwd_attend(q: torch.Tensor, v: torch.Tensor, alpha: float, W: int, o
                                       workspace.data_ptr(), workspace.numel(), _stream(q.device, stream)))
 
 
+def fibattn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, positions: torch.Tensor,
+                   alpha: float, W: int, offsets: Sequence[int], rope_theta: float = 1e4,
+                   o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, need_lse: bool = True,
+                   stream=None):
+    """(o [B, Hq, D], lse [B, Hq] or None): each sequence's new query q[b] at position positions[b]
+    (int32 on the device) against its cache rows k_cache[b], v_cache[b] ([B, Hkv, Lmax, D])."""
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and the caches [B, Hkv, Lmax, D]")
+    B, Hq, D = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    dt = _dtype_code(q)
+    args = [_dev(q, "q", (B, Hq, D), q.dtype), _dev(k_cache, "k_cache", (B, Hkv, Lmax, D), q.dtype),
+            _dev(v_cache, "v_cache", (B, Hkv, Lmax, D), q.dtype), _dev(positions, "positions", (B,), torch.int32)]
+    o = torch.empty_like(q) if o is None else o
+    if need_lse and lse is None:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    optr = _dev(o, "o", (B, Hq, D), q.dtype)
+    lptr = _dev(lse, "lse", (B, Hq), torch.float32) if lse is not None else None
+    offs, K = _i32_array(offsets)
+    with torch.cuda.device(q.device):
+        _check(lib.fibattn_decode(*args, float(alpha), int(W), offs, K, B, Lmax, Hq, Hkv, D, dt, float(rope_theta),
+                                  optr, lptr, _stream(q.device, stream)))
+    return o, lse
+
+
 def fibattn_bwd_reuses_fwd_prep(alpha: float, W: int, offsets: Sequence[int], B: int, L: int, Hq: int,
                                 Hkv: int, D: int = 64, dtype: int = BF16) -> bool:
     """Whether the backward's STAGE_PREP writes what fibattn_fwd_prep writes (then a backward whose
@@ -321,6 +349,6 @@ __all__ = [
     "fibattn_status_string", "fibattn_last_error", "fibattn_base_offsets", "fibattn_alpha_schedule",
     "fibattn_alpha_from_theta", "fibattn_round_offsets", "fibattn_plan", "fibattn_fwd_workspace_bytes", "fibattn_fwd",
     "fibattn_fwd_prep", "fibattn_fwd_attend", "fibattn_bwd_workspace_bytes", "fibattn_bwd",
-    "fibattn_bwd_stages", "fibattn_bwd_reuses_fwd_prep", "STAGE_PREP", "STAGE_QUERY", "STAGE_KEY", "STAGE_ALL",
+    "fibattn_bwd_stages", "fibattn_bwd_reuses_fwd_prep", "fibattn_decode", "STAGE_PREP", "STAGE_QUERY", "STAGE_KEY", "STAGE_ALL",
     "FibAttnError", "lib", "LIB_PATH",
 ]

@@ -28,7 +28,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Packed fp32 VALU instructions stay off: kernels use scalar fp32 FMA only.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
-SOURCES = ["fibattn_api.cpp", "fibattn_fwd.hip", "fibattn_fwd_mfma.hip", "fibattn_bwd.hip", "fibattn_bwd_mfma.hip"]
+SOURCES = ["fibattn_api.cpp", "fibattn_fwd.hip", "fibattn_fwd_mfma.hip", "fibattn_bwd.hip", "fibattn_bwd_mfma.hip",
+           "fibattn_decode.hip"]
 
 
 def hipcc() -> str:

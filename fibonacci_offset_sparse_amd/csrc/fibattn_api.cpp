@@ -366,6 +366,38 @@ fibattn_status_t fibattn_fwd(const void* q, const void* k, const void* v, double
                               workspace_bytes, stream);
 }
 
+fibattn_status_t fibattn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* positions,
+                                double alpha, int32_t W, const int32_t* offsets, int32_t K, int32_t B, int32_t Lmax,
+                                int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype, double rope_theta, void* o,
+                                float* lse, void* stream) {
+    g_error[0] = '\0';
+    FIBATTN_TRY(check_dims(B, Lmax, Hq, Hkv, D, W, dtype, rope_theta));
+    FIBATTN_TRY(check_offsets(alpha, W, offsets, K));
+    if (q == nullptr || k_cache == nullptr || v_cache == nullptr || positions == nullptr || o == nullptr)
+        return fail(FIBATTN_ERR_INVALID, "q, k_cache, v_cache, positions or o is NULL");
+    const Plan plan = make_plan(alpha, W, offsets, K);
+    DecodeArgs a{};
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.pos = positions;
+    a.o = o;
+    a.lse = lse;
+    a.B = B;
+    a.Lmax = Lmax;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.W = W;
+    a.n_off = plan.n_keep;
+    a.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(kD)));
+    a.fr = make_freq(rope_theta);
+    std::memcpy(a.off, plan.keep, sizeof(plan.keep));
+    const hipError_t e = launch_decode(dtype, a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return FIBATTN_OK;
+}
+
 size_t fibattn_bwd_workspace_bytes(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t W, int32_t K,
                                    int32_t dtype) {
     (void)D;

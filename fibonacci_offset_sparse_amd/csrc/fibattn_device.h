@@ -58,6 +58,18 @@ template <> __device__ __forceinline__ void store4<f16_t>(f16_t* p, float4 x) {
     *reinterpret_cast<uint2*>(p) = make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
 }
 
+// One element as float, and one float stored in the storage type.
+template <typename T> __device__ __forceinline__ float load_elem(const T* p);
+template <> __device__ __forceinline__ float load_elem<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load_elem<bf16_t>(const bf16_t* p) {
+    return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+}
+template <typename T> __device__ __forceinline__ void store_elem(T* p, float x);
+template <> __device__ __forceinline__ void store_elem<float>(float* p, float x) { *p = x; }
+template <> __device__ __forceinline__ void store_elem<bf16_t>(bf16_t* p, float x) {
+    *p = static_cast<bf16_t>(f32_to_bf16_bits(x));
+}
+
 // A 64-element row into registers.
 template <typename T> __device__ __forceinline__ void load_row(const T* p, float (&x)[kD]) {
 #pragma unroll

@@ -105,6 +105,20 @@ struct BwdArgs {
     int32_t xcd_map;
 };
 
+// Single-token decode: each sequence's new query against its cache.
+struct DecodeArgs {
+    const void* q;       // [B, Hq, 64] storage type: the new query of each sequence
+    const void* kc;      // [B, Hkv, Lmax, 64] storage type: unrotated keys, rows 0..pos[b] valid
+    const void* vc;      // [B, Hkv, Lmax, 64] storage type
+    const int32_t* pos;  // [B] device: the position of each sequence's new token
+    void* o;             // [B, Hq, 64]
+    float* lse;          // [B, Hq] or nullptr
+    int32_t B, Lmax, Hq, Hkv, G, W, n_off;
+    float scale;         // 1/sqrt(D)
+    RopeFreq fr;
+    OffsetSlot off[kMaxOff];
+};
+
 // Entries per query in the weight tables of the matrix-core backward: 16 window distances, 16 rungs.
 constexpr int kNW = 16, kNR = 16;
 
@@ -112,6 +126,7 @@ hipError_t launch_rope_keys(int dtype, const RopeKeysArgs& a, hipStream_t s);
 // keys and values with dims permuted (element 4m + c of a row holds dim 16c + m), and the table
 hipError_t launch_prep_kv16(const PrepArgs& a, hipStream_t s);
 hipError_t launch_fwd_attend(int dtype, const FwdArgs& a, hipStream_t s);
+hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t s);
 bool fwd_mfma_supported(const FwdArgs& a);
 hipError_t launch_fwd_mfma(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd(int dtype, const BwdArgs& a, bool want_dalpha, int stages, hipStream_t s);

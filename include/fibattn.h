@@ -177,6 +177,26 @@ fibattn_status_t fibattn_fwd_attend(const void* q, const void* v, double alpha, 
                                     double rope_theta, void* o, float* lse,
                                     const void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Single-token decode (inference with a cache): for each sequence b, its new query at position
+ * positions[b] attends to the window and offset slots of that position (§2 "Attended set"; integer
+ * offsets read one row, §2 "Implementation note"). The output is the forward pass's output row at
+ * that position for the sequence held in the cache.
+ * q: device [B, Hq, D] of `dtype`, the new queries (unrotated). k_cache, v_cache: device
+ * [B, Hkv, Lmax, D] of `dtype`, keys unrotated (as fibattn_fwd takes them); rows 0..positions[b]
+ * of sequence b are read, the new token's own key and value included (write them before the call).
+ * positions: device int32 [B]. o: device [B, Hq, D] of `dtype` (written); lse: device float32
+ * [B, Hq] (natural log, written) or NULL. No workspace. Arithmetic is float32 for both storage
+ * types (keys rotated at their own positions as they are read).
+ * A position outside [0, Lmax) is not read from: that sequence's outputs are NaN.
+ * Errors: as fibattn_fwd, with Lmax in place of L.
+ */
+fibattn_status_t fibattn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* positions, double alpha, int32_t W,
+                                const int32_t* offsets, int32_t K, int32_t B, int32_t Lmax,
+                                int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
+                                double rope_theta, void* o, float* lse, void* stream);
+
 /* Bytes of device workspace fibattn_bwd needs. */
 size_t fibattn_bwd_workspace_bytes(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D,
                                    int32_t W, int32_t K, int32_t dtype);
