@@ -64,7 +64,7 @@ def _oracle_unit(args):
     q, k, v, do = [x[b:b + 1].double().numpy() for x in (q, k, v, do)]
     fn = {"fixed": O.alpha_fixed, "linear": O.alpha_linear, "coprime": O.alpha_coprime}[w.schedule]
     alpha = fn(layer, w.n_layers)
-    base = O.FIB_BASE if w.base == "fib" else O.POW2_BASE_1024
+    base = O.FIB_BASE if w.base == "fib" else {1024: O.POW2_BASE_1024, 2048: O.POW2_BASE_2048}[workloads.pow2_max(w)]
     O.forward(q, k, v, alpha, w.W, base)
     O.backward(q, k, v, do, alpha, w.W, base)
     return 1
@@ -132,7 +132,10 @@ class Layers:
     def __init__(self, fa, w, dev, n_sets=None):
         self.fa, self.w, self.dev = fa, w, dev
         self.n_sets = w.n_layers if n_sets is None else n_sets
-        base = fa.fibattn_base_offsets(fa.BASE_FIB if w.base == "fib" else fa.BASE_POW2, 1024)
+        if w.base == "fib":
+            base = fa.fibattn_base_offsets(fa.BASE_FIB)
+        else:
+            base = fa.fibattn_base_offsets(fa.BASE_POW2, workloads.pow2_max(w))
         self.base = base
         code = {"fixed": fa.SCHEDULE_FIXED, "linear": fa.SCHEDULE_LINEAR, "coprime": fa.SCHEDULE_COPRIME}
         self.alphas, self.dadt = [], []

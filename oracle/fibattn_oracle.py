@@ -51,6 +51,8 @@ import numpy as np
 FIB_BASE: Tuple[int, ...] = (1, 2, 3, 5, 8, 13, 21, 34, 55, 89, 144, 233, 377, 610, 987)
 # §2 "Control base": a reach-matched power-of-two base; this fixed list of 11 rungs ends at 1024.
 POW2_BASE_1024: Tuple[int, ...] = tuple(2 ** n for n in range(11))
+# The same control grown with the length: rungs up to 2048 at L = 4096.
+POW2_BASE_2048: Tuple[int, ...] = tuple(2 ** n for n in range(12))
 # §3 "Models and training": RoPE theta.
 ROPE_THETA = 1.0e4
 # Reading 3: absolute tolerance under which alpha * f counts as integral.

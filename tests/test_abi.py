@@ -79,6 +79,7 @@ def test_plan_snaps_the_float64_traps():
 def test_base_offsets_match_the_oracle():
     assert fa.fibattn_base_offsets(fa.BASE_FIB) == O.FIB_BASE
     assert fa.fibattn_base_offsets(fa.BASE_POW2, 1024) == O.POW2_BASE_1024
+    assert fa.fibattn_base_offsets(fa.BASE_POW2, 2048) == O.POW2_BASE_2048
     assert fa.fibattn_base_offsets(fa.BASE_POW2, 1000)[-1] == 512
 
 

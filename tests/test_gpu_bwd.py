@@ -158,6 +158,18 @@ def test_rounded_stagger(name):
         compare(q, k, v, do, 1.0, w.W, dists, f"rounded {name}/{layer}", want_dalpha=False)
 
 
+@pytest.mark.parametrize("name,layer", [("l4096_pow2_2048_linear_bf16", 9), ("l4096_w6_coprime_bf16", 4)])
+def test_long_workload_variants(name, layer):
+    # the power-of-two base grown to 2048 and a narrower window at the 4x length shape; L reaches
+    # the largest rungs
+    w = workloads.WORKLOADS[name]
+    base = O.POW2_BASE_2048 if w.base == "pow2_2048" else O.FIB_BASE
+    fn = {"linear": O.alpha_linear, "coprime": O.alpha_coprime}[w.schedule]
+    q, k, v, do = workloads.draw(w, layer, B=1, L=2600, with_grad=True)
+    say(f"bwd {name} layer {layer} B=1 L=2600")
+    compare(q, k, v, do, fn(layer, 16), w.W, base, f"{name}/{layer}", want_dalpha=False)
+
+
 def test_staged_calls_equal_the_combined_call():
     w = workloads.WORKLOADS["l1024_learned_bf16"]
     q, k, v, do = [x.to("cuda:0") for x in workloads.draw(w, 3, B=2)]

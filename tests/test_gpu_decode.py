@@ -70,7 +70,7 @@ def alphas_of(w):
                                   "l4096_coprime_bf16"])
 def test_ragged_positions(name):
     w = workloads.WORKLOADS[name]
-    base = O.FIB_BASE if w.base == "fib" else O.POW2_BASE_1024
+    base = O.FIB_BASE if w.base == "fib" else {1024: O.POW2_BASE_1024, 2048: O.POW2_BASE_2048}[workloads.pow2_max(w)]
     L = min(w.L, 1600)
     positions = [L - 1, 0, 517, 64, 13]
     for layer in (0, 7, 15):

@@ -36,7 +36,9 @@ def say(*a):
 
 
 def base_of(w):
-    return O.FIB_BASE if w.base == "fib" else O.POW2_BASE_1024
+    if w.base == "fib":
+        return O.FIB_BASE
+    return {1024: O.POW2_BASE_1024, 2048: O.POW2_BASE_2048}[workloads.pow2_max(w)]
 
 
 def alphas_of(w):

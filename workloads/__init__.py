@@ -34,7 +34,7 @@ class Workload:
     D: int
     dtype: str         # "f32" or "bf16": storage type of q, k, v, o and the gradients
     W: int             # window: distances 0..W
-    base: str          # "fib" or "pow2_1024"
+    base: str          # "fib", or "pow2_<max>": the power-of-two control base up to <max>
     schedule: str      # "fixed", "linear", "coprime" or "learned"
     n_layers: int
     backward: bool
@@ -58,8 +58,20 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("l1024_pow2_linear_bf16", 4, 32, 1024, 8, 2, 64, "bf16", 8, "pow2_1024", "linear", 16,
                  False),
         Workload("l1024_learned_bf16", 5, 32, 1024, 8, 2, 64, "bf16", 10, "fib", "learned", 16, True),
+        # long-L variants at the 4x extrapolation shape: a power-of-two base grown with L (rung
+        # 2048), and the window sweep of the paper's run matrix (W = 12 is l4096_coprime_bf16)
+        Workload("l4096_pow2_2048_linear_bf16", 6, 8, 4096, 8, 2, 64, "bf16", 8, "pow2_2048", "linear", 16,
+                 False),
+        Workload("l4096_w6_coprime_bf16", 7, 8, 4096, 8, 2, 64, "bf16", 6, "fib", "coprime", 16, False),
+        Workload("l4096_w8_coprime_bf16", 8, 8, 4096, 8, 2, 64, "bf16", 8, "fib", "coprime", 16, False),
+        Workload("l4096_w10_coprime_bf16", 9, 8, 4096, 8, 2, 64, "bf16", 10, "fib", "coprime", 16, False),
     ]
 }
+
+
+def pow2_max(w: Workload) -> int:
+    """The largest rung of a power-of-two base workload (from its name), e.g. 1024 for "pow2_1024"."""
+    return int(w.base.split("_")[1])
 
 
 def draw(w: Workload, layer: int, B: Optional[int] = None, L: Optional[int] = None,
