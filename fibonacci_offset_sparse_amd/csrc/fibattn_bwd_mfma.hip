@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
 #pragma unroll
     for (int k = 0; k < MAXS; ++k) {
         if (k < kn) {
-            const int sl = p + kNear - ((x >> 1) ? in_sgpr(A.off[2 * k + 1].a) : in_sgpr(A.off[2 * k].a)) - (x & 1);
+            const int sl = p + kNear - pick_uniform((x >> 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a) - (x & 1);
             pair_terms(row_dot_group(q, lds0, sl * kRowBytes, swz(sl)),
                        row_dot_group(dov, lds0 + kBufBytes, sl * kRowBytes, swz(sl)), k);
         }
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
 #pragma unroll
         for (int k = 0; k < MAXS; ++k) {
             if (k < kn) {
-                const int sl = pt + kNear - ((kt >> 1) ? in_sgpr(A.off[2 * k + 1].a) : in_sgpr(A.off[2 * k].a)) - (kt & 1);
+                const int sl = pt + kNear - pick_uniform((kt >> 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a) - (kt & 1);
                 row_sum_group(o, wo[k][0], wo[k][1], lds0, sl * kRowBytes, swz(sl));
             }
         }
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     // rung 2k + (wv & 1), dS halves (wv < 2) or p halves, (near, far) times (1 - t, t)
     const int wrow = threadIdx.x >> 2, wv = threadIdx.x & 3;
     auto put_w = [&](int k) {
-        const float t = (wv & 1) ? in_sgpr(A.off[2 * k + 1].t) : in_sgpr(A.off[2 * k].t);
+        const float t = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].t, A.off[2 * k].t);
         const uint32_t en = went[k & 1][wv & 1][wrow], ef = went[k & 1][wv & 1][wrow + 1];
         const uint32_t pr = __builtin_amdgcn_perm(ef, en, (wv >> 1) ? 0x05040100u : 0x07060302u);
         const h2_t c = {static_cast<_Float16>(1.f - t), static_cast<_Float16>(t)};
@@ -623,7 +623,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int n = 2 * k + (wv & 1);
-                const int qn = j0 + wrow + ((wv & 1) ? in_sgpr(A.off[2 * k + 1].a) : in_sgpr(A.off[2 * k].a));
+                const int qn = j0 + wrow + pick_uniform((wv & 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a);
                 const bool okn = k < kn && qn < L, okf = k < kn && qn + 1 < L;
                 const uint32_t vn = wr[static_cast<int64_t>(n) * L + (okn ? qn : 0)];
                 const uint32_t vf = wr[static_cast<int64_t>(n) * L + (okf ? qn + 1 : 0)];
@@ -638,7 +638,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             if (k < kn) {
-                const float t = (wv & 1) ? in_sgpr(A.off[2 * k + 1].t) : in_sgpr(A.off[2 * k].t);
+                const float t = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].t, A.off[2 * k].t);
                 const uint32_t pr = __builtin_amdgcn_perm(efr[k], enr[k], (wv >> 1) ? 0x05040100u : 0x07060302u);
                 const h2_t c = {static_cast<_Float16>(1.f - t), static_cast<_Float16>(t)};
                 reinterpret_cast<uint32_t*>(&wnear(k)[wrow])[wv] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, pr) * c);
@@ -673,7 +673,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             if (k < kn) {
-                const int ak = (te >> 1) ? in_sgpr(A.off[2 * k + 1].a) : in_sgpr(A.off[2 * k].a);
+                const int ak = pick_uniform((te >> 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a);
                 int nadr[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) nadr[q] = blk_addr(rbase16 + q + ak + (te & 1), 0);

@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
             s[4 * kWG + 2 * k] = kNegInf;
             s[4 * kWG + 2 * k + 1] = kNegInf;
             if (k < kn) {
-                const int sl = p + kNear - ((x >> 1) ? in_sgpr(A.off[2 * k + 1].a) : in_sgpr(A.off[2 * k].a)) - (x & 1);
+                const int sl = p + kNear - pick_uniform((x >> 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a) - (x & 1);
                 score(row_dot_group(q, buf(0), sl * kRowBytes, swz(sl)), k);
             }
         }
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
 #pragma unroll
         for (int k = 0; k < MAXS; ++k) {
             if (k < kn) {
-                const int sl = pt + kNear - ((kt >> 1) ? in_sgpr(A.off[2 * k + 1].a) : in_sgpr(A.off[2 * k].a)) - (kt & 1);
+                const int sl = pt + kNear - pick_uniform((kt >> 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a) - (kt & 1);
                 row_sum_group(o, po[k][0], po[k][1], lds0, sl * kRowBytes, swz(sl));
             }
         }

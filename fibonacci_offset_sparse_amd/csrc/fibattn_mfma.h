@@ -90,13 +90,15 @@ __device__ __forceinline__ lds_ptr_t dma_dst(char* dst) {
     return (lds_ptr_t)static_cast<uintptr_t>(a);
 }
 
-// A uniform value made opaque in a scalar register. A per-lane choice between two such values
-// selects values; a choice between two entries of the kernel's offset table would otherwise
-// become one vector load from a per-lane address, which the compiler follows with a full vmcnt
-// wait, behind every staging load in flight.
-template <typename T> __device__ __forceinline__ T in_sgpr(T v) {
-    asm volatile("" : "+s"(v));
-    return v;
+// A per-lane choice between two uniform values (two entries of the kernel's offset table): both
+// are read as scalars first, each made opaque in a scalar register, and the lane then selects
+// (v_cndmask). A choice between the table entries themselves would become one vector load from a
+// per-lane kernel-argument address, which the compiler follows with a full vmcnt wait behind
+// every staging load in flight; an empty asm inside each arm of the choice would become a branch.
+template <typename T> __device__ __forceinline__ T pick_uniform(bool c, T if_true, T if_false) {
+    asm volatile("" : "+s"(if_true));
+    asm volatile("" : "+s"(if_false));
+    return c ? if_true : if_false;
 }
 
 // Wait until at most N vector-memory instructions of this wave are in flight (its LDS DMAs up to
