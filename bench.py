@@ -108,18 +108,28 @@ def cpu_baseline(name: str, budget_s: float = 15.0):
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, or None when it was taken
     on another workload or the kernel's sources have changed since."""
-    import hashlib
     if workload != TRAFFIC_WORKLOAD or not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         entry = json.load(f)["kernels"].get(kernel)
     if entry is None:
         return None
+    paths = [os.path.join(ROOT, "fibonacci_offset_sparse_amd", "csrc", fn) for fn in entry["sources"]]
+    return entry["bytes_per_launch"] if code_hash(paths) == entry["sources_sha256"] else None
+
+
+def code_hash(paths) -> str:
+    """sha256 of the sources with // comments and blank lines left out, so that a comment edit
+    does not retire a measurement of unchanged code."""
+    import hashlib
     h = hashlib.sha256()
-    for fn in entry["sources"]:
-        with open(os.path.join(ROOT, "fibonacci_offset_sparse_amd", "csrc", fn), "rb") as f:
-            h.update(f.read())
-    return entry["bytes_per_launch"] if h.hexdigest() == entry["sources_sha256"] else None
+    for p in paths:
+        with open(p) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
+    return h.hexdigest()
 
 
 # ------------------------------------------------------------------------------------------------

@@ -12,23 +12,25 @@
 // over dims (scores, dP) read them against q and do permuted the same way.
 //
 //  * bwd_q_mfma: workgroup = (batch, kv head, 4 query heads, 64 positions), lanes as in the forward
-//    (fibattn_mfma.h). Three passes over the staged blocks:
-//      A, keys: scores s (base 2), recomputed in fp32 from fp16 operands, and for every rung the
-//         difference far - near of the two row products;
-//      B, values: dP = do . value row, and far - near of it; then in registers p = softmax(s),
-//         delta = sum p dP, dS = p (dP - delta), and the d(loss)/dt terms
-//         dS (q . (k_far - k_near)) / sqrt(D) + p do . (v_far - v_near);
-//      C, keys: dq_rot = sum dS/sqrt(D) (coefficient) key row, with transposing reads of the
+//    (fibattn_mfma.h). Two passes over the staged blocks (the near block, rows i0 - 64 .. i0 + 63,
+//    for the window and the rungs with floor(d) <= 63, then far steps of two larger rungs):
+//      AB, keys and values staged together: scores s (base 2), recomputed in fp32 from fp16
+//         operands, dP = do . value row, and for every rung far - near of both products; then in
+//         registers p = softmax(s), delta = sum p dP, dS = p (dP - delta), and the d(loss)/dt
+//         terms dS (q . (k_far - k_near)) / sqrt(D) + p do . (v_far - v_near);
+//      C, keys again: dq_rot = sum dS/sqrt(D) (coefficient) key row, with transposing reads of the
 //         permuted keys (a lane then holds 16 consecutive dims of 4 heads), RoPE transposed
 //         between lanes x and x ^ 2, written as dq.
-//    It also writes the rotated queries (fp16, permuted), do as fp16 and, per key row and term,
-//    the weights the key side needs: p times the term's coefficient and dS/sqrt(D) times it, both
-//    fp16.
+//    It also writes, for the key side, the rotated queries and do (fp16, dims permuted) and per
+//    query the (p, dS/sqrt(D)) fp16 pair of every window distance and of every rung (without the
+//    rung's coefficients, which the key side applies).
 //  * bwd_k_dot: workgroup = (batch, kv head, 64 key rows). Key row j is read by query j + delta of
 //    every term (window distance d; the near row of a rung at a, coefficient 1 - t; its far row at
-//    a + 1, coefficient t): for each query head, shifted blocks of rotated queries and of do are
-//    staged and dk_rot[j] += w_ds q_rot, dv[j] += w_p do accumulate 4 terms at a time from
-//    transposing reads (a lane gets 4 rows' element 4m + x) with two v_dot2 per element.
+//    a + 1, coefficient t). For each query head, the near block of rotated queries and do (query
+//    rows j0 .. j0 + 127: the window and the rungs with floor(d) <= 63) and then far steps of two
+//    larger rungs are staged; the window runs on v_mfma_f32_16x16x16f16 as a banded product, the
+//    rung terms accumulate dk_rot[j] += w_dS q_rot, dv[j] += w_p do 4 terms at a time from
+//    transposing reads (a lane gets 4 rows' element of one block) with two v_dot2 per element.
 //  * dalpha (fibattn_bwd.hip): fixed-order sum of the per-workgroup dt partials.
 // No atomics: results are bitwise reproducible.
 #include "fibattn_mfma.h"
@@ -52,8 +54,8 @@ template <int MAXS>
 __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     constexpr int MAXK = 2 * MAXS;
     // Two item buffers used in turn, each a key part and a value part. Items: the key and value
-    // windows, then the key and value rung steps (pass AB); then the key window and key steps
-    // again (pass C, key parts only).
+    // near blocks, then the key and value far steps (pass AB); then the key near block and key
+    // far steps again (pass C, key parts only).
     __shared__ __attribute__((aligned(1024))) char lds0[2 * kBufBytes];
     __shared__ __attribute__((aligned(1024))) char lds1[2 * kBufBytes];
     __shared__ float red[4][MAXK];

@@ -12,8 +12,8 @@
 //    interpolated rung reads two rows, nearer (coefficient 1 - t) and farther (t); scores and
 //    outputs are linear in the blended row.
 //  * LDS slots are 128-byte fp16 rows; 16-byte chunk k of slot s sits at chunk k ^ ((s >> 1) & 7).
-//    A rung step holds rung 2k at slot 0 (block A) and rung 2k + 1 at slot kBlkSlots (block B,
-//    two slots up); a window holds rows i0 - W - 4 + s at slot s.
+//    A far step holds rung 2k at slot 0 (block A) and rung 2k + 1 at slot kBlkSlots (block B,
+//    two slots up); a near block holds 128 consecutive rows, row j0 + s at slot s.
 #pragma once
 
 #include "fibattn_device.h"
@@ -23,11 +23,9 @@ namespace mx {
 
 constexpr int kNT = 256;                 // 4 waves x 16 positions x 4 lanes
 constexpr int kRowBytes = kD * 2;        // one fp16 row
-constexpr int kWinPad = 4;               // window slot of row i0 - W - 4 is 0: pads stay in range
 constexpr int kBlkSlots = 72;            // 65 (+2 for the second rung) rows, 9 DMA groups
 constexpr int kBlkBytes = kBlkSlots * kRowBytes;
-constexpr int kBufBytes = 2 * kBlkBytes; // one staging buffer: a window or a rung step
-constexpr int kWinBytes = 96 * kRowBytes; // a window (rows j0 + s at slot s < 96)
+constexpr int kBufBytes = 2 * kBlkBytes; // one staging buffer: a near block or a far step
 // The near block of a tile of 64 positions i0..i0+63: key rows i0 - 64 .. i0 + 63 (slot s holds
 // row i0 - kNear + s). It holds the window (W <= 15) and both rows of every rung with a <= 63.
 constexpr int kNear = 64;
@@ -154,9 +152,9 @@ __device__ __forceinline__ void row_sum_group(f4_t (&o)[16], uint32_t w01, uint3
 // LDS DMA staging of one (batch, kv head)'s fp16 rows. A 16-byte wave instruction fills 1 KB = 8
 // slots: lane l lands on slot 8g + (l >> 3), physical chunk l & 7, and fetches that slot's row and
 // the logical chunk the swizzle puts there. A 4-byte instruction fills 2 slots: lane l lands on
-// slot 2g' + (l >> 5), physical dword l & 31. Every wave issues 3 instructions per window or rung
-// block, so the waits can count them. Rows before 0 or past L fall outside the buffer resource
-// and arrive as zeros.
+// slot 2g' + (l >> 5), physical dword l & 31. Every wave issues the same number of instructions
+// per item (4 per near block, 3 per rung block), so the waits can count them. Rows before 0 or
+// past L fall outside the buffer resource and arrive as zeros.
 // Blocks are given by the row that lands at slot 0. (Rows are passed by value: taking the address
 // of the kernel's argument struct would make the compiler copy it to scratch memory.)
 struct Stager {
@@ -181,14 +179,6 @@ struct Stager {
     }
     __device__ __forceinline__ void dma4(const __amdgpu_buffer_rsrc_t& rs, char* dst, int row0, int blk) const {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dma_dst(dst), 4, row0 * kRowBytes + (blk ? voff4_1 : voff4_0), 0, 0, 0);
-    }
-    // window: rows j0 + s at slot s, s < 96 (12 groups, 3 per wave)
-    __device__ __forceinline__ void window(const __amdgpu_buffer_rsrc_t& rs, char* dst, int j0) const {
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            const int g = wave + 4 * u;
-            dma16(rs, dst + g * 1024, j0 + 8 * g, gpar);
-        }
     }
     // near block: rows j0 + s at slot s, s < 128 (16 groups, 4 per wave)
     __device__ __forceinline__ void near(const __amdgpu_buffer_rsrc_t& rs, char* dst, int j0) const {
