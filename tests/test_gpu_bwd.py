@@ -225,3 +225,38 @@ def test_bitwise_determinism():
     for x, y in zip(a[:3], b[:3]):
         assert torch.equal(x, y)
     assert a[3] == b[3]
+
+
+def test_maximum_length_sampled_rows():
+    # L = 2^20 (the largest the library takes), one sequence, 4 query heads on one key-value head:
+    # every offset computation at its largest. Outputs at row c depend only on rows within the
+    # reach (1481 at alpha = 1.5), and RoPE scores only on relative positions, so the oracle runs
+    # on a slice around c: dq at c needs keys c - 1481 .. c, dk and dv at c need queries
+    # c .. c + 1481.
+    L, B, Hq, Hkv, D = 1 << 20, 1, 4, 1, 64
+    alpha, W = 1.4, 12
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(2024)
+    q, k, v, do = (torch.randn(B, h, L, D, generator=g).to(torch.bfloat16) for h in (Hq, Hkv, Hkv, Hq))
+    say(f"max length L={L}: forward + backward")
+    dq, dk, dv, _, _ = fa.fibattn_bwd(q.to(dev), k.to(dev), v.to(dev), None, None, do.to(dev), alpha, W, O.FIB_BASE)
+    o, _ = fa.fibattn_fwd(q.to(dev), k.to(dev), v.to(dev), alpha, W, O.FIB_BASE)
+    torch.cuda.synchronize()
+    dq, dk, dv, o = dq.cpu(), dk.cpu(), dv.cpu(), o.cpu()
+    for c in (5000, L // 2 + 77, L - 1600):
+        s0, s1 = c - 1500, min(L, c + 1500)
+        n64 = [x[:, :, s0:s1].double().numpy() for x in (q, k, v, do)]
+        o_ref, _ = O.forward(*n64[:3], alpha, W, O.FIB_BASE)
+        rq, rk, rv, _ = O.backward(*n64, alpha, W, O.FIB_BASE)
+        r = c - s0
+        check(o[:, :, c], o_ref[:, :, r], q.dtype, what=f"L=2^20 row {c} o")
+        check(dq[:, :, c], rq[:, :, r], q.dtype, what=f"L=2^20 row {c} dq")
+        check(dk[:, :, c], rk[:, :, r], q.dtype, what=f"L=2^20 row {c} dk")
+        check(dv[:, :, c], rv[:, :, r], q.dtype, what=f"L=2^20 row {c} dv")
+    # decode of the last position against the same slice rule
+    pos = torch.tensor([L - 1], dtype=torch.int32, device=dev)
+    od, _ = fa.fibattn_decode(q[:, :, L - 1].contiguous().to(dev), k.to(dev), v.to(dev), pos, alpha, W, O.FIB_BASE)
+    torch.cuda.synchronize()
+    n64 = [x[:, :, L - 3000:].double().numpy() for x in (q, k, v)]
+    o_ref, _ = O.forward(*n64, alpha, W, O.FIB_BASE)
+    check(od.cpu(), o_ref[:, :, -1], q.dtype, what="L=2^20 decode")
