@@ -230,9 +230,9 @@ def test_bitwise_determinism():
 def test_maximum_length_sampled_rows():
     # L = 2^20 (the largest the library takes), one sequence, 4 query heads on one key-value head:
     # every offset computation at its largest. Outputs at row c depend only on rows within the
-    # reach (1382 here; under 1500 for any alpha <= 1.5), and RoPE scores only on relative positions, so the oracle runs
-    # on a slice around c: dq at c needs keys c - 1382 .. c, dk and dv at c need queries
-    # c .. c + 1382.
+    # reach (1382 here; under 1500 for any alpha <= 1.5), and RoPE scores only on relative
+    # positions, so the oracle runs on a slice around c: dq at c needs keys c - 1382 .. c, dk and
+    # dv at c need queries c .. c + 1382.
     L, B, Hq, Hkv, D = 1 << 20, 1, 4, 1, 64
     alpha, W = 1.4, 12
     dev = torch.device("cuda:0")
