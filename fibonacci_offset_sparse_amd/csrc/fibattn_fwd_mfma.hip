@@ -431,7 +431,8 @@ hipError_t launch_fwd_mfma(const FwdArgs& A0, hipStream_t s) {
     FwdArgs A = A0;
     const int64_t n_tiles = (A.L + kTile - 1) / kTile;
     const int64_t n_units = static_cast<int64_t>(A.B) * A.Hkv * (A.G / 4);
-    A.xcd_map = (n_units % 8 == 0) ? 1 : 0;
+    // the forward keeps 4 workgroups per CU in one round: mix early and late tiles on each CU
+    A.xcd_map = (n_units % 8 == 0) ? 2 : 0;
     hipLaunchKernelGGL((fwd_mfma_kernel<8>), dim3(static_cast<unsigned>(n_units * n_tiles)), dim3(kNT), 0, s, A);
     return hipGetLastError();
 }

@@ -60,7 +60,7 @@ struct FwdArgs {
     void* o;             // [B, Hq, L, 64]
     float* lse;          // [B, Hq, L] or nullptr
     int32_t B, L, Hq, Hkv, G, W, n_off;
-    int32_t xcd_map;     // fast kernel: keep each (batch, kv head)'s tiles on one XCD
+    int32_t xcd_map;     // matrix-core kernels: 0 plain order, 1 each (batch, kv head) on one XCD, 2 also mix tiles per CU
     float qscale;        // log2(e) / sqrt(D): scores kept in base 2
     RopeFreq fr;
     OffsetSlot off[kMaxOff];

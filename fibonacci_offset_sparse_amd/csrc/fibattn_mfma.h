@@ -231,11 +231,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, in
                                              L * kRowBytes, kRsrcWord3);
 }
 
-// Workgroup -> (unit, tile): with the XCD map, unit u runs on XCD u % 8 for all its tiles, whose
-// L2 then holds that unit's keys and values for every tile that re-reads them.
+// Workgroup -> (unit, tile): with the XCD map (xcd_map != 0), unit u runs on XCD u % 8 for all its
+// tiles, whose L2 then holds that unit's keys and values for every tile that re-reads them. An XCD
+// hands its workgroups (slot s = w / 8 in launch order) to its 32 CUs in turn, so slots s, s + 32,
+// s + 64, ... share a CU. With xcd_map == 2, every odd row of 32 slots is taken in reverse order,
+// so that a CU holds early tiles (few rungs in reach) and late ones alike instead of four copies of
+// one tile index; a partial last row keeps its order (the map stays a permutation).
 __device__ __forceinline__ void unit_tile(int w, int n_tiles, int xcd_map, int& unit, int& tile) {
     if (xcd_map) {
-        const int sl = w >> 3;
+        int sl = w >> 3;
+        const int row = sl >> 5;
+        if (xcd_map == 2 && (row & 1) && ((row + 1) << 5) <= static_cast<int>(gridDim.x >> 3))
+            sl = (row << 5) + 31 - (sl & 31);
         unit = (sl / n_tiles) * 8 + (w & 7);
         tile = sl % n_tiles;
     } else {
