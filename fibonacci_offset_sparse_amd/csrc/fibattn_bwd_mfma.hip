@@ -435,7 +435,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         for (int u = 0; u < 8; ++u) {
             const uint4 v = *reinterpret_cast<const uint4*>(treg + lin_view_addr(lane, u));
             const int64_t row = lin_row(lin_slot(lane, u));
-            if (row >= 0) *reinterpret_cast<uint4*>(static_cast<bf16_t*>(A.dq) + row * kD + (lane & 7) * 8) = v;
+            if (row >= 0) store_nt(static_cast<bf16_t*>(A.dq) + row * kD + (lane & 7) * 8, v);
         }
     }
 
@@ -759,12 +759,12 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
             const int64_t orow = (static_cast<int64_t>(bg) * L + j) * kD + 16 * part;
             const uint4* sk = reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(lds0) + row * kD + 16 * part);
             const uint4* sv = reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(lds1) + row * kD + 16 * part);
-            uint4* gk = reinterpret_cast<uint4*>(static_cast<bf16_t*>(A.dk) + orow);
-            uint4* gv = reinterpret_cast<uint4*>(static_cast<bf16_t*>(A.dv) + orow);
-            gk[0] = sk[0];
-            gk[1] = sk[1];
-            gv[0] = sv[0];
-            gv[1] = sv[1];
+            bf16_t* gk = static_cast<bf16_t*>(A.dk) + orow;
+            bf16_t* gv = static_cast<bf16_t*>(A.dv) + orow;
+            store_nt(gk, sk[0]);
+            store_nt(gk + 8, sk[1]);
+            store_nt(gv, sv[0]);
+            store_nt(gv + 8, sv[1]);
         }
     }
 }

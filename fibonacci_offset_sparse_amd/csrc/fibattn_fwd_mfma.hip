@@ -406,11 +406,11 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
             hi.y = pack_bf2(o[10][r] * invh[r], o[11][r] * invh[r]);
             hi.z = pack_bf2(o[12][r] * invh[r], o[13][r] * invh[r]);
             hi.w = pack_bf2(o[14][r] * invh[r], o[15][r] * invh[r]);
-            *reinterpret_cast<uint4*>(orow) = lo;
-            *reinterpret_cast<uint4*>(orow + 8) = hi;
+            store_nt(orow, lo);
+            store_nt(orow + 8, hi);
         }
         if (A.lse != nullptr)
-            A.lse[(static_cast<int64_t>(b) * A.Hq + h0 + x) * L + i] = (m + log2f(l)) * 0.69314718055994530942f;
+            store_nt(A.lse + (static_cast<int64_t>(b) * A.Hq + h0 + x) * L + i, (m + log2f(l)) * 0.69314718055994530942f);
     }
 }
 
