@@ -128,8 +128,8 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             const int sl = lin_slot(lane, u);
             const int pos = min(i0 + 16 * wave + (sl & 15), L - 1);
             const int voff = ((sl >> 4) * L + pos) * kRowBytes + (((lane & 7) ^ tr_f(sl)) << 4);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs4, dma_dst(rq + u * 1024), 16, voff, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(drs4, dma_dst(rd + u * 1024), 16, voff, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs4, dma_dst(rq + u * 1024), 16, voff, 0, 0, 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(drs4, dma_dst(rd + u * 1024), 16, voff, 0, 0, 2);
         }
         const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(active ? i : 0) * (kPairs / 2) + 4 * x;
 #pragma unroll

@@ -64,9 +64,8 @@ constexpr int kWgsPerCu = 4;
 // 8u..8u+7: dims 16e + 2u (e < 4) and 16(e - 4) + 2u + 1, which hold RoPE pairs 2u, 2u + 1,
 // 16 + 2u, 17 + 2u whole (pair m: dims m and m + 32). The table is cos and sin as they are.
 // ------------------------------------------------------------------------------------------------
-// A thread takes one position j and kPrepRows (batch, head) rows of it: the cos/sin of its 4
-// RoPE pairs are computed once for all of them, and every row's loads are issued before any is
-// used.
+// A thread takes one position j and kPrepRows (batch, head) rows of it: every row's loads are
+// issued first, then the cos/sin of its 4 RoPE pairs are computed once for all of them.
 constexpr int kPrepRows = 4;
 
 __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
@@ -78,19 +77,18 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
     if (grp * kPrepRows >= A.n_bh) return;
     const bf16_t* ks = static_cast<const bf16_t*>(A.k);
     const bf16_t* vs = static_cast<const bf16_t*>(A.v);
-    // the thread's pairs 2u, 2u + 1, 16 + 2u, 17 + 2u
+    // the thread's pairs 2u, 2u + 1, 16 + 2u, 17 + 2u, and their frequencies (loaded ahead of the
+    // rows: a wait for them then does not wait for the rows too)
     int pr[4];
+    float fh[4], fl[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pr[e] = (e >> 1) * 16 + 2 * u + (e & 1);
-    float2 cs[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) rope_cos_sin(j, A.fr.hi[pr[e]], A.fr.lo[pr[e]], cs[e].x, cs[e].y);
-    if (grp == 0) {   // the table: [L][32] (cos, sin)
-        float2* t = reinterpret_cast<float2*>(A.cs) + static_cast<int64_t>(j) * kPairs;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) t[pr[e]] = cs[e];
+    for (int e = 0; e < 4; ++e) {
+        pr[e] = (e >> 1) * 16 + 2 * u + (e & 1);
+        fh[e] = A.fr.hi[pr[e]];
+        fl[e] = A.fr.lo[pr[e]];
     }
-    // loads of every row first: dims 16c + 2u, 16c + 2u + 1 (c = 0..3) of the key and the value
+    // loads of every row (dims 16c + 2u, 16c + 2u + 1, c = 0..3, of the key and the value), in
+    // flight while the cos/sin are computed
     uint32_t kw[kPrepRows][4], vw[kPrepRows][4];
 #pragma unroll
     for (int r = 0; r < kPrepRows; ++r) {
@@ -101,6 +99,14 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
             kw[r][c] = *reinterpret_cast<const uint32_t*>(ks + row + 16 * c + 2 * u);
             vw[r][c] = *reinterpret_cast<const uint32_t*>(vs + row + 16 * c + 2 * u);
         }
+    }
+    float2 cs[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rope_cos_sin(j, fh[e], fl[e], cs[e].x, cs[e].y);
+    if (grp == 0) {   // the table: [L][32] (cos, sin)
+        float2* t = reinterpret_cast<float2*>(A.cs) + static_cast<int64_t>(j) * kPairs;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[pr[e]] = cs[e];
     }
 #pragma unroll
     for (int r = 0; r < kPrepRows; ++r) {
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
             const int sl = lin_slot(lane, u);
             const int pos = min(i0 + 16 * wave + (sl & 15), L - 1);
             const int voff = ((sl >> 4) * L + pos) * kRowBytes + (((lane & 7) ^ tr_f(sl)) << 4);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs4, dma_dst(reg + u * 1024), 16, voff, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs4, dma_dst(reg + u * 1024), 16, voff, 0, 0, 2);
         }
         // the cos/sin of the position: lane x loads pairs 8x..8x+7; the rotation takes the others
         // from the quad's lanes
