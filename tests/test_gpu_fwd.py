@@ -144,6 +144,25 @@ def test_window_and_offset_extremes(W, offsets, alpha):
     compare(q, k, v, alpha, W, offsets, f"W={W} K={len(offsets)} a={alpha}")
 
 
+def test_grid_order_covers_every_tile_once():
+    # B = 20 at the paper's head counts: 40 (batch, KV head) units of 16 tiles, 80 workgroup slots
+    # per XCD, so the grid order takes one row of 32 slots in launch order, the next in reverse and
+    # leaves the last, partial row (16 slots) in order. Outputs start as NaN: a tile computed twice
+    # or never shows in the comparison over every batch element.
+    w = workloads.WORKLOADS["l1024_linear_bf16"]
+    q, k, v = workloads.draw(w, 6, B=20, L=1024, with_grad=False)
+    dev = torch.device("cuda:0")
+    o = torch.full(q.shape, float("nan"), dtype=q.dtype, device=dev)
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=dev)
+    alpha = O.alpha_linear(6, 16)
+    say("grid order: B=20 L=1024")
+    fa.fibattn_fwd(q.to(dev), k.to(dev), v.to(dev), alpha, w.W, O.FIB_BASE, o=o, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = O.forward(q.double().numpy(), k.double().numpy(), v.double().numpy(), alpha, w.W, O.FIB_BASE)
+    check(o.cpu(), o_ref, q.dtype, what="B=20 o")
+    check(lse.cpu(), lse_ref, q.dtype, what="B=20 lse", stored_bf16=False)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (4, 2), (8, 1), (6, 2), (3, 3)])
 def test_gqa_group_sizes(Hq, Hkv):
     L = 150
