@@ -37,10 +37,14 @@
 //    barrier per item after a counted vmcnt wait.
 //  * Banks: 16-byte chunk k of slot s sits at chunk k ^ ((s >> 1) & 7), so the same chunk of 16
 //    consecutive slots covers all 64 banks, and the second rung's block sits two slots up. Key
-//    reads (16 lanes per pass) are then free of bank conflicts for window and rung groups, as
-//    are the transposing value reads of window groups; those of rung groups are 2-way.
+//    reads (16 lanes per pass) are then free of bank conflicts for window groups and far steps,
+//    and for a near rung pair whose floors differ by d with d mod 32 in 0..11 or 21..27 (2-way
+//    otherwise); the transposing value reads are free for window groups and 2-way for rung
+//    groups (a 32-lane pass reads 18 distinct rows).
 //  * The grid is mapped so that all tiles of one (batch, key-value head) run on one XCD, whose L2
-//    then holds that head's keys and values for every tile that re-reads them.
+//    then holds that head's keys and values for every tile that re-reads them, and each CU mixes
+//    early and late tiles.
+//  * q arrives by non-temporal LDS DMA (read once) and o and lse leave by non-temporal stores.
 #include "fibattn_mfma.h"
 
 namespace fibattn {
