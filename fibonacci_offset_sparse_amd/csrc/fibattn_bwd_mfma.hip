@@ -32,6 +32,9 @@
 //    rung terms accumulate dk_rot[j] += w_dS q_rot, dv[j] += w_p do 4 terms at a time from
 //    transposing reads (a lane gets 4 rows' element of one block) with two v_dot2 per element.
 //  * dalpha (fibattn_bwd.hip): fixed-order sum of the per-workgroup dt partials.
+// q and do arrive by non-temporal DMA (read once) and dq, dk, dv leave by non-temporal stores; the
+// rows and weights the query side writes for the key side keep plain stores, since the key side
+// reads them right after (hinting them cost the key side more than it saved).
 // No atomics: results are bitwise reproducible.
 #include "fibattn_mfma.h"
 
