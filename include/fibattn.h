@@ -26,7 +26,9 @@
  * Layout: every tensor is contiguous [B, H, L, D] (H = Hq for q, o, do, dq; Hkv for k, v, dk,
  * dv). lse is [B, Hq, L] float32 (natural log). D must be 64.
  * Storage types: FIBATTN_F32 (float32 everywhere) or FIBATTN_BF16 (bfloat16 q, k, v, o, do, dq,
- * dk, dv; arithmetic is float32).
+ * dk, dv; dot products take fp16-rounded operands - rotated q and k, values, softmax weights,
+ * do - with float32 accumulation, and the softmax, its gradient and every reduction run in
+ * float32; decode computes in float32 throughout).
  *
  * Ownership and execution. All buffers belong to the caller. Device pointers must stay valid
  * until the stream reaches the work. `offsets` is a host array, read during the call and not
@@ -138,10 +140,12 @@ size_t fibattn_fwd_workspace_bytes(int32_t B, int32_t L, int32_t Hkv, int32_t D,
  * NULL when no backward pass will follow.
  * workspace: device, >= fibattn_fwd_workspace_bytes(...) bytes, scratch for this call only.
  * Queues two kernels on `stream`: fibattn_fwd_prep, then fibattn_fwd_attend.
- * Arithmetic: float32 for FIBATTN_F32. For FIBATTN_BF16, scores and P.V take products of fp16
- * operands (rotated q and k, values, softmax weights; each rounded to fp16, relative error
- * <= 2^-11) accumulated in float32, and interpolated keys are blended in fp16; inputs must stay
- * below 65504 in magnitude (after rotation) for this to hold.
+ * Arithmetic: float32 for FIBATTN_F32. For FIBATTN_BF16, rotated keys and values are staged as
+ * fp16, and the matrix-core kernels also round the rotated q and the softmax weights to fp16 for
+ * their products (each operand within 2^-11 relative); products accumulate in float32, and the
+ * interpolation weight t is applied in float32 (to scores and weights on the matrix cores, to
+ * the staged rows in the general kernels). Inputs must stay below 65504 in magnitude (after
+ * rotation) for this to hold.
  * Errors: INVALID (NULL pointers, B/L/Hq/Hkv < 1, Hq % Hkv != 0, W < 0, K outside [0, 32],
  * bad alpha, bad offsets, unknown dtype, rope_theta not finite and > 0), UNSUPPORTED (D != 64,
  * W > 31, L > 2^20), WORKSPACE, HIP.
