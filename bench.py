@@ -89,6 +89,11 @@ def cpu_baseline(name: str, budget_s: float = 15.0):
         wall = time.perf_counter() - t0
         pool.terminate()
     qh = done * w.L * w.Hq
+    # the rate of one single-threaded worker, on a few of the same units
+    t1 = time.perf_counter()
+    with ctx.Pool(1, initializer=_one_thread) as pool:
+        n1 = len(pool.map(_oracle_unit, units[:4]))
+    wall1 = time.perf_counter() - t1
     cpu = "unknown"
     try:
         for ln in open("/proc/cpuinfo"):
@@ -99,6 +104,7 @@ def cpu_baseline(name: str, budget_s: float = 15.0):
         pass
     return {
         "value": qh / wall, "unit": "queries*heads/s (fwd+bwd)", "cores": workers, "kind": "oracle",
+        "value_1worker": n1 * w.L * w.Hq / wall1,
         "sample": f"{done} (layer, batch element 0) units of {name}, each a float64 forward + backward at "
                   f"B=1, L={w.L}, {wall:.1f} s wall on {workers} single-threaded worker processes ({cpu}, "
                   f"{platform.machine()})",
