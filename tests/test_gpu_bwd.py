@@ -3,7 +3,8 @@
 dq, dk, dv per element; d(alpha) and d(theta) per layer. Cases: the tiny workload (integral
 offsets, no d(alpha)), float32 interpolated cases, every layer of the learned-alpha workload at a
 reduced size, the learned workload at full size (sampled batch elements for dq/dk/dv, the full
-batch for d(theta)), GQA group sizes, ragged lengths, and bitwise determinism.
+batch for d(theta)), the bench's two shapes at full size, GQA group sizes, ragged lengths, and
+bitwise determinism.
 """
 
 import sys
@@ -117,6 +118,20 @@ def test_learned_workload_full_size(layer):
     tol = DALPHA_RTOL[q.dtype]
     assert abs(da - ref) <= tol * abs(ref), (da, ref)
     assert abs(dth - ref * dadt) <= tol * abs(ref * dadt), (dth, ref * dadt)
+
+
+@pytest.mark.parametrize("name,layer", [("l1024_linear_bf16", 0), ("l1024_linear_bf16", 15),
+                                        ("l4096_coprime_bf16", 3), ("l4096_coprime_bf16", 12)])
+def test_bench_workloads_full_size(name, layer):
+    # the two shapes the bench times forward + backward on, at full size and in its launch
+    # configuration; dq, dk, dv on the first and last batch element (d(alpha) is not asked for:
+    # some layers of these schedules have integral rungs)
+    w = workloads.WORKLOADS[name]
+    fn = {"linear": O.alpha_linear, "coprime": O.alpha_coprime}[w.schedule]
+    alpha = fn(layer, w.n_layers)
+    q, k, v, do = workloads.draw(w, layer, with_grad=True)
+    say(f"bwd {name} full size layer {layer} alpha={alpha!r} B={w.B} L={w.L}")
+    compare(q, k, v, do, alpha, w.W, O.FIB_BASE, f"{name}/{layer}", want_dalpha=False, bsel=[0, w.B - 1])
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 1), (6, 2)])
