@@ -4,7 +4,8 @@ The decode output of a sequence at position p is the forward pass's output row p
 sequence's first p + 1 rows (§2 "Attended set"), so the oracle is its forward pass, read at that
 row. Cases: every schedule's layers with ragged positions per sequence (cache rows past each
 position hold NaN, so a stray read would show), the rounded-integer offsets, float32 storage at
-1e-5, a position outside the cache, and the paper's shapes at full size on sampled sequences.
+1e-5, a position outside the cache, the paper's shape at full size on sampled sequences, and the
+4x length shape with ragged positions.
 """
 
 import sys
@@ -139,3 +140,15 @@ def test_full_size_paper_shape_sampled_sequences():
         o_ref, lse_ref = O.forward(*n64, alpha, w.W, O.FIB_BASE)
         check(o[b:b + 1], o_ref[:, :, -1], q.dtype, what=f"full b={b} o")
         check(lse[b:b + 1], lse_ref[:, :, -1], q.dtype, what=f"full b={b} lse", stored_bf16=False)
+
+
+def test_long_shape_ragged_positions():
+    # the 4x length shape: B = 8 sequences of a 4096-row cache, each at its own position (the
+    # coprime stagger's layer with the largest alpha, whose rungs reach 1481 rows back)
+    w = workloads.WORKLOADS["l4096_coprime_bf16"]
+    layer = max(range(w.n_layers), key=lambda l: O.alpha_coprime(l, w.n_layers))
+    alpha = O.alpha_coprime(layer, w.n_layers)
+    q, k, v = workloads.draw(w, layer, with_grad=False)
+    positions = [w.L - 1, 3000, 1481, 1480, 700, 64, 1, 0]
+    say(f"decode l4096_coprime_bf16 layer {layer} alpha={alpha!r} positions={positions}")
+    decode_case(q, k, v, positions, alpha, w.W, O.FIB_BASE, "l4096 decode")
