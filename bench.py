@@ -319,6 +319,32 @@ def time_stages(net: Layers, sweeps: int, stages=None):
     return {k: v / sweeps for k, v in tot.items()}
 
 
+def time_layers(net: Layers, sweeps: int, stages):
+    """Per-layer call durations: median, 10th and 90th percentile over the sweeps.
+
+    Each stage runs over all layers back to back behind a short GPU spin, with an event between
+    consecutive calls, so each call's duration is the gap between the events around it."""
+    import numpy as np
+    n = net.w.n_layers
+    out = {}
+    for name, fn in stages.items():
+        samples = np.zeros((sweeps, n))
+        for s in range(sweeps):
+            torch.cuda.synchronize()
+            torch.cuda._sleep(20_000_000)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+            ev[0].record()
+            for layer in range(n):
+                fn(layer)
+                ev[layer + 1].record()
+            torch.cuda.synchronize()
+            samples[s] = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+        med, p10, p90 = (np.percentile(samples, q, axis=0) for q in (50, 10, 90))
+        out[name] = {"median": [round(x, 5) for x in med.tolist()], "p10": [round(x, 5) for x in p10.tolist()],
+                     "p90": [round(x, 5) for x in p90.tolist()], "total_median": float(med.sum())}
+    return out
+
+
 def measure(fa, name: str, steps: int, warmup: int, dev):
     w = workloads.WORKLOADS[name]
     log(f"[{name}] allocating inputs")
@@ -327,6 +353,11 @@ def measure(fa, name: str, steps: int, warmup: int, dev):
     ms_step, wall = time_steps(net, steps, warmup)
     log(f"[{name}] {ms_step:.3f} ms per step; timing stages")
     st = time_stages(net, 3)
+    log(f"[{name}] timing each layer's calls")
+    per_layer = time_layers(net, 10, {"fwd_ms": net.fwd, "bwd_ms": net.bwd})
+    per_layer["alpha"] = [round(a, 6) for a in net.alphas]
+    per_layer["what"] = ("each layer's forward and backward call (ms): median, p10, p90 over 10 sweeps; the "
+                         "event between calls drains the queue, so these read 1-4 us per call above kernels_ms")
     integer_path = None
     if w.schedule in ("linear", "coprime"):
         # the same schedule with rounded offsets on the integer path, against the interpolated
@@ -373,6 +404,7 @@ def measure(fa, name: str, steps: int, warmup: int, dev):
                 "frac_hbm_peak": bwd_bytes / (st["bwd"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 "algorithmic_bytes": bwd_bytes},
         "kernels_ms": st,
+        "per_layer": per_layer,
         "kernel_bytes": kernel_bytes,
         "integer_path": integer_path,
     }
@@ -448,6 +480,7 @@ def main():
         "fwd": main_res["fwd"],
         "bwd": main_res["bwd"],
         "kernels_ms": main_res["kernels_ms"],
+        "per_layer": main_res["per_layer"],
         "integer_path": main_res["integer_path"],
         "cpu_baseline": cpu,
     }
@@ -455,7 +488,8 @@ def main():
         lw = workloads.WORKLOADS[args.long_workload]
         line["l4096"] = {"workload": args.long_workload, "B": lw.B, "L": lw.L, "ms_per_step": long_res["ms_per_step"],
                          "qh_per_s": long_res["qh_per_s"], "fwd": long_res["fwd"], "bwd": long_res["bwd"],
-                         "kernels_ms": long_res["kernels_ms"], "integer_path": long_res["integer_path"]}
+                         "kernels_ms": long_res["kernels_ms"], "per_layer": long_res["per_layer"],
+                         "integer_path": long_res["integer_path"]}
     print(json.dumps(line), flush=True)
 
 
