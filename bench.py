@@ -391,6 +391,25 @@ def measure(fa, name: str, steps: int, warmup: int, dev):
         "bwd_key": (2 * w.Hq + 2 * w.Hkv) * rows,                               # q, dout; dk, dv
     }
     fwd_ms = st["fwd_prep"] + st["fwd_attend"]
+    # algorithmic arithmetic of the forward attention: 2 D FMA per valid (query-head, slot) for
+    # QK and P.V, plus 2 D per (key row, interpolated rung) for blending the key and value rows
+    # (shared by the group's heads); masked slots and dropped rungs are not counted
+    fma, slots = [], []
+    for a in net.alphas:
+        kind, _, _, reach = fa.fibattn_plan(a, w.W, net.base)
+        win = sum(min(w.W, i) + 1 for i in range(w.L))
+        kept = [max(0, w.L - int(r)) for kd, r in zip(kind, reach) if kd != fa.DUP]
+        interp = [max(0, w.L - int(r)) for kd, r in zip(kind, reach) if kd == fa.INTERP]
+        n_valid = w.B * w.Hq * (win + sum(kept))
+        fma.append(2 * w.D * n_valid + 2 * w.D * w.B * w.Hkv * sum(interp))
+        slots.append(n_valid / qh)
+    fma_call = sum(fma) / len(fma)
+    arith = {"fma_per_call": fma_call, "valid_slots_per_qh": sum(slots) / len(slots),
+             "achieved_tflops": 2 * fma_call / (st["fwd_attend"] * 1e-3) / 1e12,
+             "fp32_valu_peak_tflops": FP32_VALU_PEAK_TFLOPS,
+             "frac_fp32_valu_peak": 2 * fma_call / (st["fwd_attend"] * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
+             "what": "forward attention kernel, layer average; the products run on fp16 matrix cores "
+                     "(4x4x4 blocks), the peak is the fp32 vector ALUs' without packed ops"}
     res = {
         "ms_per_step": ms_step,
         "wall_s": wall,
@@ -404,6 +423,7 @@ def measure(fa, name: str, steps: int, warmup: int, dev):
                 "frac_hbm_peak": bwd_bytes / (st["bwd"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 "algorithmic_bytes": bwd_bytes},
         "kernels_ms": st,
+        "arith_fwd_attend": arith,
         "per_layer": per_layer,
         "kernel_bytes": kernel_bytes,
         "integer_path": integer_path,
@@ -480,6 +500,7 @@ def main():
         "fwd": main_res["fwd"],
         "bwd": main_res["bwd"],
         "kernels_ms": main_res["kernels_ms"],
+        "arith_fwd_attend": main_res["arith_fwd_attend"],
         "per_layer": main_res["per_layer"],
         "integer_path": main_res["integer_path"],
         "cpu_baseline": cpu,
@@ -489,6 +510,7 @@ def main():
         line["l4096"] = {"workload": args.long_workload, "B": lw.B, "L": lw.L, "ms_per_step": long_res["ms_per_step"],
                          "qh_per_s": long_res["qh_per_s"], "fwd": long_res["fwd"], "bwd": long_res["bwd"],
                          "kernels_ms": long_res["kernels_ms"], "per_layer": long_res["per_layer"],
+                         "arith_fwd_attend": long_res["arith_fwd_attend"],
                          "integer_path": long_res["integer_path"]}
     print(json.dumps(line), flush=True)
 
