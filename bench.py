@@ -345,6 +345,17 @@ def time_layers(net: Layers, sweeps: int, stages):
     return out
 
 
+def fwd_slot_counts(fa, w, alpha: float, base):
+    """(valid (query-head, slot) pairs, (key row, interpolated rung) pairs) of one forward call,
+    from the library's offset plan: window distance d is valid at query i >= d, a kept rung at
+    i >= its reach."""
+    kind, _, _, reach = fa.fibattn_plan(alpha, w.W, base)
+    win = sum(min(w.W, i) + 1 for i in range(w.L))
+    kept = sum(max(0, w.L - int(r)) for kd, r in zip(kind, reach) if kd != fa.DUP)
+    interp = sum(max(0, w.L - int(r)) for kd, r in zip(kind, reach) if kd == fa.INTERP)
+    return w.B * w.Hq * (win + kept), w.B * w.Hkv * interp
+
+
 def measure(fa, name: str, steps: int, warmup: int, dev):
     w = workloads.WORKLOADS[name]
     log(f"[{name}] allocating inputs")
@@ -396,12 +407,8 @@ def measure(fa, name: str, steps: int, warmup: int, dev):
     # (shared by the group's heads); masked slots and dropped rungs are not counted
     fma, slots = [], []
     for a in net.alphas:
-        kind, _, _, reach = fa.fibattn_plan(a, w.W, net.base)
-        win = sum(min(w.W, i) + 1 for i in range(w.L))
-        kept = [max(0, w.L - int(r)) for kd, r in zip(kind, reach) if kd != fa.DUP]
-        interp = [max(0, w.L - int(r)) for kd, r in zip(kind, reach) if kd == fa.INTERP]
-        n_valid = w.B * w.Hq * (win + sum(kept))
-        fma.append(2 * w.D * n_valid + 2 * w.D * w.B * w.Hkv * sum(interp))
+        n_valid, n_interp = fwd_slot_counts(fa, w, a, net.base)
+        fma.append(2 * w.D * n_valid + 2 * w.D * n_interp)
         slots.append(n_valid / qh)
     fma_call = sum(fma) / len(fma)
     arith = {"fma_per_call": fma_call, "valid_slots_per_qh": sum(slots) / len(slots),
