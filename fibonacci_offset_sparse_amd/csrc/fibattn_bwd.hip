@@ -426,24 +426,31 @@ __global__ __launch_bounds__(kTile * HPB) void bwd_key_kernel(BwdArgs A) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// dalpha: sum per offset over workgroups in a fixed order (double), weight by f_k.
+// dalpha: sum per offset over workgroups in a fixed order (double), weight by f_k. Thread t sums
+// column t % kMaxOff over workgroups t / kMaxOff, + kDaRows, ...: the loads of all offsets are in
+// flight together (consecutive threads read one workgroup's row), then a tree over the rows.
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void dalpha_kernel(BwdArgs A) {
-    __shared__ double red[256];
-    double acc = 0.0;
-    for (int n = 0; n < A.n_off; ++n) {
-        if (!A.off[n].interp) continue;
-        double s = 0.0;
-        for (int w = threadIdx.x; w < A.n_wg; w += 256) s += A.partial[static_cast<int64_t>(w) * kMaxOff + n];
-        red[threadIdx.x] = s;
-        __syncthreads();
-        for (int stride = 128; stride > 0; stride >>= 1) {
-            if (threadIdx.x < stride) red[threadIdx.x] += red[threadIdx.x + stride];
-            __syncthreads();
-        }
-        acc += static_cast<double>(A.off[n].f) * red[0];
+constexpr int kDaThreads = 1024, kDaRows = kDaThreads / kMaxOff;
+__global__ __launch_bounds__(kDaThreads) void dalpha_kernel(BwdArgs A) {
+    __shared__ double red[kDaThreads];
+    const int n = threadIdx.x % kMaxOff, r = threadIdx.x / kMaxOff;
+    bool use = false;                                   // interpolated kept rung (uniform loop: no
+    for (int k = 0; k < A.n_off; ++k)                   // per-lane indexing of the argument block)
+        if (k == n && A.off[k].interp) use = true;
+    double s = 0.0;
+    if (use) {
+#pragma unroll 4
+        for (int w = r; w < A.n_wg; w += kDaRows) s += A.partial[static_cast<int64_t>(w) * kMaxOff + n];
+    }
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int stride = kDaRows / 2; stride > 0; stride >>= 1) {
+        if (r < stride) red[threadIdx.x] += red[threadIdx.x + stride * kMaxOff];
         __syncthreads();
     }
+    double acc = 0.0;
+    for (int k = 0; k < A.n_off; ++k)
+        if (A.off[k].interp) acc += static_cast<double>(A.off[k].f) * red[k];
     if (threadIdx.x == 0) {
         if (A.dalpha != nullptr) A.dalpha[0] = static_cast<float>(acc);
         if (A.dtheta != nullptr) A.dtheta[0] = static_cast<float>(acc * static_cast<double>(A.dalpha_dtheta));
@@ -458,7 +465,7 @@ void launch_bwd_heads(const BwdArgs& A, bool want_dalpha, int stages, hipStream_
                            s, A);
     if (stages & kStageKey) {
         hipLaunchKernelGGL((bwd_key_kernel<T, HPB>), dim3(tiles, A.Hkv, A.B), dim3(kTile * HPB), 0, s, A);
-        if (want_dalpha) hipLaunchKernelGGL(dalpha_kernel, dim3(1), dim3(256), 0, s, A);
+        if (want_dalpha) hipLaunchKernelGGL(dalpha_kernel, dim3(1), dim3(kDaThreads), 0, s, A);
     }
 }
 
@@ -474,7 +481,7 @@ hipError_t launch_bwd_typed(const BwdArgs& A, bool want_dalpha, int stages, hipS
 }  // namespace
 
 hipError_t launch_dalpha(const BwdArgs& A, hipStream_t s) {
-    hipLaunchKernelGGL(dalpha_kernel, dim3(1), dim3(256), 0, s, A);
+    hipLaunchKernelGGL(dalpha_kernel, dim3(1), dim3(kDaThreads), 0, s, A);
     return hipGetLastError();
 }
 
