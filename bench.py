@@ -37,7 +37,9 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, 8 TB/s
 # hash of the sources each kernel was built from: a figure is used only while the sources match
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_bytes_l1024_linear.json")
 TRAFFIC_WORKLOAD = "l1024_linear_bf16"
-FP32_VALU_PEAK_TFLOPS = 78.6    # 256 CU x 2.4 GHz x 64 lanes x 2 (FMA), scalar fp32 (no packed ops)
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix-core peak (the forward's products run there)
+FWD_TARGET_FRAC = 0.60          # the forward attention's target: 60 % of peak HBM bandwidth
+STREAM_BYTES = 1 << 30          # streaming probe buffers (four times the Infinity Cache)
 
 
 def log(*a):
@@ -70,9 +72,19 @@ def _oracle_unit(args):
     return 1
 
 
+def cpu_share() -> int:
+    """Host cores this job may use: the affinity mask, capped by OMP_NUM_THREADS where the host sets
+    it (a GPU machine gives each GPU's jobs a fixed share of its cores and says so there)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        return max(1, min(n, int(os.environ.get("OMP_NUM_THREADS", n))))
+    except ValueError:
+        return n
+
+
 def cpu_baseline(name: str, budget_s: float = 15.0):
     w = workloads.WORKLOADS[name]
-    workers = min(16, len(os.sched_getaffinity(0)))
+    workers = cpu_share()
     # (layer, repeat) units, each on batch element 0 of that layer's inputs: the oracle's cost does
     # not depend on the values, and a B = 1 draw keeps input generation out of the way; more units
     # than the budget lets finish, so that the budget sets the sample
@@ -107,7 +119,8 @@ def cpu_baseline(name: str, budget_s: float = 15.0):
         "value_1worker": n1 * w.L * w.Hq / wall1,
         "sample": f"{done} (layer, batch element 0) units of {name}, each a float64 forward + backward at "
                   f"B=1, L={w.L}, {wall:.1f} s wall on {workers} single-threaded worker processes ({cpu}, "
-                  f"{platform.machine()})",
+                  f"{platform.machine()}; {len(os.sched_getaffinity(0))} cores in the affinity mask, "
+                  f"OMP_NUM_THREADS={os.environ.get('OMP_NUM_THREADS', 'unset')})",
     }
 
 
@@ -124,6 +137,22 @@ def measured_traffic(kernel: str, workload: str):
     return entry["bytes_per_launch"] if code_hash(paths) == entry["sources_sha256"] else None
 
 
+def measured_limiter(kernel: str, workload: str):
+    """What the committed counter summary names as the kernel's limiter (with its evidence), or
+    "unknown" when it was taken on another workload or the kernel's sources have changed since."""
+    path = os.path.join(ROOT, "profiles", "limiters_l1024_linear.json")
+    if workload != TRAFFIC_WORKLOAD or not os.path.exists(path):
+        return "unknown"
+    with open(path) as f:
+        entry = json.load(f)["kernels"].get(kernel)
+    if entry is None:
+        return "unknown"
+    paths = [os.path.join(ROOT, "fibonacci_offset_sparse_amd", "csrc", fn) for fn in entry["sources"]]
+    if code_hash(paths) != entry["sources_sha256"]:
+        return "unknown"
+    return {"limiter": entry["limiter"], "evidence": entry["evidence"]}
+
+
 def code_hash(paths) -> str:
     """sha256 of the sources with // comments and blank lines left out, so that a comment edit
     does not retire a measurement of unchanged code."""
@@ -136,6 +165,49 @@ def code_hash(paths) -> str:
                 if code:
                     h.update(code.encode() + b"\n")
     return h.hexdigest()
+
+
+# ------------------------------------------------------------------------------------------------
+# Streaming probe: what plain coalesced reads, writes and copies reach on this GPU's HBM
+# ------------------------------------------------------------------------------------------------
+
+def stream_probe(dev, reps: int = 10):
+    """TB/s of the probe's patterns over 1 GiB buffers (libstreamprobe.so), timed with events on the
+    current stream (the probe launches there)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "fibonacci_offset_sparse_amd", "libstreamprobe.so"))
+    lib.streamprobe_launch.restype = ctypes.c_int
+    lib.streamprobe_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_void_p]
+    lib.streamprobe_read_blocks.restype = ctypes.c_int64
+    lib.streamprobe_read_blocks.argtypes = [ctypes.c_int64]
+    a = torch.ones(STREAM_BYTES, dtype=torch.uint8, device=dev)
+    b = torch.empty(STREAM_BYTES, dtype=torch.uint8, device=dev)
+    sink = torch.empty(int(lib.streamprobe_read_blocks(STREAM_BYTES)), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for name, pat, moved in (("read", 0, 1), ("write", 1, 1), ("write_nt", 2, 1), ("copy", 3, 2)):
+        def launch():
+            rc = lib.streamprobe_launch(pat, a.data_ptr(), b.data_ptr(), sink.data_ptr(), STREAM_BYTES,
+                                        stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"stream probe launch failed ({rc})")
+        for _ in range(3):
+            launch()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            launch()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"{name}_TBps"] = moved * STREAM_BYTES / (ms * 1e-3) / 1e12
+    out["what"] = ("1 GiB buffers, 16-byte coalesced accesses, one pass per launch (libstreamprobe.so); copy "
+                   "counts bytes read plus bytes written")
+    del a, b, sink
+    torch.cuda.empty_cache()
+    return out
 
 
 # ------------------------------------------------------------------------------------------------
@@ -413,10 +485,11 @@ def measure(fa, name: str, steps: int, warmup: int, dev):
     fma_call = sum(fma) / len(fma)
     arith = {"fma_per_call": fma_call, "valid_slots_per_qh": sum(slots) / len(slots),
              "achieved_tflops": 2 * fma_call / (st["fwd_attend"] * 1e-3) / 1e12,
-             "fp32_valu_peak_tflops": FP32_VALU_PEAK_TFLOPS,
-             "frac_fp32_valu_peak": 2 * fma_call / (st["fwd_attend"] * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
-             "what": "forward attention kernel, layer average; the products run on fp16 matrix cores "
-                     "(4x4x4 blocks), the peak is the fp32 vector ALUs' without packed ops"}
+             "fp16_mfma_peak_tflops": FP16_MFMA_PEAK_TFLOPS,
+             "frac_fp16_mfma_peak": 2 * fma_call / (st["fwd_attend"] * 1e-3) / 1e12 / FP16_MFMA_PEAK_TFLOPS,
+             "what": "forward attention kernel, layer average: algorithmic flops (QK, P.V and the blend of "
+                     "interpolated rows) over its time, against the dense fp16 matrix-core peak, where its "
+                     "products run"}
     res = {
         "ms_per_step": ms_step,
         "wall_s": wall,
@@ -451,6 +524,8 @@ def main():
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
                     help="run the short counter-collection program instead of the timed bench")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="run only the streaming-bandwidth probe and print its JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -461,6 +536,9 @@ def main():
         import fibonacci_offset_sparse_amd as fa
         profile_pass(fa, args.workload, torch.device("cuda:0"))
         return
+    if args.stream_probe:
+        print(json.dumps(stream_probe(torch.device("cuda:0"))), flush=True)
+        return
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -470,6 +548,9 @@ def main():
 
     import fibonacci_offset_sparse_amd as fa
     dev = torch.device("cuda:0")
+    log("streaming probe")
+    probe = stream_probe(dev)
+    log(f"streaming probe: {probe}")
     main_res = measure(fa, args.workload, args.steps, args.warmup, dev)
     long_res = None if args.no_long else measure(fa, args.long_workload, max(3, args.steps // 4), 1, dev)
 
@@ -481,6 +562,8 @@ def main():
         achieved = nbytes / (ms * 1e-3) / 1e9
         return {"kernel": kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(kernel, args.workload),
+                "frac_of_measured_copy": achieved / (probe["copy_TBps"] * 1e3),
+                "limiter": measured_limiter(kernel, args.workload),
                 "traffic_unit": "bytes per launch", "avg_launch_ms": ms, "algorithmic_bytes_per_launch": nbytes}
     kernel_names = {"fwd_attend": "fwd_mfma_kernel", "bwd_query": "bwd_q_mfma_kernel",
                     "bwd_key": "bwd_k_dot_kernel"}
@@ -511,7 +594,18 @@ def main():
         "per_layer": main_res["per_layer"],
         "integer_path": main_res["integer_path"],
         "cpu_baseline": cpu,
+        "stream_probe": probe,
     }
+    # the forward's target: 60 % of peak HBM bandwidth at L = 1024 and L = 4096, for the attention
+    # kernel on its own and for the whole forward call (prep included)
+    target = {"target_frac": FWD_TARGET_FRAC}
+    for key, res in (("l1024", main_res), ("l4096", long_res)):
+        if res is None:
+            continue
+        att = res["kernel_bytes"]["fwd_attend"] / (res["kernels_ms"]["fwd_attend"] * 1e-3) / 1e9 / HBM_PEAK_GBS
+        target[key] = {"attend_frac": att, "call_frac": res["fwd"]["frac_hbm_peak"],
+                       "attend_met": att >= FWD_TARGET_FRAC, "call_met": res["fwd"]["frac_hbm_peak"] >= FWD_TARGET_FRAC}
+    line["fwd_hbm_target"] = target
     if long_res is not None:
         lw = workloads.WORKLOADS[args.long_workload]
         line["l4096"] = {"workload": args.long_workload, "B": lw.B, "L": lw.L, "ms_per_step": long_res["ms_per_step"],

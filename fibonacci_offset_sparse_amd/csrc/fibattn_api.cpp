@@ -148,7 +148,7 @@ size_t fwd_ws_bytes(int32_t B, int32_t L, int32_t Hkv) { return krot_bytes(B, L,
 // cos/sin table (the forward's layout of the same sizes), the rotated queries (fp16), the per key
 // row term weights, and the per-workgroup d(loss)/dt partials.
 struct BwdFastLayout {
-    size_t qrot, do16, wwin, wrung, part, total;
+    size_t qrot, do16, wwin, wrung, part, klo, total;
 };
 BwdFastLayout bwd_fast_layout(int32_t B, int32_t L, int32_t Hq, int32_t Hkv) {
     BwdFastLayout f;
@@ -158,7 +158,9 @@ BwdFastLayout bwd_fast_layout(int32_t B, int32_t L, int32_t Hq, int32_t Hkv) {
     f.wrung = f.wwin + align256(static_cast<size_t>(B) * Hq * L * kNW * sizeof(uint32_t));
     f.part = f.wrung + align256(static_cast<size_t>(B) * Hq * L * kNR * sizeof(uint32_t));
     const size_t n_wg = static_cast<size_t>(bwd_query_workgroups(B, L, Hkv, Hq / Hkv));
-    f.total = f.part + align256(n_wg * kMaxOff * sizeof(float));
+    f.klo = f.part + align256(n_wg * kMaxOff * sizeof(float));
+    // low parts of the rotated keys (fp16), for the precise scores of a call that asks for d(alpha)
+    f.total = f.klo + align256(half_rows_bytes(B, L, Hkv));
     return f;
 }
 
@@ -309,6 +311,8 @@ fibattn_status_t fibattn_fwd_prep(const void* k, const void* v, int32_t B, int32
         a.n_bh = B * Hkv;
         a.L = L;
         a.fr = make_freq(rope_theta);
+        a.k16lo = nullptr;
+        a.main = 1;
         e = launch_prep_kv16(a, static_cast<hipStream_t>(stream));
     }
     if (e != hipSuccess) return hip_fail(e, "forward prep launch");
@@ -505,17 +509,29 @@ fibattn_status_t fibattn_bwd_stages(int32_t stages, const void* q, const void* k
             pa.n_bh = B * Hkv;
             pa.L = L;
             pa.fr = a.fr;
+            pa.main = 1;
+            pa.k16lo = nullptr;
             a.kstage = pa.k16;
             a.vstage = pa.v16;
+            a.kstage_lo = w0 + f.klo;
             a.cstab = pa.cs;
             a.qrot16 = w0 + f.qrot;
             a.do16 = w0 + f.do16;
             a.wwin = reinterpret_cast<uint32_t*>(w0 + f.wwin);
             a.wrung = reinterpret_cast<uint32_t*>(w0 + f.wrung);
             a.partial = reinterpret_cast<float*>(w0 + f.part);
+            // with d(alpha) requested the query stage takes precise scores, from the low parts of
+            // the rotated keys as well: written with the prep when both run in this call, else
+            // by a pass of their own ahead of the query stage
+            if (want_dalpha && (stages & (FIBATTN_STAGE_PREP | FIBATTN_STAGE_QUERY)))
+                pa.k16lo = reinterpret_cast<_Float16*>(w0 + f.klo);
             if (stages & FIBATTN_STAGE_PREP) {
                 e = launch_prep_kv16(pa, s);
                 if (e != hipSuccess) return hip_fail(e, "backward prep launch");
+            } else if (pa.k16lo != nullptr && (stages & FIBATTN_STAGE_QUERY)) {
+                pa.main = 0;
+                e = launch_prep_kv16(pa, s);
+                if (e != hipSuccess) return hip_fail(e, "key low-part launch");
             }
             if (stages & (FIBATTN_STAGE_QUERY | FIBATTN_STAGE_KEY)) {
                 e = launch_bwd_mfma(a, want_dalpha, stages, s);

@@ -53,7 +53,12 @@ __device__ __forceinline__ uint32_t pack_p_ds(float p, float ds) { return pack_h
 // ------------------------------------------------------------------------------------------------
 // bwd_q_mfma
 // ------------------------------------------------------------------------------------------------
-template <int MAXS>
+// PRECISE: scores from split operands (q and the staged keys each as a high and a low fp16 part),
+// for calls that ask for d(alpha): that one scalar sums every (query, head, rung) term with heavy
+// cancellation and would otherwise inherit the 2^-11 rounding of q and k relative to its
+// (small) value. Pass AB then runs as pass A (keys and their low parts: scores) and pass B
+// (values: dP).
+template <int MAXS, bool PRECISE>
 __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     constexpr int MAXK = 2 * MAXS;
     // Two item buffers used in turn, each a key part and a value part. Items: the key and value
@@ -95,6 +100,8 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     const int64_t kv_row0 = static_cast<int64_t>(bg) * L;
     const __amdgpu_buffer_rsrc_t krs = rows_rsrc(A.kstage, kv_row0, L);
     const __amdgpu_buffer_rsrc_t vrs = rows_rsrc(A.vstage, kv_row0, L);
+    // the second half of each pass-A item: the values (fused pass AB) or the keys' low parts
+    const __amdgpu_buffer_rsrc_t hrs = PRECISE ? rows_rsrc(A.kstage_lo, kv_row0, L) : vrs;
     Stager st;
     st.init(lane, wave);
     auto step = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int k) {
@@ -102,7 +109,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     };
     auto kv_step = [&](char* dst, int k) {         // 12 DMA instructions per wave
         step(krs, dst, k);
-        step(vrs, dst + kBufBytes, k);
+        step(hrs, dst + kBufBytes, k);
     };
     auto buf = [&](int j) -> char* { return (j & 1) ? lds1 : lds0; };
     const int jn = i0 - kNear;                          // the near block's row at slot 0
@@ -148,12 +155,14 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         asm volatile("" ::: "memory");
     }
     st.near(krs, lds0, jn);
-    st.near(vrs, lds0 + kBufBytes, jn);
+    st.near(hrs, lds0 + kBufBytes, jn);
     kv_step(lds1, kn);
 
     // q rotated at its position (unscaled), fp16, in the keys' permuted order: word 2m holds dims
-    // (m, 16 + m), word 2m + 1 dims (32 + m, 48 + m); register chunk c = words 4c..4c+3
+    // (m, 16 + m), word 2m + 1 dims (32 + m, 48 + m); register chunk c = words 4c..4c+3. PRECISE
+    // also keeps what the fp16 rounding left out (ql, same layout).
     uint32_t q[8][4];
+    uint32_t ql[PRECISE ? 8 : 1][4];
     {
         float r[kD];
 #pragma unroll
@@ -175,7 +184,12 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
 #pragma unroll
         for (int w = 0; w < 32; ++w) {
             const int m = w >> 1;
-            q[w >> 2][w & 3] = (w & 1) ? pack_h2(r[32 + m], r[48 + m]) : pack_h2(r[m], r[16 + m]);
+            const float a0 = (w & 1) ? r[32 + m] : r[m], a1 = (w & 1) ? r[48 + m] : r[16 + m];
+            q[w >> 2][w & 3] = pack_h2(a0, a1);
+            if constexpr (PRECISE) {
+                const h2_t hi = __builtin_bit_cast(h2_t, q[w >> 2][w & 3]);
+                ql[w >> 2][w & 3] = pack_h2(a0 - static_cast<float>(hi.x), a1 - static_cast<float>(hi.y));
+            }
         }
     }
     // do as fp16 in the values' permuted order (word 2m: dims (m, 16 + m), word 2m + 1: dims
@@ -197,13 +211,13 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     publish<12>();                                      // the key and value near blocks have landed
 
     // ---- pass AB: scores s (base 2) with the keys, dP = do . value row with the values, and for
-    // each rung far - near of both products ----
+    // each rung far - near of both products (PRECISE: pass A, the scores, then pass B, dP) ----
     float s[4 * kWG + MAXK], sd[MAXK], dp[4 * kWG + MAXK], dpd[MAXK];
     const int s0 = p - x + kNear;                       // window: lane x reads distance 4g + x
     const int rslot = p + ((x >> 1) ? kBlkSlots + 2 : 0) + ((x & 1) ? 0 : 1);   // far-step rung rows
     const int rbase = rslot * kRowBytes, rsw = swz(rslot);
     // a rung pair's products (lane x: rung 2k + (x >> 1), near row for x even, far row for x odd)
-    auto pair_terms = [&](const f4_t& acc, const f4_t& accv, int k) {
+    auto score_terms = [&](const f4_t& acc, int k) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int n = 2 * k + e;
@@ -214,11 +228,29 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
                 const bool ok = active && i >= A.off[n].a + A.off[n].interp;
                 s[4 * kWG + n] = ok ? sc : kNegInf;
                 sd[n] = ok ? dd : 0.f;
+            }
+        }
+    };
+    auto dp_terms = [&](const f4_t& accv, int k) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int n = 2 * k + e;
+            if (n < n_reach) {
                 const float dv = accv[2 * e + 1] - accv[2 * e];
-                dp[4 * kWG + n] = fmaf(t, dv, accv[2 * e]);
+                dp[4 * kWG + n] = fmaf(A.off[n].t, dv, accv[2 * e]);
                 dpd[n] = dv;
             }
         }
+    };
+    // scores of one group: the row at slot byte offset base of buffer b (and its low part)
+    auto qk = [&](const char* b, int base, int F) -> f4_t {
+        if constexpr (PRECISE)
+            return row_dot_group_x3(q, ql, b, b + kBufBytes, base, F);
+        else
+            return row_dot_group(q, b, base, F);
+    };
+    auto near_slot = [&](int k) {   // near rung pair k: near row i - a at slot p + 64 - a, far one down
+        return p + kNear - pick_uniform((x >> 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a) - (x & 1);
     };
 #pragma unroll
     for (int k = 0; k < MAXK; ++k) {
@@ -227,12 +259,14 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         dp[4 * kWG + k] = 0.f;
         dpd[k] = 0.f;
     }
+    // values in the second half of each item (fused) or in the first (pass B)
+    const int voff = PRECISE ? 0 : kBufBytes;
 #pragma unroll
     for (int g = 0; g < kWG; ++g) {
         f4_t acc = {0.f, 0.f, 0.f, 0.f}, accv = {0.f, 0.f, 0.f, 0.f};
         if (4 * g <= W) {
-            acc = row_dot_group(q, lds0, (s0 - 4 * g) * kRowBytes, swz(s0 - 4 * g));
-            accv = row_dot_group(dov, lds0 + kBufBytes, (s0 - 4 * g) * kRowBytes, swz(s0 - 4 * g));
+            acc = qk(lds0, (s0 - 4 * g) * kRowBytes, swz(s0 - 4 * g));
+            if constexpr (!PRECISE) accv = row_dot_group(dov, lds0 + voff, (s0 - 4 * g) * kRowBytes, swz(s0 - 4 * g));
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -241,13 +275,12 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             dp[d] = accv[r];
         }
     }
-    // near rung pairs: near row i - a at slot p + 64 - a, far row one slot down
 #pragma unroll
     for (int k = 0; k < MAXS; ++k) {
         if (k < kn) {
-            const int sl = p + kNear - pick_uniform((x >> 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a) - (x & 1);
-            pair_terms(row_dot_group(q, lds0, sl * kRowBytes, swz(sl)),
-                       row_dot_group(dov, lds0 + kBufBytes, sl * kRowBytes, swz(sl)), k);
+            const int sl = near_slot(k);
+            score_terms(qk(lds0, sl * kRowBytes, swz(sl)), k);
+            if constexpr (!PRECISE) dp_terms(row_dot_group(dov, lds0 + voff, sl * kRowBytes, swz(sl)), k);
         }
     }
     publish<0>();                                       // far step kn has landed, buffer 0 is free
@@ -255,8 +288,38 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     for (int k = 0; k < MAXS; ++k) {
         if (k >= kn && k < n_steps) {
             if (k + 1 < n_steps) kv_step(buf(k + 2), k + 1);
-            pair_terms(row_dot_group(q, buf(k + 1), rbase, rsw), row_dot_group(dov, buf(k + 1) + kBufBytes, rbase, rsw), k);
+            score_terms(qk(buf(k + 1), rbase, rsw), k);
+            if constexpr (!PRECISE) dp_terms(row_dot_group(dov, buf(k + 1) + voff, rbase, rsw), k);
             publish<0>();
+        }
+    }
+    if constexpr (PRECISE) {
+        // ---- pass B: the values alone (near block into buffer 0, far step kn into buffer 1) ----
+        st.near(vrs, lds0, jn);
+        step(vrs, lds1, kn);
+        publish<6>();                                   // the value near block has landed
+#pragma unroll
+        for (int g = 0; g < kWG; ++g) {
+            f4_t accv = {0.f, 0.f, 0.f, 0.f};
+            if (4 * g <= W) accv = row_dot_group(dov, lds0, (s0 - 4 * g) * kRowBytes, swz(s0 - 4 * g));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dp[4 * g + r] = accv[r];
+        }
+#pragma unroll
+        for (int k = 0; k < MAXS; ++k) {
+            if (k < kn) {
+                const int sl = near_slot(k);
+                dp_terms(row_dot_group(dov, lds0, sl * kRowBytes, swz(sl)), k);
+            }
+        }
+        publish<0>();
+#pragma unroll
+        for (int k = 0; k < MAXS; ++k) {
+            if (k >= kn && k < n_steps) {
+                if (k + 1 < n_steps) step(vrs, buf(k + 2), k + 1);
+                dp_terms(row_dot_group(dov, buf(k + 1), rbase, rsw), k);
+                publish<0>();
+            }
         }
     }
 
@@ -786,8 +849,11 @@ hipError_t launch_bwd_mfma(const BwdArgs& A0, bool want_dalpha, int stages, hipS
     A.n_wg = static_cast<int32_t>(q_units * n_tiles);
     if (stages & kStageQuery) {
         A.xcd_map = (q_units % 8 == 0) ? 1 : 0;
-        hipLaunchKernelGGL((bwd_q_mfma_kernel<8>), dim3(static_cast<unsigned>(q_units * n_tiles)), dim3(kNT), 0, s,
-                           A);
+        const dim3 grid(static_cast<unsigned>(q_units * n_tiles));
+        if (want_dalpha)
+            hipLaunchKernelGGL((bwd_q_mfma_kernel<8, true>), grid, dim3(kNT), 0, s, A);
+        else
+            hipLaunchKernelGGL((bwd_q_mfma_kernel<8, false>), grid, dim3(kNT), 0, s, A);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -101,13 +101,13 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             kw[r][c] = *reinterpret_cast<const uint32_t*>(ks + row + 16 * c + 2 * u);
-            vw[r][c] = *reinterpret_cast<const uint32_t*>(vs + row + 16 * c + 2 * u);
+            vw[r][c] = A.main ? *reinterpret_cast<const uint32_t*>(vs + row + 16 * c + 2 * u) : 0u;
         }
     }
     float2 cs[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) rope_cos_sin(j, fh[e], fl[e], cs[e].x, cs[e].y);
-    if (grp == 0) {   // the table: [L][32] (cos, sin)
+    if (grp == 0 && A.main) {   // the table: [L][32] (cos, sin)
         float2* t = reinterpret_cast<float2*>(A.cs) + static_cast<int64_t>(j) * kPairs;
 #pragma unroll
         for (int e = 0; e < 4; ++e) t[pr[e]] = cs[e];
@@ -127,12 +127,21 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
             ry[e] = y[e] * cs[e].x + x[e] * cs[e].y;
         }
         // element 8u + e: e < 4 is dim 16e + 2u, e >= 4 is dim 16(e - 4) + 2u + 1
-        store4<f16_t>(A.k16 + row + 8 * u, make_float4(rx[0], rx[2], ry[0], ry[2]));
-        store4<f16_t>(A.k16 + row + 8 * u + 4, make_float4(rx[1], rx[3], ry[1], ry[3]));
-        store4<f16_t>(A.v16 + row + 8 * u,
-                      make_float4(bf16_lo(vw[r][0]), bf16_lo(vw[r][1]), bf16_lo(vw[r][2]), bf16_lo(vw[r][3])));
-        store4<f16_t>(A.v16 + row + 8 * u + 4,
-                      make_float4(bf16_hi(vw[r][0]), bf16_hi(vw[r][1]), bf16_hi(vw[r][2]), bf16_hi(vw[r][3])));
+        if (A.main) {
+            store4<f16_t>(A.k16 + row + 8 * u, make_float4(rx[0], rx[2], ry[0], ry[2]));
+            store4<f16_t>(A.k16 + row + 8 * u + 4, make_float4(rx[1], rx[3], ry[1], ry[3]));
+            store4<f16_t>(A.v16 + row + 8 * u,
+                          make_float4(bf16_lo(vw[r][0]), bf16_lo(vw[r][1]), bf16_lo(vw[r][2]), bf16_lo(vw[r][3])));
+            store4<f16_t>(A.v16 + row + 8 * u + 4,
+                          make_float4(bf16_hi(vw[r][0]), bf16_hi(vw[r][1]), bf16_hi(vw[r][2]), bf16_hi(vw[r][3])));
+        }
+        if (A.k16lo != nullptr) {
+            // what fp16 rounding left out of each rotated key element: a second fp16 operand
+            // whose product with q restores the score to about 2^-22 relative
+            auto lo = [](float x) { return x - static_cast<float>(static_cast<_Float16>(x)); };
+            store4<f16_t>(A.k16lo + row + 8 * u, make_float4(lo(rx[0]), lo(rx[2]), lo(ry[0]), lo(ry[2])));
+            store4<f16_t>(A.k16lo + row + 8 * u + 4, make_float4(lo(rx[1]), lo(rx[3]), lo(ry[1]), lo(ry[3])));
+        }
     }
 }
 

@@ -45,6 +45,10 @@ struct PrepArgs {
     _Float16* k16;       // [B*Hkv, L, 64] rotated keys, dims permuted
     _Float16* v16;       // [B*Hkv, L, 64] values, dims permuted
     float* cs;           // [L, 32, 2] cos and sin of every position and RoPE pair
+    // the low parts of the rotated keys, krot - fp16(krot) as fp16 (same layout as k16), or
+    // nullptr; with main == 0 only these are written (k16, v16 and cs are left alone)
+    _Float16* k16lo;
+    int32_t main;
     int32_t n_bh;
     int32_t L;
     RopeFreq fr;
@@ -94,6 +98,7 @@ struct BwdArgs {
     const void* kstage;  // [B*Hkv, L, 64] fp16 rotated keys, dims permuted
     const void* vstage;  // [B*Hkv, L, 64] fp16 values, dims permuted
     const float* cstab;  // [L, 32, 2] cos, sin
+    const void* kstage_lo;  // [B*Hkv, L, 64] fp16 low parts of the rotated keys (precise scores)
     void* qrot16;        // [B, Hq, L, 64] fp16 rotated queries, dims permuted
     void* do16;          // [B, Hq, L, 64] fp16 copy of dout, dims permuted
     // per query and head, fp16 pairs (p low, dS/sqrt(D) high): the window distances 0..15 of each

@@ -125,6 +125,29 @@ __device__ __forceinline__ f4_t row_dot_group(const uint32_t (&x)[8][4], const c
     return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
+// row_dot_group with both operands split into a high and a low fp16 part (x = xh + xl, the staged
+// rows = hi + lo): xh.hi + xl.hi + xh.lo, the product to about 2^-22 relative (xl.lo is below
+// that). The two staged halves sit at the same slot offset of lds_hi and lds_lo.
+__device__ __forceinline__ f4_t row_dot_group_x3(const uint32_t (&xh)[8][4], const uint32_t (&xl)[8][4],
+                                                 const char* lds_hi, const char* lds_lo, int base, int F) {
+    f4_t a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] = (f4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int addr = base | ((c << 4) ^ F);
+        const uint4 k = lds16(lds_hi, addr);
+        const uint4 kl = lds16(lds_lo, addr);
+        a[(2 * c) & 3] = mfma4(k.x, k.y, xh[c][0], xh[c][1], a[(2 * c) & 3]);
+        a[(2 * c + 1) & 3] = mfma4(k.z, k.w, xh[c][2], xh[c][3], a[(2 * c + 1) & 3]);
+        a[(2 * c) & 3] = mfma4(k.x, k.y, xl[c][0], xl[c][1], a[(2 * c) & 3]);
+        a[(2 * c + 1) & 3] = mfma4(k.z, k.w, xl[c][2], xl[c][3], a[(2 * c + 1) & 3]);
+        a[(2 * c) & 3] = mfma4(kl.x, kl.y, xh[c][0], xh[c][1], a[(2 * c) & 3]);
+        a[(2 * c + 1) & 3] = mfma4(kl.z, kl.w, xh[c][2], xh[c][3], a[(2 * c + 1) & 3]);
+    }
+    return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
 // ds_read_b64_tr_b16 at lds + addr: 4 fp16 (or bf16) elements, as a whole. (Splitting the result
 // into its two dwords is left to the callers that need it: an optimisation has been seen to fold
 // the second dword of this builtin's result onto the first.)

@@ -57,6 +57,14 @@ def test_plan_bit_exact_against_the_oracle_on_every_schedule(schedule, W, base):
         _plan_equal(alpha, W, offsets)
 
 
+def test_coprime_schedule_is_the_printed_permutation():
+    from golden import loader
+    perm = loader.int_list("coprime_permutation.txt")
+    for layer in range(16):
+        assert fa.fibattn_alpha_schedule(fa.SCHEDULE_COPRIME, layer, 16) == \
+            fa.fibattn_alpha_schedule(fa.SCHEDULE_LINEAR, perm[layer], 16)
+
+
 def test_plan_bit_exact_on_random_and_learned_alphas():
     rng = np.random.default_rng(7)
     for alpha in rng.uniform(0.5, 1.5, 10000):

@@ -82,16 +82,21 @@ def test_every_layer_at_reduced_size(name):
         compare(q, k, v, alpha, w.W, base, f"{name}/{layer}")
 
 
-@pytest.mark.parametrize("name", [n for n in workloads.WORKLOADS if n != "tiny_fixed_f32"])
-def test_full_size_sampled_batches(name):
+FULL = [n for n in workloads.WORKLOADS if n != "tiny_fixed_f32"]
+
+
+@pytest.mark.parametrize("name,layer", [(n, l) for n in FULL for l in range(workloads.WORKLOADS[n].n_layers)])
+def test_full_size_every_layer(name, layer):
+    # every layer of every workload at its full shape, launched as the bench launches it (the whole
+    # batch, so every far rung of the layer's alpha is staged at every length it reaches); one batch
+    # element per layer is checked against the oracle (batch elements never mix), a different one
+    # from layer to layer
     w = workloads.WORKLOADS[name]
-    base = base_of(w)
-    alphas = alphas_of(w)
-    for layer in (0, w.n_layers // 2 + 1, w.n_layers - 1):
-        q, k, v = workloads.draw(w, layer, with_grad=False)
-        bsel = sorted({0, w.B // 2, w.B - 1})
-        say(f"{name} full size layer {layer} B={w.B} L={w.L}, checking batches {bsel}")
-        compare(q, k, v, alphas[layer], w.W, base, f"{name}/{layer}", bsel=bsel)
+    alpha = alphas_of(w)[layer]
+    q, k, v = workloads.draw(w, layer, with_grad=False)
+    b = (7 * layer + 3) % w.B
+    say(f"{name} full size layer {layer} alpha={alpha!r} B={w.B} L={w.L}, checking batch {b}")
+    compare(q, k, v, alpha, w.W, base_of(w), f"{name}/{layer}", bsel=[b])
 
 
 @pytest.mark.parametrize("name", ["l1024_linear_bf16", "l4096_coprime_bf16", "l1024_pow2_linear_bf16"])

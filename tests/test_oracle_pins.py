@@ -160,6 +160,16 @@ def test_coprime_schedule_is_a_permutation_with_the_same_multiset():
     assert min(steps) >= min(stride, n - stride)
 
 
+def test_coprime_schedule_is_the_printed_permutation():
+    # the exact map, not only its properties: a shifted (1-indexed) or mirrored map keeps the
+    # multiset and the step sizes but not this list
+    perm = loader.int_list("coprime_permutation.txt")
+    n = int(loader.table("schedules.txt")["n_layers"])
+    assert [O.coprime_index(l, n) for l in range(n)] == perm
+    for l in range(n):
+        assert O.alpha_coprime(l, n) == O.alpha_linear(perm[l], n)
+
+
 def test_learned_alpha_parameterisation():
     g = loader.table("schedules.txt")
     assert O.alpha_from_theta(0.0) == g["alpha_at_theta_zero"]
