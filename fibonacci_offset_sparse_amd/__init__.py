@@ -51,6 +51,10 @@ def _load() -> ctypes.CDLL:
         "fibattn_fwd_attend": (ctypes.c_int, [_c_ptr, _c_ptr, _c_f64, _c_i32, _P(_c_i32), _c_i32,
                                                _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f64,
                                                _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
+        "fibattn_fwd_noalloc": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_f64, _c_i32, _P(_c_i32), _c_i32,
+                                                _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f64,
+                                                _c_ptr, _c_ptr, _c_ptr]),
+        "fibattn_fwd_noalloc_max_bytes": (_c_size, []),
         "fibattn_decode": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_f64, _c_i32, _P(_c_i32), _c_i32,
                                            _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f64, _c_ptr,
                                            _c_ptr, _c_ptr]),
@@ -223,6 +227,28 @@ def fibattn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float,
     return o, lse
 
 
+def fibattn_fwd_noalloc_max_bytes() -> int:
+    return int(lib.fibattn_fwd_noalloc_max_bytes())
+
+
+def fibattn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, W: int,
+                        offsets: Sequence[int], o: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                        rope_theta: float = 1e4, stream=None) -> None:
+    """The allocation-free forward: o (and lse if given) written in place, no workspace (the library
+    holds fibattn_fwd_noalloc_max_bytes() of device scratch per GPU). Calls that overlap on one GPU
+    race on that scratch."""
+    B, Hq, L, D, Hkv = _shapes(q, k)
+    dt = _dtype_code(q)
+    args = [_dev(q, "q", (B, Hq, L, D), q.dtype), _dev(k, "k", (B, Hkv, L, D), q.dtype),
+            _dev(v, "v", (B, Hkv, L, D), q.dtype)]
+    optr = _dev(o, "o", (B, Hq, L, D), q.dtype)
+    lptr = _dev(lse, "lse", (B, Hq, L), torch.float32) if lse is not None else None
+    offs, K = _i32_array(offsets)
+    with torch.cuda.device(q.device):
+        _check(lib.fibattn_fwd_noalloc(*args, float(alpha), int(W), offs, K, B, L, Hq, Hkv, D, dt, float(rope_theta),
+                                       optr, lptr, _stream(q.device, stream)))
+
+
 def fibattn_fwd_prep(k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor, rope_theta: float = 1e4,
                      stream=None):
     """First forward stage: rotated keys (and fp16 values for bf16) into `workspace`."""
@@ -348,7 +374,7 @@ def fibattn_bwd(q, k, v, o, lse, dout, alpha: float, W: int, offsets: Sequence[i
 __all__ = [
     "fibattn_status_string", "fibattn_last_error", "fibattn_base_offsets", "fibattn_alpha_schedule",
     "fibattn_alpha_from_theta", "fibattn_round_offsets", "fibattn_plan", "fibattn_fwd_workspace_bytes", "fibattn_fwd",
-    "fibattn_fwd_prep", "fibattn_fwd_attend", "fibattn_bwd_workspace_bytes", "fibattn_bwd",
+    "fibattn_fwd_prep", "fibattn_fwd_attend", "fibattn_fwd_noalloc", "fibattn_fwd_noalloc_max_bytes", "fibattn_bwd_workspace_bytes", "fibattn_bwd",
     "fibattn_bwd_stages", "fibattn_bwd_reuses_fwd_prep", "fibattn_decode", "STAGE_PREP", "STAGE_QUERY", "STAGE_KEY", "STAGE_ALL",
     "FibAttnError", "lib", "LIB_PATH",
 ]

@@ -33,7 +33,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 SOURCES = ["fibattn_api.cpp", "fibattn_fwd.hip", "fibattn_fwd_mfma.hip", "fibattn_bwd.hip", "fibattn_bwd_mfma.hip",
-           "fibattn_decode.hip"]
+           "fibattn_decode.hip", "fibattn_noalloc.hip"]
 
 
 def hipcc() -> str:

@@ -164,6 +164,18 @@ BwdFastLayout bwd_fast_layout(int32_t B, int32_t L, int32_t Hq, int32_t Hkv) {
     return f;
 }
 
+}  // namespace
+
+int fibattn::report_error(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_error, sizeof(g_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+namespace {
+
 #define FIBATTN_TRY(expr)                        \
     do {                                         \
         const fibattn_status_t st_ = (expr);     \

@@ -127,6 +127,10 @@ struct DecodeArgs {
 // Entries per query in the weight tables of the matrix-core backward: 16 window distances, 16 rungs.
 constexpr int kNW = 16, kNR = 16;
 
+// Sets the calling thread's error text (fibattn_last_error) and returns status (an int of
+// fibattn_status_t).
+int report_error(int status, const char* fmt, ...);
+
 hipError_t launch_rope_keys(int dtype, const RopeKeysArgs& a, hipStream_t s);
 // keys and values with dims permuted (element 4m + c of a row holds dim 16c + m), and the table
 hipError_t launch_prep_kv16(const PrepArgs& a, hipStream_t s);

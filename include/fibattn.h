@@ -32,9 +32,10 @@
  *
  * Ownership and execution. All buffers belong to the caller. Device pointers must stay valid
  * until the stream reaches the work. `offsets` is a host array, read during the call and not
- * kept. The library keeps no allocation and no state between calls; calls are asynchronous on
- * `stream` (a hipStream_t; NULL is the null stream) and are re-entrant. Outputs are overwritten,
- * never accumulated.
+ * kept. The library keeps no allocation and no state between calls (except the device array of
+ * the allocation-free forward, fibattn_fwd_noalloc); calls are asynchronous on `stream` (a
+ * hipStream_t; NULL is the null stream) and are re-entrant. Outputs are overwritten, never
+ * accumulated.
  *
  * Errors. Arguments are checked on the host before anything is launched; on error no work is
  * queued and an error status is returned. fibattn_last_error() gives the calling thread's last
@@ -180,6 +181,27 @@ fibattn_status_t fibattn_fwd_attend(const void* q, const void* v, double alpha, 
                                     int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
                                     double rope_theta, void* o, float* lse,
                                     const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free forward, for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid allocation): fibattn_fwd with its workspace in a
+ * device array the library holds instead of one the caller passes. The array is
+ * fibattn_fwd_noalloc_max_bytes() bytes (32 MiB); each GPU the library runs on holds its own copy
+ * until the process ends. Arguments, outputs and errors as fibattn_fwd; WORKSPACE (nothing queued)
+ * when the call needs more than the array holds, i.e. fibattn_fwd_workspace_bytes(B, L, Hkv, D,
+ * dtype) > fibattn_fwd_noalloc_max_bytes(). The call allocates and frees no device memory.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents (nothing in it
+ * needs to start at zero: the prep writes every row the attention reads): calls that overlap on one
+ * GPU (other streams, other threads) race, and the caller must order them. Call it with the
+ * stream's device current.
+ */
+fibattn_status_t fibattn_fwd_noalloc(const void* q, const void* k, const void* v, double alpha, int32_t W,
+                                     const int32_t* offsets, int32_t K, int32_t B, int32_t L, int32_t Hq,
+                                     int32_t Hkv, int32_t D, int32_t dtype, double rope_theta, void* o,
+                                     float* lse, void* stream);
+
+/* Bytes of the allocation-free forward's device array (per GPU). */
+size_t fibattn_fwd_noalloc_max_bytes(void);
 
 /*
  * Single-token decode (inference with a cache): for each sequence b, its new query at position
