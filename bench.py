@@ -303,8 +303,8 @@ class Layers:
         self.fa.fibattn_fwd_prep(self.inputs[layer][1], self.inputs[layer][2], self.ws)
 
     def attend(self, layer):
-        q, _, v, _ = self.inputs[layer]
-        self.fa.fibattn_fwd_attend(q, v, self.alphas[layer], self.w.W, self.base, self.ws, self.o[layer],
+        q, k, v, _ = self.inputs[layer]
+        self.fa.fibattn_fwd_attend(q, k, v, self.alphas[layer], self.w.W, self.base, self.ws, self.o[layer],
                                    self.lse[layer])
 
     def bwd_stages(self, layer, stages):

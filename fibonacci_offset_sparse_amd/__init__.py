@@ -48,7 +48,7 @@ def _load() -> ctypes.CDLL:
                                         _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
         "fibattn_fwd_prep": (ctypes.c_int, [_c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                              _c_f64, _c_ptr, _c_size, _c_ptr]),
-        "fibattn_fwd_attend": (ctypes.c_int, [_c_ptr, _c_ptr, _c_f64, _c_i32, _P(_c_i32), _c_i32,
+        "fibattn_fwd_attend": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_f64, _c_i32, _P(_c_i32), _c_i32,
                                                _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f64,
                                                _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
         "fibattn_fwd_noalloc": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_f64, _c_i32, _P(_c_i32), _c_i32,
@@ -261,21 +261,21 @@ def fibattn_fwd_prep(k: torch.Tensor, v: torch.Tensor, workspace: torch.Tensor, 
                                     workspace.data_ptr(), workspace.numel(), _stream(k.device, stream)))
 
 
-def fibattn_fwd_attend(q: torch.Tensor, v: torch.Tensor, alpha: float, W: int, offsets: Sequence[int],
-                       workspace: torch.Tensor, o: torch.Tensor, lse: Optional[torch.Tensor] = None,
-                       rope_theta: float = 1e4, stream=None):
+def fibattn_fwd_attend(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float, W: int,
+                       offsets: Sequence[int], workspace: torch.Tensor, o: torch.Tensor,
+                       lse: Optional[torch.Tensor] = None, rope_theta: float = 1e4, stream=None):
     """Second forward stage; reads what fibattn_fwd_prep left in `workspace`."""
-    B, Hq, L, D = q.shape
-    Hkv = v.shape[1]
+    B, Hq, L, D, Hkv = _shapes(q, k)
     dt = _dtype_code(q)
     _dev(q, "q", (B, Hq, L, D), q.dtype)
+    _dev(k, "k", (B, Hkv, L, D), q.dtype)
     _dev(v, "v", (B, Hkv, L, D), q.dtype)
     _dev(o, "o", (B, Hq, L, D), q.dtype)
     lptr = _dev(lse, "lse", (B, Hq, L), torch.float32) if lse is not None else None
     offs, K = _i32_array(offsets)
     with torch.cuda.device(q.device):
-        _check(lib.fibattn_fwd_attend(q.data_ptr(), v.data_ptr(), float(alpha), int(W), offs, K, B, L, Hq,
-                                      Hkv, D, dt, float(rope_theta), o.data_ptr(), lptr,
+        _check(lib.fibattn_fwd_attend(q.data_ptr(), k.data_ptr(), v.data_ptr(), float(alpha), int(W), offs, K, B, L,
+                                      Hq, Hkv, D, dt, float(rope_theta), o.data_ptr(), lptr,
                                       workspace.data_ptr(), workspace.numel(), _stream(q.device, stream)))
 
 

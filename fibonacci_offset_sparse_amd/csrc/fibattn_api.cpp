@@ -142,7 +142,19 @@ size_t half_rows_bytes(int32_t B, int32_t L, int32_t Hkv) {
 }
 // cos/sin table [L, 32, 2] float32 after the staged rows (bf16 storage)
 size_t cs_table_bytes(int32_t L) { return align256(static_cast<size_t>(L) * kPairs * 2 * sizeof(float)); }
-size_t fwd_ws_bytes(int32_t B, int32_t L, int32_t Hkv) { return krot_bytes(B, L, Hkv) + cs_table_bytes(L); }
+int32_t flag_blocks(int32_t L) { return (L + kFlagRows - 1) / kFlagRows; }
+// range flags of the staged rows (bf16 storage): one word per (group of kPrepRowGroup (batch, head)
+// rows, block of kFlagRows positions), after the table
+size_t flags_bytes(int32_t B, int32_t L, int32_t Hkv) {
+    const size_t groups = (static_cast<size_t>(B) * Hkv + kPrepRowGroup - 1) / kPrepRowGroup;
+    return align256(groups * flag_blocks(L) * sizeof(uint32_t));
+}
+size_t fwd_ws_bytes(int32_t B, int32_t L, int32_t Hkv) {
+    return krot_bytes(B, L, Hkv) + cs_table_bytes(L) + flags_bytes(B, L, Hkv);
+}
+uint32_t* flags_at(void* ws, int32_t B, int32_t L, int32_t Hkv) {
+    return reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + krot_bytes(B, L, Hkv) + cs_table_bytes(L));
+}
 
 // Workspace of the matrix-core backward (bfloat16 storage): staged fp16 keys and values and the
 // cos/sin table (the forward's layout of the same sizes), the rotated queries (fp16), the per key
@@ -325,20 +337,23 @@ fibattn_status_t fibattn_fwd_prep(const void* k, const void* v, int32_t B, int32
         a.fr = make_freq(rope_theta);
         a.k16lo = nullptr;
         a.main = 1;
+        a.flags = flags_at(workspace, B, L, Hkv);
+        a.n_blk = flag_blocks(L);
         e = launch_prep_kv16(a, static_cast<hipStream_t>(stream));
     }
     if (e != hipSuccess) return hip_fail(e, "forward prep launch");
     return FIBATTN_OK;
 }
 
-fibattn_status_t fibattn_fwd_attend(const void* q, const void* v, double alpha, int32_t W, const int32_t* offsets,
-                                    int32_t K, int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32_t D,
-                                    int32_t dtype, double rope_theta, void* o, float* lse, const void* workspace,
-                                    size_t workspace_bytes, void* stream) {
+fibattn_status_t fibattn_fwd_attend(const void* q, const void* k, const void* v, double alpha, int32_t W,
+                                    const int32_t* offsets, int32_t K, int32_t B, int32_t L, int32_t Hq, int32_t Hkv,
+                                    int32_t D, int32_t dtype, double rope_theta, void* o, float* lse,
+                                    const void* workspace, size_t workspace_bytes, void* stream) {
     g_error[0] = '\0';
     FIBATTN_TRY(check_dims(B, L, Hq, Hkv, D, W, dtype, rope_theta));
     FIBATTN_TRY(check_offsets(alpha, W, offsets, K));
-    if (q == nullptr || v == nullptr || o == nullptr) return fail(FIBATTN_ERR_INVALID, "q, v or o is NULL");
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+        return fail(FIBATTN_ERR_INVALID, "q, k, v or o is NULL");
     const size_t need = fwd_ws_bytes(B, L, Hkv);
     if (workspace == nullptr || workspace_bytes < need)
         return fail(FIBATTN_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
@@ -348,7 +363,10 @@ fibattn_status_t fibattn_fwd_attend(const void* q, const void* v, double alpha, 
     a.kstage = workspace;
     a.vstage = dtype == FIBATTN_F32 ? v : static_cast<const char*>(workspace) + half_rows_bytes(B, L, Hkv);
     a.cstab = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + krot_bytes(B, L, Hkv));
+    a.kvflags = flags_at(const_cast<void*>(workspace), B, L, Hkv);
+    a.n_blk = flag_blocks(L);
     a.v = v;
+    a.k = k;
     a.xcd_map = 0;
     a.o = o;
     a.lse = lse;
@@ -378,7 +396,7 @@ fibattn_status_t fibattn_fwd(const void* q, const void* k, const void* v, double
     if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
         return fail(FIBATTN_ERR_INVALID, "q, k, v or o is NULL");
     FIBATTN_TRY(fibattn_fwd_prep(k, v, B, L, Hkv, D, dtype, rope_theta, workspace, workspace_bytes, stream));
-    return fibattn_fwd_attend(q, v, alpha, W, offsets, K, B, L, Hq, Hkv, D, dtype, rope_theta, o, lse, workspace,
+    return fibattn_fwd_attend(q, k, v, alpha, W, offsets, K, B, L, Hq, Hkv, D, dtype, rope_theta, o, lse, workspace,
                               workspace_bytes, stream);
 }
 
@@ -523,6 +541,11 @@ fibattn_status_t fibattn_bwd_stages(int32_t stages, const void* q, const void* k
             pa.fr = a.fr;
             pa.main = 1;
             pa.k16lo = nullptr;
+            pa.flags = flags_at(w0, B, L, Hkv);
+            pa.n_blk = flag_blocks(L);
+            a.kvflags = pa.flags;
+            a.n_blk = pa.n_blk;
+            a.k = k;
             a.kstage = pa.k16;
             a.vstage = pa.v16;
             a.kstage_lo = w0 + f.klo;

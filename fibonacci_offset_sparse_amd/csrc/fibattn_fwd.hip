@@ -71,6 +71,32 @@ __device__ __forceinline__ void stage_rows(float* buf, const T* base, int j0, in
     }
 }
 
+// Rows [j0, j0 + nrows) of the caller's bf16 keys into LDS as float32, each rotated at its own
+// position (cos/sin from the table): the general kernel's bf16 path reads the caller's rows, so
+// that no value leaves the range it can hold. Thread item e: row e / 8, RoPE pairs 4c .. 4c + 3
+// (c = e % 8), i.e. dims 4c .. 4c + 3 and 32 + 4c .. 32 + 4c + 3.
+template <int NT>
+__device__ __forceinline__ void stage_rows_rot(float* buf, const bf16_t* base, const float* cstab, int j0, int nrows,
+                                               int L) {
+    for (int e = threadIdx.x; e < nrows * 8; e += NT) {
+        const int r = e >> 3, c = e & 7;
+        const int j = j0 + r;
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
+        if (j >= 0 && j < L) {
+            const float4 a = load4<bf16_t>(base + static_cast<int64_t>(j) * kD + 4 * c);
+            const float4 b = load4<bf16_t>(base + static_cast<int64_t>(j) * kD + kPairs + 4 * c);
+            const float4* cs = reinterpret_cast<const float4*>(cstab + static_cast<int64_t>(j) * 2 * kPairs + 8 * c);
+            const float4 t0 = cs[0], t1 = cs[1];         // (cos, sin) of pairs 4c .. 4c + 3
+            x = make_float4(a.x * t0.x - b.x * t0.y, a.y * t0.z - b.y * t0.w, a.z * t1.x - b.z * t1.y,
+                            a.w * t1.z - b.w * t1.w);
+            y = make_float4(b.x * t0.x + a.x * t0.y, b.y * t0.z + a.y * t0.w, b.z * t1.x + a.z * t1.y,
+                            b.w * t1.z + a.w * t1.w);
+        }
+        *reinterpret_cast<float4*>(buf + r * kPitch + 4 * c) = x;
+        *reinterpret_cast<float4*>(buf + r * kPitch + kPairs + 4 * c) = y;
+    }
+}
+
 __device__ __forceinline__ float dot_row(const float (&q)[kD], const float* row) {
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
@@ -126,7 +152,8 @@ __device__ __forceinline__ void axpy_blend(float (&o)[kD], float p, const float*
 
 // The general kernel: any GQA group, W <= 31, up to 32 offsets, float32 arithmetic on staged
 // rows. T is the storage type of q and o; KT and VT are the element types of the staged keys and
-// values (float32 input for float32 storage, fp16 rows from prep_kv16 for bf16 storage).
+// values: float32 rotated keys and the float32 input for float32 storage; for bf16 storage the
+// caller's bf16 keys (rotated as they are staged, from the cos/sin table) and values.
 // HPB query heads per workgroup (the heads of one key-value head, or a chunk of them).
 // Thread t: position p = t / HPB of the tile, head h = t % HPB of the chunk, so the HPB heads
 // of one position sit in adjacent lanes and read the same LDS row.
@@ -167,23 +194,22 @@ __global__ __launch_bounds__(kTile * HPB) void fwd_attend_kernel(FwdArgs A) {
     rope_apply(q, cs_tab[p]);
 #pragma unroll
     for (int e = 0; e < kD; ++e) q[e] *= A.qscale;
-    if constexpr (std::is_same<KT, f16_t>::value) {
-        // the staged fp16 keys have their dims permuted (element 4m + c holds dim 16c + m): the
-        // scores take q in the same order
-        float t[kD];
-#pragma unroll
-        for (int e = 0; e < kD; ++e) t[e] = q[e];
-#pragma unroll
-        for (int e = 0; e < kD; ++e) q[e] = t[16 * (e & 3) + (e >> 2)];
-    }
 
     const int64_t kv_base = (static_cast<int64_t>(b) * A.Hkv + g) * L * kD;
     const KT* krot = static_cast<const KT*>(A.kstage) + kv_base;
     const VT* vsrc = static_cast<const VT*>(A.vstage) + kv_base;
 
+    // keys: float32 rotated (float32 storage), or the caller's bf16 rows rotated as staged
+    auto stage_keys = [&](int j0, int nrows) {
+        if constexpr (std::is_same<KT, bf16_t>::value)
+            stage_rows_rot<NT>(buf, krot, A.cstab, j0, nrows, L);
+        else
+            stage_rows<KT, NT>(buf, krot, j0, nrows, L);
+    };
+
     // ---- pass 1: scores (base 2), window then offsets ----
     float sw[kMaxWin], so[kMaxOff];
-    stage_rows<KT, NT>(buf, krot, i0 - W, kTile + W, L);
+    stage_keys(i0 - W, kTile + W);
     __syncthreads();
 #pragma unroll
     for (int d = 0; d < kMaxWin; ++d) {
@@ -198,7 +224,7 @@ __global__ __launch_bounds__(kTile * HPB) void fwd_attend_kernel(FwdArgs A) {
             const int a = A.off[n].a;
             const int reach = a + A.off[n].interp;
             if (i0 + kTile - 1 >= reach) {                     // some query of the tile reads it
-                stage_rows<KT, NT>(buf, krot, i0 - a - 1, kTile + 1, L);
+                stage_keys(i0 - a - 1, kTile + 1);
                 __syncthreads();
                 const float* near = buf + (p + 1) * kPitch;
                 if (active && i >= reach)
@@ -296,10 +322,11 @@ hipError_t launch_rope_keys(int dtype, const RopeKeysArgs& A, hipStream_t s) {
 hipError_t launch_fwd_attend(int dtype, const FwdArgs& A, hipStream_t s) {
     if (dtype == 0) return launch_fwd_typed<float, float, float>(A, s);
     if (fwd_mfma_supported(A)) return launch_fwd_mfma(A, s);
-    // the staged fp16 values are laid out for the matrix-core kernel: read the caller's values
+    // the caller's rows, keys rotated as they are staged: any finite bf16 input
     FwdArgs B = A;
+    B.kstage = A.k;
     B.vstage = A.v;
-    return launch_fwd_typed<bf16_t, f16_t, bf16_t>(B, s);
+    return launch_fwd_typed<bf16_t, bf16_t, bf16_t>(B, s);
 }
 
 }  // namespace fibattn

@@ -69,16 +69,29 @@ constexpr int kWgsPerCu = 4;
 // 16 + 2u, 17 + 2u whole (pair m: dims m and m + 32). The table is cos and sin as they are.
 // ------------------------------------------------------------------------------------------------
 // A thread takes one position j and kPrepRows (batch, head) rows of it: every row's loads are
-// issued first, then the cos/sin of its 4 RoPE pairs are computed once for all of them.
-constexpr int kPrepRows = 4;
+// issued first, then the cos/sin of its 4 RoPE pairs are computed once for all of them. Workgroup
+// (x, y) = (row group x: kPrepRows consecutive (batch, head) rows, positions 32y .. 32y + 31).
+//
+// Range flags. fp16 holds a rotated key or value row exactly enough only inside a range: every
+// element below 2^15 in magnitude (65504 is fp16's largest) and, unless the row is zero, a row
+// maximum of at least 2^-10 (below that the row's largest elements come near fp16's subnormals,
+// 2^-14, where relative precision is lost). Each workgroup writes one word, nonzero when a key or
+// value row of its block lies outside; the attention kernels check the words of the rows they read
+// and compute such tiles in float32 from the caller's bf16 rows instead.
+constexpr int kPrepRows = kPrepRowGroup;
+constexpr float kFp16Big = 32768.0f;               // 2^15
+constexpr float kFp16Small = 0.0009765625f;        // 2^-10
+
+__device__ __forceinline__ bool outside_fp16(float rowmax, float elemmax) {
+    return elemmax >= kFp16Big || (rowmax > 0.0f && rowmax < kFp16Small);
+}
 
 __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
-    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int u = static_cast<int>(gid & 7);
-    const int64_t pj = gid >> 3;                        // (row group, position)
-    const int j = static_cast<int>(pj % A.L);
-    const int grp = static_cast<int>(pj / A.L);
-    if (grp * kPrepRows >= A.n_bh) return;
+    const int u = threadIdx.x & 7;
+    const int grp = blockIdx.x;
+    const int j = 32 * blockIdx.y + (threadIdx.x >> 3);
+    const bool active = j < A.L;
+    const int jc = active ? j : 0;                      // rows past L are never read
     const bf16_t* ks = static_cast<const bf16_t*>(A.k);
     const bf16_t* vs = static_cast<const bf16_t*>(A.v);
     // the thread's pairs 2u, 2u + 1, 16 + 2u, 17 + 2u, and their frequencies (loaded ahead of the
@@ -97,7 +110,7 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
 #pragma unroll
     for (int r = 0; r < kPrepRows; ++r) {
         const int bh = grp * kPrepRows + r;
-        const int64_t row = (static_cast<int64_t>(bh < A.n_bh ? bh : 0) * A.L + j) * kD;
+        const int64_t row = (static_cast<int64_t>(bh < A.n_bh ? bh : 0) * A.L + jc) * kD;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             kw[r][c] = *reinterpret_cast<const uint32_t*>(ks + row + 16 * c + 2 * u);
@@ -106,26 +119,42 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
     }
     float2 cs[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) rope_cos_sin(j, fh[e], fl[e], cs[e].x, cs[e].y);
-    if (grp == 0 && A.main) {   // the table: [L][32] (cos, sin)
+    for (int e = 0; e < 4; ++e) rope_cos_sin(jc, fh[e], fl[e], cs[e].x, cs[e].y);
+    if (grp == 0 && A.main && active) {   // the table: [L][32] (cos, sin)
         float2* t = reinterpret_cast<float2*>(A.cs) + static_cast<int64_t>(j) * kPairs;
 #pragma unroll
         for (int e = 0; e < 4; ++e) t[pr[e]] = cs[e];
     }
+    bool outside = false;
 #pragma unroll
     for (int r = 0; r < kPrepRows; ++r) {
         const int bh = grp * kPrepRows + r;
-        if (bh >= A.n_bh) break;
-        const int64_t row = (static_cast<int64_t>(bh) * A.L + j) * kD;
+        const bool live = active && bh < A.n_bh;        // uniform over the 8 threads of a row
+        const int64_t row = (static_cast<int64_t>(live ? bh : 0) * A.L + jc) * kD;
         // x, y of pairs 2u, 2u + 1 (dims 2u, 2u + 1 and 32 + ..) and 16 + 2u, 17 + 2u
         const float x[4] = {bf16_lo(kw[r][0]), bf16_hi(kw[r][0]), bf16_lo(kw[r][1]), bf16_hi(kw[r][1])};
         const float y[4] = {bf16_lo(kw[r][2]), bf16_hi(kw[r][2]), bf16_lo(kw[r][3]), bf16_hi(kw[r][3])};
         float rx[4], ry[4];
+        float kmax = 0.f, vmax = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             rx[e] = x[e] * cs[e].x - y[e] * cs[e].y;
             ry[e] = y[e] * cs[e].x + x[e] * cs[e].y;
+            kmax = fmaxf(kmax, fmaxf(fabsf(rx[e]), fabsf(ry[e])));
         }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) vmax = fmaxf(vmax, fmaxf(fabsf(bf16_lo(vw[r][c])), fabsf(bf16_hi(vw[r][c]))));
+        if (A.main) {
+            // the row's maxima over its 8 threads (lanes 8 jj .. 8 jj + 7)
+            float kr = kmax, vr = vmax;
+#pragma unroll
+            for (int off = 1; off < 8; off <<= 1) {
+                kr = fmaxf(kr, __shfl_xor(kr, off, 8));
+                vr = fmaxf(vr, __shfl_xor(vr, off, 8));
+            }
+            outside |= live && (outside_fp16(kr, kmax) || outside_fp16(vr, vmax));
+        }
+        if (!live) continue;
         // element 8u + e: e < 4 is dim 16e + 2u, e >= 4 is dim 16(e - 4) + 2u + 1
         if (A.main) {
             store4<f16_t>(A.k16 + row + 8 * u, make_float4(rx[0], rx[2], ry[0], ry[2]));
@@ -138,11 +167,155 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
         if (A.k16lo != nullptr) {
             // what fp16 rounding left out of each rotated key element: a second fp16 operand
             // whose product with q restores the score to about 2^-22 relative
-            auto lo = [](float x) { return x - static_cast<float>(static_cast<_Float16>(x)); };
+            auto lo = [](float v) { return v - static_cast<float>(static_cast<_Float16>(v)); };
             store4<f16_t>(A.k16lo + row + 8 * u, make_float4(lo(rx[0]), lo(rx[2]), lo(ry[0]), lo(ry[2])));
             store4<f16_t>(A.k16lo + row + 8 * u + 4, make_float4(lo(rx[1]), lo(rx[3]), lo(ry[1]), lo(ry[3])));
         }
     }
+    if (A.main) {
+        const int any = __syncthreads_or(outside ? 1 : 0);
+        if (threadIdx.x == 0) A.flags[static_cast<int64_t>(grp) * A.n_blk + blockIdx.y] = any ? 1u : 0u;
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// The float32 tile: a tile computed from the caller's bf16 rows (q, k, v) and the cos/sin table,
+// for tiles whose rows lie outside the range the fp16 staging holds (the prep's range flags, or q
+// itself). Thread 8p' + e takes dims 8e .. 8e + 7 of position i0 + p' (an 8-lane group holds a whole
+// row; sums over dims close with three DPP steps), 32 positions at a time, one query head after
+// another, with an online softmax over the slots in the order window, rungs. Rows come straight from
+// global memory: slow, and only for such tiles. It runs inside the matrix-core kernels, so it is
+// written to need few registers.
+// ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ float oct_sum(float v) {
+    v += quad_f<0xB1>(v);                               // quad_perm [1, 0, 3, 2]
+    v += quad_f<kXor2>(v);                              // quad_perm [2, 3, 0, 1]
+    v += quad_f<0x141>(v);                              // row_half_mirror: the other quad of the 8
+    return v;
+}
+
+// Dims 8e .. 8e + 7 of a bf16 row, rotated at position j (cos/sin from the table). Dim d pairs
+// with d + 32 (e < 4: x' = x cos - y sin) or d - 32 (e >= 4: y' = y cos + x sin): dims of e ^ 4.
+__device__ __forceinline__ void rot_eighth(const bf16_t* row, const float* cstab, int j, int e, float (&out)[8]) {
+    const float sg = (e < 4) ? -1.f : 1.f;
+    const uint4 ow = reinterpret_cast<const uint4*>(row)[e];
+    const uint4 pw = reinterpret_cast<const uint4*>(row)[e ^ 4];
+    const float4* cs = reinterpret_cast<const float4*>(cstab + static_cast<int64_t>(j) * 2 * kPairs + 16 * (e & 3));
+    const uint32_t o4[4] = {ow.x, ow.y, ow.z, ow.w}, p4[4] = {pw.x, pw.y, pw.z, pw.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const float4 t = cs[h];                          // (cos, sin) of dims 8e + 2h, + 1
+        out[2 * h] = fmaf(sg * bf16_lo(p4[h]), t.y, bf16_lo(o4[h]) * t.x);
+        out[2 * h + 1] = fmaf(sg * bf16_hi(p4[h]), t.w, bf16_hi(o4[h]) * t.z);
+    }
+}
+
+__device__ __forceinline__ void fwd_tile_fp32(const FwdArgs& A, int b, int bg, int h0, int i0) {
+    constexpr float kNegInf = -__builtin_huge_valf();
+    const int e = threadIdx.x & 7, L = A.L;
+    const bf16_t* kb = static_cast<const bf16_t*>(A.k) + static_cast<int64_t>(bg) * L * kD;
+    const bf16_t* vb = static_cast<const bf16_t*>(A.v) + static_cast<int64_t>(bg) * L * kD;
+    const int n_slots = A.W + 1 + A.n_off;
+#pragma unroll 1
+    for (int it = 0; it < 2 * 4; ++it) {                // (half of the tile, head)
+        const int i = i0 + 32 * (it & 1) + (threadIdx.x >> 3);
+        if (i >= L) continue;                           // whole 8-lane groups skip together
+        const int64_t qrow = (static_cast<int64_t>(b) * A.Hq + h0 + (it >> 1)) * L + i;
+        float qv[8], o[8], row[8];
+        rot_eighth(static_cast<const bf16_t*>(A.q) + qrow * kD, A.cstab, i, e, qv);
+        float m = kNegInf, l = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            qv[u] *= A.qscale;                          // scores in base 2
+            o[u] = 0.f;
+        }
+#pragma unroll 1
+        for (int sl = 0; sl < n_slots; ++sl) {
+            // slot sl: window distance sl, or kept rung sl - W - 1: rows j (weight 1 - t), j - 1 (t)
+            int j;
+            float t = 0.f;
+            if (sl <= A.W) {
+                j = i - sl;
+            } else {
+                const int n = sl - A.W - 1;
+                j = i - A.off[n].a;
+                if (A.off[n].interp) {
+                    t = A.off[n].t;
+                    --j;                                 // the far row must exist too
+                }
+                if (j < 0) continue;
+                j += A.off[n].interp;
+            }
+            if (j < 0) continue;
+            // the score and the value are linear in the blended row: each row once
+            float sc = 0.f;
+#pragma unroll 1
+            for (int r = 0; r < (t != 0.f ? 2 : 1); ++r) {
+                rot_eighth(kb + static_cast<int64_t>(j - r) * kD, A.cstab, j - r, e, row);
+                float d = 0.f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) d = fmaf(qv[u], row[u], d);
+                sc += (r ? t : 1.f - t) * oct_sum(d);
+            }
+            const float mn = fmaxf(m, sc);
+            const float keep = __builtin_amdgcn_exp2f(m - mn), w = __builtin_amdgcn_exp2f(sc - mn);
+            l = fmaf(l, keep, w);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) o[u] *= keep;
+#pragma unroll 1
+            for (int r = 0; r < (t != 0.f ? 2 : 1); ++r) {
+                const uint4 vw = reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(j - r) * kD)[e];
+                const uint32_t v4[4] = {vw.x, vw.y, vw.z, vw.w};
+                const float wr = w * (r ? t : 1.f - t);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    o[2 * h] = fmaf(wr, bf16_lo(v4[h]), o[2 * h]);
+                    o[2 * h + 1] = fmaf(wr, bf16_hi(v4[h]), o[2 * h + 1]);
+                }
+            }
+            m = mn;
+        }
+        const float inv = 1.0f / l;
+        const uint4 ov = make_uint4(pack_bf2(o[0] * inv, o[1] * inv), pack_bf2(o[2] * inv, o[3] * inv),
+                                    pack_bf2(o[4] * inv, o[5] * inv), pack_bf2(o[6] * inv, o[7] * inv));
+        store_nt(static_cast<bf16_t*>(A.o) + qrow * kD + 8 * e, ov);
+        if (e == 0 && A.lse != nullptr) store_nt(A.lse + qrow, (m + log2f(l)) * 0.69314718055994530942f);
+    }
+}
+
+// Whether a query row (64 bf16 values in r) scaled by qscale lies outside what fp16 holds exactly
+// enough once rotated (rotation moves each element by at most a factor sqrt(2) either way).
+__device__ __forceinline__ bool q_outside_fp16(const uint4 (&r)[8], float qscale) {
+    float mx = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t w[4] = {r[c].x, r[c].y, r[c].z, r[c].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
+    }
+    mx *= qscale;
+    return mx >= 0.5f * kFp16Big || (mx > 0.f && mx < 2.f * kFp16Small);
+}
+
+// The range flag of the staged rows that thread t of a tile checks: threads 0..3 the near block
+// (rows i0 - 64 .. i0 + 63), thread 4 + 4n + u the u-th flag block of kept rung n's rows
+// i0 - a - 1 .. i0 + 63 - a (clipped at 0), for rungs the tile reaches; every other thread none.
+template <typename Args>
+__device__ __forceinline__ bool rows_flagged(const Args& A, int grp, int i0, int n_reach) {
+    const int t = threadIdx.x;
+    int blk = -1;
+    if (t < 4) {
+        blk = i0 / kFlagRows - 2 + t;
+    } else if (t < 4 + 4 * kMaxOff) {
+        const int n = (t - 4) >> 2, u = (t - 4) & 3;
+        if (n < n_reach) {
+            const int a = A.off[n].a;
+            const int lo = max(i0 - a - 1, 0), hi = min(i0 + kTile - 1 - a, A.L - 1);
+            if (lo / kFlagRows + u <= hi / kFlagRows) blk = lo / kFlagRows + u;
+        }
+    }
+    if (blk < 0 || blk >= A.n_blk) return false;
+    return A.kvflags[static_cast<int64_t>(grp) * A.n_blk + blk] != 0u;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -210,6 +383,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     // key near block (item 0) and item 1 (key far step kn) ----
     uint4 qraw[8];
     float4 ctab[4];
+    int outside;                                        // uniform: some row of the tile lies outside fp16's range
     {
         char* const reg = (wave < 2 ? lds0 : lds1) + (wave & 1) * 8192;
         // the 4 heads' rows (4 L rows of 128 bytes: within 32 bits for L <= 2^20); positions
@@ -227,11 +401,16 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
         const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(active ? i : 0) * (kPairs / 2) + 4 * x;
 #pragma unroll
         for (int u = 0; u < 4; ++u) ctab[u] = ct[u];
+        // the range flags of the staged rows this tile reads (in flight with q)
+        const bool flagged = rows_flagged(A, bg / kPrepRowGroup, i0, n_reach);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
         for (int c = 0; c < 8; ++c) qraw[c] = *reinterpret_cast<const uint4*>(reg + row_view_addr(pq, x, c));
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();                   // every wave is done with its rows
+        // every wave is done with its rows (the barrier), and whether some row of the tile lies
+        // outside the fp16 range: then the whole tile is computed in float32
+        outside = __builtin_amdgcn_readfirstlane(
+            __syncthreads_or((flagged || (active && q_outside_fp16(qraw, A.qscale))) ? 1 : 0));
         asm volatile("" ::: "memory");
     }
     st.near(krs, lds0, jn);
@@ -412,7 +591,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     invh[1] = quad_f<kBcast1>(inv);
     invh[2] = quad_f<kBcast2>(inv);
     invh[3] = quad_f<kBcast3>(inv);
-    if (active) {
+    if (active && !outside) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             bf16_t* orow = static_cast<bf16_t*>(A.o) + ((static_cast<int64_t>(b) * A.Hq + h0 + r) * L + i) * kD + 16 * x;
@@ -431,14 +610,20 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
         if (A.lse != nullptr)
             store_nt(A.lse + (static_cast<int64_t>(b) * A.Hq + h0 + x) * L + i, (m + log2f(l)) * 0.69314718055994530942f);
     }
+    if (outside) {
+        // Some row of the tile lies outside fp16's range: what the matrix cores computed is not
+        // stored, and the tile is computed in float32 from the caller's rows instead (here at the
+        // end, where nothing of the matrix-core path is live: the fallback's registers are its own).
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        fwd_tile_fp32(A, b, bg, h0, i0);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_prep_kv16(const PrepArgs& A, hipStream_t s) {
-    const int64_t threads = static_cast<int64_t>((A.n_bh + kPrepRows - 1) / kPrepRows) * A.L * 8;
-    const unsigned blocks = static_cast<unsigned>((threads + 255) / 256);
-    hipLaunchKernelGGL(prep_kv16_kernel, dim3(blocks), dim3(256), 0, s, A);
+    const dim3 grid(static_cast<unsigned>((A.n_bh + kPrepRows - 1) / kPrepRows), static_cast<unsigned>(A.n_blk));
+    hipLaunchKernelGGL(prep_kv16_kernel, grid, dim3(256), 0, s, A);
     return hipGetLastError();
 }
 

@@ -15,6 +15,11 @@ constexpr int kMaxOff = 32;   // base rungs
 // backward stages (the bit values of the public stage mask)
 constexpr int kStagePrep = 1, kStageQuery = 2, kStageKey = 4;
 
+// Range flags of the staged rows: one word per (group of kPrepRowGroup consecutive (batch, head)
+// rows, block of kFlagRows positions).
+constexpr int kPrepRowGroup = 4;
+constexpr int kFlagRows = 32;
+
 // One kept offset of the plan (DUP rungs are removed before launch).
 struct OffsetSlot {
     int32_t a;       // distance of the nearer row, floor(d)
@@ -49,6 +54,10 @@ struct PrepArgs {
     // nullptr; with main == 0 only these are written (k16, v16 and cs are left alone)
     _Float16* k16lo;
     int32_t main;
+    // per (group of kPrepRowGroup (batch, head) rows, block of 32 positions): nonzero when a key or
+    // value row of the block lies outside the range fp16 holds exactly enough (written when main)
+    uint32_t* flags;
+    int32_t n_blk;       // ceil(L / 32)
     int32_t n_bh;
     int32_t L;
     RopeFreq fr;
@@ -60,7 +69,10 @@ struct FwdArgs {
                          // with dims permuted, element 4m + c holding dim 16c + m (bf16 storage)
     const void* vstage;  // [B, Hkv, L, 64] values: the input (f32 storage) or fp16, dims permuted
     const void* v;       // [B, Hkv, L, 64] the caller's values
+    const void* k;       // [B, Hkv, L, 64] the caller's keys (unrotated)
     const float* cstab;  // [L, 32, 2] cos/sin table (bf16 storage)
+    const uint32_t* kvflags;  // range flags of the staged rows (bf16 storage), see PrepArgs
+    int32_t n_blk;
     void* o;             // [B, Hq, L, 64]
     float* lse;          // [B, Hq, L] or nullptr
     int32_t B, L, Hq, Hkv, G, W, n_off;
@@ -98,6 +110,9 @@ struct BwdArgs {
     const void* kstage;  // [B*Hkv, L, 64] fp16 rotated keys, dims permuted
     const void* vstage;  // [B*Hkv, L, 64] fp16 values, dims permuted
     const float* cstab;  // [L, 32, 2] cos, sin
+    const uint32_t* kvflags;  // range flags of the staged rows, see PrepArgs
+    int32_t n_blk;
+    const void* k;       // [B, Hkv, L, 64] the caller's keys (unrotated)
     const void* kstage_lo;  // [B*Hkv, L, 64] fp16 low parts of the rotated keys (precise scores)
     void* qrot16;        // [B, Hq, L, 64] fp16 rotated queries, dims permuted
     void* do16;          // [B, Hq, L, 64] fp16 copy of dout, dims permuted

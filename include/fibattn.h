@@ -173,10 +173,12 @@ fibattn_status_t fibattn_fwd_prep(const void* k, const void* v, int32_t B, int32
 /*
  * Second stage of fibattn_fwd: the attention itself. Reads what fibattn_fwd_prep left in
  * `workspace` (same shapes, dtype and rope_theta), so it must follow it on the same stream with the
- * workspace untouched in between. v is read directly for FIBATTN_F32 (and ignored for
- * FIBATTN_BF16, whose values are in the workspace).
+ * workspace untouched in between. q, k, v are the caller's tensors as fibattn_fwd takes them: for
+ * FIBATTN_F32, v is read directly (the rotated keys come from the workspace); for FIBATTN_BF16, the
+ * staged fp16 keys and values are read, and the caller's k and v only by tiles whose rows the prep
+ * found outside fp16's range (see fibattn_fwd), which are computed in float32 from them.
  */
-fibattn_status_t fibattn_fwd_attend(const void* q, const void* v, double alpha, int32_t W,
+fibattn_status_t fibattn_fwd_attend(const void* q, const void* k, const void* v, double alpha, int32_t W,
                                     const int32_t* offsets, int32_t K, int32_t B, int32_t L,
                                     int32_t Hq, int32_t Hkv, int32_t D, int32_t dtype,
                                     double rope_theta, void* o, float* lse,

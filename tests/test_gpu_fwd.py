@@ -220,7 +220,53 @@ def test_staged_entry_points_equal_the_combined_call():
     o2 = torch.empty_like(q)
     l2 = torch.empty_like(l1)
     fa.fibattn_fwd_prep(k, v, ws)
-    fa.fibattn_fwd_attend(q, v, alpha, w.W, O.FIB_BASE, ws, o2, l2)
-    fa.fibattn_fwd_attend(q, v, alpha, w.W, O.FIB_BASE, ws, o2, None)      # inference: no lse
+    fa.fibattn_fwd_attend(q, k, v, alpha, w.W, O.FIB_BASE, ws, o2, l2)
+    fa.fibattn_fwd_attend(q, k, v, alpha, w.W, O.FIB_BASE, ws, o2, None)      # inference: no lse
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---- inputs outside fp16's range: tiles whose rows fp16 cannot hold exactly enough are computed in
+# float32 from the caller's bf16 rows (the prep's range flags, and each tile's own q rows) ----
+
+def _scaled_case(scales, seed, L=300, W=7, alpha=0.83):
+    q, k, v = (workloads.randn_like_seeded(sh, seed + i) * s for i, (sh, s) in
+               enumerate(zip([(1, 8, L, 64), (1, 2, L, 64), (1, 2, L, 64)], scales)))
+    return tuple(x.to(torch.bfloat16) for x in (q, k, v)) + (alpha, W)
+
+
+@pytest.mark.parametrize("scales,W", [
+    ((3e5, 3e-6, 3e5), 7),       # q and v far above fp16's range, scores of order 1
+    ((3e-6, 3e5, 1.0), 7),       # k far above, q far below
+    ((1e-6, 1e-6, 1e-6), 7),     # everything below fp16's normal range
+    ((1.0, 1.0, 1e-6), 7),       # values only
+    ((3e5, 3e-6, 3e5), 20),      # the general kernel (W > 15)
+])
+def test_inputs_outside_fp16_range(scales, W):
+    q, k, v, alpha, W = _scaled_case(scales, 80, W=W)
+    say(f"range q,k,v x {scales} W={W}")
+    o, lse = run_fwd(q, k, v, alpha, W, O.FIB_BASE)
+    o_ref, lse_ref = O.forward(q.double().numpy(), k.double().numpy(), v.double().numpy(), alpha, W, O.FIB_BASE)
+    # bf16 outputs: each within 2^-8 of its own magnitude plus 1e-3 of the output's scale
+    g, r = o.double().numpy(), o_ref
+    assert np.all(np.isfinite(g))
+    assert np.all(np.abs(g - r) <= 2.0 ** -8 * np.abs(r) + 1e-3 * np.abs(r).max()), np.abs(g - r).max()
+    # lse: the scores are of order 1 in every case; the log-normaliser shifts with log of the scale
+    assert np.max(np.abs(lse.double().numpy() - lse_ref)) <= 1e-3 * max(1.0, np.abs(lse_ref).max())
+
+
+def test_one_value_outside_fp16_range_in_a_row_few_queries_read():
+    # one value element of 1e5 (fp16 would make it inf, and 0 * inf a NaN in every query whose
+    # slots do not read that row but whose matrix products touch it): the tiles reading its block
+    # compute in float32, the others on the matrix cores; every output is checked
+    L = 300
+    q, k, v = randn((1, 8, L, 64), 90, torch.bfloat16), randn((1, 2, L, 64), 91, torch.bfloat16), \
+        randn((1, 2, L, 64), 92, torch.bfloat16)
+    v[0, 1, 133, 17] = 1e5
+    k[0, 0, 200:240] = 0                                  # zero rows (padding) stay on the matrix cores
+    say("one value of 1e5 at row 133, zero key rows 200..239")
+    o, lse = run_fwd(q, k, v, 0.91, 9, O.FIB_BASE)
+    o_ref, lse_ref = O.forward(q.double().numpy(), k.double().numpy(), v.double().numpy(), 0.91, 9, O.FIB_BASE)
+    assert torch.isfinite(o.float()).all()
+    check(o, o_ref, torch.bfloat16, what="one big value o")
+    check(lse, lse_ref, torch.bfloat16, what="one big value lse", stored_bf16=False)
