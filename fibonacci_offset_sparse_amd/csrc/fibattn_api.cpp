@@ -160,7 +160,7 @@ uint32_t* flags_at(void* ws, int32_t B, int32_t L, int32_t Hkv) {
 // cos/sin table (the forward's layout of the same sizes), the rotated queries (fp16), the per key
 // row term weights, and the per-workgroup d(loss)/dt partials.
 struct BwdFastLayout {
-    size_t qrot, do16, wwin, wrung, part, klo, total;
+    size_t qrot, do16, wwin, wrung, part, klo, exps, total;
 };
 BwdFastLayout bwd_fast_layout(int32_t B, int32_t L, int32_t Hq, int32_t Hkv) {
     BwdFastLayout f;
@@ -172,7 +172,9 @@ BwdFastLayout bwd_fast_layout(int32_t B, int32_t L, int32_t Hq, int32_t Hkv) {
     const size_t n_wg = static_cast<size_t>(bwd_query_workgroups(B, L, Hkv, Hq / Hkv));
     f.klo = f.part + align256(n_wg * kMaxOff * sizeof(float));
     // low parts of the rotated keys (fp16), for the precise scores of a call that asks for d(alpha)
-    f.total = f.klo + align256(half_rows_bytes(B, L, Hkv));
+    f.exps = f.klo + align256(half_rows_bytes(B, L, Hkv));
+    // the query tiles' scale exponents [B, Hq, tiles]
+    f.total = f.exps + align256(static_cast<size_t>(B) * Hq * ((L + kTile - 1) / kTile) * sizeof(uint32_t));
     return f;
 }
 
@@ -555,6 +557,7 @@ fibattn_status_t fibattn_bwd_stages(int32_t stages, const void* q, const void* k
             a.wwin = reinterpret_cast<uint32_t*>(w0 + f.wwin);
             a.wrung = reinterpret_cast<uint32_t*>(w0 + f.wrung);
             a.partial = reinterpret_cast<float*>(w0 + f.part);
+            a.exps = reinterpret_cast<uint32_t*>(w0 + f.exps);
             // with d(alpha) requested the query stage takes precise scores, from the low parts of
             // the rotated keys as well: written with the prep when both run in this call, else
             // by a pass of their own ahead of the query stage

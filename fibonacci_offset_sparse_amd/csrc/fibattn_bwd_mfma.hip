@@ -50,6 +50,316 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // fp16 p in the low half, fp16 ds in the high half (bf16 p loses too much of dv: 2^-9 per term)
 __device__ __forceinline__ uint32_t pack_p_ds(float p, float ds) { return pack_h2(p, ds); }
 
+// Power-of-two scaling. fp16 holds a row exactly enough only near the unit scale, so q, do and
+// the score gradients are kept as row / 2^e, e the exponent of the row's largest element (its
+// floor(log2), clamped to [-126, 126]: then 2^-e is a normal float): the scaled row's largest
+// element lies in [1, 2), whatever the magnitude of the inputs. Products of scaled rows are scaled
+// back exactly in float32. An all-zero row has no exponent (kNoExp) and is kept as it is.
+constexpr int kNoExp = -1000;
+constexpr int kExpBias = 128;                          // exponents stored in bytes of the exps word
+
+__device__ __forceinline__ int floor_log2(float x) {   // x >= 0
+    if (!(x > 0.f)) return kNoExp;
+    return min(max(__builtin_amdgcn_frexp_expf(x) - 1, -126), 126);
+}
+__device__ __forceinline__ float pow2f(int e) { return __builtin_amdgcn_ldexpf(1.0f, e); }
+// A query tile's exponents for the key side, one word per (batch, head, tile): q scaled by 2^-tq,
+// do by 2^-td, dS/sqrt(D) by 2^-ts (bytes 0, 1, 2, each biased by kExpBias; clamped to a byte).
+__device__ __forceinline__ uint32_t pack_exps(int tq, int td, int ts) {
+    auto byte = [](int e) { return static_cast<uint32_t>(min(max(e, -127), 127) + kExpBias); };
+    return byte(tq) | (byte(td) << 8) | (byte(ts) << 16);
+}
+__device__ __forceinline__ int exps_tq(uint32_t w) { return static_cast<int>(w & 0xffu) - kExpBias; }
+__device__ __forceinline__ int exps_td(uint32_t w) { return static_cast<int>((w >> 8) & 0xffu) - kExpBias; }
+__device__ __forceinline__ int exps_ts(uint32_t w) { return static_cast<int>((w >> 16) & 0xffu) - kExpBias; }
+// query heads per key-value head the key side takes (its factor table)
+constexpr int kMaxGKey = 8;
+// an h2 whose halves are 2^e (0 below fp16's subnormals)
+__device__ __forceinline__ uint32_t pow2_h2(int e_lo, int e_hi) {
+    return pack_h2(e_lo < -30 ? 0.f : pow2f(e_lo), e_hi < -30 ? 0.f : pow2f(e_hi));
+}
+__device__ __forceinline__ uint32_t mul_h2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, a) * __builtin_bit_cast(h2_t, b));
+}
+__device__ __forceinline__ float max_abs_bf16_row(const uint4 (&r)[8]) {
+    float mx = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t w[4] = {r[c].x, r[c].y, r[c].z, r[c].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
+    }
+    return mx;
+}
+// the largest of v over the 16 lanes of a wave with the same quad lane x (one head's positions)
+__device__ __forceinline__ int head_max(int v) {
+#pragma unroll
+    for (int off = 4; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// ------------------------------------------------------------------------------------------------
+// The float32 tiles of the backward: for tiles that read staged key or value rows outside fp16's
+// range. A query tile so flagged leaves its outputs to bwd_fp32_kernel, and marks its exps word;
+// every key tile that reads from a marked query tile leaves its outputs to it too. Both are
+// computed from the caller's bf16 rows and the cos/sin table: thread 8p' + e takes dims
+// 8e .. 8e + 7 of a row (32 rows at a time). Slot sl of query i: sl < 16 is window distance sl,
+// 16 + n kept rung n. Rows come straight from global memory: slow, and only for such tiles.
+// ------------------------------------------------------------------------------------------------
+constexpr int kFbSlots = 32;
+constexpr uint32_t kExpsFallback = 1u << 24;         // exps word of a query tile left to the float32 tiles
+
+__device__ __forceinline__ void load_eighth(const bf16_t* row, int e, float (&out)[8]) {
+    const uint4 w = reinterpret_cast<const uint4*>(row)[e];
+    const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        out[2 * h] = bf16_lo(v[h]);
+        out[2 * h + 1] = bf16_hi(v[h]);
+    }
+}
+
+struct FbRows {                                        // one unit's key and value rows
+    const bf16_t* k;
+    const bf16_t* v;
+    const float* cstab;
+    int e;
+    // x . (rotated key row j), or (value row j), over the 64 dims of the group
+    __device__ __forceinline__ float dot_k(const float (&x)[8], int j) const {
+        float r[8];
+        rot_eighth(k + static_cast<int64_t>(j) * kD, cstab, j, e, r);
+        float d = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) d = fmaf(x[u], r[u], d);
+        return oct_sum(d);
+    }
+    __device__ __forceinline__ float dot_v(const float (&x)[8], int j) const {
+        float r[8];
+        load_eighth(v + static_cast<int64_t>(j) * kD, e, r);
+        float d = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) d = fmaf(x[u], r[u], d);
+        return oct_sum(d);
+    }
+};
+
+// Slot sl of query i: rows j (weight 1 - t) and j - 1 (weight t), or j = -1 (not attended).
+__device__ __forceinline__ void fb_slot_rows(const BwdArgs& A, int sl, int i, int& j, float& t) {
+    t = 0.f;
+    j = -1;
+    if (sl < 16) {
+        if (sl <= A.W && i >= sl) j = i - sl;
+    } else if (sl - 16 < A.n_off) {
+        const int n = sl - 16;
+        if (i >= A.off[n].a + A.off[n].interp) {
+            j = i - A.off[n].a;
+            t = A.off[n].interp ? A.off[n].t : 0.f;
+        }
+    }
+}
+
+// Softmax statistics of query i (rotated q, do in the lane's 8 dims): the largest score m (base 2),
+// l = sum 2^(s - m), delta = sum p dP; and slot sl0's score and dP.
+__device__ __forceinline__ void fb_query_stats(const BwdArgs& A, const FbRows& R, int i, const float (&qv)[8],
+                                               const float (&dov)[8], int sl0, float& m, float& l, float& delta,
+                                               float& s0, float& dp0) {
+    constexpr float kNegInf = -__builtin_huge_valf();
+    m = kNegInf;
+#pragma unroll 1
+    for (int sl = 0; sl < kFbSlots; ++sl) {
+        int j;
+        float t;
+        fb_slot_rows(A, sl, i, j, t);
+        if (j < 0) continue;
+        float sc = R.dot_k(qv, j);
+        if (t != 0.f) sc = fmaf(t, R.dot_k(qv, j - 1) - sc, sc);
+        m = fmaxf(m, sc * A.qscale);
+    }
+    l = 0.f;
+    float dsum = 0.f;
+    s0 = kNegInf;
+    dp0 = 0.f;
+#pragma unroll 1
+    for (int sl = 0; sl < kFbSlots; ++sl) {
+        int j;
+        float t;
+        fb_slot_rows(A, sl, i, j, t);
+        if (j < 0) continue;
+        float sc = R.dot_k(qv, j), dpv = R.dot_v(dov, j);
+        if (t != 0.f) {
+            sc = fmaf(t, R.dot_k(qv, j - 1) - sc, sc);
+            dpv = fmaf(t, R.dot_v(dov, j - 1) - dpv, dpv);
+        }
+        sc *= A.qscale;
+        const float ex = __builtin_amdgcn_exp2f(sc - m);
+        l += ex;
+        dsum = fmaf(ex, dpv, dsum);
+        if (sl == sl0) {
+            s0 = sc;
+            dp0 = dpv;
+        }
+    }
+    delta = dsum / l;
+}
+
+// dq and the d(loss)/dt partials of one query tile (the workgroup's), in float32.
+__device__ __forceinline__ void bwd_q_tile_fp32(const BwdArgs& A, int b, int bg, int h0, int i0, char* lds) {
+    float* dtbuf = reinterpret_cast<float*>(lds);                  // [64][16] d(loss)/dt per rung
+    const int e = threadIdx.x & 7, gi = threadIdx.x >> 3, L = A.L;
+    const FbRows R{static_cast<const bf16_t*>(A.k) + static_cast<int64_t>(bg) * L * kD,
+                   static_cast<const bf16_t*>(A.v) + static_cast<int64_t>(bg) * L * kD, A.cstab, e};
+    float dt_sum = 0.f;                                             // thread n < 16: rung n's partial
+#pragma unroll 1
+    for (int hh = 0; hh < 4; ++hh) {
+        for (int u = threadIdx.x; u < kTile * 16; u += kNT) dtbuf[u] = 0.f;
+        __syncthreads();
+        const int h = h0 + hh;
+#pragma unroll 1
+        for (int half = 0; half < 2; ++half) {
+            const int pp = 32 * half + gi, i = i0 + pp;
+            if (i >= L) continue;                                   // whole groups skip together
+            const int64_t qrow = (static_cast<int64_t>(b) * A.Hq + h) * L + i;
+            float qv[8], dov[8];
+            rot_eighth(static_cast<const bf16_t*>(A.q) + qrow * kD, A.cstab, i, e, qv);
+            load_eighth(static_cast<const bf16_t*>(A.dout) + qrow * kD, e, dov);
+            float m, l, delta, s0, dp0;
+            fb_query_stats(A, R, i, qv, dov, -1, m, l, delta, s0, dp0);
+            float dq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+            for (int sl = 0; sl < kFbSlots; ++sl) {
+                int j;
+                float t;
+                fb_slot_rows(A, sl, i, j, t);
+                if (j < 0) continue;
+                float kn[8];
+                rot_eighth(R.k + static_cast<int64_t>(j) * kD, A.cstab, j, e, kn);
+                float sc = 0.f, dpv = R.dot_v(dov, j);
+                {
+                    float d = 0.f;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) d = fmaf(qv[u], kn[u], d);
+                    sc = oct_sum(d);
+                }
+                float gk = 0.f, gv = 0.f;
+                if (t != 0.f) {
+                    float kf[8];
+                    rot_eighth(R.k + static_cast<int64_t>(j - 1) * kD, A.cstab, j - 1, e, kf);
+                    float d = 0.f;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        d = fmaf(qv[u], kf[u], d);
+                        kn[u] = fmaf(t, kf[u] - kn[u], kn[u]);     // the blended key row
+                    }
+                    const float sf = oct_sum(d), dvf = R.dot_v(dov, j - 1);
+                    gk = sf - sc;                                   // q . (k_far - k_near)
+                    gv = dvf - dpv;                                 // do . (v_far - v_near)
+                    sc = fmaf(t, gk, sc);
+                    dpv = fmaf(t, gv, dpv);
+                }
+                const float pr = __builtin_amdgcn_exp2f(sc * A.qscale - m) / l;
+                const float ds = pr * (dpv - delta) * A.scale;     // dS / sqrt(D)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) dq[u] = fmaf(ds, kn[u], dq[u]);
+                if (sl >= 16 && t != 0.f && e == 0) dtbuf[pp * 16 + (sl - 16)] = fmaf(ds, gk, pr * gv);
+            }
+            // dq = RoPE transposed at i: x = x' c + y' s (dims below 32), y = y' c - x' s; the pair's
+            // other half is in lane e ^ 4 of the group
+            const float4* cs = reinterpret_cast<const float4*>(A.cstab + static_cast<int64_t>(i) * 2 * kPairs + 16 * (e & 3));
+            const float sg = (e < 4) ? 1.f : -1.f;
+            float out[8];
+#pragma unroll
+            for (int hp = 0; hp < 4; ++hp) {
+                const float4 t = cs[hp];
+                const float o0 = __shfl_xor(dq[2 * hp], 4, 64), o1 = __shfl_xor(dq[2 * hp + 1], 4, 64);
+                out[2 * hp] = fmaf(sg * o0, t.y, dq[2 * hp] * t.x);
+                out[2 * hp + 1] = fmaf(sg * o1, t.w, dq[2 * hp + 1] * t.z);
+            }
+            store_nt(static_cast<bf16_t*>(A.dq) + qrow * kD + 8 * e,
+                     make_uint4(pack_bf2(out[0], out[1]), pack_bf2(out[2], out[3]), pack_bf2(out[4], out[5]),
+                                pack_bf2(out[6], out[7])));
+        }
+        __syncthreads();                                            // dtbuf is complete
+        if (threadIdx.x < 16) {
+            for (int pp = 0; pp < kTile; ++pp)
+                if (i0 + pp < L) dt_sum += dtbuf[pp * 16 + threadIdx.x];
+        }
+        __syncthreads();                                            // before the next head's buffer
+    }
+    if (threadIdx.x < static_cast<unsigned>(A.n_off))
+        A.partial[static_cast<int64_t>(blockIdx.x) * kMaxOff + threadIdx.x] = threadIdx.x < 16 ? dt_sum : 0.f;
+}
+
+// dk and dv of one key tile (rows j0 .. j0 + 63 of unit bg, key-value head g), in float32: key row j
+// is read by query j + d of window distance d, by query j + a (weight 1 - t, or 1 if integral) as
+// the nearer row of rung a and by query j + a + 1 (weight t) as the farther one; each such term
+// recomputes its query's softmax statistics.
+__device__ __forceinline__ void bwd_k_tile_fp32(const BwdArgs& A, int b, int bg, int g, int j0) {
+    const int e = threadIdx.x & 7, gi = threadIdx.x >> 3, L = A.L;
+    const FbRows R{static_cast<const bf16_t*>(A.k) + static_cast<int64_t>(bg) * L * kD,
+                   static_cast<const bf16_t*>(A.v) + static_cast<int64_t>(bg) * L * kD, A.cstab, e};
+    const int n_terms = 16 + 2 * A.n_off;
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+        const int j = j0 + 32 * half + gi;
+        if (j >= L) continue;
+        float dk[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, dv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+        for (int hh = 0; hh < A.G; ++hh) {
+            const int h = g * A.G + hh;
+#pragma unroll 1
+            for (int tm = 0; tm < n_terms; ++tm) {
+                // term tm: window distance tm (< 16), or rung n = (tm - 16) / 2 as nearer / farther row
+                int i, sl;
+                float coef = 1.f;
+                if (tm < 16) {
+                    if (tm > A.W) continue;
+                    i = j + tm;
+                    sl = tm;
+                } else {
+                    const int n = (tm - 16) >> 1, far = (tm - 16) & 1;
+                    const int a = A.off[n].a, ip = A.off[n].interp;
+                    const float t = A.off[n].t;
+                    if (far && !ip) continue;
+                    i = j + a + far;
+                    if (i < a + ip) continue;                       // the query does not attend this rung
+                    sl = 16 + n;
+                    coef = ip ? (far ? t : 1.f - t) : 1.f;
+                }
+                if (i >= L) continue;
+                const int64_t qrow = (static_cast<int64_t>(b) * A.Hq + h) * L + i;
+                float qv[8], dov[8];
+                rot_eighth(static_cast<const bf16_t*>(A.q) + qrow * kD, A.cstab, i, e, qv);
+                load_eighth(static_cast<const bf16_t*>(A.dout) + qrow * kD, e, dov);
+                float m, l, delta, s0, dp0;
+                fb_query_stats(A, R, i, qv, dov, sl, m, l, delta, s0, dp0);
+                const float pr = __builtin_amdgcn_exp2f(s0 - m) / l;
+                const float ds = pr * (dp0 - delta) * A.scale;     // dS / sqrt(D)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    dk[u] = fmaf(coef * ds, qv[u], dk[u]);
+                    dv[u] = fmaf(coef * pr, dov[u], dv[u]);
+                }
+            }
+        }
+        // dk = RoPE transposed at j (the pair's other half in lane e ^ 4)
+        const float4* cs = reinterpret_cast<const float4*>(A.cstab + static_cast<int64_t>(j) * 2 * kPairs + 16 * (e & 3));
+        const float sg = (e < 4) ? 1.f : -1.f;
+        float out[8];
+#pragma unroll
+        for (int hp = 0; hp < 4; ++hp) {
+            const float4 t = cs[hp];
+            const float o0 = __shfl_xor(dk[2 * hp], 4, 64), o1 = __shfl_xor(dk[2 * hp + 1], 4, 64);
+            out[2 * hp] = fmaf(sg * o0, t.y, dk[2 * hp] * t.x);
+            out[2 * hp + 1] = fmaf(sg * o1, t.w, dk[2 * hp + 1] * t.z);
+        }
+        const int64_t krow = (static_cast<int64_t>(bg) * L + j) * kD + 8 * e;
+        store_nt(static_cast<bf16_t*>(A.dk) + krow, make_uint4(pack_bf2(out[0], out[1]), pack_bf2(out[2], out[3]),
+                                                                 pack_bf2(out[4], out[5]), pack_bf2(out[6], out[7])));
+        store_nt(static_cast<bf16_t*>(A.dv) + krow, make_uint4(pack_bf2(dv[0], dv[1]), pack_bf2(dv[2], dv[3]),
+                                                                 pack_bf2(dv[4], dv[5]), pack_bf2(dv[6], dv[7])));
+    }
+}
+
 // ------------------------------------------------------------------------------------------------
 // bwd_q_mfma
 // ------------------------------------------------------------------------------------------------
@@ -67,6 +377,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     __shared__ __attribute__((aligned(1024))) char lds0[2 * kBufBytes];
     __shared__ __attribute__((aligned(1024))) char lds1[2 * kBufBytes];
     __shared__ float red[4][MAXK];
+    __shared__ int ered[4][4][3];                       // [wave][head]: largest exponents of q, do, dS
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -125,6 +436,8 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     };
     uint4 qraw[8], draw[8];
     float4 ctq[4];                                      // cos/sin of pairs 8x..8x+7 at position i
+    int eq, ed;                                         // the row exponents of q and do (0 for a zero row)
+    int outside;                                        // uniform: a staged row lies outside fp16's range
     {
         // the 4 heads' rows (4 L rows of 128 bytes: within 32 bits for L <= 2^20); positions past
         // L read row L - 1 (finite, never used)
@@ -144,6 +457,8 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(active ? i : 0) * (kPairs / 2) + 4 * x;
 #pragma unroll
         for (int u = 0; u < 4; ++u) ctq[u] = ct[u];
+        // the range flags of the staged key and value rows this tile reads (in flight with q, do)
+        const bool flagged = rows_flagged(A, bg / kPrepRowGroup, i0, n_reach);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -151,9 +466,34 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             draw[c] = *reinterpret_cast<const uint4*>(rd + row_view_addr(pq, x, c));
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();                   // every wave is done with its rows
+        // row exponents (|q_rot| <= sqrt(2) max|q|: one more binade of headroom) and each head's
+        // largest over the wave's positions
+        eq = floor_log2(max_abs_bf16_row(qraw));
+        ed = floor_log2(max_abs_bf16_row(draw));
+        {
+            const int mq = head_max(active ? eq : kNoExp), md = head_max(active ? ed : kNoExp);
+            if (pq == 0) {
+                ered[wave][x][0] = mq;
+                ered[wave][x][1] = md;
+            }
+        }
+        if (eq == kNoExp) eq = 0;
+        if (ed == kNoExp) ed = 0;
+        // every wave is done with its rows (the barrier), and whether a staged row this tile reads
+        // lies outside fp16's range: then its outputs come from the float32 tile at the end
+        outside = __builtin_amdgcn_readfirstlane(__syncthreads_or(flagged ? 1 : 0));
         asm volatile("" ::: "memory");
+        // then bwd_fp32_kernel writes dq and the partials, and the key tiles that read this tile's
+        // hand-off (marked here) leave theirs to it too
+        if (outside && threadIdx.x < 4)
+            A.exps[(static_cast<int64_t>(b) * A.Hq + h0 + x) * n_tiles + tile] = kExpsFallback;
     }
+    // head x's largest q and do exponents over the tile (read from LDS where needed: registers
+    // are short here)
+    auto tile_exp = [&](int k) {
+        const int f = max(max(ered[0][x][k], ered[1][x][k]), max(ered[2][x][k], ered[3][x][k]));
+        return f == kNoExp ? 0 : f;
+    };
     st.near(krs, lds0, jn);
     st.near(hrs, lds0 + kBufBytes, jn);
     kv_step(lds1, kn);
@@ -163,7 +503,9 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     // also keeps what the fp16 rounding left out (ql, same layout).
     uint32_t q[8][4];
     uint32_t ql[PRECISE ? 8 : 1][4];
+    const float qsc = A.qscale * pow2f(eq);             // the score scale of the lane's scaled row
     {
+        const float sq = pow2f(-eq);
         float r[kD];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -175,10 +517,10 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
                 const float x0 = bf16_lo(lw[m]), x1 = bf16_hi(lw[m]);
                 const float y0 = bf16_lo(hw[m]), y1 = bf16_hi(hw[m]);
                 const int j = 8 * c + 2 * m;
-                r[j] = x0 * t.x - y0 * t.y;
-                r[j + 1] = x1 * t.z - y1 * t.w;
-                r[j + 32] = y0 * t.x + x0 * t.y;
-                r[j + 33] = y1 * t.z + x1 * t.w;
+                r[j] = (x0 * t.x - y0 * t.y) * sq;
+                r[j + 1] = (x1 * t.z - y1 * t.w) * sq;
+                r[j + 32] = (y0 * t.x + x0 * t.y) * sq;
+                r[j + 33] = (y1 * t.z + x1 * t.w) * sq;
             }
         }
 #pragma unroll
@@ -202,10 +544,11 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             const uint32_t v = w == 0 ? r.x : w == 1 ? r.y : w == 2 ? r.z : r.w;
             return (d & 1) ? bf16_hi(v) : bf16_lo(v);
         };
+        const float sdo = pow2f(-ed);                   // do / 2^ed
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
-            dov[m >> 1][2 * (m & 1)] = pack_h2(dim(m), dim(16 + m));
-            dov[m >> 1][2 * (m & 1) + 1] = pack_h2(dim(32 + m), dim(48 + m));
+            dov[m >> 1][2 * (m & 1)] = pack_h2(dim(m) * sdo, dim(16 + m) * sdo);
+            dov[m >> 1][2 * (m & 1) + 1] = pack_h2(dim(32 + m) * sdo, dim(48 + m) * sdo);
         }
     }
     publish<12>();                                      // the key and value near blocks have landed
@@ -223,8 +566,8 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             const int n = 2 * k + e;
             if (n < n_reach) {
                 const float t = A.off[n].t;
-                const float dd = (acc[2 * e + 1] - acc[2 * e]) * A.qscale;
-                const float sc = fmaf(t, dd, acc[2 * e] * A.qscale);
+                const float dd = (acc[2 * e + 1] - acc[2 * e]) * qsc;
+                const float sc = fmaf(t, dd, acc[2 * e] * qsc);
                 const bool ok = active && i >= A.off[n].a + A.off[n].interp;
                 s[4 * kWG + n] = ok ? sc : kNegInf;
                 sd[n] = ok ? dd : 0.f;
@@ -271,7 +614,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int d = 4 * g + r;
-            s[d] = (active && d <= W && i >= d) ? acc[r] * A.qscale : kNegInf;
+            s[d] = (active && d <= W && i >= d) ? acc[r] * qsc : kNegInf;
             dp[d] = accv[r];
         }
     }
@@ -329,19 +672,27 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     // from here on the value halves of both buffers are free: 8 KB per wave
     char* const treg = (wave < 2 ? lds0 : lds1) + kBufBytes + (wave & 1) * 8192;
     // rotated q and do (fp16) for the key side, through treg: 1 KB contiguous stores (they count
-    // in vmcnt after the key DMAs; the wait before pass C counts them conservatively)
+    // in vmcnt after the key DMAs; the wait before pass C counts them conservatively). Each head's
+    // rows are scaled to a common power of two over the tile, q by 2^-tq and do by 2^-td (exps
+    // records tq, td for the key side)
+    if (!outside) {
+        const int tq = tile_exp(0), td = tile_exp(1);
+        const uint32_t fqh = pow2_h2(eq - tq, eq - tq), fdh = pow2_h2(ed - td, ed - td);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-            *reinterpret_cast<uint4*>(treg + row_view_addr(pq, x, c)) =
-                t ? make_uint4(dov[c][0], dov[c][1], dov[c][2], dov[c][3]) : make_uint4(q[c][0], q[c][1], q[c][2], q[c][3]);
+            for (int c = 0; c < 8; ++c)
+                *reinterpret_cast<uint4*>(treg + row_view_addr(pq, x, c)) =
+                    t ? make_uint4(mul_h2(dov[c][0], fdh), mul_h2(dov[c][1], fdh), mul_h2(dov[c][2], fdh),
+                                   mul_h2(dov[c][3], fdh))
+                      : make_uint4(mul_h2(q[c][0], fqh), mul_h2(q[c][1], fqh), mul_h2(q[c][2], fqh), mul_h2(q[c][3], fqh));
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const uint4 v = *reinterpret_cast<const uint4*>(treg + lin_view_addr(lane, u));
-            const int64_t row = lin_row(lin_slot(lane, u));
-            if (row >= 0)
-                *reinterpret_cast<uint4*>(static_cast<f16_t*>(t ? A.do16 : A.qrot16) + row * kD + (lane & 7) * 8) = v;
+            for (int u = 0; u < 8; ++u) {
+                const uint4 v = *reinterpret_cast<const uint4*>(treg + lin_view_addr(lane, u));
+                const int64_t row = lin_row(lin_slot(lane, u));
+                if (row >= 0)
+                    *reinterpret_cast<uint4*>(static_cast<f16_t*>(t ? A.do16 : A.qrot16) + row * kD + (lane & 7) * 8) = v;
+            }
         }
     }
 
@@ -373,11 +724,26 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         // (dS / sqrt(D)) sd ln2 sqrt(D) = dS (q . dk) / sqrt(D)
         dt[n] = fmaf(dp[4 * kWG + n] * (kLn2 / A.scale), sd[n], s[4 * kWG + n] * dpd[n]);
     }
-    // the key side's weights of this query: (p, dS/sqrt(D)) per window distance and per rung
-    // (without the rung's coefficients), fp16 pairs; stored at the end
-    uint32_t wq[4 * kWG + MAXK];
+    // dS/sqrt(D), dP and the dt terms are in units of 2^-ed (do was scaled by it): dt to true units
 #pragma unroll
-    for (int y = 0; y < 4 * kWG + MAXK; ++y) wq[y] = pack_p_ds(s[y], dp[y]);
+    for (int n = 0; n < MAXK; ++n) dt[n] *= pow2f(ed);
+    // the key side's weights of this query: (p, dS/sqrt(D)) per window distance and per rung
+    // (without the rung's coefficients), fp16 pairs, dS scaled by the row's 2^-es (its largest
+    // element in [1, 2)); stored at the end, once the tile's common exponent is known
+    int es;
+    {
+        float mxd = 0.f;
+#pragma unroll
+        for (int y = 0; y < 4 * kWG + MAXK; ++y) mxd = fmaxf(mxd, fabsf(dp[y]));
+        es = floor_log2(mxd);
+    }
+    uint32_t wq[4 * kWG + MAXK];
+    {
+        const float sds = pow2f(es == kNoExp ? 0 : -es);
+#pragma unroll
+        for (int y = 0; y < 4 * kWG + MAXK; ++y) wq[y] = pack_p_ds(s[y], dp[y] * sds);
+    }
+    es = (es == kNoExp || !active) ? kNoExp : es + ed;  // the row's dS exponent in true units
     // pass C weights: dS/sqrt(D) times the coefficients, fp16, groups of 4
     uint32_t ww[kWG][2], wo[MAXS][2];
 #pragma unroll
@@ -438,74 +804,8 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // (pass C read only the key halves: treg is still the wave's own)
-    // ---- the key side's weights: the window row of this query (64 bytes; through treg as 16
-    // rows per head, chunk c at c ^ x, 1 KB contiguous stores) and one entry of each rung's row
-    // (rung-major, so a wave's stores of one rung are contiguous) ----
-#pragma unroll
-    for (int c = 0; c < kNW / 4; ++c)
-        *reinterpret_cast<uint4*>(treg + (16 * x + pq) * (kNW * 4) + ((c ^ x) << 4)) =
-            make_uint4(wq[4 * c], wq[4 * c + 1], wq[4 * c + 2], wq[4 * c + 3]);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int sl = 16 * u + (lane >> 2), c = lane & 3;
-        const uint4 v = *reinterpret_cast<const uint4*>(treg + sl * (kNW * 4) + ((c ^ u) << 4));
-        const int64_t row = lin_row(sl);
-        if (row >= 0) *reinterpret_cast<uint4*>(A.wwin + row * kNW + 4 * c) = v;
-    }
-    if (active) {
-        uint32_t* rr = A.wrung + (static_cast<int64_t>(b) * A.Hq + h0 + x) * kNR * L + i;
-#pragma unroll
-        for (int n = 0; n < kNR; ++n) rr[static_cast<int64_t>(n) * L] = (n < MAXK) ? wq[4 * kWG + n] : 0u;
-    }
-    {
-        // ---- dq: RoPE transposed at position i. Lane x holds dims 16x + m of heads 0..3; the
-        // other half of pair (16x + m) mod 32 is in lane x ^ 2. Rows go through treg: 1 KB
-        // contiguous stores ----
-        // pair 16 (x & 1) + m: lane 2 (x & 1) + (m >> 3) holds it (each lane loads pairs
-        // 8x..8x+7), at entry (m & 7) >> 1 of its quarter
-        const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(active ? i : 0) * (kPairs / 2) + 4 * x;
-        float4 cq[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) cq[u] = ct[u];
-        float2 cs[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const float4& t = cq[(m & 7) >> 1];
-            const float c = (m & 1) ? t.z : t.x, sn = (m & 1) ? t.w : t.y;
-            cs[m] = (m < 8) ? make_float2(quad_f<kPerm0202>(c), quad_f<kPerm0202>(sn))
-                            : make_float2(quad_f<kPerm1313>(c), quad_f<kPerm1313>(sn));
-        }
-        const float sg = (x < 2) ? 1.f : -1.f;         // x' = x c + y s;  y' = y c - x s
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float v[16];
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                const float other = quad_f<kXor2>(o[m][r]);
-                v[m] = fmaf(sg * other, cs[m].y, o[m][r] * cs[m].x);
-            }
-            uint4 lo, hi;
-            lo.x = pack_bf2(v[0], v[1]);
-            lo.y = pack_bf2(v[2], v[3]);
-            lo.z = pack_bf2(v[4], v[5]);
-            lo.w = pack_bf2(v[6], v[7]);
-            hi.x = pack_bf2(v[8], v[9]);
-            hi.y = pack_bf2(v[10], v[11]);
-            hi.z = pack_bf2(v[12], v[13]);
-            hi.w = pack_bf2(v[14], v[15]);
-            *reinterpret_cast<uint4*>(treg + row_view_addr(pq, r, 2 * x)) = lo;
-            *reinterpret_cast<uint4*>(treg + row_view_addr(pq, r, 2 * x + 1)) = hi;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const uint4 v = *reinterpret_cast<const uint4*>(treg + lin_view_addr(lane, u));
-            const int64_t row = lin_row(lin_slot(lane, u));
-            if (row >= 0) store_nt(static_cast<bf16_t*>(A.dq) + row * kD + (lane & 7) * 8, v);
-        }
-    }
-
-    // ---- d(loss)/dt partial sums of this workgroup, fixed order ----
+    // ---- d(loss)/dt partial sums of this workgroup (fixed order), and each head's largest dS
+    // exponent over the tile ----
 #pragma unroll
     for (int n = 0; n < MAXK; ++n) {
         float v = active ? dt[n] : 0.f;
@@ -513,19 +813,158 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
         if (lane == 0) red[wave][n] = v;
     }
-    // an LDS-only barrier: the stores above need not have landed (__syncthreads would wait for
-    // every one of them)
+    {
+        const int ms = head_max(es);
+        if (pq == 0) ered[wave][x][2] = ms;
+    }
+    // an LDS-only barrier: the stores in flight need not have landed (__syncthreads would wait
+    // for every one of them)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (threadIdx.x < static_cast<unsigned>(A.n_off)) {
-        float v = 0.f;
-        if (threadIdx.x < MAXK) v = ((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) + red[3][threadIdx.x];
-        A.partial[static_cast<int64_t>(blockIdx.x) * kMaxOff + threadIdx.x] = v;
+    int ts = max(max(ered[0][x][2], ered[1][x][2]), max(ered[2][x][2], ered[3][x][2]));
+    if (ts == kNoExp) ts = 0;
 
+    if (!outside) {
+        // (pass C read only the key halves: treg is still the wave's own)
+        // ---- the key side's weights: dS scaled from the row's exponent to the tile's, 2^-ts; the
+        // window row of this query (64 bytes; through treg as 16 rows per head, chunk c at c ^ x,
+        // 1 KB contiguous stores) and one entry of each rung's row (rung-major, so a wave's stores
+        // of one rung are contiguous) ----
+        const uint32_t fs = pow2_h2(0, es == kNoExp ? 0 : es - ts);
+#pragma unroll
+        for (int y = 0; y < 4 * kWG + MAXK; ++y) wq[y] = mul_h2(wq[y], fs);
+#pragma unroll
+        for (int c = 0; c < kNW / 4; ++c)
+            *reinterpret_cast<uint4*>(treg + (16 * x + pq) * (kNW * 4) + ((c ^ x) << 4)) =
+                make_uint4(wq[4 * c], wq[4 * c + 1], wq[4 * c + 2], wq[4 * c + 3]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int sl = 16 * u + (lane >> 2), c = lane & 3;
+            const uint4 v = *reinterpret_cast<const uint4*>(treg + sl * (kNW * 4) + ((c ^ u) << 4));
+            const int64_t row = lin_row(sl);
+            if (row >= 0) *reinterpret_cast<uint4*>(A.wwin + row * kNW + 4 * c) = v;
+        }
+        if (active) {
+            uint32_t* rr = A.wrung + (static_cast<int64_t>(b) * A.Hq + h0 + x) * kNR * L + i;
+#pragma unroll
+            for (int n = 0; n < kNR; ++n) rr[static_cast<int64_t>(n) * L] = (n < MAXK) ? wq[4 * kWG + n] : 0u;
+        }
+        {
+            // ---- dq: to true units (head r's 2^ed from lane r of the quad), RoPE transposed at
+            // position i. Lane x holds dims 16x + m of heads 0..3; the other half of pair
+            // (16x + m) mod 32 is in lane x ^ 2. Rows go through treg: 1 KB contiguous stores ----
+            // pair 16 (x & 1) + m: lane 2 (x & 1) + (m >> 3) holds it (each lane loads pairs
+            // 8x..8x+7), at entry (m & 7) >> 1 of its quarter
+            const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(active ? i : 0) * (kPairs / 2) + 4 * x;
+            float4 cq[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) cq[u] = ct[u];
+            float2 cs[16];
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const float4& t = cq[(m & 7) >> 1];
+                const float c = (m & 1) ? t.z : t.x, sn = (m & 1) ? t.w : t.y;
+                cs[m] = (m < 8) ? make_float2(quad_f<kPerm0202>(c), quad_f<kPerm0202>(sn))
+                                : make_float2(quad_f<kPerm1313>(c), quad_f<kPerm1313>(sn));
+            }
+            const float edf = pow2f(ed);
+            const float eh[4] = {quad_f<kBcast0>(edf), quad_f<kBcast1>(edf), quad_f<kBcast2>(edf), quad_f<kBcast3>(edf)};
+            const float sg = (x < 2) ? 1.f : -1.f;         // x' = x c + y s;  y' = y c - x s
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v[16];
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                    const float other = quad_f<kXor2>(o[m][r]);
+                    v[m] = fmaf(sg * other, cs[m].y, o[m][r] * cs[m].x) * eh[r];
+                }
+                uint4 lo, hi;
+                lo.x = pack_bf2(v[0], v[1]);
+                lo.y = pack_bf2(v[2], v[3]);
+                lo.z = pack_bf2(v[4], v[5]);
+                lo.w = pack_bf2(v[6], v[7]);
+                hi.x = pack_bf2(v[8], v[9]);
+                hi.y = pack_bf2(v[10], v[11]);
+                hi.z = pack_bf2(v[12], v[13]);
+                hi.w = pack_bf2(v[14], v[15]);
+                *reinterpret_cast<uint4*>(treg + row_view_addr(pq, r, 2 * x)) = lo;
+                *reinterpret_cast<uint4*>(treg + row_view_addr(pq, r, 2 * x + 1)) = hi;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint4 v = *reinterpret_cast<const uint4*>(treg + lin_view_addr(lane, u));
+                const int64_t row = lin_row(lin_slot(lane, u));
+                if (row >= 0) store_nt(static_cast<bf16_t*>(A.dq) + row * kD + (lane & 7) * 8, v);
+            }
+        }
+        if (threadIdx.x < static_cast<unsigned>(A.n_off)) {
+            float v = 0.f;
+            if (threadIdx.x < MAXK) v = ((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) + red[3][threadIdx.x];
+            A.partial[static_cast<int64_t>(blockIdx.x) * kMaxOff + threadIdx.x] = v;
+        }
+        // the tile's exponents of head x for the key side
+        if (threadIdx.x < 4)
+            A.exps[(static_cast<int64_t>(b) * A.Hq + h0 + x) * n_tiles + tile] = pack_exps(tile_exp(0), tile_exp(1), ts);
     }
 }
 
+// ------------------------------------------------------------------------------------------------
+// bwd_fp32: the float32 tiles, after the matrix-core kernels. Workgroups below n_qwg are query tiles
+// (plain order; a tile runs when it reads a flagged staged row, as bwd_q_mfma decides), the others
+// key tiles (a tile runs when a query tile it reads from is marked, as bwd_k_dot decides); every
+// other workgroup leaves at once.
+// ------------------------------------------------------------------------------------------------
+// Whether key tile `tile` of (b, g) reads from a query tile that left its outputs to the float32
+// tiles: the exps words of every query tile its terms read (window and near pairs: t0 .. t0 + 2;
+// rung n: ((j0 + a_n) >> 6) + 0, 1).
+__device__ __forceinline__ bool key_tile_marked(const BwdArgs& A, int b, int g, int tile, int n_reach, int n_tiles) {
+    const int t = threadIdx.x;
+    const int slots = 3 + 2 * n_reach;
+    bool marked = false;
+    for (int e = t; e < A.G * slots; e += kNT) {
+        const int hh = e / slots, sl = e % slots;
+        int tl = tile + sl;
+        if (sl >= 3) tl = ((tile * kTile + A.off[(sl - 3) >> 1].a) >> 6) + ((sl - 3) & 1);
+        if (tl < n_tiles)
+            marked |= (A.exps[(static_cast<int64_t>(b) * A.Hq + g * A.G + hh) * n_tiles + tl] & kExpsFallback) != 0u;
+    }
+    return __syncthreads_or(marked ? 1 : 0) != 0;
+}
+
+__global__ __launch_bounds__(kNT) void bwd_fp32_kernel(BwdArgs A, int n_qwg) {
+    __shared__ __attribute__((aligned(16))) char lds[kTile * 16 * 4];
+    const int L = A.L;
+    const int n_tiles = (L + kTile - 1) / kTile;
+    if (static_cast<int>(blockIdx.x) < n_qwg) {
+        // the matrix-core query kernel's tile order (its xcd_map is 0 or 1, which does not depend on
+        // the grid's size): workgroup blockIdx.x takes the tile, and the partials slot, of that
+        // kernel's workgroup blockIdx.x
+        const int n_chunk = A.G >> 2;
+        int unit, tile;
+        unit_tile(blockIdx.x, n_tiles, A.xcd_map, unit, tile);
+        const int chunk = unit % n_chunk;
+        const int bg = unit / n_chunk;
+        const int b = bg / A.Hkv;
+        const int h0 = (bg % A.Hkv) * A.G + chunk * 4;
+        const int i0 = tile * kTile;
+        int n_reach = 0;
+        for (int n = 0; n < A.n_off; ++n)
+            if (i0 + kTile - 1 >= A.off[n].a + A.off[n].interp) n_reach = n + 1;
+        if (!__syncthreads_or(rows_flagged(A, bg / kPrepRowGroup, i0, n_reach) ? 1 : 0)) return;
+        bwd_q_tile_fp32(A, b, bg, h0, i0, lds);
+    } else {
+        const int w = blockIdx.x - n_qwg;
+        const int bg = w / n_tiles, tile = w % n_tiles;
+        const int b = bg / A.Hkv, g = bg % A.Hkv;
+        const int j0 = tile * kTile;
+        int n_reach = 0;
+        for (int n = 0; n < A.n_off; ++n)
+            if (j0 + A.off[n].a < L) n_reach = n + 1;
+        if (!key_tile_marked(A, b, g, tile, n_reach, n_tiles)) return;
+        bwd_k_tile_fp32(A, b, bg, g, j0);
+    }
+}
 // ------------------------------------------------------------------------------------------------
 // bwd_k_dot
 // ------------------------------------------------------------------------------------------------
@@ -543,6 +982,11 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     // the (p, dS) entries of a step's two rungs for queries j0 + a + 0..127 (step s: buffer s % 2),
     // staged by the item before the step's own
     __shared__ uint32_t went[2][2][128];
+    // per head and query-tile slot: the factors (2^(td - Ev) low, 2^(ts + tq - Ek) high, fp16) that
+    // bring the query side's per-tile scaling to the workgroup's common one (see below)
+    constexpr int kSlotsF = 3 + 2 * 2 * MAXS;
+    __shared__ uint32_t fac[kMaxGKey][kSlotsF];
+    __shared__ int emax[3];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -622,13 +1066,6 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     // rung step weights: thread (row wrow, part wv) builds one word of wst for key row j0 + wrow:
     // rung 2k + (wv & 1), dS halves (wv < 2) or p halves, (near, far) times (1 - t, t)
     const int wrow = threadIdx.x >> 2, wv = threadIdx.x & 3;
-    auto put_w = [&](int k) {
-        const float t = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].t, A.off[2 * k].t);
-        const uint32_t en = went[k & 1][wv & 1][wrow], ef = went[k & 1][wv & 1][wrow + 1];
-        const uint32_t pr = __builtin_amdgcn_perm(ef, en, (wv >> 1) ? 0x05040100u : 0x07060302u);
-        const h2_t c = {static_cast<_Float16>(1.f - t), static_cast<_Float16>(t)};
-        reinterpret_cast<uint32_t*>(&wst[k & 1][wrow])[wv] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, pr) * c);
-    };
 
     // 4 terms of key rows 16w + 4 lg + q at block nb: the lane reads (as a source) term te's row
     // at element block tb and receives the 4 terms' element E(nb, lr); two v_dot2 per element.
@@ -662,7 +1099,102 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
         }
     };
 
+    // ---- the query side scaled each head's rows of a query tile by powers of two of the tile's
+    // own (q by 2^-tq, do by 2^-td, dS by 2^-ts; exps). Per head, slot s < 3 is query tile t0 + s
+    // (the window and the near pairs), slot 3 + 2n + u is tile ((j0 + a_n) >> 6) + u (rung n). Ev
+    // and Ek are the largest td and ts + tq over the workgroup's heads and slots, and each weight
+    // takes its query tile's factor 2^(td - Ev) (p) or 2^(ts + tq - Ek) (dS), at most 1: dv and dk
+    // accumulate in units of 2^-Ev and 2^-Ek, scaled back at the end. Wave 0 loads the exponents
+    // ahead of the first near item's DMAs and builds the table behind them. ----
+    const int t0 = tile;
+    constexpr int kFacLoads = (kMaxGKey * kSlotsF + 63) / 64;
+    uint32_t ew[kFacLoads];
+    if (wave == 0) {
+#pragma unroll
+        for (int r = 0; r < kFacLoads; ++r) {
+            const int e = lane + 64 * r;
+            const int hh = e / kSlotsF, sl = e % kSlotsF;
+            int tl = t0 + sl;
+            bool ok = hh < A.G;
+            if (sl >= 3) {
+                const int n = (sl - 3) >> 1;
+                int a = 0;
+#pragma unroll
+                for (int m = 0; m < 2 * MAXS; ++m) a = (n == m) ? A.off[m].a : a;   // uniform table, lane's pick
+                tl = ((j0 + a) >> 6) + ((sl - 3) & 1);
+                ok = ok && n < n_reach;
+            }
+            ok = ok && tl < n_tiles;
+            ew[r] = ok ? A.exps[(static_cast<int64_t>(b) * A.Hq + g * A.G + hh) * n_tiles + tl] : 0xffffffffu;
+        }
+    }
     near_item(g * A.G);
+    if (wave == 0) {
+        int mv = kNoExp, mk = kNoExp, marked = 0;
+#pragma unroll
+        for (int r = 0; r < kFacLoads; ++r) {
+            if (ew[r] != 0xffffffffu) {
+                mv = max(mv, exps_td(ew[r]));
+                mk = max(mk, exps_ts(ew[r]) + exps_tq(ew[r]));
+                marked |= (ew[r] & kExpsFallback) ? 1 : 0;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            mv = max(mv, __shfl_xor(mv, off, 64));
+            mk = max(mk, __shfl_xor(mk, off, 64));
+            marked |= __shfl_xor(marked, off, 64);
+        }
+        if (mv == kNoExp) mv = 0;
+        if (mk == kNoExp) mk = 0;
+#pragma unroll
+        for (int r = 0; r < kFacLoads; ++r) {
+            const int e = lane + 64 * r;
+            if (e < kMaxGKey * kSlotsF)
+                fac[e / kSlotsF][e % kSlotsF] =
+                    (ew[r] == 0xffffffffu) ? 0u : pow2_h2(exps_td(ew[r]) - mv, exps_ts(ew[r]) + exps_tq(ew[r]) - mk);
+        }
+        if (lane == 0) {
+            emax[0] = mv;
+            emax[1] = mk;
+            emax[2] = marked;
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // an LDS-only barrier: the DMAs stay in flight
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (__builtin_amdgcn_readfirstlane(emax[2])) {
+        // a query tile this tile reads from left its hand-off to the float32 tiles: so does this
+        // one (bwd_fp32_kernel); the staging in flight lands before the workgroup leaves
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        return;
+    }
+    const int Ev = emax[0], Ek = emax[1];
+    // the factor of one entry half: p (use_p) or dS, of head hh's slot sl, as an fp16 in the low 16 bits
+    auto fac_half = [&](int hh, int sl, bool use_p) -> uint32_t {
+        const uint32_t f = fac[hh][sl];
+        return use_p ? (f & 0xffffu) : (f >> 16);
+    };
+    // (1 - t, t) times the factors of the near and far query rows of rung n for key row j0 + wrow
+    auto coef = [&](int hh, int n, int a, float t, bool use_p) -> h2_t {
+        const int qn = j0 + wrow + a;
+        const int base = (n < 2 * kn) ? -t0 : 3 + 2 * n - ((j0 + a) >> 6);
+        const uint32_t f = fac_half(hh, base + (qn >> 6), use_p) | (fac_half(hh, base + ((qn + 1) >> 6), use_p) << 16);
+        const h2_t c = {static_cast<_Float16>(1.f - t), static_cast<_Float16>(t)};
+        return c * __builtin_bit_cast(h2_t, f);
+    };
+    // rung step weights of head hh: thread (row wrow, part wv) builds one word of wst for key row
+    // j0 + wrow: rung 2k + (wv & 1), dS halves (wv < 2) or p halves, (near, far) times (1 - t, t)
+    // and the query tiles' factors
+    auto put_w = [&](int hh, int k) {
+        const float t = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].t, A.off[2 * k].t);
+        const int a = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a);
+        const uint32_t en = went[k & 1][wv & 1][wrow], ef = went[k & 1][wv & 1][wrow + 1];
+        const uint32_t pr = __builtin_amdgcn_perm(ef, en, (wv >> 1) ? 0x05040100u : 0x07060302u);
+        const h2_t c = coef(hh, 2 * k + (wv & 1), a, t, (wv >> 1) != 0);
+        reinterpret_cast<uint32_t*>(&wst[k & 1][wrow])[wv] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, pr) * c);
+    };
+
     for (int hh = 0; hh < A.G; ++hh) {
         const int h = g * A.G + hh;
         const int64_t hrow0 = (static_cast<int64_t>(b) * A.Hq + h) * L;
@@ -707,8 +1239,9 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
         for (int k = 0; k < 4; ++k) {
             if (k < kn) {
                 const float t = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].t, A.off[2 * k].t);
+                const int a = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a);
                 const uint32_t pr = __builtin_amdgcn_perm(efr[k], enr[k], (wv >> 1) ? 0x05040100u : 0x07060302u);
-                const h2_t c = {static_cast<_Float16>(1.f - t), static_cast<_Float16>(t)};
+                const h2_t c = coef(hh, 2 * k + (wv & 1), a, t, (wv >> 1) != 0);
                 reinterpret_cast<uint32_t*>(&wnear(k)[wrow])[wv] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, pr) * c);
             }
         }
@@ -720,7 +1253,11 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
         {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const uint32_t (&e4)[4] = e4w[kb];
+                // each query's (p, dS) pair times its query tile's factors
+                uint32_t e4[4];
+#pragma unroll
+                for (int ee = 0; ee < 4; ++ee)
+                    e4[ee] = mul_h2(e4w[kb][ee], fac[hh][((j0 + 16 * wave + 16 * kb + 4 * lg + ee) >> 6) - t0]);
                 // (p, dS) pairs: dS in the high halves (dk), p in the low halves (dv)
                 const u2_t a_dk = {__builtin_amdgcn_perm(e4[1], e4[0], 0x07060302u),
                                    __builtin_amdgcn_perm(e4[3], e4[2], 0x07060302u)};
@@ -752,7 +1289,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
                 sum_rungs(dv, w, true, lds0 + kBufBytes, nadr);
             }
         }
-        put_w(kn);
+        put_w(hh, kn);
         publish<0>();                                   // far pair kn and its weights are in place, lds0 is free
 
         // ---- far steps: pair k (kn <= k < n_far) in lds(k + 1) % 2 ----
@@ -773,12 +1310,21 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
                     sum_rungs(dk, w, false, buf(k + 1), radr);
                     sum_rungs(dv, w, true, buf(k + 1) + kBufBytes, radr);
                 }
-                if (k + 1 < n_steps) put_w(k + 1);
+                if (k + 1 < n_steps) put_w(hh, k + 1);
                 publish<0>();
             }
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // to true units (the weights carried 2^-Ek and 2^-Ev)
+    {
+        const float fk = pow2f(Ek), fv = pow2f(Ev);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            dk[nb] *= fk;
+            dv[nb] *= fv;
+        }
+    }
 
     // ---- dk: RoPE transposed at each key position. Element 4m + c of the permuted rows is dim
     // 16c + m; the lane's element E = 8 ch + 4 (b' & 1) + c is dim 16c + 2 ch + (b' & 1); its
@@ -838,7 +1384,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
 }  // namespace
 
 bool bwd_mfma_supported(const BwdArgs& A) {
-    return A.G % 4 == 0 && A.W <= 15 && A.n_off <= 16;
+    return A.G % 4 == 0 && A.G <= kMaxGKey && A.W <= 15 && A.n_off <= 16;
 }
 
 hipError_t launch_bwd_mfma(const BwdArgs& A0, bool want_dalpha, int stages, hipStream_t s) {
@@ -847,24 +1393,37 @@ hipError_t launch_bwd_mfma(const BwdArgs& A0, bool want_dalpha, int stages, hipS
     const int64_t q_units = static_cast<int64_t>(A.B) * A.Hkv * (A.G / 4);
     const int64_t k_units = static_cast<int64_t>(A.B) * A.Hkv;
     A.n_wg = static_cast<int32_t>(q_units * n_tiles);
+    const int q_map = (q_units % 8 == 0) ? 1 : 0;
+    hipError_t e;
     if (stages & kStageQuery) {
-        A.xcd_map = (q_units % 8 == 0) ? 1 : 0;
+        A.xcd_map = q_map;
         const dim3 grid(static_cast<unsigned>(q_units * n_tiles));
         if (want_dalpha)
             hipLaunchKernelGGL((bwd_q_mfma_kernel<8, true>), grid, dim3(kNT), 0, s, A);
         else
             hipLaunchKernelGGL((bwd_q_mfma_kernel<8, false>), grid, dim3(kNT), 0, s, A);
-        const hipError_t e = hipGetLastError();
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (stages & kStageKey) {
         A.xcd_map = (k_units % 8 == 0) ? 1 : 0;
         hipLaunchKernelGGL((bwd_k_dot_kernel<8>), dim3(static_cast<unsigned>(k_units * n_tiles)), dim3(kNT), 0, s,
                            A);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess || !want_dalpha) return e;
-        return launch_dalpha(A, s);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
+    // the float32 tiles of the stages run here (their workgroups leave at once where no staged row
+    // lies outside fp16's range)
+    {
+        A.xcd_map = q_map;
+        const int64_t n_q = (stages & kStageQuery) ? q_units * n_tiles : 0;
+        const int64_t n_k = (stages & kStageKey) ? k_units * n_tiles : 0;
+        hipLaunchKernelGGL(bwd_fp32_kernel, dim3(static_cast<unsigned>(n_q + n_k)), dim3(kNT), 0, s, A,
+                           static_cast<int>(n_q));
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if ((stages & kStageKey) && want_dalpha) return launch_dalpha(A, s);
     return hipSuccess;
 }
 

@@ -121,6 +121,9 @@ struct BwdArgs {
     // ([B, Hq, kNR, L])
     uint32_t* wwin;
     uint32_t* wrung;
+    // per (batch, head, query tile): the powers of two the query side scaled that tile's hand-off
+    // by (q, do, dS; bytes of one word)
+    uint32_t* exps;
     float qscale;        // log2(e)/sqrt(D)
     int32_t xcd_map;
 };

@@ -274,5 +274,58 @@ __device__ __forceinline__ void unit_tile(int w, int n_tiles, int xcd_map, int& 
     }
 }
 
+// ---- rows outside fp16's range, and the float32 tiles that take them ----
+// fp16 holds a row exactly enough only inside a range: every element below 2^15 in magnitude
+// (65504 is fp16's largest) and, unless the row is zero, a row maximum of at least 2^-10 (below
+// that the row's largest elements come near fp16's subnormals, 2^-14, where relative precision is
+// lost).
+constexpr float kFp16Big = 32768.0f;               // 2^15
+constexpr float kFp16Small = 0.0009765625f;        // 2^-10
+
+// Sum over the 8 lanes 8p' .. 8p' + 7 (an 8-lane group holds a row in the float32 tiles).
+__device__ __forceinline__ float oct_sum(float v) {
+    v += quad_f<0xB1>(v);                               // quad_perm [1, 0, 3, 2]
+    v += quad_f<kXor2>(v);                              // quad_perm [2, 3, 0, 1]
+    v += quad_f<0x141>(v);                              // row_half_mirror: the other quad of the 8
+    return v;
+}
+
+// Dims 8e .. 8e + 7 of a bf16 row, rotated at position j (cos/sin from the table). Dim d pairs
+// with d + 32 (e < 4: x' = x cos - y sin) or d - 32 (e >= 4: y' = y cos + x sin): dims of e ^ 4.
+__device__ __forceinline__ void rot_eighth(const bf16_t* row, const float* cstab, int j, int e, float (&out)[8]) {
+    const float sg = (e < 4) ? -1.f : 1.f;
+    const uint4 ow = reinterpret_cast<const uint4*>(row)[e];
+    const uint4 pw = reinterpret_cast<const uint4*>(row)[e ^ 4];
+    const float4* cs = reinterpret_cast<const float4*>(cstab + static_cast<int64_t>(j) * 2 * kPairs + 16 * (e & 3));
+    const uint32_t o4[4] = {ow.x, ow.y, ow.z, ow.w}, p4[4] = {pw.x, pw.y, pw.z, pw.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const float4 t = cs[h];                          // (cos, sin) of dims 8e + 2h, + 1
+        out[2 * h] = fmaf(sg * bf16_lo(p4[h]), t.y, bf16_lo(o4[h]) * t.x);
+        out[2 * h + 1] = fmaf(sg * bf16_hi(p4[h]), t.w, bf16_hi(o4[h]) * t.z);
+    }
+}
+
+// The range flag of the staged rows that thread t of a tile checks: threads 0..3 the near block
+// (rows i0 - 64 .. i0 + 63), thread 4 + 4n + u the u-th flag block of kept rung n's rows
+// i0 - a - 1 .. i0 + 63 - a (clipped at 0), for rungs the tile reaches; every other thread none.
+template <typename Args>
+__device__ __forceinline__ bool rows_flagged(const Args& A, int grp, int i0, int n_reach) {
+    const int t = threadIdx.x;
+    int blk = -1;
+    if (t < 4) {
+        blk = i0 / kFlagRows - 2 + t;
+    } else if (t < 4 + 4 * kMaxOff) {
+        const int n = (t - 4) >> 2, u = (t - 4) & 3;
+        if (n < n_reach) {
+            const int a = A.off[n].a;
+            const int lo = max(i0 - a - 1, 0), hi = min(i0 + kTile - 1 - a, A.L - 1);
+            if (lo / kFlagRows + u <= hi / kFlagRows) blk = lo / kFlagRows + u;
+        }
+    }
+    if (blk < 0 || blk >= A.n_blk) return false;
+    return A.kvflags[static_cast<int64_t>(grp) * A.n_blk + blk] != 0u;
+}
+
 }  // namespace mx
 }  // namespace fibattn

@@ -312,3 +312,52 @@ def test_maximum_length_sampled_rows():
     n64 = [x[:, :, L - 3000:].double().numpy() for x in (q, k, v)]
     o_ref, _ = O.forward(*n64, alpha, W, O.FIB_BASE)
     check(od.cpu(), o_ref[:, :, -1], q.dtype, what="L=2^20 decode")
+
+
+# ---- inputs and gradients far from the unit scale: q and do are carried as row / 2^e in fp16
+# (exact power-of-two scaling, undone in float32), the query side's hand-off to the key side per
+# tile likewise; tiles that read key or value rows outside fp16's range are computed in float32 ----
+
+def _close(gpu, ref, what):
+    # bf16 outputs: within 2^-8 of their own magnitude plus 2e-3 of the tensor's scale
+    g, r = gpu.double().numpy(), ref
+    assert np.all(np.isfinite(g)), f"{what}: non-finite"
+    bound = 2.0 ** -8 * np.abs(r) + 2e-3 * np.abs(r).max()
+    assert np.all(np.abs(g - r) <= bound), f"{what}: max excess {np.max(np.abs(g - r) - bound):.3e} (scale {np.abs(r).max():.3e})"
+
+
+@pytest.mark.parametrize("scales", [
+    (1.0, 1.0, 1.0, 2.0 ** -20),     # gradients of a loss averaged over many tokens
+    (1.0, 1.0, 1.0, 2.0 ** 20),
+    (3e5, 3e-6, 1.0, 1.0),           # q far above fp16's range (k far below: the float32 tiles)
+    (1.0, 1.0, 3e5, 2.0 ** -10),     # values far above
+    (1e-6, 1e-6, 1e-6, 1e-6),        # everything far below
+])
+def test_inputs_and_gradients_far_from_unit_scale(scales):
+    L = 300
+    sh = [(1, 8, L, 64), (1, 2, L, 64), (1, 2, L, 64), (1, 8, L, 64)]
+    q, k, v, do = ((workloads.randn_like_seeded(s_, 110 + i) * f).to(torch.bfloat16) for i, (s_, f) in
+                   enumerate(zip(sh, scales)))
+    th = 0.37
+    alpha, dadt = O.alpha_from_theta(th), O.dalpha_dtheta(th)
+    say(f"bwd scales q,k,v,do x {scales}")
+    dq, dk, dv, da, dth = run(q, k, v, do, alpha, 9, O.FIB_BASE, True, dadt)
+    n64 = [x.double().numpy() for x in (q, k, v, do)]
+    rq, rk, rv, ra = O.backward(*n64, alpha, 9, O.FIB_BASE)
+    _close(dq, rq, "dq")
+    _close(dk, rk, "dk")
+    _close(dv, rv, "dv")
+    assert abs(da - ra) <= 1e-3 * abs(ra), (da, ra)
+    assert abs(dth - ra * dadt) <= 1e-3 * abs(ra * dadt), (dth, ra * dadt)
+
+
+def test_one_value_outside_fp16_range_backward():
+    # one value element of 1e5 at row 211 of KV head 1: the query tiles that read its block take the
+    # float32 tile, the others the matrix cores; their hand-offs to the key side (scaled per tile)
+    # meet in the key rows both reach
+    L = 400
+    q, k, v, do = (randn(s_, 120 + i, torch.bfloat16) for i, s_ in
+                   enumerate([(2, 8, L, 64), (2, 2, L, 64), (2, 2, L, 64), (2, 8, L, 64)]))
+    v[1, 1, 211, 5] = 1e5
+    say("bwd one value of 1e5")
+    compare(q, k, v, do, 0.77, 8, O.FIB_BASE, "one big value", want_dalpha=False)
