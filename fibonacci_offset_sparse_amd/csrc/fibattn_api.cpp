@@ -125,6 +125,8 @@ fibattn_status_t check_dims(int32_t B, int32_t L, int32_t Hq, int32_t Hkv, int32
     if (W > FIBATTN_MAX_W) return fail(FIBATTN_ERR_UNSUPPORTED, "W = %d > %d", W, FIBATTN_MAX_W);
     if (L > kMaxL) return fail(FIBATTN_ERR_UNSUPPORTED, "L = %d > %d", L, kMaxL);
     if (B > 65535 || Hq > 65535) return fail(FIBATTN_ERR_UNSUPPORTED, "B or Hq above 65535");
+    if (static_cast<int64_t>(B) * Hkv > 4 * 65535)
+        return fail(FIBATTN_ERR_UNSUPPORTED, "B * Hkv above %d", 4 * 65535);
     return FIBATTN_OK;
 }
 
@@ -160,7 +162,7 @@ uint32_t* flags_at(void* ws, int32_t B, int32_t L, int32_t Hkv) {
 // cos/sin table (the forward's layout of the same sizes), the rotated queries (fp16), the per key
 // row term weights, and the per-workgroup d(loss)/dt partials.
 struct BwdFastLayout {
-    size_t qrot, do16, wwin, wrung, part, klo, exps, total;
+    size_t qrot, do16, wwin, wrung, part, klo, exps, seqw, total;
 };
 BwdFastLayout bwd_fast_layout(int32_t B, int32_t L, int32_t Hq, int32_t Hkv) {
     BwdFastLayout f;
@@ -174,7 +176,9 @@ BwdFastLayout bwd_fast_layout(int32_t B, int32_t L, int32_t Hq, int32_t Hkv) {
     // low parts of the rotated keys (fp16), for the precise scores of a call that asks for d(alpha)
     f.exps = f.klo + align256(half_rows_bytes(B, L, Hkv));
     // the query tiles' scale exponents [B, Hq, tiles]
-    f.total = f.exps + align256(static_cast<size_t>(B) * Hq * ((L + kTile - 1) / kTile) * sizeof(uint32_t));
+    f.seqw = f.exps + align256(static_cast<size_t>(B) * Hq * ((L + kTile - 1) / kTile) * sizeof(uint32_t));
+    // two call numbers: the last query stage run over this workspace, the last one with float32 tiles
+    f.total = f.seqw + 256;
     return f;
 }
 
@@ -558,6 +562,7 @@ fibattn_status_t fibattn_bwd_stages(int32_t stages, const void* q, const void* k
             a.wrung = reinterpret_cast<uint32_t*>(w0 + f.wrung);
             a.partial = reinterpret_cast<float*>(w0 + f.part);
             a.exps = reinterpret_cast<uint32_t*>(w0 + f.exps);
+            a.seqw = reinterpret_cast<uint64_t*>(w0 + f.seqw);
             // with d(alpha) requested the query stage takes precise scores, from the low parts of
             // the rotated keys as well: written with the prep when both run in this call, else
             // by a pass of their own ahead of the query stage

@@ -36,6 +36,9 @@
 // rows and weights the query side writes for the key side keep plain stores, since the key side
 // reads them right after (hinting them cost the key side more than it saved).
 // No atomics: results are bitwise reproducible.
+#include <algorithm>
+#include <atomic>
+
 #include "fibattn_mfma.h"
 
 namespace fibattn {
@@ -81,16 +84,16 @@ __device__ __forceinline__ uint32_t pow2_h2(int e_lo, int e_hi) {
 __device__ __forceinline__ uint32_t mul_h2(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, a) * __builtin_bit_cast(h2_t, b));
 }
-__device__ __forceinline__ float max_abs_bf16_row(const uint4 (&r)[8]) {
-    float mx = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const uint32_t w[4] = {r[c].x, r[c].y, r[c].z, r[c].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
-    }
-    return mx;
+// floor(log2) of a largest magnitude given as bf16 bits (kNoExp for 0), clamped as floor_log2
+__device__ __forceinline__ int floor_log2_bits(uint32_t m) {
+    if (m == 0u) return kNoExp;
+    return min(max(static_cast<int>(m >> 7) - 127, -126), 126);
 }
+// A row's scaling exponent where fp16 holds rows with a largest magnitude in [2^-10, 2^15) well as
+// they are: 0 there, else floor(log2) (the row scaled into [1, 2)); kNoExp stays.
+__device__ __forceinline__ int banded(int e) { return (e >= -10 && e <= 14) ? 0 : e; }
+// whether pred holds on some lane of the wave (uniform)
+__device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 // the largest of v over the 16 lanes of a wave with the same quad lane x (one head's positions)
 __device__ __forceinline__ int head_max(int v) {
 #pragma unroll
@@ -203,7 +206,7 @@ __device__ __forceinline__ void fb_query_stats(const BwdArgs& A, const FbRows& R
 }
 
 // dq and the d(loss)/dt partials of one query tile (the workgroup's), in float32.
-__device__ __forceinline__ void bwd_q_tile_fp32(const BwdArgs& A, int b, int bg, int h0, int i0, char* lds) {
+__device__ __forceinline__ void bwd_q_tile_fp32(const BwdArgs& A, int b, int bg, int h0, int i0, int slot, char* lds) {
     float* dtbuf = reinterpret_cast<float*>(lds);                  // [64][16] d(loss)/dt per rung
     const int e = threadIdx.x & 7, gi = threadIdx.x >> 3, L = A.L;
     const FbRows R{static_cast<const bf16_t*>(A.k) + static_cast<int64_t>(bg) * L * kD,
@@ -286,7 +289,7 @@ __device__ __forceinline__ void bwd_q_tile_fp32(const BwdArgs& A, int b, int bg,
         __syncthreads();                                            // before the next head's buffer
     }
     if (threadIdx.x < static_cast<unsigned>(A.n_off))
-        A.partial[static_cast<int64_t>(blockIdx.x) * kMaxOff + threadIdx.x] = threadIdx.x < 16 ? dt_sum : 0.f;
+        A.partial[static_cast<int64_t>(slot) * kMaxOff + threadIdx.x] = threadIdx.x < 16 ? dt_sum : 0.f;
 }
 
 // dk and dv of one key tile (rows j0 .. j0 + 63 of unit bg, key-value head g), in float32: key row j
@@ -378,6 +381,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     __shared__ __attribute__((aligned(1024))) char lds1[2 * kBufBytes];
     __shared__ float red[4][MAXK];
     __shared__ int ered[4][4][3];                       // [wave][head]: largest exponents of q, do, dS
+    __shared__ int votes[4];                            // per wave: a staged row it checks lies outside fp16's range
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -436,8 +440,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     };
     uint4 qraw[8], draw[8];
     float4 ctq[4];                                      // cos/sin of pairs 8x..8x+7 at position i
-    int eq, ed;                                         // the row exponents of q and do (0 for a zero row)
-    int outside;                                        // uniform: a staged row lies outside fp16's range
+    bool flagged;                                       // a staged row the lane checks lies outside fp16's range
     {
         // the 4 heads' rows (4 L rows of 128 bytes: within 32 bits for L <= 2^20); positions past
         // L read row L - 1 (finite, never used)
@@ -458,7 +461,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) ctq[u] = ct[u];
         // the range flags of the staged key and value rows this tile reads (in flight with q, do)
-        const bool flagged = rows_flagged(A, bg / kPrepRowGroup, i0, n_reach);
+        flagged = rows_flagged(A, bg / kPrepRowGroup, i0, n_reach);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -466,37 +469,40 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             draw[c] = *reinterpret_cast<const uint4*>(rd + row_view_addr(pq, x, c));
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        // row exponents (|q_rot| <= sqrt(2) max|q|: one more binade of headroom) and each head's
-        // largest over the wave's positions
-        eq = floor_log2(max_abs_bf16_row(qraw));
-        ed = floor_log2(max_abs_bf16_row(draw));
-        {
-            const int mq = head_max(active ? eq : kNoExp), md = head_max(active ? ed : kNoExp);
-            if (pq == 0) {
-                ered[wave][x][0] = mq;
-                ered[wave][x][1] = md;
-            }
+        __builtin_amdgcn_s_barrier();                   // every wave is done with its rows
+        asm volatile("" ::: "memory");
+    }
+    st.near(krs, lds0, jn);
+    st.near(hrs, lds0 + kBufBytes, jn);
+    kv_step(lds1, kn);
+    // Row exponents, behind the staging: q and do are carried as row / 2^e in fp16 (|q_rot| <=
+    // sqrt(2) max|q|: one more binade of headroom). Rows fp16 holds well as they are keep e = 0,
+    // except q for the scores when they must be precise (its low part needs the row near 1); q's
+    // hand-off to the key side takes the banded exponent either way. Each head's largest hand-off
+    // exponent over the wave's positions goes to ered; whether a staged row this tile reads lies
+    // outside fp16's range is voted on (read after the next barrier).
+    int eq, ed;                                         // (0 for a zero row)
+    {
+        const int fq = floor_log2_bits(max_abs_bf16_bits(qraw));
+        const int eqh = banded(fq);
+        eq = PRECISE ? fq : eqh;
+        ed = banded(floor_log2_bits(max_abs_bf16_bits(draw)));
+        const int mq = head_max(active ? eqh : kNoExp), md = head_max(active ? ed : kNoExp);
+        if (pq == 0) {
+            ered[wave][x][0] = mq;
+            ered[wave][x][1] = md;
         }
         if (eq == kNoExp) eq = 0;
         if (ed == kNoExp) ed = 0;
-        // every wave is done with its rows (the barrier), and whether a staged row this tile reads
-        // lies outside fp16's range: then its outputs come from the float32 tile at the end
-        outside = __builtin_amdgcn_readfirstlane(__syncthreads_or(flagged ? 1 : 0));
-        asm volatile("" ::: "memory");
-        // then bwd_fp32_kernel writes dq and the partials, and the key tiles that read this tile's
-        // hand-off (marked here) leave theirs to it too
-        if (outside && threadIdx.x < 4)
-            A.exps[(static_cast<int64_t>(b) * A.Hq + h0 + x) * n_tiles + tile] = kExpsFallback;
+        post_vote(votes, wave, flagged);
     }
+    const bool wscaled = wave_any(eq != 0 || ed != 0);  // uniform: some row of the wave is scaled
     // head x's largest q and do exponents over the tile (read from LDS where needed: registers
     // are short here)
     auto tile_exp = [&](int k) {
         const int f = max(max(ered[0][x][k], ered[1][x][k]), max(ered[2][x][k], ered[3][x][k]));
         return f == kNoExp ? 0 : f;
     };
-    st.near(krs, lds0, jn);
-    st.near(hrs, lds0 + kBufBytes, jn);
-    kv_step(lds1, kn);
 
     // q rotated at its position (unscaled), fp16, in the keys' permuted order: word 2m holds dims
     // (m, 16 + m), word 2m + 1 dims (32 + m, 48 + m); register chunk c = words 4c..4c+3. PRECISE
@@ -505,7 +511,6 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     uint32_t ql[PRECISE ? 8 : 1][4];
     const float qsc = A.qscale * pow2f(eq);             // the score scale of the lane's scaled row
     {
-        const float sq = pow2f(-eq);
         float r[kD];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -517,11 +522,16 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
                 const float x0 = bf16_lo(lw[m]), x1 = bf16_hi(lw[m]);
                 const float y0 = bf16_lo(hw[m]), y1 = bf16_hi(hw[m]);
                 const int j = 8 * c + 2 * m;
-                r[j] = (x0 * t.x - y0 * t.y) * sq;
-                r[j + 1] = (x1 * t.z - y1 * t.w) * sq;
-                r[j + 32] = (y0 * t.x + x0 * t.y) * sq;
-                r[j + 33] = (y1 * t.z + x1 * t.w) * sq;
+                r[j] = x0 * t.x - y0 * t.y;
+                r[j + 1] = x1 * t.z - y1 * t.w;
+                r[j + 32] = y0 * t.x + x0 * t.y;
+                r[j + 33] = y1 * t.z + x1 * t.w;
             }
+        }
+        if (wscaled) {
+            const float sq = pow2f(-eq);
+#pragma unroll
+            for (int j = 0; j < kD; ++j) r[j] *= sq;
         }
 #pragma unroll
         for (int w = 0; w < 32; ++w) {
@@ -544,14 +554,32 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             const uint32_t v = w == 0 ? r.x : w == 1 ? r.y : w == 2 ? r.z : r.w;
             return (d & 1) ? bf16_hi(v) : bf16_lo(v);
         };
-        const float sdo = pow2f(-ed);                   // do / 2^ed
+        if (wscaled) {
+            const float sdo = pow2f(-ed);               // do / 2^ed
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            dov[m >> 1][2 * (m & 1)] = pack_h2(dim(m) * sdo, dim(16 + m) * sdo);
-            dov[m >> 1][2 * (m & 1) + 1] = pack_h2(dim(32 + m) * sdo, dim(48 + m) * sdo);
+            for (int m = 0; m < 16; ++m) {
+                dov[m >> 1][2 * (m & 1)] = pack_h2(dim(m) * sdo, dim(16 + m) * sdo);
+                dov[m >> 1][2 * (m & 1) + 1] = pack_h2(dim(32 + m) * sdo, dim(48 + m) * sdo);
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                dov[m >> 1][2 * (m & 1)] = pack_h2(dim(m), dim(16 + m));
+                dov[m >> 1][2 * (m & 1) + 1] = pack_h2(dim(32 + m), dim(48 + m));
+            }
         }
     }
     publish<12>();                                      // the key and value near blocks have landed
+    // whether a staged row this tile reads lies outside fp16's range: then its outputs come from
+    // the float32 tiles (bwd_fp32_kernel writes dq and the partials, and the key tiles that read
+    // this tile's hand-off, marked here, leave theirs to it too)
+    const int outside = or_votes(votes);
+    if (outside && threadIdx.x < 4)
+        A.exps[(static_cast<int64_t>(b) * A.Hq + h0 + x) * n_tiles + tile] = kExpsFallback;
+    if (threadIdx.x == 0) {
+        if (blockIdx.x == 0) A.seqw[0] = A.seq;
+        if (outside) A.seqw[1] = A.seq;
+    }
 
     // ---- pass AB: scores s (base 2) with the keys, dP = do . value row with the values, and for
     // each rung far - near of both products (PRECISE: pass A, the scores, then pass B, dP) ----
@@ -677,15 +705,18 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     // records tq, td for the key side)
     if (!outside) {
         const int tq = tile_exp(0), td = tile_exp(1);
+        const bool tscaled = wave_any(eq != tq || ed != td);
         const uint32_t fqh = pow2_h2(eq - tq, eq - tq), fdh = pow2_h2(ed - td, ed - td);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
+            for (int c = 0; c < 8; ++c) {
+                const uint32_t(&v)[4] = t ? dov[c] : q[c];
+                const uint32_t f = t ? fdh : fqh;
                 *reinterpret_cast<uint4*>(treg + row_view_addr(pq, x, c)) =
-                    t ? make_uint4(mul_h2(dov[c][0], fdh), mul_h2(dov[c][1], fdh), mul_h2(dov[c][2], fdh),
-                                   mul_h2(dov[c][3], fdh))
-                      : make_uint4(mul_h2(q[c][0], fqh), mul_h2(q[c][1], fqh), mul_h2(q[c][2], fqh), mul_h2(q[c][3], fqh));
+                    tscaled ? make_uint4(mul_h2(v[0], f), mul_h2(v[1], f), mul_h2(v[2], f), mul_h2(v[3], f))
+                            : make_uint4(v[0], v[1], v[2], v[3]);
+            }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const uint4 v = *reinterpret_cast<const uint4*>(treg + lin_view_addr(lane, u));
@@ -725,8 +756,10 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         dt[n] = fmaf(dp[4 * kWG + n] * (kLn2 / A.scale), sd[n], s[4 * kWG + n] * dpd[n]);
     }
     // dS/sqrt(D), dP and the dt terms are in units of 2^-ed (do was scaled by it): dt to true units
+    if (wscaled) {
 #pragma unroll
-    for (int n = 0; n < MAXK; ++n) dt[n] *= pow2f(ed);
+        for (int n = 0; n < MAXK; ++n) dt[n] *= pow2f(ed);
+    }
     // the key side's weights of this query: (p, dS/sqrt(D)) per window distance and per rung
     // (without the rung's coefficients), fp16 pairs, dS scaled by the row's 2^-es (its largest
     // element in [1, 2)); stored at the end, once the tile's common exponent is known
@@ -735,13 +768,16 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         float mxd = 0.f;
 #pragma unroll
         for (int y = 0; y < 4 * kWG + MAXK; ++y) mxd = fmaxf(mxd, fabsf(dp[y]));
-        es = floor_log2(mxd);
+        es = banded(floor_log2(mxd));
     }
     uint32_t wq[4 * kWG + MAXK];
-    {
+    if (wave_any(es != kNoExp && es != 0)) {
         const float sds = pow2f(es == kNoExp ? 0 : -es);
 #pragma unroll
         for (int y = 0; y < 4 * kWG + MAXK; ++y) wq[y] = pack_p_ds(s[y], dp[y] * sds);
+    } else {
+#pragma unroll
+        for (int y = 0; y < 4 * kWG + MAXK; ++y) wq[y] = pack_p_ds(s[y], dp[y]);
     }
     es = (es == kNoExp || !active) ? kNoExp : es + ed;  // the row's dS exponent in true units
     // pass C weights: dS/sqrt(D) times the coefficients, fp16, groups of 4
@@ -831,9 +867,11 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         // window row of this query (64 bytes; through treg as 16 rows per head, chunk c at c ^ x,
         // 1 KB contiguous stores) and one entry of each rung's row (rung-major, so a wave's stores
         // of one rung are contiguous) ----
-        const uint32_t fs = pow2_h2(0, es == kNoExp ? 0 : es - ts);
+        if (wave_any(es != kNoExp && es != ts)) {
+            const uint32_t fs = pow2_h2(0, es == kNoExp ? 0 : es - ts);
 #pragma unroll
-        for (int y = 0; y < 4 * kWG + MAXK; ++y) wq[y] = mul_h2(wq[y], fs);
+            for (int y = 0; y < 4 * kWG + MAXK; ++y) wq[y] = mul_h2(wq[y], fs);
+        }
 #pragma unroll
         for (int c = 0; c < kNW / 4; ++c)
             *reinterpret_cast<uint4*>(treg + (16 * x + pq) * (kNW * 4) + ((c ^ x) << 4)) =
@@ -877,7 +915,11 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
 #pragma unroll
                 for (int m = 0; m < 16; ++m) {
                     const float other = quad_f<kXor2>(o[m][r]);
-                    v[m] = fmaf(sg * other, cs[m].y, o[m][r] * cs[m].x) * eh[r];
+                    v[m] = fmaf(sg * other, cs[m].y, o[m][r] * cs[m].x);
+                }
+                if (wscaled) {
+#pragma unroll
+                    for (int m = 0; m < 16; ++m) v[m] *= eh[r];
                 }
                 uint4 lo, hi;
                 lo.x = pack_bf2(v[0], v[1]);
@@ -903,17 +945,23 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             if (threadIdx.x < MAXK) v = ((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) + red[3][threadIdx.x];
             A.partial[static_cast<int64_t>(blockIdx.x) * kMaxOff + threadIdx.x] = v;
         }
-        // the tile's exponents of head x for the key side
-        if (threadIdx.x < 4)
-            A.exps[(static_cast<int64_t>(b) * A.Hq + h0 + x) * n_tiles + tile] = pack_exps(tile_exp(0), tile_exp(1), ts);
+        // the tile's exponents of head x for the key side (and the call number, where they are not
+        // all 0, for the key side to read them)
+        if (threadIdx.x < 4) {
+            const int tq = tile_exp(0), td = tile_exp(1);
+            A.exps[(static_cast<int64_t>(b) * A.Hq + h0 + x) * n_tiles + tile] = pack_exps(tq, td, ts);
+            if ((tq | td | ts) != 0) A.seqw[2] = A.seq;
+        }
     }
 }
 
 // ------------------------------------------------------------------------------------------------
-// bwd_fp32: the float32 tiles, after the matrix-core kernels. Workgroups below n_qwg are query tiles
-// (plain order; a tile runs when it reads a flagged staged row, as bwd_q_mfma decides), the others
-// key tiles (a tile runs when a query tile it reads from is marked, as bwd_k_dot decides); every
-// other workgroup leaves at once.
+// bwd_fp32: the float32 tiles, after the matrix-core kernels. Virtual workgroups below n_qwg are
+// query tiles (a tile runs when the query kernel marked it), the others key tiles (a tile runs when
+// a query tile it reads from is marked, as bwd_k_dot decides). The call numbers the query kernel
+// leaves in the workspace gate the whole grid with one load: the query part runs only when a tile
+// of this call's query stage was marked, the key part only when one of the query stage its hand-off
+// comes from was. The grid is capped; each workgroup strides over the virtual ones.
 // ------------------------------------------------------------------------------------------------
 // Whether key tile `tile` of (b, g) reads from a query tile that left its outputs to the float32
 // tiles: the exps words of every query tile its terms read (window and near pairs: t0 .. t0 + 2;
@@ -932,37 +980,44 @@ __device__ __forceinline__ bool key_tile_marked(const BwdArgs& A, int b, int g, 
     return __syncthreads_or(marked ? 1 : 0) != 0;
 }
 
-__global__ __launch_bounds__(kNT) void bwd_fp32_kernel(BwdArgs A, int n_qwg) {
+constexpr int kFp32Grid = 1024;
+
+__global__ __launch_bounds__(kNT) void bwd_fp32_kernel(BwdArgs A, int n_qwg, int n_kwg) {
     __shared__ __attribute__((aligned(16))) char lds[kTile * 16 * 4];
+    const uint64_t s_last = A.seqw[0], s_fb = A.seqw[1];
+    const bool run_q = n_qwg > 0 && s_fb == A.seq;
+    const bool run_k = n_kwg > 0 && s_fb == s_last;
+    if (!run_q && !run_k) return;
     const int L = A.L;
     const int n_tiles = (L + kTile - 1) / kTile;
-    if (static_cast<int>(blockIdx.x) < n_qwg) {
-        // the matrix-core query kernel's tile order (its xcd_map is 0 or 1, which does not depend on
-        // the grid's size): workgroup blockIdx.x takes the tile, and the partials slot, of that
-        // kernel's workgroup blockIdx.x
-        const int n_chunk = A.G >> 2;
-        int unit, tile;
-        unit_tile(blockIdx.x, n_tiles, A.xcd_map, unit, tile);
-        const int chunk = unit % n_chunk;
-        const int bg = unit / n_chunk;
-        const int b = bg / A.Hkv;
-        const int h0 = (bg % A.Hkv) * A.G + chunk * 4;
-        const int i0 = tile * kTile;
-        int n_reach = 0;
-        for (int n = 0; n < A.n_off; ++n)
-            if (i0 + kTile - 1 >= A.off[n].a + A.off[n].interp) n_reach = n + 1;
-        if (!__syncthreads_or(rows_flagged(A, bg / kPrepRowGroup, i0, n_reach) ? 1 : 0)) return;
-        bwd_q_tile_fp32(A, b, bg, h0, i0, lds);
-    } else {
-        const int w = blockIdx.x - n_qwg;
-        const int bg = w / n_tiles, tile = w % n_tiles;
-        const int b = bg / A.Hkv, g = bg % A.Hkv;
-        const int j0 = tile * kTile;
-        int n_reach = 0;
-        for (int n = 0; n < A.n_off; ++n)
-            if (j0 + A.off[n].a < L) n_reach = n + 1;
-        if (!key_tile_marked(A, b, g, tile, n_reach, n_tiles)) return;
-        bwd_k_tile_fp32(A, b, bg, g, j0);
+    if (run_q) {
+        for (int w = blockIdx.x; w < n_qwg; w += gridDim.x) {
+            // the matrix-core query kernel's tile order (its xcd_map is 0 or 1, which does not
+            // depend on the grid's size): virtual workgroup w takes the tile, and the partials slot,
+            // of that kernel's workgroup w
+            const int n_chunk = A.G >> 2;
+            int unit, tile;
+            unit_tile(w, n_tiles, A.xcd_map, unit, tile);
+            const int chunk = unit % n_chunk;
+            const int bg = unit / n_chunk;
+            const int b = bg / A.Hkv;
+            const int h0 = (bg % A.Hkv) * A.G + chunk * 4;
+            if (!(A.exps[(static_cast<int64_t>(b) * A.Hq + h0) * n_tiles + tile] & kExpsFallback)) continue;
+            bwd_q_tile_fp32(A, b, bg, h0, tile * kTile, w, lds);
+            __syncthreads();                    // lds is free for the next tile
+        }
+    }
+    if (run_k) {
+        for (int w = blockIdx.x; w < n_kwg; w += gridDim.x) {
+            const int bg = w / n_tiles, tile = w % n_tiles;
+            const int b = bg / A.Hkv, g = bg % A.Hkv;
+            const int j0 = tile * kTile;
+            int n_reach = 0;
+            for (int n = 0; n < A.n_off; ++n)
+                if (j0 + A.off[n].a < L) n_reach = n + 1;
+            if (!key_tile_marked(A, b, g, tile, n_reach, n_tiles)) continue;
+            bwd_k_tile_fp32(A, b, bg, g, j0);
+        }
     }
 }
 // ------------------------------------------------------------------------------------------------
@@ -986,7 +1041,6 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     // bring the query side's per-tile scaling to the workgroup's common one (see below)
     constexpr int kSlotsF = 3 + 2 * 2 * MAXS;
     __shared__ uint32_t fac[kMaxGKey][kSlotsF];
-    __shared__ int emax[3];
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -1104,12 +1158,30 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     // (the window and the near pairs), slot 3 + 2n + u is tile ((j0 + a_n) >> 6) + u (rung n). Ev
     // and Ek are the largest td and ts + tq over the workgroup's heads and slots, and each weight
     // takes its query tile's factor 2^(td - Ev) (p) or 2^(ts + tq - Ek) (dS), at most 1: dv and dk
-    // accumulate in units of 2^-Ev and 2^-Ek, scaled back at the end. Wave 0 loads the exponents
-    // ahead of the first near item's DMAs and builds the table behind them. ----
+    // accumulate in units of 2^-Ev and 2^-Ek, scaled back at the end. The query stage leaves its
+    // call number in seqw[1] when a tile fell back to float32 and in seqw[2] when some tile's
+    // exponents are not all 0; where neither holds (the usual case: rows fp16 holds as they are
+    // carry exponent 0) every factor is 1 and no exponent is read. Every wave builds the whole
+    // table (the same words), so no barrier is needed; the weights always take their factors
+    // (multiplies without branches). ----
     const int t0 = tile;
-    constexpr int kFacLoads = (kMaxGKey * kSlotsF + 63) / 64;
-    uint32_t ew[kFacLoads];
-    if (wave == 0) {
+    const uint64_t seq_last = A.seqw[0], seq_fb = A.seqw[1], seq_sc = A.seqw[2];
+    near_item(g * A.G);
+    int Ev = 0, Ek = 0;
+    bool allone = true;                                 // uniform: every factor of the table is 1
+    // the table; false when a query tile this tile reads from left its hand-off to the float32
+    // tiles (then so does this one)
+    auto build_factors = [&]() -> bool {
+        constexpr int kFacLoads = (kMaxGKey * kSlotsF + 63) / 64;
+        if (__builtin_amdgcn_readfirstlane((seq_fb != seq_last && seq_sc != seq_last) ? 1 : 0)) {
+#pragma unroll
+            for (int r = 0; r < kFacLoads; ++r) {
+                const int e = lane + 64 * r;
+                if (e < kMaxGKey * kSlotsF) fac[e / kSlotsF][e % kSlotsF] = 0x3c003c00u;   // (1, 1)
+            }
+            return true;
+        }
+        uint32_t ew[kFacLoads];
 #pragma unroll
         for (int r = 0; r < kFacLoads; ++r) {
             const int e = lane + 64 * r;
@@ -1127,49 +1199,36 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
             ok = ok && tl < n_tiles;
             ew[r] = ok ? A.exps[(static_cast<int64_t>(b) * A.Hq + g * A.G + hh) * n_tiles + tl] : 0xffffffffu;
         }
-    }
-    near_item(g * A.G);
-    if (wave == 0) {
-        int mv = kNoExp, mk = kNoExp, marked = 0;
+        int mv = kNoExp, mk = kNoExp;
+        bool marked = false;
 #pragma unroll
         for (int r = 0; r < kFacLoads; ++r) {
             if (ew[r] != 0xffffffffu) {
                 mv = max(mv, exps_td(ew[r]));
                 mk = max(mk, exps_ts(ew[r]) + exps_tq(ew[r]));
-                marked |= (ew[r] & kExpsFallback) ? 1 : 0;
+                marked = marked || (ew[r] & kExpsFallback) != 0u;
             }
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
             mv = max(mv, __shfl_xor(mv, off, 64));
             mk = max(mk, __shfl_xor(mk, off, 64));
-            marked |= __shfl_xor(marked, off, 64);
         }
-        if (mv == kNoExp) mv = 0;
-        if (mk == kNoExp) mk = 0;
+        if (wave_any(marked)) return false;
+        Ev = __builtin_amdgcn_readfirstlane(mv == kNoExp ? 0 : mv);
+        Ek = __builtin_amdgcn_readfirstlane(mk == kNoExp ? 0 : mk);
+        bool other = false;
 #pragma unroll
         for (int r = 0; r < kFacLoads; ++r) {
             const int e = lane + 64 * r;
+            const bool real = ew[r] != 0xffffffffu;
+            other = other || (real && (exps_td(ew[r]) != Ev || exps_ts(ew[r]) + exps_tq(ew[r]) != Ek));
             if (e < kMaxGKey * kSlotsF)
-                fac[e / kSlotsF][e % kSlotsF] =
-                    (ew[r] == 0xffffffffu) ? 0u : pow2_h2(exps_td(ew[r]) - mv, exps_ts(ew[r]) + exps_tq(ew[r]) - mk);
+                fac[e / kSlotsF][e % kSlotsF] = real ? pow2_h2(exps_td(ew[r]) - Ev, exps_ts(ew[r]) + exps_tq(ew[r]) - Ek) : 0u;
         }
-        if (lane == 0) {
-            emax[0] = mv;
-            emax[1] = mk;
-            emax[2] = marked;
-        }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // an LDS-only barrier: the DMAs stay in flight
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (__builtin_amdgcn_readfirstlane(emax[2])) {
-        // a query tile this tile reads from left its hand-off to the float32 tiles: so does this
-        // one (bwd_fp32_kernel); the staging in flight lands before the workgroup leaves
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        return;
-    }
-    const int Ev = emax[0], Ek = emax[1];
+        allone = !wave_any(other);
+        return true;
+    };
     // the factor of one entry half: p (use_p) or dS, of head hh's slot sl, as an fp16 in the low 16 bits
     auto fac_half = [&](int hh, int sl, bool use_p) -> uint32_t {
         const uint32_t f = fac[hh][sl];
@@ -1177,22 +1236,33 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     };
     // (1 - t, t) times the factors of the near and far query rows of rung n for key row j0 + wrow
     auto coef = [&](int hh, int n, int a, float t, bool use_p) -> h2_t {
+        const h2_t c = {static_cast<_Float16>(1.f - t), static_cast<_Float16>(t)};
         const int qn = j0 + wrow + a;
         const int base = (n < 2 * kn) ? -t0 : 3 + 2 * n - ((j0 + a) >> 6);
         const uint32_t f = fac_half(hh, base + (qn >> 6), use_p) | (fac_half(hh, base + ((qn + 1) >> 6), use_p) << 16);
-        const h2_t c = {static_cast<_Float16>(1.f - t), static_cast<_Float16>(t)};
         return c * __builtin_bit_cast(h2_t, f);
     };
+    // the thread's coefficient of each rung pair k (rung 2k + (wv & 1), dS halves for wv < 2, else
+    // p halves): (1 - t, t), times the factors of its near and far query rows where not every
+    // factor is 1 (then recomputed per head)
+    uint32_t cw[MAXS];
+    auto set_cw = [&](int hh, bool with_factors) {
+#pragma unroll
+        for (int k = 0; k < MAXS; ++k) {
+            const float t = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].t, A.off[2 * k].t);
+            const int a = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a);
+            const h2_t c = with_factors ? coef(hh, 2 * k + (wv & 1), a, t, (wv >> 1) != 0)
+                                        : (h2_t){static_cast<_Float16>(1.f - t), static_cast<_Float16>(t)};
+            cw[k] = __builtin_bit_cast(uint32_t, c);
+        }
+    };
+    set_cw(0, false);
     // rung step weights of head hh: thread (row wrow, part wv) builds one word of wst for key row
-    // j0 + wrow: rung 2k + (wv & 1), dS halves (wv < 2) or p halves, (near, far) times (1 - t, t)
-    // and the query tiles' factors
-    auto put_w = [&](int hh, int k) {
-        const float t = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].t, A.off[2 * k].t);
-        const int a = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a);
+    // j0 + wrow: rung 2k + (wv & 1), dS halves (wv < 2) or p halves, times the coefficient
+    auto put_w = [&](int k) {
         const uint32_t en = went[k & 1][wv & 1][wrow], ef = went[k & 1][wv & 1][wrow + 1];
         const uint32_t pr = __builtin_amdgcn_perm(ef, en, (wv >> 1) ? 0x05040100u : 0x07060302u);
-        const h2_t c = coef(hh, 2 * k + (wv & 1), a, t, (wv >> 1) != 0);
-        reinterpret_cast<uint32_t*>(&wst[k & 1][wrow])[wv] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, pr) * c);
+        reinterpret_cast<uint32_t*>(&wst[k & 1][wrow])[wv] = mul_h2(pr, cw[k]);
     };
 
     for (int hh = 0; hh < A.G; ++hh) {
@@ -1234,17 +1304,23 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
         step(qrs, lds1, kn);
         step(drs, lds1 + kBufBytes, kn);
         entries(h, kn + 1);
+        if (hh == 0 && !__builtin_amdgcn_readfirstlane(build_factors() ? 1 : 0)) {
+            // the staging in flight lands before the workgroup leaves
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            return;
+        }
+        if (!__builtin_amdgcn_readfirstlane(allone ? 1 : 0)) set_cw(hh, true);
         // the near pairs' weights (same words as the far steps' table)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             if (k < kn) {
-                const float t = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].t, A.off[2 * k].t);
-                const int a = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a);
                 const uint32_t pr = __builtin_amdgcn_perm(efr[k], enr[k], (wv >> 1) ? 0x05040100u : 0x07060302u);
-                const h2_t c = coef(hh, 2 * k + (wv & 1), a, t, (wv >> 1) != 0);
-                reinterpret_cast<uint32_t*>(&wnear(k)[wrow])[wv] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, pr) * c);
+                reinterpret_cast<uint32_t*>(&wnear(k)[wrow])[wv] = mul_h2(pr, cw[k]);
             }
         }
+        // the window's factors: the wave's queries 16w + 16 kb + 0..15 lie in query tile t0, but
+        // for wave 3, kb = 1 (tile t0 + 1)
+        const uint32_t fw0 = fac[hh][0], fw1 = fac[hh][wave == 3 ? 1 : 0];
         publish<13>();                                  // this head's near item and weights are in place
 
         // ---- window terms on the matrix cores: for the wave's key rows 16w + rr and queries
@@ -1256,8 +1332,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
                 // each query's (p, dS) pair times its query tile's factors
                 uint32_t e4[4];
 #pragma unroll
-                for (int ee = 0; ee < 4; ++ee)
-                    e4[ee] = mul_h2(e4w[kb][ee], fac[hh][((j0 + 16 * wave + 16 * kb + 4 * lg + ee) >> 6) - t0]);
+                for (int ee = 0; ee < 4; ++ee) e4[ee] = mul_h2(e4w[kb][ee], kb ? fw1 : fw0);
                 // (p, dS) pairs: dS in the high halves (dk), p in the low halves (dv)
                 const u2_t a_dk = {__builtin_amdgcn_perm(e4[1], e4[0], 0x07060302u),
                                    __builtin_amdgcn_perm(e4[3], e4[2], 0x07060302u)};
@@ -1289,7 +1364,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
                 sum_rungs(dv, w, true, lds0 + kBufBytes, nadr);
             }
         }
-        put_w(hh, kn);
+        put_w(kn);
         publish<0>();                                   // far pair kn and its weights are in place, lds0 is free
 
         // ---- far steps: pair k (kn <= k < n_far) in lds(k + 1) % 2 ----
@@ -1310,7 +1385,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
                     sum_rungs(dk, w, false, buf(k + 1), radr);
                     sum_rungs(dv, w, true, buf(k + 1) + kBufBytes, radr);
                 }
-                if (k + 1 < n_steps) put_w(hh, k + 1);
+                if (k + 1 < n_steps) put_w(k + 1);
                 publish<0>();
             }
         }
@@ -1388,7 +1463,9 @@ bool bwd_mfma_supported(const BwdArgs& A) {
 }
 
 hipError_t launch_bwd_mfma(const BwdArgs& A0, bool want_dalpha, int stages, hipStream_t s) {
+    static std::atomic<uint64_t> calls{0};
     BwdArgs A = A0;
+    A.seq = calls.fetch_add(1, std::memory_order_relaxed) + 1;
     const int64_t n_tiles = (A.L + kTile - 1) / kTile;
     const int64_t q_units = static_cast<int64_t>(A.B) * A.Hkv * (A.G / 4);
     const int64_t k_units = static_cast<int64_t>(A.B) * A.Hkv;
@@ -1412,14 +1489,15 @@ hipError_t launch_bwd_mfma(const BwdArgs& A0, bool want_dalpha, int stages, hipS
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    // the float32 tiles of the stages run here (their workgroups leave at once where no staged row
-    // lies outside fp16's range)
+    // the float32 tiles of the stages run here (the kernel leaves at once unless the query stage
+    // marked a tile)
     {
         A.xcd_map = q_map;
         const int64_t n_q = (stages & kStageQuery) ? q_units * n_tiles : 0;
         const int64_t n_k = (stages & kStageKey) ? k_units * n_tiles : 0;
-        hipLaunchKernelGGL(bwd_fp32_kernel, dim3(static_cast<unsigned>(n_q + n_k)), dim3(kNT), 0, s, A,
-                           static_cast<int>(n_q));
+        const int64_t grid = std::min<int64_t>(std::max(n_q, n_k), kFp32Grid);
+        hipLaunchKernelGGL(bwd_fp32_kernel, dim3(static_cast<unsigned>(grid)), dim3(kNT), 0, s, A,
+                           static_cast<int>(n_q), static_cast<int>(n_k));
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -70,24 +70,37 @@ constexpr int kWgsPerCu = 4;
 // ------------------------------------------------------------------------------------------------
 // A thread takes one position j and kPrepRows (batch, head) rows of it: every row's loads are
 // issued first, then the cos/sin of its 4 RoPE pairs are computed once for all of them. Workgroup
-// (x, y) = (row group x: kPrepRows consecutive (batch, head) rows, positions 32y .. 32y + 31).
+// (x, y) = (positions 32x .. 32x + 31, row group y: kPrepRows consecutive (batch, head) rows).
 //
 // Range flags. fp16 holds a rotated key or value row exactly enough only inside a range: every
 // element below 2^15 in magnitude (65504 is fp16's largest) and, unless the row is zero, a row
 // maximum of at least 2^-10 (below that the row's largest elements come near fp16's subnormals,
-// 2^-14, where relative precision is lost). Each workgroup writes one word, nonzero when a key or
-// value row of its block lies outside; the attention kernels check the words of the rows they read
-// and compute such tiles in float32 from the caller's bf16 rows instead.
+// 2^-14, where relative precision is lost). Each wave writes one byte of its workgroup's word (its
+// 8 positions of the block), nonzero when a key or value row there lies outside; the attention
+// kernels check the words of the rows they read and compute such tiles in float32 from the
+// caller's bf16 rows instead. A row's 8 threads are one byte of the wave's ballot masks.
 constexpr int kPrepRows = kPrepRowGroup;
 
-__device__ __forceinline__ bool outside_fp16(float rowmax, float elemmax) {
-    return elemmax >= kFp16Big || (rowmax > 0.0f && rowmax < kFp16Small);
+// bit 8r of the result: some bit of byte r of m is set
+__device__ __forceinline__ uint64_t byte_any(uint64_t m) {
+    m |= m >> 4;
+    m |= m >> 2;
+    m |= m >> 1;
+    return m & 0x0101010101010101ull;
+}
+// whether some row of the wave lies outside fp16's range, from each thread's largest magnitude
+// over its 8 elements (0 for threads without a row)
+__device__ __forceinline__ bool rows_outside_fp16(float mx) {
+    const uint64_t huge = __builtin_amdgcn_ballot_w64(mx >= kFp16Big);
+    const uint64_t nz = __builtin_amdgcn_ballot_w64(mx > 0.0f);
+    const uint64_t big = __builtin_amdgcn_ballot_w64(mx >= kFp16Small);
+    return huge != 0 || (byte_any(nz) & ~byte_any(big)) != 0;
 }
 
 __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
     const int u = threadIdx.x & 7;
-    const int grp = blockIdx.x;
-    const int j = 32 * blockIdx.y + (threadIdx.x >> 3);
+    const int grp = blockIdx.y;
+    const int j = 32 * blockIdx.x + (threadIdx.x >> 3);
     const bool active = j < A.L;
     const int jc = active ? j : 0;                      // rows past L are never read
     const bf16_t* ks = static_cast<const bf16_t*>(A.k);
@@ -142,16 +155,7 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) vmax = fmaxf(vmax, fmaxf(fabsf(bf16_lo(vw[r][c])), fabsf(bf16_hi(vw[r][c]))));
-        if (A.main) {
-            // the row's maxima over its 8 threads (lanes 8 jj .. 8 jj + 7)
-            float kr = kmax, vr = vmax;
-#pragma unroll
-            for (int off = 1; off < 8; off <<= 1) {
-                kr = fmaxf(kr, __shfl_xor(kr, off, 8));
-                vr = fmaxf(vr, __shfl_xor(vr, off, 8));
-            }
-            outside |= live && (outside_fp16(kr, kmax) || outside_fp16(vr, vmax));
-        }
+        if (A.main) outside |= rows_outside_fp16(live ? kmax : 0.f) || rows_outside_fp16(live ? vmax : 0.f);
         if (!live) continue;
         // element 8u + e: e < 4 is dim 16e + 2u, e >= 4 is dim 16(e - 4) + 2u + 1
         if (A.main) {
@@ -170,10 +174,9 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
             store4<f16_t>(A.k16lo + row + 8 * u + 4, make_float4(lo(rx[1]), lo(rx[3]), lo(ry[1]), lo(ry[3])));
         }
     }
-    if (A.main) {
-        const int any = __syncthreads_or(outside ? 1 : 0);
-        if (threadIdx.x == 0) A.flags[static_cast<int64_t>(grp) * A.n_blk + blockIdx.y] = any ? 1u : 0u;
-    }
+    if (A.main && (threadIdx.x & 63) == 0)
+        reinterpret_cast<uint8_t*>(A.flags)[(static_cast<int64_t>(grp) * A.n_blk + blockIdx.x) * 4 + (threadIdx.x >> 6)] =
+            outside ? 1 : 0;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -261,14 +264,7 @@ __device__ __forceinline__ void fwd_tile_fp32(const FwdArgs& A, int b, int bg, i
 // Whether a query row (64 bf16 values in r) scaled by qscale lies outside what fp16 holds exactly
 // enough once rotated (rotation moves each element by at most a factor sqrt(2) either way).
 __device__ __forceinline__ bool q_outside_fp16(const uint4 (&r)[8], float qscale) {
-    float mx = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const uint32_t w[4] = {r[c].x, r[c].y, r[c].z, r[c].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
-    }
-    mx *= qscale;
+    const float mx = bf16_bits_value(max_abs_bf16_bits(r)) * qscale;
     return mx >= 0.5f * kFp16Big || (mx > 0.f && mx < 2.f * kFp16Small);
 }
 
@@ -287,6 +283,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     // DMA in flight fills.
     __shared__ __attribute__((aligned(1024))) char lds0[kBufBytes];
     __shared__ __attribute__((aligned(1024))) char lds1[kBufBytes];
+    __shared__ int votes[4];                            // per wave: a row of the tile lies outside fp16's range
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -337,7 +334,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     // key near block (item 0) and item 1 (key far step kn) ----
     uint4 qraw[8];
     float4 ctab[4];
-    int outside;                                        // uniform: some row of the tile lies outside fp16's range
+    bool flagged;                                       // a staged row the lane checks lies outside fp16's range
     {
         char* const reg = (wave < 2 ? lds0 : lds1) + (wave & 1) * 8192;
         // the 4 heads' rows (4 L rows of 128 bytes: within 32 bits for L <= 2^20); positions
@@ -356,19 +353,19 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) ctab[u] = ct[u];
         // the range flags of the staged rows this tile reads (in flight with q)
-        const bool flagged = rows_flagged(A, bg / kPrepRowGroup, i0, n_reach);
+        flagged = rows_flagged(A, bg / kPrepRowGroup, i0, n_reach);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
         for (int c = 0; c < 8; ++c) qraw[c] = *reinterpret_cast<const uint4*>(reg + row_view_addr(pq, x, c));
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        // every wave is done with its rows (the barrier), and whether some row of the tile lies
-        // outside the fp16 range: then the whole tile is computed in float32
-        outside = __builtin_amdgcn_readfirstlane(
-            __syncthreads_or((flagged || (active && q_outside_fp16(qraw, A.qscale))) ? 1 : 0));
+        __builtin_amdgcn_s_barrier();                   // every wave is done with its rows
         asm volatile("" ::: "memory");
     }
     st.near(krs, lds0, jn);
     step(krs, lds1, kn);                                // (zero rows when no far rung is reached)
+    // whether some row of the tile lies outside the fp16 range (then the whole tile is computed in
+    // float32): each wave's vote, read after a later barrier
+    post_vote(votes, wave, flagged || (active && q_outside_fp16(qraw, A.qscale)));
 
     // q of head h0 + x, rotated at its position and scaled by qscale, fp16, in the keys' permuted
     // order: word 2m holds dims (m, 16 + m), word 2m + 1 dims (32 + m, 48 + m), i.e. the x and y
@@ -545,6 +542,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     invh[1] = quad_f<kBcast1>(inv);
     invh[2] = quad_f<kBcast2>(inv);
     invh[3] = quad_f<kBcast3>(inv);
+    const int outside = or_votes(votes);                // (posted before the first publish)
     if (active && !outside) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -576,7 +574,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
 }  // namespace
 
 hipError_t launch_prep_kv16(const PrepArgs& A, hipStream_t s) {
-    const dim3 grid(static_cast<unsigned>((A.n_bh + kPrepRows - 1) / kPrepRows), static_cast<unsigned>(A.n_blk));
+    const dim3 grid(static_cast<unsigned>(A.n_blk), static_cast<unsigned>((A.n_bh + kPrepRows - 1) / kPrepRows));
     hipLaunchKernelGGL(prep_kv16_kernel, grid, dim3(256), 0, s, A);
     return hipGetLastError();
 }

@@ -16,7 +16,7 @@ constexpr int kMaxOff = 32;   // base rungs
 constexpr int kStagePrep = 1, kStageQuery = 2, kStageKey = 4;
 
 // Range flags of the staged rows: one word per (group of kPrepRowGroup consecutive (batch, head)
-// rows, block of kFlagRows positions).
+// rows, block of kFlagRows positions), byte w of it for positions 8w .. 8w + 7 of the block.
 constexpr int kPrepRowGroup = 4;
 constexpr int kFlagRows = 32;
 
@@ -124,6 +124,11 @@ struct BwdArgs {
     // per (batch, head, query tile): the powers of two the query side scaled that tile's hand-off
     // by (q, do, dS; bytes of one word)
     uint32_t* exps;
+    // [0]: the call number of the last query stage run over this workspace; [1]: that of the last
+    // query stage that left some tile to the float32 kernel; [2]: that of the last query stage
+    // with some tile's exponents not all 0 (written by the query kernel)
+    uint64_t* seqw;
+    uint64_t seq;        // this call's number (the host's count of backward calls, from 1)
     float qscale;        // log2(e)/sqrt(D)
     int32_t xcd_map;
 };

@@ -282,6 +282,37 @@ __device__ __forceinline__ void unit_tile(int w, int n_tiles, int xcd_map, int& 
 constexpr float kFp16Big = 32768.0f;               // 2^15
 constexpr float kFp16Small = 0.0009765625f;        // 2^-10
 
+// The bits of the largest magnitude among a row's 64 bf16 values (15 bits, sign cleared): bf16
+// magnitudes order as unsigned integers, so packed 16-bit maxima find it without a conversion.
+__device__ __forceinline__ uint32_t max_abs_bf16_bits(const uint4 (&r)[8]) {
+    typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+    u16x2_t m[4];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const uint32_t w[4] = {r[c].x, r[c].y, r[c].z, r[c].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const u16x2_t v = __builtin_bit_cast(u16x2_t, w[e] & 0x7fff7fffu);
+            m[e] = (c == 0) ? v : __builtin_elementwise_max(m[e], v);
+        }
+    }
+    const u16x2_t a = __builtin_elementwise_max(__builtin_elementwise_max(m[0], m[1]), __builtin_elementwise_max(m[2], m[3]));
+    return max(static_cast<uint32_t>(a.x), static_cast<uint32_t>(a.y));
+}
+// The value of such bits.
+__device__ __forceinline__ float bf16_bits_value(uint32_t m) { return __uint_as_float(m << 16); }
+
+// An OR over the workgroup's waves that does not wait for the loads in flight (__syncthreads_or
+// would): each wave posts its vote into words[wave] here; after the next barrier that also waits
+// for LDS (publish), or_votes reads the workgroup's OR.
+__device__ __forceinline__ void post_vote(int* words, int wave, bool pred) {
+    const bool any = __builtin_amdgcn_ballot_w64(pred) != 0;
+    if ((threadIdx.x & 63) == 0) words[wave] = any ? 1 : 0;
+}
+__device__ __forceinline__ int or_votes(const int* words) {
+    return __builtin_amdgcn_readfirstlane(words[0] | words[1] | words[2] | words[3]);
+}
+
 // Sum over the 8 lanes 8p' .. 8p' + 7 (an 8-lane group holds a row in the float32 tiles).
 __device__ __forceinline__ float oct_sum(float v) {
     v += quad_f<0xB1>(v);                               // quad_perm [1, 0, 3, 2]
@@ -308,17 +339,22 @@ __device__ __forceinline__ void rot_eighth(const bf16_t* row, const float* cstab
 
 // The range flag of the staged rows that thread t of a tile checks: threads 0..3 the near block
 // (rows i0 - 64 .. i0 + 63), thread 4 + 4n + u the u-th flag block of kept rung n's rows
-// i0 - a - 1 .. i0 + 63 - a (clipped at 0), for rungs the tile reaches; every other thread none.
+// i0 - a - 1 .. i0 + 63 - a (clipped at 0), for rungs the tile reaches (at most 16: the matrix-core
+// kernels' limit); every other thread none. The rung's floor comes from the uniform offset table by
+// a per-lane choice among scalars: a per-lane index into the kernel arguments would be a vector
+// load followed by a full wait behind every load in flight (here: the q burst).
 template <typename Args>
 __device__ __forceinline__ bool rows_flagged(const Args& A, int grp, int i0, int n_reach) {
     const int t = threadIdx.x;
     int blk = -1;
     if (t < 4) {
         blk = i0 / kFlagRows - 2 + t;
-    } else if (t < 4 + 4 * kMaxOff) {
+    } else if (t < 4 + 4 * 16) {
         const int n = (t - 4) >> 2, u = (t - 4) & 3;
         if (n < n_reach) {
-            const int a = A.off[n].a;
+            int a = 0;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) a = (n == m) ? A.off[m].a : a;
             const int lo = max(i0 - a - 1, 0), hi = min(i0 + kTile - 1 - a, A.L - 1);
             if (lo / kFlagRows + u <= hi / kFlagRows) blk = lo / kFlagRows + u;
         }
