@@ -103,8 +103,8 @@ __device__ __forceinline__ int head_max(int v) {
 
 // ------------------------------------------------------------------------------------------------
 // The float32 tiles of the backward: for tiles that read staged key or value rows outside fp16's
-// range. A query tile so flagged leaves its outputs to bwd_fp32_kernel, and marks its exps word;
-// every key tile that reads from a marked query tile leaves its outputs to it too. Both are
+// range. A query tile so flagged leaves its outputs to its float32 tile, and marks its exps word;
+// every key tile that reads from a marked query tile computes its outputs in float32 too. Both are
 // computed from the caller's bf16 rows and the cos/sin table: thread 8p' + e takes dims
 // 8e .. 8e + 7 of a row (32 rows at a time). Slot sl of query i: sl < 16 is window distance sl,
 // 16 + n kept rung n. Rows come straight from global memory: slow, and only for such tiles.
@@ -570,16 +570,6 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         }
     }
     publish<12>();                                      // the key and value near blocks have landed
-    // whether a staged row this tile reads lies outside fp16's range: then its outputs come from
-    // the float32 tiles (bwd_fp32_kernel writes dq and the partials, and the key tiles that read
-    // this tile's hand-off, marked here, leave theirs to it too)
-    const int outside = or_votes(votes);
-    if (outside && threadIdx.x < 4)
-        A.exps[(static_cast<int64_t>(b) * A.Hq + h0 + x) * n_tiles + tile] = kExpsFallback;
-    if (threadIdx.x == 0) {
-        if (blockIdx.x == 0) A.seqw[0] = A.seq;
-        if (outside) A.seqw[1] = A.seq;
-    }
 
     // ---- pass AB: scores s (base 2) with the keys, dP = do . value row with the values, and for
     // each rung far - near of both products (PRECISE: pass A, the scores, then pass B, dP) ----
@@ -599,6 +589,24 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
                 const bool ok = active && i >= A.off[n].a + A.off[n].interp;
                 s[4 * kWG + n] = ok ? sc : kNegInf;
                 sd[n] = ok ? dd : 0.f;
+            }
+        }
+    };
+    // both products of a rung pair at once (one read of each rung's parameters)
+    auto pair_terms = [&](const f4_t& acc, const f4_t& accv, int k) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int n = 2 * k + e;
+            if (n < n_reach) {
+                const float t = A.off[n].t;
+                const float dd = (acc[2 * e + 1] - acc[2 * e]) * qsc;
+                const float sc = fmaf(t, dd, acc[2 * e] * qsc);
+                const bool ok = active && i >= A.off[n].a + A.off[n].interp;
+                s[4 * kWG + n] = ok ? sc : kNegInf;
+                sd[n] = ok ? dd : 0.f;
+                const float dv = accv[2 * e + 1] - accv[2 * e];
+                dp[4 * kWG + n] = fmaf(t, dv, accv[2 * e]);
+                dpd[n] = dv;
             }
         }
     };
@@ -650,8 +658,13 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     for (int k = 0; k < MAXS; ++k) {
         if (k < kn) {
             const int sl = near_slot(k);
-            score_terms(qk(lds0, sl * kRowBytes, swz(sl)), k);
-            if constexpr (!PRECISE) dp_terms(row_dot_group(dov, lds0 + voff, sl * kRowBytes, swz(sl)), k);
+            // (both products issued before either's terms: the second overlaps the first's latency)
+            const f4_t acc = qk(lds0, sl * kRowBytes, swz(sl));
+            if constexpr (!PRECISE) {
+                pair_terms(acc, row_dot_group(dov, lds0 + voff, sl * kRowBytes, swz(sl)), k);
+            } else {
+                score_terms(acc, k);
+            }
         }
     }
     publish<0>();                                       // far step kn has landed, buffer 0 is free
@@ -659,8 +672,12 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     for (int k = 0; k < MAXS; ++k) {
         if (k >= kn && k < n_steps) {
             if (k + 1 < n_steps) kv_step(buf(k + 2), k + 1);
-            score_terms(qk(buf(k + 1), rbase, rsw), k);
-            if constexpr (!PRECISE) dp_terms(row_dot_group(dov, buf(k + 1) + voff, rbase, rsw), k);
+            const f4_t acc = qk(buf(k + 1), rbase, rsw);
+            if constexpr (!PRECISE) {
+                pair_terms(acc, row_dot_group(dov, buf(k + 1) + voff, rbase, rsw), k);
+            } else {
+                score_terms(acc, k);
+            }
             publish<0>();
         }
     }
@@ -703,7 +720,11 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     // in vmcnt after the key DMAs; the wait before pass C counts them conservatively). Each head's
     // rows are scaled to a common power of two over the tile, q by 2^-tq and do by 2^-td (exps
     // records tq, td for the key side)
-    if (!outside) {
+    // whether a staged row this tile reads lies outside fp16's range (the votes, read where needed
+    // rather than held): then its outputs come from the float32 tiles (its float32 tile writes dq
+    // and the partials, and the key tiles that read this tile's hand-off, marked at the end,
+    // compute theirs in float32 too)
+    if (!or_votes(votes)) {
         const int tq = tile_exp(0), td = tile_exp(1);
         const bool tscaled = wave_any(eq != tq || ed != td);
         const uint32_t fqh = pow2_h2(eq - tq, eq - tq), fdh = pow2_h2(ed - td, ed - td);
@@ -840,38 +861,14 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // ---- d(loss)/dt partial sums of this workgroup (fixed order), and each head's largest dS
-    // exponent over the tile ----
-#pragma unroll
-    for (int n = 0; n < MAXK; ++n) {
-        float v = active ? dt[n] : 0.f;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-        if (lane == 0) red[wave][n] = v;
-    }
-    {
-        const int ms = head_max(es);
-        if (pq == 0) ered[wave][x][2] = ms;
-    }
-    // an LDS-only barrier: the stores in flight need not have landed (__syncthreads would wait
-    // for every one of them)
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    int ts = max(max(ered[0][x][2], ered[1][x][2]), max(ered[2][x][2], ered[3][x][2]));
-    if (ts == kNoExp) ts = 0;
-
-    if (!outside) {
-        // (pass C read only the key halves: treg is still the wave's own)
-        // ---- the key side's weights: dS scaled from the row's exponent to the tile's, 2^-ts; the
-        // window row of this query (64 bytes; through treg as 16 rows per head, chunk c at c ^ x,
-        // 1 KB contiguous stores) and one entry of each rung's row (rung-major, so a wave's stores
-        // of one rung are contiguous) ----
-        if (wave_any(es != kNoExp && es != ts)) {
-            const uint32_t fs = pow2_h2(0, es == kNoExp ? 0 : es - ts);
-#pragma unroll
-            for (int y = 0; y < 4 * kWG + MAXK; ++y) wq[y] = mul_h2(wq[y], fs);
-        }
+    // ---- the key side's weights: the window row of this query (64 bytes; through treg as 16
+    // rows per head, chunk c at c ^ x, 1 KB contiguous stores) and one entry of each rung's row
+    // (rung-major, so a wave's stores of one rung are contiguous). dS is carried scaled by the
+    // tile's 2^-ts (the largest row exponent of the head over the tile), known only after the
+    // barrier below: a wave whose rows need no scaling (exponent 0) stores them ahead of it, and
+    // stores them again, scaled, when another wave's rows set ts otherwise (the same lanes write
+    // the same words, in order). (Pass C read only the key halves: treg is still the wave's own.)
+    auto store_w = [&]() {
 #pragma unroll
         for (int c = 0; c < kNW / 4; ++c)
             *reinterpret_cast<uint4*>(treg + (16 * x + pq) * (kNW * 4) + ((c ^ x) << 4)) =
@@ -888,6 +885,10 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
 #pragma unroll
             for (int n = 0; n < kNR; ++n) rr[static_cast<int64_t>(n) * L] = (n < MAXK) ? wq[4 * kWG + n] : 0u;
         }
+    };
+    const bool wplain = !wave_any(es != kNoExp && es != 0);
+    if (!or_votes(votes)) {
+        if (wplain) store_w();
         {
             // ---- dq: to true units (head r's 2^ed from lane r of the quad), RoPE transposed at
             // position i. Lane x holds dims 16x + m of heads 0..3; the other half of pair
@@ -940,6 +941,45 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
                 if (row >= 0) store_nt(static_cast<bf16_t*>(A.dq) + row * kD + (lane & 7) * 8, v);
             }
         }
+    }
+
+    // ---- d(loss)/dt partial sums of this workgroup (fixed order), and each head's largest dS
+    // exponent over the tile ----
+#pragma unroll
+    for (int n = 0; n < MAXK; ++n) {
+        float v = active ? dt[n] : 0.f;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (lane == 0) red[wave][n] = v;
+    }
+    {
+        const int ms = head_max(es);
+        if (pq == 0) ered[wave][x][2] = ms;
+    }
+    // an LDS-only barrier: the stores in flight need not have landed (__syncthreads would wait
+    // for every one of them)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    int ts = max(max(ered[0][x][2], ered[1][x][2]), max(ered[2][x][2], ered[3][x][2]));
+    if (ts == kNoExp) ts = 0;
+
+    const int outside = or_votes(votes);
+    if (threadIdx.x == 0) {
+        if (blockIdx.x == 0) A.seqw[0] = A.seq;
+        if (outside) A.seqw[1] = A.seq;
+    }
+    if (outside) {
+        // the marker for the key side
+        if (threadIdx.x < 4) A.exps[(static_cast<int64_t>(b) * A.Hq + h0 + x) * n_tiles + tile] = kExpsFallback;
+    } else {
+        if (!wplain || wave_any(es != kNoExp && es != ts)) {
+            // dS from the row's exponent to the tile's
+            const uint32_t fs = pow2_h2(0, es == kNoExp ? 0 : es - ts);
+#pragma unroll
+            for (int y = 0; y < 4 * kWG + MAXK; ++y) wq[y] = mul_h2(wq[y], fs);
+            store_w();
+        }
         if (threadIdx.x < static_cast<unsigned>(A.n_off)) {
             float v = 0.f;
             if (threadIdx.x < MAXK) v = ((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) + red[3][threadIdx.x];
@@ -956,69 +996,39 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// bwd_fp32: the float32 tiles, after the matrix-core kernels. Virtual workgroups below n_qwg are
-// query tiles (a tile runs when the query kernel marked it), the others key tiles (a tile runs when
-// a query tile it reads from is marked, as bwd_k_dot decides). The call numbers the query kernel
-// leaves in the workspace gate the whole grid with one load: the query part runs only when a tile
-// of this call's query stage was marked, the key part only when one of the query stage its hand-off
-// comes from was. The grid is capped; each workgroup strides over the virtual ones.
+// The float32 tiles of the backward, after the matrix-core kernels. A query tile runs when the
+// query kernel marked it (its exps words); a key tile runs when a query tile it reads from is
+// marked (bwd_k_dot decides, and runs it in place of its own). The query tiles of a call run at
+// the end of bwd_k_dot where the key stage runs in the same call, else in bwd_fp32_kernel; either
+// way one load of the call numbers the query kernel leaves in the workspace skips them unless a
+// tile of this call's query stage was marked. Workgroups stride over the query kernel's ones.
 // ------------------------------------------------------------------------------------------------
-// Whether key tile `tile` of (b, g) reads from a query tile that left its outputs to the float32
-// tiles: the exps words of every query tile its terms read (window and near pairs: t0 .. t0 + 2;
-// rung n: ((j0 + a_n) >> 6) + 0, 1).
-__device__ __forceinline__ bool key_tile_marked(const BwdArgs& A, int b, int g, int tile, int n_reach, int n_tiles) {
-    const int t = threadIdx.x;
-    const int slots = 3 + 2 * n_reach;
-    bool marked = false;
-    for (int e = t; e < A.G * slots; e += kNT) {
-        const int hh = e / slots, sl = e % slots;
-        int tl = tile + sl;
-        if (sl >= 3) tl = ((tile * kTile + A.off[(sl - 3) >> 1].a) >> 6) + ((sl - 3) & 1);
-        if (tl < n_tiles)
-            marked |= (A.exps[(static_cast<int64_t>(b) * A.Hq + g * A.G + hh) * n_tiles + tl] & kExpsFallback) != 0u;
+// The marked query tiles of this call's query stage, workgroups first, first + stride, ... of the
+// query kernel's n_qwg (its tile order: q_map is 0 or 1, which does not depend on the grid's size;
+// virtual workgroup w takes the tile, and the partials slot, of that kernel's workgroup w).
+__device__ __forceinline__ void query_fp32_tiles(const BwdArgs& A, int n_qwg, int q_map, int first, int stride, char* lds) {
+    if (n_qwg <= 0 || !__builtin_amdgcn_readfirstlane(A.seqw[1] == A.seq ? 1 : 0)) return;
+    const int n_tiles = (A.L + kTile - 1) / kTile;
+    const int n_chunk = A.G >> 2;
+    for (int w = first; w < n_qwg; w += stride) {
+        int unit, tile;
+        unit_tile(w, n_tiles, q_map, unit, tile);
+        const int chunk = unit % n_chunk;
+        const int bg = unit / n_chunk;
+        const int b = bg / A.Hkv;
+        const int h0 = (bg % A.Hkv) * A.G + chunk * 4;
+        if (!(A.exps[(static_cast<int64_t>(b) * A.Hq + h0) * n_tiles + tile] & kExpsFallback)) continue;
+        __syncthreads();                        // lds is free
+        bwd_q_tile_fp32(A, b, bg, h0, tile * kTile, w, lds);
     }
-    return __syncthreads_or(marked ? 1 : 0) != 0;
 }
 
 constexpr int kFp32Grid = 1024;
 
-__global__ __launch_bounds__(kNT) void bwd_fp32_kernel(BwdArgs A, int n_qwg, int n_kwg) {
+// The query float32 tiles of a call whose key stage does not run.
+__global__ __launch_bounds__(kNT) void bwd_fp32_kernel(BwdArgs A) {
     __shared__ __attribute__((aligned(16))) char lds[kTile * 16 * 4];
-    const uint64_t s_last = A.seqw[0], s_fb = A.seqw[1];
-    const bool run_q = n_qwg > 0 && s_fb == A.seq;
-    const bool run_k = n_kwg > 0 && s_fb == s_last;
-    if (!run_q && !run_k) return;
-    const int L = A.L;
-    const int n_tiles = (L + kTile - 1) / kTile;
-    if (run_q) {
-        for (int w = blockIdx.x; w < n_qwg; w += gridDim.x) {
-            // the matrix-core query kernel's tile order (its xcd_map is 0 or 1, which does not
-            // depend on the grid's size): virtual workgroup w takes the tile, and the partials slot,
-            // of that kernel's workgroup w
-            const int n_chunk = A.G >> 2;
-            int unit, tile;
-            unit_tile(w, n_tiles, A.xcd_map, unit, tile);
-            const int chunk = unit % n_chunk;
-            const int bg = unit / n_chunk;
-            const int b = bg / A.Hkv;
-            const int h0 = (bg % A.Hkv) * A.G + chunk * 4;
-            if (!(A.exps[(static_cast<int64_t>(b) * A.Hq + h0) * n_tiles + tile] & kExpsFallback)) continue;
-            bwd_q_tile_fp32(A, b, bg, h0, tile * kTile, w, lds);
-            __syncthreads();                    // lds is free for the next tile
-        }
-    }
-    if (run_k) {
-        for (int w = blockIdx.x; w < n_kwg; w += gridDim.x) {
-            const int bg = w / n_tiles, tile = w % n_tiles;
-            const int b = bg / A.Hkv, g = bg % A.Hkv;
-            const int j0 = tile * kTile;
-            int n_reach = 0;
-            for (int n = 0; n < A.n_off; ++n)
-                if (j0 + A.off[n].a < L) n_reach = n + 1;
-            if (!key_tile_marked(A, b, g, tile, n_reach, n_tiles)) continue;
-            bwd_k_tile_fp32(A, b, bg, g, j0);
-        }
-    }
+    query_fp32_tiles(A, A.q_fp32_wg, A.xcd_map, blockIdx.x, gridDim.x, lds);
 }
 // ------------------------------------------------------------------------------------------------
 // bwd_k_dot
@@ -1041,6 +1051,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     // bring the query side's per-tile scaling to the workgroup's common one (see below)
     constexpr int kSlotsF = 3 + 2 * 2 * MAXS;
     __shared__ uint32_t fac[kMaxGKey][kSlotsF];
+    __shared__ int emax[4][2];                          // per wave: the common exponents Ev, Ek
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -1167,7 +1178,6 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     const int t0 = tile;
     const uint64_t seq_last = A.seqw[0], seq_fb = A.seqw[1], seq_sc = A.seqw[2];
     near_item(g * A.G);
-    int Ev = 0, Ek = 0;
     bool allone = true;                                 // uniform: every factor of the table is 1
     // the table; false when a query tile this tile reads from left its hand-off to the float32
     // tiles (then so does this one)
@@ -1179,6 +1189,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
                 const int e = lane + 64 * r;
                 if (e < kMaxGKey * kSlotsF) fac[e / kSlotsF][e % kSlotsF] = 0x3c003c00u;   // (1, 1)
             }
+            if (lane == 0) emax[wave][0] = emax[wave][1] = 0;
             return true;
         }
         uint32_t ew[kFacLoads];
@@ -1215,8 +1226,12 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
             mk = max(mk, __shfl_xor(mk, off, 64));
         }
         if (wave_any(marked)) return false;
-        Ev = __builtin_amdgcn_readfirstlane(mv == kNoExp ? 0 : mv);
-        Ek = __builtin_amdgcn_readfirstlane(mk == kNoExp ? 0 : mk);
+        const int Ev = __builtin_amdgcn_readfirstlane(mv == kNoExp ? 0 : mv);
+        const int Ek = __builtin_amdgcn_readfirstlane(mk == kNoExp ? 0 : mk);
+        if (lane == 0) {
+            emax[wave][0] = Ev;
+            emax[wave][1] = Ek;
+        }
         bool other = false;
 #pragma unroll
         for (int r = 0; r < kFacLoads; ++r) {
@@ -1265,6 +1280,14 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
         reinterpret_cast<uint32_t*>(&wst[k & 1][wrow])[wv] = mul_h2(pr, cw[k]);
     };
 
+    if (!__builtin_amdgcn_readfirstlane(build_factors() ? 1 : 0)) {
+        // a query tile this tile reads from left its hand-off to the float32 tiles: so does this
+        // one (the staging in flight lands first)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        bwd_k_tile_fp32(A, b, bg, g, j0);
+        query_fp32_tiles(A, A.q_fp32_wg, A.q_xcd_map, blockIdx.x, gridDim.x, lds0);
+        return;
+    }
     for (int hh = 0; hh < A.G; ++hh) {
         const int h = g * A.G + hh;
         const int64_t hrow0 = (static_cast<int64_t>(b) * A.Hq + h) * L;
@@ -1304,11 +1327,6 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
         step(qrs, lds1, kn);
         step(drs, lds1 + kBufBytes, kn);
         entries(h, kn + 1);
-        if (hh == 0 && !__builtin_amdgcn_readfirstlane(build_factors() ? 1 : 0)) {
-            // the staging in flight lands before the workgroup leaves
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            return;
-        }
         if (!__builtin_amdgcn_readfirstlane(allone ? 1 : 0)) set_cw(hh, true);
         // the near pairs' weights (same words as the far steps' table)
 #pragma unroll
@@ -1393,7 +1411,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     // to true units (the weights carried 2^-Ek and 2^-Ev)
     {
-        const float fk = pow2f(Ek), fv = pow2f(Ev);
+        const float fk = pow2f(emax[wave][1]), fv = pow2f(emax[wave][0]);
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
             dk[nb] *= fk;
@@ -1454,6 +1472,8 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
             store_nt(gv + 8, sv[1]);
         }
     }
+    // the query tiles this call's query stage left to float32
+    query_fp32_tiles(A, A.q_fp32_wg, A.q_xcd_map, blockIdx.x, gridDim.x, lds0);
 }
 
 }  // namespace
@@ -1482,6 +1502,9 @@ hipError_t launch_bwd_mfma(const BwdArgs& A0, bool want_dalpha, int stages, hipS
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    // the query float32 tiles run at the end of the key kernel where it runs in this call
+    A.q_fp32_wg = (stages & kStageQuery) ? static_cast<int32_t>(q_units * n_tiles) : 0;
+    A.q_xcd_map = q_map;
     if (stages & kStageKey) {
         A.xcd_map = (k_units % 8 == 0) ? 1 : 0;
         hipLaunchKernelGGL((bwd_k_dot_kernel<8>), dim3(static_cast<unsigned>(k_units * n_tiles)), dim3(kNT), 0, s,
@@ -1489,15 +1512,10 @@ hipError_t launch_bwd_mfma(const BwdArgs& A0, bool want_dalpha, int stages, hipS
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    // the float32 tiles of the stages run here (the kernel leaves at once unless the query stage
-    // marked a tile)
-    {
+    if ((stages & kStageQuery) && !(stages & kStageKey)) {
         A.xcd_map = q_map;
-        const int64_t n_q = (stages & kStageQuery) ? q_units * n_tiles : 0;
-        const int64_t n_k = (stages & kStageKey) ? k_units * n_tiles : 0;
-        const int64_t grid = std::min<int64_t>(std::max(n_q, n_k), kFp32Grid);
-        hipLaunchKernelGGL(bwd_fp32_kernel, dim3(static_cast<unsigned>(grid)), dim3(kNT), 0, s, A,
-                           static_cast<int>(n_q), static_cast<int>(n_k));
+        const int64_t grid = std::min<int64_t>(q_units * n_tiles, kFp32Grid);
+        hipLaunchKernelGGL(bwd_fp32_kernel, dim3(static_cast<unsigned>(grid)), dim3(kNT), 0, s, A);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -78,25 +78,11 @@ constexpr int kWgsPerCu = 4;
 // 2^-14, where relative precision is lost). Each wave writes one byte of its workgroup's word (its
 // 8 positions of the block), nonzero when a key or value row there lies outside; the attention
 // kernels check the words of the rows they read and compute such tiles in float32 from the
-// caller's bf16 rows instead. A row's 8 threads are one byte of the wave's ballot masks.
+// caller's bf16 rows instead. A row's 8 threads find its largest magnitude over 8 lanes (DPP).
 constexpr int kPrepRows = kPrepRowGroup;
 
-// bit 8r of the result: some bit of byte r of m is set
-__device__ __forceinline__ uint64_t byte_any(uint64_t m) {
-    m |= m >> 4;
-    m |= m >> 2;
-    m |= m >> 1;
-    return m & 0x0101010101010101ull;
-}
-// whether some row of the wave lies outside fp16's range, from each thread's largest magnitude
-// over its 8 elements (0 for threads without a row)
-__device__ __forceinline__ bool rows_outside_fp16(float mx) {
-    const uint64_t huge = __builtin_amdgcn_ballot_w64(mx >= kFp16Big);
-    const uint64_t nz = __builtin_amdgcn_ballot_w64(mx > 0.0f);
-    const uint64_t big = __builtin_amdgcn_ballot_w64(mx >= kFp16Small);
-    return huge != 0 || (byte_any(nz) & ~byte_any(big)) != 0;
-}
-
+// MAIN: the staged rows, the table and the flags; LO: the low parts of the rotated keys.
+template <bool MAIN, bool LO>
 __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
     const int u = threadIdx.x & 7;
     const int grp = blockIdx.y;
@@ -125,18 +111,27 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             kw[r][c] = *reinterpret_cast<const uint32_t*>(ks + row + 16 * c + 2 * u);
-            vw[r][c] = A.main ? *reinterpret_cast<const uint32_t*>(vs + row + 16 * c + 2 * u) : 0u;
+            vw[r][c] = MAIN ? *reinterpret_cast<const uint32_t*>(vs + row + 16 * c + 2 * u) : 0u;
         }
     }
+    // the cos/sin: computed by the main pass, read back from its table by a pass that writes only
+    // the low parts (so both rotate the key with the very same values)
     float2 cs[4];
+    if constexpr (MAIN) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) rope_cos_sin(jc, fh[e], fl[e], cs[e].x, cs[e].y);
-    if (grp == 0 && A.main && active) {   // the table: [L][32] (cos, sin)
+        for (int e = 0; e < 4; ++e) rope_cos_sin(jc, fh[e], fl[e], cs[e].x, cs[e].y);
+    } else {
+        const float2* t = reinterpret_cast<const float2*>(A.cs) + static_cast<int64_t>(jc) * kPairs;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cs[e] = t[pr[e]];
+    }
+    if (MAIN && grp == 0 && active) {   // the table: [L][32] (cos, sin)
         float2* t = reinterpret_cast<float2*>(A.cs) + static_cast<int64_t>(j) * kPairs;
 #pragma unroll
         for (int e = 0; e < 4; ++e) t[pr[e]] = cs[e];
     }
-    bool outside = false;
+    bool outside = false;                               // a row of the thread's group lies outside
+    float elem_max = 0.f;                               // the thread's largest element of every row
 #pragma unroll
     for (int r = 0; r < kPrepRows; ++r) {
         const int bh = grp * kPrepRows + r;
@@ -149,16 +144,25 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
         float kmax = 0.f, vmax = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            rx[e] = x[e] * cs[e].x - y[e] * cs[e].y;
-            ry[e] = y[e] * cs[e].x + x[e] * cs[e].y;
+            // the rotated key rounded to float32 first, in every instantiation alike (the staged
+            // fp16 row and its low part may come from different passes): explicit fused forms, and
+            // an empty asm that keeps the compiler from folding the fp16 conversion into the fma
+            // (which would round the exact value once instead)
+            rx[e] = fmaf(x[e], cs[e].x, -(y[e] * cs[e].y));
+            ry[e] = fmaf(y[e], cs[e].x, x[e] * cs[e].y);
+            asm volatile("" : "+v"(rx[e]), "+v"(ry[e]));
             kmax = fmaxf(kmax, fmaxf(fabsf(rx[e]), fabsf(ry[e])));
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) vmax = fmaxf(vmax, fmaxf(fabsf(bf16_lo(vw[r][c])), fabsf(bf16_hi(vw[r][c]))));
-        if (A.main) outside |= rows_outside_fp16(live ? kmax : 0.f) || rows_outside_fp16(live ? vmax : 0.f);
+        if constexpr (MAIN) {
+            const float km = oct_max(live ? kmax : 0.f), vm = oct_max(live ? vmax : 0.f);
+            outside |= (km > 0.f && km < kFp16Small) || (vm > 0.f && vm < kFp16Small);
+            elem_max = fmaxf(elem_max, live ? fmaxf(kmax, vmax) : 0.f);
+        }
         if (!live) continue;
         // element 8u + e: e < 4 is dim 16e + 2u, e >= 4 is dim 16(e - 4) + 2u + 1
-        if (A.main) {
+        if constexpr (MAIN) {
             store4<f16_t>(A.k16 + row + 8 * u, make_float4(rx[0], rx[2], ry[0], ry[2]));
             store4<f16_t>(A.k16 + row + 8 * u + 4, make_float4(rx[1], rx[3], ry[1], ry[3]));
             store4<f16_t>(A.v16 + row + 8 * u,
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
             store4<f16_t>(A.v16 + row + 8 * u + 4,
                           make_float4(bf16_hi(vw[r][0]), bf16_hi(vw[r][1]), bf16_hi(vw[r][2]), bf16_hi(vw[r][3])));
         }
-        if (A.k16lo != nullptr) {
+        if constexpr (LO) {
             // what fp16 rounding left out of each rotated key element: a second fp16 operand
             // whose product with q restores the score to about 2^-22 relative
             auto lo = [](float v) { return v - static_cast<float>(static_cast<_Float16>(v)); };
@@ -174,9 +178,12 @@ __global__ __launch_bounds__(256) void prep_kv16_kernel(PrepArgs A) {
             store4<f16_t>(A.k16lo + row + 8 * u + 4, make_float4(lo(rx[1]), lo(rx[3]), lo(ry[1]), lo(ry[3])));
         }
     }
-    if (A.main && (threadIdx.x & 63) == 0)
-        reinterpret_cast<uint8_t*>(A.flags)[(static_cast<int64_t>(grp) * A.n_blk + blockIdx.x) * 4 + (threadIdx.x >> 6)] =
-            outside ? 1 : 0;
+    if constexpr (MAIN) {
+        const bool any = __builtin_amdgcn_ballot_w64(outside || elem_max >= kFp16Big) != 0;
+        if ((threadIdx.x & 63) == 0)
+            reinterpret_cast<uint8_t*>(A.flags)[(static_cast<int64_t>(grp) * A.n_blk + blockIdx.x) * 4 + (threadIdx.x >> 6)] =
+                any ? 1 : 0;
+    }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -575,7 +582,12 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
 
 hipError_t launch_prep_kv16(const PrepArgs& A, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(A.n_blk), static_cast<unsigned>((A.n_bh + kPrepRows - 1) / kPrepRows));
-    hipLaunchKernelGGL(prep_kv16_kernel, grid, dim3(256), 0, s, A);
+    if (A.main && A.k16lo != nullptr)
+        hipLaunchKernelGGL((prep_kv16_kernel<true, true>), grid, dim3(256), 0, s, A);
+    else if (A.main)
+        hipLaunchKernelGGL((prep_kv16_kernel<true, false>), grid, dim3(256), 0, s, A);
+    else if (A.k16lo != nullptr)
+        hipLaunchKernelGGL((prep_kv16_kernel<false, true>), grid, dim3(256), 0, s, A);
     return hipGetLastError();
 }
 

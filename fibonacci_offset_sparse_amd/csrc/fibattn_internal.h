@@ -129,6 +129,8 @@ struct BwdArgs {
     // with some tile's exponents not all 0 (written by the query kernel)
     uint64_t* seqw;
     uint64_t seq;        // this call's number (the host's count of backward calls, from 1)
+    int32_t q_fp32_wg;   // workgroups of this call's query stage (0 without it): its float32 tiles
+    int32_t q_xcd_map;   // the query kernel's tile order
     float qscale;        // log2(e)/sqrt(D)
     int32_t xcd_map;
 };

@@ -321,6 +321,14 @@ __device__ __forceinline__ float oct_sum(float v) {
     return v;
 }
 
+// Largest of v over the same 8 lanes.
+__device__ __forceinline__ float oct_max(float v) {
+    v = fmaxf(v, quad_f<0xB1>(v));
+    v = fmaxf(v, quad_f<kXor2>(v));
+    v = fmaxf(v, quad_f<0x141>(v));
+    return v;
+}
+
 // Dims 8e .. 8e + 7 of a bf16 row, rotated at position j (cos/sin from the table). Dim d pairs
 // with d + 32 (e < 4: x' = x cos - y sin) or d - 32 (e >= 4: y' = y cos + x sin): dims of e ^ 4.
 __device__ __forceinline__ void rot_eighth(const bf16_t* row, const float* cstab, int j, int e, float (&out)[8]) {
