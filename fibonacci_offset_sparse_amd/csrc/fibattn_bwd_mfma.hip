@@ -440,7 +440,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     };
     uint4 qraw[8], draw[8];
     float4 ctq[4];                                      // cos/sin of pairs 8x..8x+7 at position i
-    bool flagged;                                       // a staged row the lane checks lies outside fp16's range
+    uint32_t flagged;                                   // nonzero: a staged row the lane checks lies outside fp16's range
     {
         // the 4 heads' rows (4 L rows of 128 bytes: within 32 bits for L <= 2^20); positions past
         // L read row L - 1 (finite, never used)
@@ -494,7 +494,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         }
         if (eq == kNoExp) eq = 0;
         if (ed == kNoExp) ed = 0;
-        post_vote(votes, wave, flagged);
+        post_vote(votes, wave, flagged != 0u);
     }
     const bool wscaled = wave_any(eq != 0 || ed != 0);  // uniform: some row of the wave is scaled
     // head x's largest q and do exponents over the tile (read from LDS where needed: registers

@@ -335,44 +335,31 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     const int jn = i0 - kNear;                          // the near block's row at slot 0
     auto buf = [&](int j) -> char* { return (j & 1) ? lds1 : lds0; };
 
-    // ---- prologue: q of the wave's 16 positions and 4 heads by LDS DMA into the wave's 8 KB
-    // (1 KB contiguous per instruction; lane l lands on slot 8u + (l >> 3), physical chunk l & 7,
-    // and fetches the logical chunk the swizzle puts there), read back one row per lane; then the
-    // key near block (item 0) and item 1 (key far step kn) ----
+    // ---- prologue: q of the lane's row (head h0 + x, position i; past L the row L - 1, finite
+    // and never used) straight into registers, 16 bytes at a time, then the key near block (item
+    // 0) and item 1 (key far step kn): all in flight together, and the q build below waits for q
+    // alone (loads count in vmcnt in issue order) ----
     uint4 qraw[8];
     float4 ctab[4];
-    bool flagged;                                       // a staged row the lane checks lies outside fp16's range
+    uint32_t flagged;                                   // nonzero: a staged row the lane checks lies outside fp16's range
     {
-        char* const reg = (wave < 2 ? lds0 : lds1) + (wave & 1) * 8192;
-        // the 4 heads' rows (4 L rows of 128 bytes: within 32 bits for L <= 2^20); positions
-        // past L read row L - 1 (finite, never used)
-        const __amdgpu_buffer_rsrc_t qrs4 = rows_rsrc(A.q, (static_cast<int64_t>(b) * A.Hq + h0) * L, 4 * L);
+        const uint4* qrow = reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(A.q) +
+                                                           ((static_cast<int64_t>(b) * A.Hq + h0 + x) * L + min(i, L - 1)) * kD);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int sl = lin_slot(lane, u);
-            const int pos = min(i0 + 16 * wave + (sl & 15), L - 1);
-            const int voff = ((sl >> 4) * L + pos) * kRowBytes + (((lane & 7) ^ tr_f(sl)) << 4);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs4, dma_dst(reg + u * 1024), 16, voff, 0, 0, 2);
-        }
+        for (int c = 0; c < 8; ++c) qraw[c] = qrow[c];
         // the cos/sin of the position: lane x loads pairs 8x..8x+7; the rotation takes the others
         // from the quad's lanes
         const float4* ct = reinterpret_cast<const float4*>(A.cstab) + static_cast<int64_t>(active ? i : 0) * (kPairs / 2) + 4 * x;
 #pragma unroll
         for (int u = 0; u < 4; ++u) ctab[u] = ct[u];
-        // the range flags of the staged rows this tile reads (in flight with q)
+        // the range flags of the staged rows this tile reads
         flagged = rows_flagged(A, bg / kPrepRowGroup, i0, n_reach);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-        for (int c = 0; c < 8; ++c) qraw[c] = *reinterpret_cast<const uint4*>(reg + row_view_addr(pq, x, c));
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();                   // every wave is done with its rows
-        asm volatile("" ::: "memory");
     }
     st.near(krs, lds0, jn);
     step(krs, lds1, kn);                                // (zero rows when no far rung is reached)
     // whether some row of the tile lies outside the fp16 range (then the whole tile is computed in
     // float32): each wave's vote, read after a later barrier
-    post_vote(votes, wave, flagged || (active && q_outside_fp16(qraw, A.qscale)));
+    post_vote(votes, wave, flagged != 0u || (active && q_outside_fp16(qraw, A.qscale)));
 
     // q of head h0 + x, rotated at its position and scaled by qscale, fp16, in the keys' permuted
     // order: word 2m holds dims (m, 16 + m), word 2m + 1 dims (32 + m, 48 + m), i.e. the x and y

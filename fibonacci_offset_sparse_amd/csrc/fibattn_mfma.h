@@ -345,14 +345,14 @@ __device__ __forceinline__ void rot_eighth(const bf16_t* row, const float* cstab
     }
 }
 
-// The range flag of the staged rows that thread t of a tile checks: threads 0..3 the near block
+// The range flag word (nonzero: flagged) of the staged rows that thread t of a tile checks: threads 0..3 the near block
 // (rows i0 - 64 .. i0 + 63), thread 4 + 4n + u the u-th flag block of kept rung n's rows
 // i0 - a - 1 .. i0 + 63 - a (clipped at 0), for rungs the tile reaches (at most 16: the matrix-core
 // kernels' limit); every other thread none. The rung's floor comes from the uniform offset table by
 // a per-lane choice among scalars: a per-lane index into the kernel arguments would be a vector
 // load followed by a full wait behind every load in flight (here: the q burst).
 template <typename Args>
-__device__ __forceinline__ bool rows_flagged(const Args& A, int grp, int i0, int n_reach) {
+__device__ __forceinline__ uint32_t rows_flagged(const Args& A, int grp, int i0, int n_reach) {
     const int t = threadIdx.x;
     int blk = -1;
     if (t < 4) {
@@ -367,8 +367,11 @@ __device__ __forceinline__ bool rows_flagged(const Args& A, int grp, int i0, int
             if (lo / kFlagRows + u <= hi / kFlagRows) blk = lo / kFlagRows + u;
         }
     }
-    if (blk < 0 || blk >= A.n_blk) return false;
-    return A.kvflags[static_cast<int64_t>(grp) * A.n_blk + blk] != 0u;
+    // every lane loads (word 0 where it checks none), so that the test of the word can wait until
+    // the caller needs it instead of stalling the loads issued after this one
+    const bool real = blk >= 0 && blk < A.n_blk;
+    const uint32_t w = A.kvflags[real ? static_cast<int64_t>(grp) * A.n_blk + blk : 0];
+    return real ? w : 0u;
 }
 
 }  // namespace mx

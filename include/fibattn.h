@@ -28,7 +28,11 @@
  * Storage types: FIBATTN_F32 (float32 everywhere) or FIBATTN_BF16 (bfloat16 q, k, v, o, do, dq,
  * dk, dv; dot products take fp16-rounded operands - rotated q and k, values, softmax weights,
  * do - with float32 accumulation, and the softmax, its gradient and every reduction run in
- * float32; decode computes in float32 throughout).
+ * float32; decode computes in float32 throughout). Every finite bf16 input is accepted: rows
+ * that fp16 does not hold well as they are (an element of 2^15 or more, or a nonzero row whose
+ * largest element is below 2^-10) are either carried scaled by a power of two, which the kernels
+ * undo exactly in float32 (q, do and the backward's hand-off of dS), or, for keys and values,
+ * make every tile that reads them compute in float32 from the caller's bf16 rows.
  *
  * Ownership and execution. All buffers belong to the caller. Device pointers must stay valid
  * until the stream reaches the work. `offsets` is a host array, read during the call and not
@@ -145,8 +149,10 @@ size_t fibattn_fwd_workspace_bytes(int32_t B, int32_t L, int32_t Hkv, int32_t D,
  * fp16, and the matrix-core kernels also round the rotated q and the softmax weights to fp16 for
  * their products (each operand within 2^-11 relative); products accumulate in float32, and the
  * interpolation weight t is applied in float32 (to scores and weights on the matrix cores, to
- * the staged rows in the general kernels). Inputs must stay below 65504 in magnitude (after
- * rotation) for this to hold.
+ * the staged rows in the general kernels). The prep flags blocks of key and value rows that
+ * fp16 does not hold well (see Storage types above); a tile that reads a flagged row, or whose
+ * own q row (times 1/sqrt(D)) lies outside fp16's range, is computed in float32 from the
+ * caller's bf16 rows instead, so any finite input is handled.
  * Errors: INVALID (NULL pointers, B/L/Hq/Hkv < 1, Hq % Hkv != 0, W < 0, K outside [0, 32],
  * bad alpha, bad offsets, unknown dtype, rope_theta not finite and > 0), UNSUPPORTED (D != 64,
  * W > 31, L > 2^20), WORKSPACE, HIP.
@@ -162,7 +168,9 @@ fibattn_status_t fibattn_fwd(const void* q, const void* k, const void* v, double
  * key row at its position once (RoPE before the gather, §2 "Attended set") into the workspace.
  * For FIBATTN_F32 the rotated keys are stored as float32; for FIBATTN_BF16 the rotated keys and
  * the values are stored as fp16 rows (bf16 values of magnitude below 65504 convert exactly), with
- * the cos/sin table of every position. The backward's FIBATTN_STAGE_PREP writes the same arrays
+ * the cos/sin table of every position and one range flag per block of 32 positions of 4 (batch,
+ * head) rows (nonzero where a key or value row there lies outside what fp16 holds well: an
+ * element of 2^15 or more, or a nonzero row maximum below 2^-10). The backward's FIBATTN_STAGE_PREP writes the same arrays
  * at the same places of its (larger) workspace where fibattn_bwd_reuses_fwd_prep says so.
  * k, v: device [B, Hkv, L, D] of `dtype`. Errors as fibattn_fwd.
  */
