@@ -39,7 +39,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_bytes_l1024_linear.json")
 TRAFFIC_WORKLOAD = "l1024_linear_bf16"
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix-core peak (the forward's products run there)
 FWD_TARGET_FRAC = 0.60          # the forward attention's target: 60 % of peak HBM bandwidth
-STREAM_BYTES = 1 << 30          # streaming probe buffers (four times the Infinity Cache)
+STREAM_BYTES = 1 << 30
+LDS_PROBE_BYTES = 16 << 20          # streaming probe buffers (four times the Infinity Cache)
 
 
 def log(*a):
@@ -203,8 +204,30 @@ def stream_probe(dev, reps: int = 10):
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
         out[f"{name}_TBps"] = moved * STREAM_BYTES / (ms * 1e-3) / 1e12
+    # LDS staging from a buffer that stays on chip (the attention kernels' staging instruction and
+    # grain), 16 MiB read 16 times per launch
+    lib.streamprobe_lds_bytes.restype = ctypes.c_int64
+    lib.streamprobe_lds_bytes.argtypes = [ctypes.c_int64]
+    small = LDS_PROBE_BYTES
+    moved = int(lib.streamprobe_lds_bytes(small))
+
+    def launch_lds():
+        rc = lib.streamprobe_launch(4, a.data_ptr(), b.data_ptr(), sink.data_ptr(), small, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"stream probe launch failed ({rc})")
+    for _ in range(3):
+        launch_lds()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        launch_lds()
+    e1.record()
+    torch.cuda.synchronize()
+    out["lds_stage_TBps"] = moved / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
     out["what"] = ("1 GiB buffers, 16-byte coalesced accesses, one pass per launch (libstreamprobe.so); copy "
-                   "counts bytes read plus bytes written")
+                   "counts bytes read plus bytes written; lds_stage: 1 KB buffer-to-LDS transfers (the "
+                   "attention kernels' staging) from a 16 MiB buffer that stays on chip, read 16 times")
     del a, b, sink
     torch.cuda.empty_cache()
     return out
@@ -428,6 +451,40 @@ def fwd_slot_counts(fa, w, alpha: float, base):
     return w.B * w.Hq * (win + kept), w.B * w.Hkv * interp
 
 
+def fwd_staged_bytes(fa, w, alpha: float, base) -> int:
+    """Bytes the matrix-core forward stages from the staged key and value rows into LDS in one call
+    (rows inside [0, L) only: the rest arrive as zeros without a memory access). Per workgroup
+    (64 queries, 4 heads of one key-value head): for keys and for values, the near block (rows
+    i0 - 64 .. i0 + 63) and each rung step from the first far pair on (two blocks of 72 rows,
+    i0 - a - 1 and i0 - a' - 3 on, a block only where its rung is reached)."""
+    kind, a_all, _, reach = fa.fibattn_plan(alpha, w.W, base)
+    kept = [(int(a), int(r) - int(a)) for kd, a, r in zip(kind, a_all, reach) if kd != fa.DUP]
+    L = w.L
+
+    def rows(j0, n):
+        return max(0, min(j0 + n, L) - max(j0, 0))
+    per_unit = 0
+    for i0 in range(0, L, 64):
+        n_reach = 0
+        for n, (a, it) in enumerate(kept):
+            if i0 + 63 >= a + it:
+                n_reach = n + 1
+        n_steps = (n_reach + 1) >> 1
+        n_near = 0
+        for n in range(n_reach):
+            if kept[n][0] <= 63:
+                n_near = n + 1
+        kn = (n_near >> 1) & ~1
+        r = rows(i0 - 64, 128)
+        for k in range(kn, n_steps):
+            if 2 * k < n_reach:
+                r += rows(i0 - kept[2 * k][0] - 1, 72)
+            if 2 * k + 1 < n_reach:
+                r += rows(i0 - kept[2 * k + 1][0] - 3, 72)
+        per_unit += 2 * r * w.D * 2                      # keys and values, fp16 rows
+    return per_unit * w.B * w.Hkv * (w.Hq // w.Hkv // 4)
+
+
 def measure(fa, name: str, steps: int, warmup: int, dev):
     w = workloads.WORKLOADS[name]
     log(f"[{name}] allocating inputs")
@@ -490,6 +547,10 @@ def measure(fa, name: str, steps: int, warmup: int, dev):
              "what": "forward attention kernel, layer average: algorithmic flops (QK, P.V and the blend of "
                      "interpolated rows) over its time, against the dense fp16 matrix-core peak, where its "
                      "products run"}
+    staged = sum(fwd_staged_bytes(fa, w, a, net.base) for a in net.alphas) / len(net.alphas)
+    staging = {"bytes_per_call": staged, "TBps": staged / (st["fwd_attend"] * 1e-3) / 1e12,
+               "what": "forward attention kernel, layer average: bytes it stages from the on-chip-resident "
+                       "staged key and value rows into LDS, over its time"}
     res = {
         "ms_per_step": ms_step,
         "wall_s": wall,
@@ -504,6 +565,7 @@ def measure(fa, name: str, steps: int, warmup: int, dev):
                 "algorithmic_bytes": bwd_bytes},
         "kernels_ms": st,
         "arith_fwd_attend": arith,
+        "staging_fwd_attend": staging,
         "per_layer": per_layer,
         "kernel_bytes": kernel_bytes,
         "integer_path": integer_path,
@@ -591,6 +653,8 @@ def main():
         "bwd": main_res["bwd"],
         "kernels_ms": main_res["kernels_ms"],
         "arith_fwd_attend": main_res["arith_fwd_attend"],
+        "staging_fwd_attend": dict(main_res["staging_fwd_attend"],
+                                   frac_of_lds_stage_probe=main_res["staging_fwd_attend"]["TBps"] / probe["lds_stage_TBps"]),
         "per_layer": main_res["per_layer"],
         "integer_path": main_res["integer_path"],
         "cpu_baseline": cpu,
@@ -612,6 +676,9 @@ def main():
                          "qh_per_s": long_res["qh_per_s"], "fwd": long_res["fwd"], "bwd": long_res["bwd"],
                          "kernels_ms": long_res["kernels_ms"], "per_layer": long_res["per_layer"],
                          "arith_fwd_attend": long_res["arith_fwd_attend"],
+                         "staging_fwd_attend": dict(long_res["staging_fwd_attend"],
+                                                    frac_of_lds_stage_probe=long_res["staging_fwd_attend"]["TBps"]
+                                                    / probe["lds_stage_TBps"]),
                          "integer_path": long_res["integer_path"]}
     print(json.dumps(line), flush=True)
 

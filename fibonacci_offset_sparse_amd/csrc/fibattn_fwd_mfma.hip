@@ -438,18 +438,27 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     // far steps: lane x reads rung 2k + (x >> 1), near (x even) or far row
     const int rslot = p + ((x >> 1) ? kBlkSlots + 2 : 0) + ((x & 1) ? 0 : 1);
     const int rbase = rslot * kRowBytes, rsw = swz(rslot);
+    // The last far step computes from buffer 1 when there is an odd number of them (kn is even):
+    // buffer 0 is free then, and the value near block goes ahead under that step (its barrier
+    // waits for the step's loads only: the near block's 4 transfers per wave stay in flight).
+    const bool near_ahead = n_steps > kn && ((n_steps - kn) & 1) != 0;
 #pragma unroll
     for (int k = 0; k < MAXS; ++k) {
         if (k >= kn && k < n_steps) {                   // buffer (k + 1) % 2
-            if (k + 1 < n_steps) step(krs, buf(k + 2), k + 1);
+            const bool last = k + 1 >= n_steps;
+            if (!last) step(krs, buf(k + 2), k + 1);
+            else if ((k & 1) == 0) st.near(vrs, lds0, jn);
             score(row_dot_group(q, buf(k + 1), rbase, rsw), k);
-            publish<0>();
+            if (last && (k & 1) == 0)
+                publish<4>();
+            else
+                publish<0>();
         }
     }
 
-    // ---- value near block into buffer 0 and value far step kn into buffer 1 (both free after
-    // the last barrier), under the softmax ----
-    st.near(vrs, lds0, jn);
+    // ---- value near block into buffer 0 (unless it went ahead) and value far step kn into
+    // buffer 1 (both free after the last barrier), under the softmax ----
+    if (!near_ahead) st.near(vrs, lds0, jn);
     step(vrs, lds1, kn);
 
     // ---- exact softmax; weights as fp16 groups of 4 ----

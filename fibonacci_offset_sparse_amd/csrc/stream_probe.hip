@@ -3,11 +3,13 @@
 // library's interface: libstreamprobe.so is loaded by the benchmark only.
 //
 // Three patterns over buffers far larger than the 256 MB Infinity Cache, 16-byte accesses, every
-// lane touching consecutive 16-byte chunks of its wave's 1 KB span (fully coalesced):
+// lane touching consecutive 16-byte chunks of its wave's 1 KB span (fully coalesced), and one of
+// buffer-to-LDS staging from a buffer small enough to stay on chip:
 //   read  : sum every chunk (one float per thread written at the end, so nothing is optimised away)
 //   write : fill every chunk (plain stores, or non-temporal)
 //   copy  : read a chunk, write it elsewhere
-// One thread per kChunks chunks; the grid covers the buffer once.
+//   lds   : stage a buffer of a few tens of MB into LDS, over and over (see lds_read_kernel)
+// One thread per kChunks chunks; the grid covers the buffer once (lds: a fixed grid).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -64,6 +66,40 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const uint4* __restrict_
     }
 }
 
+// LDS staging from a buffer that stays on chip (sized like the attention kernels' staged rows:
+// a few tens of MB, read over and over from the caches in front of HBM): each workgroup issues
+// 1 KB contiguous buffer-to-LDS transfers, 16 bytes per lane, into its 16 KB of LDS, chunk after
+// chunk with no compute, and waits for them at the end. The attention kernels stage their rows
+// with the same instruction and grain.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// The LDS address of a __shared__ location (an address-space cast, kept in an SGPR: the same for
+// the whole wave), as the buffer-to-LDS transfer takes it.
+__device__ __forceinline__ lds_ptr_t lds_addr(char* p) {
+    uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+    asm volatile("" : "+s"(a));
+    return (lds_ptr_t)static_cast<uintptr_t>(a);
+}
+
+constexpr int kLdsChunk = 16384;   // one workgroup's chunk: 16 transfers of 1 KB (4 per wave)
+constexpr int kLdsGrid = 2048;     // 8 workgroups per CU
+constexpr int kLdsPasses = 16;     // times the buffer is read
+
+__global__ __launch_bounds__(kThreads) void lds_read_kernel(const uint4* __restrict__ src, int64_t chunks, int64_t per_wg) {
+    __shared__ __attribute__((aligned(1024))) char buf[kLdsChunk];
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(src), 0, 0x7fffffff, 0x00020000);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    for (int64_t k = 0; k < per_wg; ++k) {
+        const int64_t c = (static_cast<int64_t>(blockIdx.x) + k * gridDim.x) % chunks;
+        const int base = static_cast<int>(c * kLdsChunk);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int g = wave + 4 * u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_addr(buf + g * 1024), 16, base + g * 1024 + lane * 16, 0, 0, 0);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 unsigned blocks_for(int64_t n) {
     return static_cast<unsigned>((n + static_cast<int64_t>(kThreads) * kChunks - 1) / (static_cast<int64_t>(kThreads) * kChunks));
 }
@@ -72,13 +108,22 @@ unsigned blocks_for(int64_t n) {
 
 extern "C" {
 
-// pattern: 0 read, 1 write, 2 write (non-temporal), 3 copy. a, b: device buffers of `bytes`
-// bytes (b unused by read and write; sink: device float[blocks] for read). bytes: a multiple of 16.
-// Returns the hipError_t of the launch (0 on success). The caller times the launch on `stream`.
+// pattern: 0 read, 1 write, 2 write (non-temporal), 3 copy, 4 LDS staging of a resident buffer.
+// a, b: device buffers of `bytes` bytes (b unused by read, write and 4; sink: device
+// float[blocks] for read). bytes: a multiple of 16 (of 16384 for 4). Pattern 4 moves `passes`
+// times `bytes` into LDS (passes: the caller's; `b` is ignored there, and the byte count to time
+// against is streamprobe_lds_bytes). Returns the hipError_t of the launch (0 on success). The
+// caller times the launch on `stream`.
 int streamprobe_launch(int pattern, void* a, void* b, float* sink, int64_t bytes, void* stream) {
     const int64_t n = bytes / 16;
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (pattern) {
+        case 4: {
+            const int64_t chunks = bytes / kLdsChunk;
+            hipLaunchKernelGGL(lds_read_kernel, dim3(kLdsGrid), dim3(kThreads), 0, s, static_cast<const uint4*>(a), chunks,
+                               chunks * kLdsPasses / kLdsGrid);
+            break;
+        }
         case 0: hipLaunchKernelGGL(read_kernel, dim3(blocks_for(n)), dim3(kThreads), 0, s, static_cast<const uint4*>(a), n, sink); break;
         case 1: hipLaunchKernelGGL((write_kernel<false>), dim3(blocks_for(n)), dim3(kThreads), 0, s, static_cast<uint4*>(a), n); break;
         case 2: hipLaunchKernelGGL((write_kernel<true>), dim3(blocks_for(n)), dim3(kThreads), 0, s, static_cast<uint4*>(a), n); break;
@@ -90,5 +135,11 @@ int streamprobe_launch(int pattern, void* a, void* b, float* sink, int64_t bytes
 
 // Blocks of the read pattern for `bytes` (the sink's length).
 int64_t streamprobe_read_blocks(int64_t bytes) { return blocks_for(bytes / 16); }
+
+// Bytes pattern 4 moves for a buffer of `bytes`.
+int64_t streamprobe_lds_bytes(int64_t bytes) {
+    const int64_t chunks = bytes / kLdsChunk;
+    return chunks * kLdsPasses / kLdsGrid * kLdsGrid * kLdsChunk;
+}
 
 }  // extern "C"
