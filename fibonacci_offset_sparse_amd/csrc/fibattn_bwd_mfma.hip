@@ -371,8 +371,13 @@ __device__ __forceinline__ void bwd_k_tile_fp32(const BwdArgs& A, int b, int bg,
 // cancellation and would otherwise inherit the 2^-11 rounding of q and k relative to its
 // (small) value. Pass AB then runs as pass A (keys and their low parts: scores) and pass B
 // (values: dP).
-template <int MAXS, bool PRECISE>
+// INT: every kept rung is integral (the integer-offset path of §2 "Implementation note"; d(alpha)
+// is not defined there, so never with PRECISE): as in the forward, the rungs with a <= 64 come from
+// the near block four to a group (at most two groups) and far steps stage 64-row blocks of the
+// near rows alone. The hand-off to the key side stays indexed by rung.
+template <int MAXS, bool PRECISE, bool INT>
 __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
+    static_assert(!(PRECISE && INT), "d(alpha) is not defined for integral rungs");
     constexpr int MAXK = 2 * MAXS;
     // Two item buffers used in turn, each a key part and a value part. Items: the key and value
     // near blocks, then the key and value far steps (pass AB); then the key near block and key
@@ -403,14 +408,20 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     int n_reach = 0;
     for (int n = 0; n < A.n_off; ++n)
         if (i0 + kTile - 1 >= A.off[n].a + A.off[n].interp) n_reach = n + 1;
-    const int n_steps = (n_reach + 1) >> 1;
     // near rungs: the prefix with a <= 63 (near and far rows inside the near block, key rows
-    // i0 - 64 .. i0 + 63). Rung pairs k < kn come from the near block, kn even; pairs
-    // kn .. n_steps - 1 are far steps, pair k in buffer (k + 1) % 2.
+    // i0 - 64 .. i0 + 63; INT: a <= 64, the one row). Steps k < kn come from the near block, kn
+    // even: rung pairs 2k, 2k + 1, or (INT) for even k a group of the four rungs 2k .. 2k + 3
+    // (those past nn are padding). Steps kn .. n_steps - 1 are far steps, step k in buffer
+    // (k + 1) % 2, holding rungs 2k - ro and 2k - ro + 1 (ro = 0 unless INT). Products of step k
+    // go to slots 2k and 2k + 1 (a near group: 2k .. 2k + 3).
     int n_near = 0;
     for (int n = 0; n < n_reach; ++n)
-        if (A.off[n].a <= kNear - 1) n_near = n + 1;
-    const int kn = (n_near >> 1) & ~1;
+        if (A.off[n].a <= kNear - (INT ? 0 : 1)) n_near = n + 1;
+    const int nn = INT ? min(n_near, 8) : 0;
+    const int kn = INT ? 2 * ((nn + 3) >> 2) : (n_near >> 1) & ~1;
+    const int ro = INT ? 2 * kn - nn : 0;
+    const int n_steps = INT ? kn + ((n_reach - nn + 1) >> 1) : (n_reach + 1) >> 1;
+    constexpr int kStepDmas = INT ? 4 : 6;              // DMA instructions per wave of a far step
 
     const int64_t kv_row0 = static_cast<int64_t>(bg) * L;
     const __amdgpu_buffer_rsrc_t krs = rows_rsrc(A.kstage, kv_row0, L);
@@ -419,10 +430,16 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     const __amdgpu_buffer_rsrc_t hrs = PRECISE ? rows_rsrc(A.kstage_lo, kv_row0, L) : vrs;
     Stager st;
     st.init(lane, wave);
+    // (INT: the near row of position p at slot p or 72 + p)
     auto step = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int k) {
-        st.step(rs, dst, 2 * k < n_reach, i0 - A.off[2 * k].a - 1, 2 * k + 1 < n_reach, i0 - A.off[2 * k + 1].a - 3);
+        if constexpr (INT) {
+            const int n = 2 * k - ro;
+            st.step64(rs, dst, n < n_reach, i0 - A.off[n].a, n + 1 < n_reach, i0 - A.off[n + 1].a);
+        } else {
+            st.step(rs, dst, 2 * k < n_reach, i0 - A.off[2 * k].a - 1, 2 * k + 1 < n_reach, i0 - A.off[2 * k + 1].a - 3);
+        }
     };
-    auto kv_step = [&](char* dst, int k) {         // 12 DMA instructions per wave
+    auto kv_step = [&](char* dst, int k) {         // 2 kStepDmas DMA instructions per wave
         step(krs, dst, k);
         step(hrs, dst + kBufBytes, k);
     };
@@ -569,13 +586,14 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             }
         }
     }
-    publish<12>();                                      // the key and value near blocks have landed
+    publish<2 * kStepDmas>();                           // the key and value near blocks have landed
 
     // ---- pass AB: scores s (base 2) with the keys, dP = do . value row with the values, and for
     // each rung far - near of both products (PRECISE: pass A, the scores, then pass B, dP) ----
     float s[4 * kWG + MAXK], sd[MAXK], dp[4 * kWG + MAXK], dpd[MAXK];
     const int s0 = p - x + kNear;                       // window: lane x reads distance 4g + x
-    const int rslot = p + ((x >> 1) ? kBlkSlots + 2 : 0) + ((x & 1) ? 0 : 1);   // far-step rung rows
+    const int rslot = INT ? p + ((x >> 1) ? kBlkSlots : 0)                      // far-step rung rows
+                          : p + ((x >> 1) ? kBlkSlots + 2 : 0) + ((x & 1) ? 0 : 1);
     const int rbase = rslot * kRowBytes, rsw = swz(rslot);
     // a rung pair's products (lane x: rung 2k + (x >> 1), near row for x even, far row for x odd)
     auto score_terms = [&](const f4_t& acc, int k) {
@@ -592,8 +610,21 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             }
         }
     };
-    // both products of a rung pair at once (one read of each rung's parameters)
+    // both products of a rung pair at once (one read of each rung's parameters); INT: the near
+    // rows of rungs 2k - ro + e in columns 2e, slots 2k + e
     auto pair_terms = [&](const f4_t& acc, const f4_t& accv, int k) {
+        if constexpr (INT) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int n = 2 * k + e - ro;
+                if (n < n_reach) {
+                    const bool ok = active && i >= A.off[n].a;
+                    s[4 * kWG + 2 * k + e] = ok ? acc[2 * e] * qsc : kNegInf;
+                    dp[4 * kWG + 2 * k + e] = accv[2 * e];
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int n = 2 * k + e;
@@ -631,6 +662,10 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     auto near_slot = [&](int k) {   // near rung pair k: near row i - a at slot p + 64 - a, far one down
         return p + kNear - pick_uniform((x >> 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a) - (x & 1);
     };
+    // INT, near group of step k (even): the distance of rung 2k + c, 0 (the window's own row, a
+    // staged row) for padding; lane c reads rung 2k + c at slot p + 64 - a (pass C: position pt)
+    auto near_a = [&](int k, int c) -> int { return 2 * k + c < nn ? A.off[2 * k + c].a : 0; };
+    auto group_a = [&](int k, int c) -> int { return pick4(c, near_a(k, 0), near_a(k, 1), near_a(k, 2), near_a(k, 3)); };
 #pragma unroll
     for (int k = 0; k < MAXK; ++k) {
         s[4 * kWG + k] = kNegInf;
@@ -656,7 +691,21 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     }
 #pragma unroll
     for (int k = 0; k < MAXS; ++k) {
-        if (k < kn) {
+        if constexpr (INT) {
+            if ((k & 1) == 0 && k < kn) {
+                const int sl = p + kNear - group_a(k, x);
+                const f4_t acc = qk(lds0, sl * kRowBytes, swz(sl));
+                const f4_t accv = row_dot_group(dov, lds0 + voff, sl * kRowBytes, swz(sl));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int n = 2 * k + c;
+                    if (n < nn) {
+                        s[4 * kWG + n] = (active && i >= A.off[n].a) ? acc[c] * qsc : kNegInf;
+                        dp[4 * kWG + n] = accv[c];
+                    }
+                }
+            }
+        } else if (k < kn) {
             const int sl = near_slot(k);
             // (both products issued before either's terms: the second overlaps the first's latency)
             const f4_t acc = qk(lds0, sl * kRowBytes, swz(sl));
@@ -810,19 +859,28 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     }
 #pragma unroll
     for (int k = 0; k < MAXS; ++k) {
-        float w[4];
+        if constexpr (INT) {
+            // a near group (even k < kn): slots 2k .. 2k + 3; a far step: slots 2k, 2k + 1 in
+            // group slots 0 and 2 (slots 1 and 3 weigh 0)
+            auto dn = [&](int y) { return y < MAXK ? dp[4 * kWG + y] : 0.f; };
+            const bool grp = k < kn && (k & 1) == 0;
+            wo[k][0] = pack_h2(dn(2 * k), grp ? dn(2 * k + 1) : 0.f);
+            wo[k][1] = grp ? pack_h2(dn(2 * k + 2), dn(2 * k + 3)) : pack_h2(dn(2 * k + 1), 0.f);
+        } else {
+            float w[4];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int n = 2 * k + e;
-            const float dn = dp[4 * kWG + n];
-            const float far = (n < n_reach) ? dn * A.off[n].t : 0.f;
-            w[2 * e] = dn - far;
-            w[2 * e + 1] = far;
+            for (int e = 0; e < 2; ++e) {
+                const int n = 2 * k + e;
+                const float dn = dp[4 * kWG + n];
+                const float far = (n < n_reach) ? dn * A.off[n].t : 0.f;
+                w[2 * e] = dn - far;
+                w[2 * e + 1] = far;
+            }
+            wo[k][0] = pack_h2(w[0], w[1]);
+            wo[k][1] = pack_h2(w[2], w[3]);
         }
-        wo[k][0] = pack_h2(w[0], w[1]);
-        wo[k][1] = pack_h2(w[2], w[3]);
     }
-    publish<6>();                                       // the key near block has landed
+    publish<kStepDmas>();                               // the key near block has landed
 
     // ---- pass C: dq_rot = sum of weighted key rows (transposing reads of the permuted keys:
     // lane x gets element 4m + x, which is dim 16x + m) ----
@@ -840,7 +898,12 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         // pt + 64 - a, far row one slot down
 #pragma unroll
         for (int k = 0; k < MAXS; ++k) {
-            if (k < kn) {
+            if constexpr (INT) {
+                if ((k & 1) == 0 && k < kn) {
+                    const int sl = pt + kNear - group_a(k, kt);
+                    row_sum_group(o, wo[k][0], wo[k][1], lds0, sl * kRowBytes, swz(sl));
+                }
+            } else if (k < kn) {
                 const int sl = pt + kNear - pick_uniform((kt >> 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a) - (kt & 1);
                 row_sum_group(o, wo[k][0], wo[k][1], lds0, sl * kRowBytes, swz(sl));
             }
@@ -848,7 +911,8 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         publish<0>();
     }
     {
-        const int sv = (kt < 2) ? pt + 1 - kt : kBlkSlots + pt + 5 - kt;
+        // (INT: the near rows of the step's rungs, slots pt and 72 + pt, each read twice)
+        const int sv = INT ? pt + ((kt < 2) ? 0 : kBlkSlots) : (kt < 2) ? pt + 1 - kt : kBlkSlots + pt + 5 - kt;
         const int vbase = sv * kRowBytes, vsw = swz(sv);
 #pragma unroll
         for (int k = 0; k < MAXS; ++k) {
@@ -882,8 +946,21 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         }
         if (active) {
             uint32_t* rr = A.wrung + (static_cast<int64_t>(b) * A.Hq + h0 + x) * kNR * L + i;
+            // rung n's entry: slot n (INT: n + ro past the near groups)
+            auto wslot = [&](int y) -> uint32_t { return y < MAXK ? wq[4 * kWG + y] : 0u; };
 #pragma unroll
-            for (int n = 0; n < kNR; ++n) rr[static_cast<int64_t>(n) * L] = (n < MAXK) ? wq[4 * kWG + n] : 0u;
+            for (int n = 0; n < kNR; ++n) {
+                uint32_t v = wslot(n);
+                if constexpr (INT) {
+                    // the candidates as register values first (a choice among the array's entries
+                    // would become an indexed array in scratch memory)
+                    uint32_t c1 = wslot(n + 1), c2 = wslot(n + 2), c3 = wslot(n + 3);
+                    asm volatile("" : "+v"(v), "+v"(c1), "+v"(c2), "+v"(c3));
+                    const int sh = n < nn ? 0 : ro;
+                    v = sh == 0 ? v : sh == 1 ? c1 : sh == 2 ? c2 : c3;
+                }
+                rr[static_cast<int64_t>(n) * L] = v;
+            }
         }
     };
     const bool wplain = !wave_any(es != kNoExp && es != 0);
@@ -1031,9 +1108,12 @@ __global__ __launch_bounds__(kNT) void bwd_fp32_kernel(BwdArgs A) {
     query_fp32_tiles(A, A.q_fp32_wg, A.xcd_map, blockIdx.x, gridDim.x, lds);
 }
 // ------------------------------------------------------------------------------------------------
-// bwd_k_dot
+// bwd_k_dot. INT: every kept rung is integral (§2 "Implementation note"): a key row receives one
+// query row per rung, so the rungs with a <= 64 come from the near block four to a group (at most
+// two groups: terms te = 0..3 are four rungs' rows), and a far step stages 64-row blocks of its two
+// rungs' rows (terms 1 and 3, which would be the second rows, read the first ones with weight 0).
 // ------------------------------------------------------------------------------------------------
-template <int MAXS>
+template <int MAXS, bool INT>
 __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     // Two item buffers used in turn, each a rotated-query part and a do part (kBufBytes each).
     // Items of a query head: its near block (query rows j0 .. j0 + 127 of the rotated queries and
@@ -1067,16 +1147,20 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     int n_reach = 0;
     for (int n = 0; n < A.n_off; ++n)
         if (j0 + A.off[n].a < L) n_reach = n + 1;
-    const int n_steps = (n_reach + 1) >> 1;
     // near rungs: the prefix with a <= 63 (both query rows of every key row of the tile inside the
-    // near block). Pairs k < kn come from the near block (kn even, at most 4); pairs
-    // kn .. n_far - 1 are far steps, pair k in buffer (k + 1) % 2, n_far odd so that the last one
-    // sits in lds1.
+    // near block; INT: a <= 64, the one row). Pairs k < kn come from the near block (kn even, at
+    // most 4; INT: for even k a group of the four rungs 2k .. 2k + 3, those past nn padding);
+    // pairs kn .. n_far - 1 are far steps, pair k in buffer (k + 1) % 2, n_far odd so that the last
+    // one sits in lds1; far pair k holds rungs 2k - ro and 2k - ro + 1 (ro = 0 unless INT).
     int n_near = 0;
     for (int n = 0; n < n_reach; ++n)
-        if (A.off[n].a <= kNear - 1) n_near = n + 1;
-    const int kn = min((n_near >> 1) & ~1, 4);
+        if (A.off[n].a <= kNear - (INT ? 0 : 1)) n_near = n + 1;
+    const int nn = INT ? min(n_near, 8) : 0;
+    const int kn = INT ? 2 * ((nn + 3) >> 2) : min((n_near >> 1) & ~1, 4);
+    const int ro = INT ? 2 * kn - nn : 0;
+    const int n_steps = INT ? kn + ((n_reach - nn + 1) >> 1) : (n_reach + 1) >> 1;
     const int n_far = max(n_steps, kn + 1) | 1;
+    constexpr int kStepDmas = INT ? 4 : 6;              // DMA instructions per wave of a far step part
 
     // Lanes follow v_mfma_f32_16x16x16f16: lane l = 16 lg + lr holds A[lr][4 lg + 0..3],
     // B[4 lg + 0..3][lr] and D[4 lg + 0..3][lr]. Its outputs (window and rungs alike) are key rows
@@ -1100,14 +1184,20 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     // rung step k: rung 2k rows j0 + a + s at slot s (near of key row r at r, far at r + 1), rung
     // 2k + 1 rows j0 + a' - 2 + s at slot 72 + s (near at 72 + r + 2, far at 72 + r + 3); steps past
     // n_steps stage zeros
+    // (INT: 64 rows each, the row of key row r at slot r or 72 + r)
     auto step = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int k) {
-        st.step(rs, dst, 2 * k < n_reach, j0 + A.off[2 * k].a, 2 * k + 1 < n_reach, j0 + A.off[2 * k + 1].a - 2);
+        if constexpr (INT) {
+            const int n = 2 * k - ro;
+            st.step64(rs, dst, n < n_reach, j0 + A.off[n].a, n + 1 < n_reach, j0 + A.off[n + 1].a);
+        } else {
+            st.step(rs, dst, 2 * k < n_reach, j0 + A.off[2 * k].a, 2 * k + 1 < n_reach, j0 + A.off[2 * k + 1].a - 2);
+        }
     };
     auto buf = [&](int it) -> char* { return (it & 1) ? lds1 : lds0; };
     // the rung entries of step k of head h into went[k % 2]: one 4-byte DMA per wave (rung
     // 2k + (w & 1), queries j0 + a + 64 (w >> 1) + lane; zeros past L or past the reach)
     auto entries = [&](int h, int k) {
-        const int n = 2 * k + (wave & 1);
+        const int n = 2 * k - ro + (wave & 1);
         const bool real = n < n_reach;
         const uint32_t* wrn = A.wrung + ((static_cast<int64_t>(b) * A.Hq + h) * kNR + (real ? n : 0)) * L;
         const __amdgpu_buffer_rsrc_t rs =
@@ -1140,9 +1230,12 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     const int rbase16 = 16 * wave + 4 * lg;
     // far steps: term te of key row r: near / far of rung 2k at slots r, r + 1, of rung 2k + 1 at
     // 74 + r, 75 + r; element block nb of it is at radr[q] ^ (nb << 4)
+    // (INT: terms 0 and 1 at slot r, terms 2 and 3 at 72 + r)
     int radr[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) radr[q] = blk_addr(rbase16 + q + (te & 1) + (te >> 1) * (kBlkSlots + 2), 0);
+    for (int q = 0; q < 4; ++q)
+        radr[q] = INT ? blk_addr(rbase16 + q + (te >> 1) * kBlkSlots, 0)
+                      : blk_addr(rbase16 + q + (te & 1) + (te >> 1) * (kBlkSlots + 2), 0);
     auto sum_rungs = [&](f4_t (&acc)[4], const uint4 (&w)[4], bool use_p, const char* lds, const int (&radr)[4]) {
 #pragma unroll
         for (int q0 = 0; q0 < 4; q0 += 2) {
@@ -1260,15 +1353,37 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     // the thread's coefficient of each rung pair k (rung 2k + (wv & 1), dS halves for wv < 2, else
     // p halves): (1 - t, t), times the factors of its near and far query rows where not every
     // factor is 1 (then recomputed per head)
+    // INT: a near group (even k < kn) has no (1 - t, t): its words pair two rungs (2k + 2 (wv & 1)
+    // and the next), each with its own query row's factor; a far pair k has (1, 0) (rung
+    // 2k - ro + (wv & 1))
+    auto near_a = [&](int k, int c) -> int { return 2 * k + c < nn ? A.off[2 * k + c].a : 0; };
     uint32_t cw[MAXS];
     auto set_cw = [&](int hh, bool with_factors) {
 #pragma unroll
         for (int k = 0; k < MAXS; ++k) {
-            const float t = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].t, A.off[2 * k].t);
-            const int a = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a);
-            const h2_t c = with_factors ? coef(hh, 2 * k + (wv & 1), a, t, (wv >> 1) != 0)
-                                        : (h2_t){static_cast<_Float16>(1.f - t), static_cast<_Float16>(t)};
-            cw[k] = __builtin_bit_cast(uint32_t, c);
+            if constexpr (INT) {
+                const bool use_p = (wv >> 1) != 0;
+                if (k < kn) {
+                    const int a0 = pick_uniform((wv & 1) != 0, near_a(k, 2), near_a(k, 0));
+                    const int a1 = pick_uniform((wv & 1) != 0, near_a(k, 3), near_a(k, 1));
+                    const uint32_t f = with_factors ? fac_half(hh, ((j0 + wrow + a0) >> 6) - t0, use_p) |
+                                                          (fac_half(hh, ((j0 + wrow + a1) >> 6) - t0, use_p) << 16)
+                                                    : 0x3c003c00u;
+                    cw[k] = f;
+                } else {
+                    const int n = 2 * k - ro + (wv & 1);
+                    const int a = pick_uniform((wv & 1) != 0, A.off[2 * k - ro + 1].a, A.off[2 * k - ro].a);
+                    const uint32_t f = with_factors ? fac_half(hh, 3 + 2 * n + ((j0 + wrow + a) >> 6) - ((j0 + a) >> 6), use_p)
+                                                    : 0x3c00u;
+                    cw[k] = f & 0xffffu;
+                }
+            } else {
+                const float t = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].t, A.off[2 * k].t);
+                const int a = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a);
+                const h2_t c = with_factors ? coef(hh, 2 * k + (wv & 1), a, t, (wv >> 1) != 0)
+                                            : (h2_t){static_cast<_Float16>(1.f - t), static_cast<_Float16>(t)};
+                cw[k] = __builtin_bit_cast(uint32_t, c);
+            }
         }
     };
     set_cw(0, false);
@@ -1315,23 +1430,36 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
             const uint32_t* wr = A.wrung + hrow0 * kNR;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int n = 2 * k + (wv & 1);
-                const int qn = j0 + wrow + pick_uniform((wv & 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a);
-                const bool okn = k < kn && qn < L, okf = k < kn && qn + 1 < L;
-                const uint32_t vn = wr[static_cast<int64_t>(n) * L + (okn ? qn : 0)];
-                const uint32_t vf = wr[static_cast<int64_t>(n) * L + (okf ? qn + 1 : 0)];
-                enr[k] = okn ? vn : 0u;
-                efr[k] = okf ? vf : 0u;
+                if constexpr (INT) {
+                    // group k (even): rungs n0 = 2k + 2 (wv & 1) and n0 + 1 at their query rows
+                    const int n0 = 2 * k + 2 * (wv & 1);
+                    const int q0 = j0 + wrow + pick_uniform((wv & 1) != 0, near_a(k, 2), near_a(k, 0));
+                    const int q1 = j0 + wrow + pick_uniform((wv & 1) != 0, near_a(k, 3), near_a(k, 1));
+                    const bool ok0 = (k & 1) == 0 && k < kn && n0 < nn && q0 < L;
+                    const bool ok1 = (k & 1) == 0 && k < kn && n0 + 1 < nn && q1 < L;
+                    const uint32_t v0 = wr[static_cast<int64_t>(ok0 ? n0 : 0) * L + (ok0 ? q0 : 0)];
+                    const uint32_t v1 = wr[static_cast<int64_t>(ok1 ? n0 + 1 : 0) * L + (ok1 ? q1 : 0)];
+                    enr[k] = ok0 ? v0 : 0u;
+                    efr[k] = ok1 ? v1 : 0u;
+                } else {
+                    const int n = 2 * k + (wv & 1);
+                    const int qn = j0 + wrow + pick_uniform((wv & 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a);
+                    const bool okn = k < kn && qn < L, okf = k < kn && qn + 1 < L;
+                    const uint32_t vn = wr[static_cast<int64_t>(n) * L + (okn ? qn : 0)];
+                    const uint32_t vf = wr[static_cast<int64_t>(n) * L + (okf ? qn + 1 : 0)];
+                    enr[k] = okn ? vn : 0u;
+                    efr[k] = okf ? vf : 0u;
+                }
             }
         }
         step(qrs, lds1, kn);
         step(drs, lds1 + kBufBytes, kn);
         entries(h, kn + 1);
         if (!__builtin_amdgcn_readfirstlane(allone ? 1 : 0)) set_cw(hh, true);
-        // the near pairs' weights (same words as the far steps' table)
+        // the near pairs' weights (same words as the far steps' table; INT: the groups', even k)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            if (k < kn) {
+            if (k < kn && (!INT || (k & 1) == 0)) {
                 const uint32_t pr = __builtin_amdgcn_perm(efr[k], enr[k], (wv >> 1) ? 0x05040100u : 0x07060302u);
                 reinterpret_cast<uint32_t*>(&wnear(k)[wrow])[wv] = mul_h2(pr, cw[k]);
             }
@@ -1339,7 +1467,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
         // the window's factors: the wave's queries 16w + 16 kb + 0..15 lie in query tile t0, but
         // for wave 3, kb = 1 (tile t0 + 1)
         const uint32_t fw0 = fac[hh][0], fw1 = fac[hh][wave == 3 ? 1 : 0];
-        publish<13>();                                  // this head's near item and weights are in place
+        publish<2 * kStepDmas + 1>();                   // this head's near item and weights are in place
 
         // ---- window terms on the matrix cores: for the wave's key rows 16w + rr and queries
         // 16w + c (c < 32), dk_rot[rr] += sum_c A[rr][c] qrot[c], A[rr][c] = dS of query c at
@@ -1368,13 +1496,20 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
         }
         // ---- near rung pairs: term te of key row r is rung 2k + (te >> 1), near row j + a at
         // slot r + a (te even) or far row one slot up ----
+        // (INT, even k: term te is rung 2k + te, query row j + a at slot r + a)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            if (k < kn) {
-                const int ak = pick_uniform((te >> 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a);
+            if (k < kn && (!INT || (k & 1) == 0)) {
                 int nadr[4];
+                if constexpr (INT) {
+                    const int ak = pick4(te, near_a(k, 0), near_a(k, 1), near_a(k, 2), near_a(k, 3));
 #pragma unroll
-                for (int q = 0; q < 4; ++q) nadr[q] = blk_addr(rbase16 + q + ak + (te & 1), 0);
+                    for (int q = 0; q < 4; ++q) nadr[q] = blk_addr(rbase16 + q + ak, 0);
+                } else {
+                    const int ak = pick_uniform((te >> 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) nadr[q] = blk_addr(rbase16 + q + ak + (te & 1), 0);
+                }
                 uint4 w[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) w[q] = wnear(k)[rbase16 + q];
@@ -1496,9 +1631,11 @@ hipError_t launch_bwd_mfma(const BwdArgs& A0, bool want_dalpha, int stages, hipS
         A.xcd_map = q_map;
         const dim3 grid(static_cast<unsigned>(q_units * n_tiles));
         if (want_dalpha)
-            hipLaunchKernelGGL((bwd_q_mfma_kernel<8, true>), grid, dim3(kNT), 0, s, A);
+            hipLaunchKernelGGL((bwd_q_mfma_kernel<8, true, false>), grid, dim3(kNT), 0, s, A);
+        else if (int_path_fits(A.off, A.n_off, 8))
+            hipLaunchKernelGGL((bwd_q_mfma_kernel<8, false, true>), grid, dim3(kNT), 0, s, A);
         else
-            hipLaunchKernelGGL((bwd_q_mfma_kernel<8, false>), grid, dim3(kNT), 0, s, A);
+            hipLaunchKernelGGL((bwd_q_mfma_kernel<8, false, false>), grid, dim3(kNT), 0, s, A);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1507,7 +1644,11 @@ hipError_t launch_bwd_mfma(const BwdArgs& A0, bool want_dalpha, int stages, hipS
     A.q_xcd_map = q_map;
     if (stages & kStageKey) {
         A.xcd_map = (k_units % 8 == 0) ? 1 : 0;
-        hipLaunchKernelGGL((bwd_k_dot_kernel<8>), dim3(static_cast<unsigned>(k_units * n_tiles)), dim3(kNT), 0, s,
+        if (int_path_fits(A.off, A.n_off, 8))
+            hipLaunchKernelGGL((bwd_k_dot_kernel<8, true>), dim3(static_cast<unsigned>(k_units * n_tiles)), dim3(kNT), 0, s,
+                               A);
+        else
+            hipLaunchKernelGGL((bwd_k_dot_kernel<8, false>), dim3(static_cast<unsigned>(k_units * n_tiles)), dim3(kNT), 0, s,
                            A);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -277,8 +277,11 @@ __device__ __forceinline__ bool q_outside_fp16(const uint4 (&r)[8], float qscale
 
 // ------------------------------------------------------------------------------------------------
 // fwd_mfma: W <= 15 (4 window groups), kept rungs <= 2 MAXS, query heads per key-value head % 4 == 0.
+// INT: every kept rung is integral (the integer-offset path of §2 "Implementation note"): a rung
+// reads one row, so the rungs with a <= 64 are read from the near block four to a group (at most
+// two groups), and a far step stages its two rungs as 64-row blocks, with no blending of rows.
 // ------------------------------------------------------------------------------------------------
-template <int MAXS>
+template <int MAXS, bool INT>
 __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     constexpr float kNegInf = -__builtin_huge_valf();
     constexpr int MAXK = 2 * MAXS;
@@ -313,14 +316,19 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     int n_reach = 0;
     for (int n = 0; n < A.n_off; ++n)
         if (i0 + kTile - 1 >= A.off[n].a + A.off[n].interp) n_reach = n + 1;
-    const int n_steps = (n_reach + 1) >> 1;
-    // near rungs: the prefix with a <= 63 (near and far rows inside the near block). Rung pairs
-    // k < kn come from the near block, kn even; pairs kn .. n_steps - 1 are far steps, pair k in
-    // buffer (k + 1) % 2.
+    // near rungs: the prefix with a <= 63 (near and far rows inside the near block; INT: a <= 64,
+    // the one row). Steps k < kn come from the near block, kn even: rung pairs 2k, 2k + 1, or (INT)
+    // for even k a group of the four rungs 2k .. 2k + 3 (those past nn are padding). Steps kn ..
+    // n_steps - 1 are far steps, step k in buffer (k + 1) % 2, holding rungs 2k - ro and
+    // 2k - ro + 1 (ro = 0 unless INT).
     int n_near = 0;
     for (int n = 0; n < n_reach; ++n)
-        if (A.off[n].a <= kNear - 1) n_near = n + 1;
-    const int kn = (n_near >> 1) & ~1;
+        if (A.off[n].a <= kNear - (INT ? 0 : 1)) n_near = n + 1;
+    const int nn = INT ? min(n_near, 8) : 0;
+    const int kn = INT ? 2 * ((nn + 3) >> 2) : (n_near >> 1) & ~1;
+    const int ro = INT ? 2 * kn - nn : 0;
+    const int n_steps = INT ? kn + ((n_reach - nn + 1) >> 1) : (n_reach + 1) >> 1;
+    constexpr int kStepDmas = INT ? 4 : 6;              // DMA instructions per wave of a far step
 
     const int64_t kv_row0 = static_cast<int64_t>(bg) * L;
     const __amdgpu_buffer_rsrc_t krs = rows_rsrc(A.kstage, kv_row0, L);
@@ -329,8 +337,14 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     st.init(lane, wave);
     // rung step k: rungs 2k and 2k + 1 (zeros past the reach); the far row of position p sits at
     // slot p (block A) or 72 + p + 2 (block B), the near row one slot up
+    // (INT: the near row of position p at slot p or 72 + p)
     auto step = [&](const __amdgpu_buffer_rsrc_t& rs, char* dst, int k) {
-        st.step(rs, dst, 2 * k < n_reach, i0 - A.off[2 * k].a - 1, 2 * k + 1 < n_reach, i0 - A.off[2 * k + 1].a - 3);
+        if constexpr (INT) {
+            const int n = 2 * k - ro;
+            st.step64(rs, dst, n < n_reach, i0 - A.off[n].a, n + 1 < n_reach, i0 - A.off[n + 1].a);
+        } else {
+            st.step(rs, dst, 2 * k < n_reach, i0 - A.off[2 * k].a - 1, 2 * k + 1 < n_reach, i0 - A.off[2 * k + 1].a - 3);
+        }
     };
     const int jn = i0 - kNear;                          // the near block's row at slot 0
     auto buf = [&](int j) -> char* { return (j & 1) ? lds1 : lds0; };
@@ -391,24 +405,28 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
             q[m >> 1][2 * (m & 1) + 1] = pack_h2((y0 * t0.x + x0 * t0.y) * qs, (y1 * t1.x + x1 * t1.y) * qs);
         }
     }
-    publish<6>();                                       // the key near block has landed
+    publish<kStepDmas>();                               // the key near block has landed
 
     // ---- phase A: scores of the lane's head x (base 2) ----
     // Far step k computes from buffer (k + 1) % 2 after issuing step k + 1 into the other buffer
     // (the barrier that ended the item before released it); the wait before each barrier is for
     // step k + 1, the only load in flight.
     float s[4 * kWG + MAXK];
-    // lane x of a rung group: rung 2k + (x >> 1), near (x even) or far row
+    // lane x of a rung group: rung 2k + (x >> 1), near (x even) or far row (INT: the near rows of
+    // rungs 2k - ro and 2k - ro + 1 in columns 0 and 2); the scores go to slots 2k and 2k + 1
     auto score = [&](const f4_t& acc, int k) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int n = 2 * k + e;
+            const int n = 2 * k + e - ro;
             if (n < n_reach) {
-                const float sc = fmaf(A.off[n].t, acc[2 * e + 1] - acc[2 * e], acc[2 * e]);
-                s[4 * kWG + n] = (active && i >= A.off[n].a + A.off[n].interp) ? sc : kNegInf;
+                const float sc = INT ? acc[2 * e] : fmaf(A.off[n].t, acc[2 * e + 1] - acc[2 * e], acc[2 * e]);
+                s[4 * kWG + 2 * k + e] = (active && i >= A.off[n].a + A.off[n].interp) ? sc : kNegInf;
             }
         }
     };
+    // INT, near group of step k (even): the distance of rung 2k + c, 0 (the window's own row, a
+    // staged row) for padding
+    auto near_a = [&](int k, int c) -> int { return 2 * k + c < nn ? A.off[2 * k + c].a : 0; };
     {
         // item 0: lane x reads window distance d = 4g + x, slot p - d + 64 (pads d > W read
         // staged rows); then the near rung pairs: rung 2k + (x >> 1), near row i - a at slot
@@ -425,18 +443,30 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
             }
         }
 #pragma unroll
+        for (int y = 4 * kWG; y < 4 * kWG + MAXK; ++y) s[y] = kNegInf;
+#pragma unroll
         for (int k = 0; k < MAXS; ++k) {
-            s[4 * kWG + 2 * k] = kNegInf;
-            s[4 * kWG + 2 * k + 1] = kNegInf;
-            if (k < kn) {
+            if constexpr (INT) {
+                // lane x reads rung 2k + x, row i - a at slot p + 64 - a
+                if ((k & 1) == 0 && k < kn) {
+                    const int sl = p + kNear - pick4(x, near_a(k, 0), near_a(k, 1), near_a(k, 2), near_a(k, 3));
+                    const f4_t acc = row_dot_group(q, buf(0), sl * kRowBytes, swz(sl));
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const int n = 2 * k + c;
+                        if (n < nn) s[4 * kWG + n] = (active && i >= A.off[n].a) ? acc[c] : kNegInf;
+                    }
+                }
+            } else if (k < kn) {
                 const int sl = p + kNear - pick_uniform((x >> 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a) - (x & 1);
                 score(row_dot_group(q, buf(0), sl * kRowBytes, swz(sl)), k);
             }
         }
         publish<0>();                                   // item 1 has landed, buffer 0 is free
     }
-    // far steps: lane x reads rung 2k + (x >> 1), near (x even) or far row
-    const int rslot = p + ((x >> 1) ? kBlkSlots + 2 : 0) + ((x & 1) ? 0 : 1);
+    // far steps: lane x reads rung 2k + (x >> 1), near (x even) or far row (INT: the near row,
+    // for x even and odd alike)
+    const int rslot = INT ? p + ((x >> 1) ? kBlkSlots : 0) : p + ((x >> 1) ? kBlkSlots + 2 : 0) + ((x & 1) ? 0 : 1);
     const int rbase = rslot * kRowBytes, rsw = swz(rslot);
     // The last far step computes from buffer 1 when there is an odd number of them (kn is even):
     // buffer 0 is free then, and the value near block goes ahead under that step (its barrier
@@ -481,17 +511,26 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     }
 #pragma unroll
     for (int k = 0; k < MAXS; ++k) {
-        float w[4];
+        if constexpr (INT) {
+            // a near group (even k < kn): slots 2k .. 2k + 3, one row each; a far step: the near
+            // rows of its two rungs in group slots 0 and 2 (slots 1 and 3 weigh 0)
+            auto ev = [&](int y) { return y < MAXK ? s[4 * kWG + y] : 0.f; };
+            const bool grp = k < kn && (k & 1) == 0;
+            po[k][0] = pack_h2(ev(2 * k), grp ? ev(2 * k + 1) : 0.f);
+            po[k][1] = grp ? pack_h2(ev(2 * k + 2), ev(2 * k + 3)) : pack_h2(ev(2 * k + 1), 0.f);
+        } else {
+            float w[4];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int n = 2 * k + e;
-            const float ev = s[4 * kWG + n];
-            const float far = (n < n_reach) ? ev * A.off[n].t : 0.f;   // ev is 0 past the reach
-            w[2 * e] = ev - far;
-            w[2 * e + 1] = far;
+            for (int e = 0; e < 2; ++e) {
+                const int n = 2 * k + e;
+                const float ev = s[4 * kWG + n];
+                const float far = (n < n_reach) ? ev * A.off[n].t : 0.f;   // ev is 0 past the reach
+                w[2 * e] = ev - far;
+                w[2 * e + 1] = far;
+            }
+            po[k][0] = pack_h2(w[0], w[1]);
+            po[k][1] = pack_h2(w[2], w[3]);
         }
-        po[k][0] = pack_h2(w[0], w[1]);
-        po[k][1] = pack_h2(w[2], w[3]);
     }
 
     // ---- phase B: P.V ----
@@ -506,7 +545,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[e] = (f4_t){0.f, 0.f, 0.f, 0.f};
     {
-        publish<6>();                                   // the value near block has landed
+        publish<kStepDmas>();                           // the value near block has landed
         // window group g: slot pt - 4g - kt + 64
         const int sv = pt - kt + kNear;
 #pragma unroll
@@ -514,9 +553,15 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
             if (4 * g <= W) row_sum_group(o, pw[g][0], pw[g][1], lds0, (sv - 4 * g) * kRowBytes, swz(sv - 4 * g));
         // near rung pairs: slot kt of the group is rung 2k + (kt >> 1), near row pt - a at slot
         // pt + 64 - a (kt even) or far row one slot down
+        // (INT: slot kt of the group is rung 2k + kt, for even k)
 #pragma unroll
         for (int k = 0; k < MAXS; ++k) {
-            if (k < kn) {
+            if constexpr (INT) {
+                if ((k & 1) == 0 && k < kn) {
+                    const int sl = pt + kNear - pick4(kt, near_a(k, 0), near_a(k, 1), near_a(k, 2), near_a(k, 3));
+                    row_sum_group(o, po[k][0], po[k][1], lds0, sl * kRowBytes, swz(sl));
+                }
+            } else if (k < kn) {
                 const int sl = pt + kNear - pick_uniform((kt >> 1) != 0, A.off[2 * k + 1].a, A.off[2 * k].a) - (kt & 1);
                 row_sum_group(o, po[k][0], po[k][1], lds0, sl * kRowBytes, swz(sl));
             }
@@ -525,8 +570,9 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     }
     {
         // slot k of a far step's group: near and far of rung 2k (block A, slots pt + 1, pt) and
-        // of rung 2k + 1 (block B, slots pt + 3, pt + 2); value step k sits in buffer (k + 1) % 2
-        const int sv = (kt < 2) ? pt + 1 - kt : kBlkSlots + pt + 5 - kt;
+        // of rung 2k + 1 (block B, slots pt + 3, pt + 2) (INT: the near rows, slots pt and
+        // 72 + pt, each read twice); value step k sits in buffer (k + 1) % 2
+        const int sv = INT ? pt + ((kt < 2) ? 0 : kBlkSlots) : (kt < 2) ? pt + 1 - kt : kBlkSlots + pt + 5 - kt;
         const int vbase = sv * kRowBytes, vsw = swz(sv);
 #pragma unroll
         for (int k = 0; k < MAXS; ++k) {
@@ -597,7 +643,11 @@ hipError_t launch_fwd_mfma(const FwdArgs& A0, hipStream_t s) {
     const int64_t n_units = static_cast<int64_t>(A.B) * A.Hkv * (A.G / 4);
     // the forward keeps 4 workgroups per CU in one round: mix early and late tiles on each CU
     A.xcd_map = (n_units % 8 == 0) ? 2 : 0;
-    hipLaunchKernelGGL((fwd_mfma_kernel<8>), dim3(static_cast<unsigned>(n_units * n_tiles)), dim3(kNT), 0, s, A);
+    const dim3 grid(static_cast<unsigned>(n_units * n_tiles));
+    if (int_path_fits(A.off, A.n_off, 8))
+        hipLaunchKernelGGL((fwd_mfma_kernel<8, true>), grid, dim3(kNT), 0, s, A);
+    else
+        hipLaunchKernelGGL((fwd_mfma_kernel<8, false>), grid, dim3(kNT), 0, s, A);
     return hipGetLastError();
 }
 

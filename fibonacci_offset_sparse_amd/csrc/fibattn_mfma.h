@@ -99,6 +99,31 @@ template <typename T> __device__ __forceinline__ T pick_uniform(bool c, T if_tru
     return c ? if_true : if_false;
 }
 
+// pick_uniform among four: lane choice c (0..3) of four uniform values.
+template <typename T> __device__ __forceinline__ T pick4(int c, T v0, T v1, T v2, T v3) {
+    asm volatile("" : "+s"(v0));
+    asm volatile("" : "+s"(v1));
+    asm volatile("" : "+s"(v2));
+    asm volatile("" : "+s"(v3));
+    const T lo = (c & 1) ? v1 : v0, hi = (c & 1) ? v3 : v2;
+    return (c & 2) ? hi : lo;
+}
+
+// Whether a plan takes the integer-offset kernels: every kept rung integral, and the steps of a
+// tile that reaches every rung fit in maxs: the rungs with a <= 64 (at most 8) come from the near
+// block four to a group (two steps per group), the others two to a far step. (The count only
+// grows with the rungs a tile reaches.)
+inline bool int_path_fits(const OffsetSlot* off, int n_off, int maxs) {
+    if (n_off == 0) return false;
+    int n_near = 0;
+    for (int n = 0; n < n_off; ++n) {
+        if (off[n].interp) return false;
+        if (off[n].a <= kNear) n_near = n + 1;
+    }
+    const int nn = n_near < 8 ? n_near : 8;
+    return 2 * ((nn + 3) / 4) + (n_off - nn + 1) / 2 <= maxs;
+}
+
 // Wait until at most N vector-memory instructions of this wave are in flight (its LDS DMAs up to
 // the block the next step reads have landed) and its LDS reads are done, then the workgroup
 // barrier. __syncthreads would also drain every staging load in flight.
@@ -220,6 +245,18 @@ struct Stager {
         dma16(rs, dst + wave * 1024, j0 + 8 * wave, gpar ^ blk);
         dma16(rs, dst + (wave + 4) * 1024, j0 + 8 * (wave + 4), gpar ^ blk);
         dma4(rs, dst + 64 * kRowBytes + wave * 256, j0 + 64 + 2 * wave, blk);
+    }
+    // a rung block of 64 rows (integral rungs: no second row), slots 0..63 of the block
+    __device__ __forceinline__ void rung64(const __amdgpu_buffer_rsrc_t& rs, char* dst, bool real, int j0_real,
+                                           int blk) const {
+        const int j0 = real ? j0_real : -(kTile + kBlkSlots + 8);
+        dma16(rs, dst + wave * 1024, j0 + 8 * wave, gpar ^ blk);
+        dma16(rs, dst + (wave + 4) * 1024, j0 + 8 * (wave + 4), gpar ^ blk);
+    }
+    __device__ __forceinline__ void step64(const __amdgpu_buffer_rsrc_t& rs, char* dst, bool r0, int j0a, bool r1,
+                                           int j0b) const {
+        rung64(rs, dst, r0, j0a, 0);
+        rung64(rs, dst + kBlkBytes, r1, j0b, 1);
     }
     // a rung step: block A from row j0a, block B from row j0b
     __device__ __forceinline__ void step(const __amdgpu_buffer_rsrc_t& rs, char* dst, bool r0, int j0a, bool r1,

@@ -196,6 +196,26 @@ def test_integral_offsets_with_pow2_base_and_window_extremes():
     compare(q, k, v, do, 1.0, 5, [], "no offsets", want_dalpha=False)
 
 
+# Integral plans (alpha = 1) in bf16 on the matrix-core kernels' integer-offset path: no rung
+# within 64 rows, one, rungs at 64 and 65 (the near block's last row and the first far one), two
+# groups of four (the second partial), more than eight, and a plan whose far steps do not fit that
+# path (the interpolating kernels take it, with t = 0).
+INT_PLANS = [
+    (4, [70, 100, 150, 290]), (4, [10, 100, 150, 250, 290]), (2, [3, 5, 64, 65, 200]),
+    (2, [3, 5, 8, 13, 21, 100, 200]), (0, list(range(1, 11)) + [64, 65, 66, 200]),
+    (0, [1] + list(range(70, 85))),
+]
+
+
+@pytest.mark.parametrize("W,offsets", INT_PLANS)
+def test_integer_offset_plans(W, offsets):
+    L = 300
+    q, k, v, do = (randn((2, 8, L, 64), 71, torch.bfloat16), randn((2, 2, L, 64), 72, torch.bfloat16),
+                   randn((2, 2, L, 64), 73, torch.bfloat16), randn((2, 8, L, 64), 74, torch.bfloat16))
+    say(f"bwd integral plan W={W} offsets={offsets} L={L}")
+    compare(q, k, v, do, 1.0, W, offsets, f"int W={W} K={len(offsets)}", want_dalpha=False)
+
+
 @pytest.mark.parametrize("name", ["l1024_linear_bf16", "l4096_coprime_bf16"])
 def test_rounded_stagger(name):
     # the integer path at alpha = 1 with the rounded offsets of §2 "Implementation note"; d(alpha)

@@ -149,6 +149,27 @@ def test_window_and_offset_extremes(W, offsets, alpha):
     compare(q, k, v, alpha, W, offsets, f"W={W} K={len(offsets)} a={alpha}")
 
 
+# Integral plans (alpha = 1) in bf16, which the matrix-core kernels take on their integer-offset
+# path: no rung within 64 rows, one, a group of four with rungs at 64 and 65 (the near block's
+# last row and the first far one), two groups (the second partial), more than eight (the ninth
+# goes to a far step), and a plan whose far steps do not fit that path (the interpolating kernels
+# take it, with t = 0).
+INT_PLANS = [
+    (4, [70, 100, 150, 290]), (4, [10, 100, 150, 250, 290]), (2, [3, 5, 64, 65, 200]),
+    (2, [3, 5, 8, 13, 21, 100, 200]), (0, list(range(1, 11)) + [64, 65, 66, 200]),
+    (0, [1] + list(range(70, 85))),
+]
+
+
+@pytest.mark.parametrize("W,offsets", INT_PLANS)
+@pytest.mark.parametrize("L", [300, 1100])
+def test_integer_offset_plans(W, offsets, L):
+    q, k, v = (randn((2, 8, L, 64), 61, torch.bfloat16), randn((2, 2, L, 64), 62, torch.bfloat16),
+               randn((2, 2, L, 64), 63, torch.bfloat16))
+    say(f"integral plan W={W} offsets={offsets} L={L}")
+    compare(q, k, v, 1.0, W, offsets, f"int W={W} K={len(offsets)} L={L}")
+
+
 def test_grid_order_covers_every_tile_once():
     # B = 20 at the paper's head counts: 40 (batch, KV head) units of 16 tiles, 80 workgroup slots
     # per XCD, so the grid order takes one row of 32 slots in launch order, the next in reverse and
