@@ -1111,7 +1111,8 @@ __global__ __launch_bounds__(kNT) void bwd_fp32_kernel(BwdArgs A) {
 // bwd_k_dot. INT: every kept rung is integral (§2 "Implementation note"): a key row receives one
 // query row per rung, so the rungs with a <= 64 come from the near block four to a group (at most
 // two groups: terms te = 0..3 are four rungs' rows), and a far step stages 64-row blocks of its two
-// rungs' rows (terms 1 and 3, which would be the second rows, read the first ones with weight 0).
+// rungs' rows, whose terms pair the two rungs at two elements per transposing read (one v_dot2 per
+// element, half an interpolated step's).
 // ------------------------------------------------------------------------------------------------
 template <int MAXS, bool INT>
 __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
@@ -1230,11 +1231,12 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     const int rbase16 = 16 * wave + 4 * lg;
     // far steps: term te of key row r: near / far of rung 2k at slots r, r + 1, of rung 2k + 1 at
     // 74 + r, 75 + r; element block nb of it is at radr[q] ^ (nb << 4)
-    // (INT: terms 0 and 1 at slot r, terms 2 and 3 at 72 + r)
+    // (INT: term te of key row r is rung 2k - ro + (te & 1), slot r or 72 + r, at element block
+    // nb + (te >> 1) for the read of element blocks nb and nb + 1, nb even)
     int radr[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-        radr[q] = INT ? blk_addr(rbase16 + q + (te >> 1) * kBlkSlots, 0)
+        radr[q] = INT ? blk_addr(rbase16 + q + (te & 1) * kBlkSlots, 0) ^ ((te >> 1) << 4)
                       : blk_addr(rbase16 + q + (te & 1) + (te >> 1) * (kBlkSlots + 2), 0);
     auto sum_rungs = [&](f4_t (&acc)[4], const uint4 (&w)[4], bool use_p, const char* lds, const int (&radr)[4]) {
 #pragma unroll
@@ -1254,6 +1256,26 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
                 acc[nb][q] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, w01), __builtin_bit_cast(h2_t, lo), acc[nb][q], false);
                 acc[nb][q] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, w23), __builtin_bit_cast(h2_t, hi), acc[nb][q], false);
             }
+        }
+    };
+
+    // INT far steps: one read gives the two rungs' elements E(nb) and E(nb + 1) (nb even); the
+    // weight word pairs the two rungs (dS halves in w.x, p halves in w.z)
+    auto sum_pairs = [&](f4_t (&acc)[4], const uint4 (&w)[4], bool use_p, const char* lds, const int (&radr)[4]) {
+        unsigned long long rv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int q = u >> 1, nb = 2 * (u & 1);
+            rv[u] = __builtin_bit_cast(unsigned long long, tr_read_h4(lds, radr[q] ^ (nb << 4)));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int q = u >> 1, nb = 2 * (u & 1);
+            asm volatile("" : "+v"(rv[u]));
+            const uint32_t lo = static_cast<uint32_t>(rv[u]), hi = static_cast<uint32_t>(rv[u] >> 32);
+            const h2_t wab = __builtin_bit_cast(h2_t, use_p ? w[q].z : w[q].x);
+            acc[nb][q] = __builtin_amdgcn_fdot2(wab, __builtin_bit_cast(h2_t, lo), acc[nb][q], false);
+            acc[nb + 1][q] = __builtin_amdgcn_fdot2(wab, __builtin_bit_cast(h2_t, hi), acc[nb + 1][q], false);
         }
     };
 
@@ -1353,9 +1375,8 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     // the thread's coefficient of each rung pair k (rung 2k + (wv & 1), dS halves for wv < 2, else
     // p halves): (1 - t, t), times the factors of its near and far query rows where not every
     // factor is 1 (then recomputed per head)
-    // INT: a near group (even k < kn) has no (1 - t, t): its words pair two rungs (2k + 2 (wv & 1)
-    // and the next), each with its own query row's factor; a far pair k has (1, 0) (rung
-    // 2k - ro + (wv & 1))
+    // INT: no (1 - t, t): a word pairs two rungs, each with its own query row's factor; a near
+    // group (even k < kn) rungs 2k + 2 (wv & 1) and the next, a far pair k rungs 2k - ro and the next
     auto near_a = [&](int k, int c) -> int { return 2 * k + c < nn ? A.off[2 * k + c].a : 0; };
     uint32_t cw[MAXS];
     auto set_cw = [&](int hh, bool with_factors) {
@@ -1371,11 +1392,11 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
                                                     : 0x3c003c00u;
                     cw[k] = f;
                 } else {
-                    const int n = 2 * k - ro + (wv & 1);
-                    const int a = pick_uniform((wv & 1) != 0, A.off[2 * k - ro + 1].a, A.off[2 * k - ro].a);
-                    const uint32_t f = with_factors ? fac_half(hh, 3 + 2 * n + ((j0 + wrow + a) >> 6) - ((j0 + a) >> 6), use_p)
-                                                    : 0x3c00u;
-                    cw[k] = f & 0xffffu;
+                    const int n = 2 * k - ro;
+                    const int a0 = A.off[n].a, a1 = A.off[n + 1].a;
+                    cw[k] = with_factors ? fac_half(hh, 3 + 2 * n + ((j0 + wrow + a0) >> 6) - ((j0 + a0) >> 6), use_p) |
+                                               (fac_half(hh, 5 + 2 * n + ((j0 + wrow + a1) >> 6) - ((j0 + a1) >> 6), use_p) << 16)
+                                         : 0x3c003c00u;
                 }
             } else {
                 const float t = pick_uniform((wv & 1) != 0, A.off[2 * k + 1].t, A.off[2 * k].t);
@@ -1389,8 +1410,9 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     set_cw(0, false);
     // rung step weights of head hh: thread (row wrow, part wv) builds one word of wst for key row
     // j0 + wrow: rung 2k + (wv & 1), dS halves (wv < 2) or p halves, times the coefficient
+    // (INT: the entries of the pair's two rungs at their near query rows, for every wv)
     auto put_w = [&](int k) {
-        const uint32_t en = went[k & 1][wv & 1][wrow], ef = went[k & 1][wv & 1][wrow + 1];
+        const uint32_t en = went[k & 1][INT ? 0 : wv & 1][wrow], ef = went[k & 1][INT ? 1 : wv & 1][wrow + (INT ? 0 : 1)];
         const uint32_t pr = __builtin_amdgcn_perm(ef, en, (wv >> 1) ? 0x05040100u : 0x07060302u);
         reinterpret_cast<uint32_t*>(&wst[k & 1][wrow])[wv] = mul_h2(pr, cw[k]);
     };
@@ -1535,8 +1557,13 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
                     uint4 w[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) w[q] = wst[k & 1][rbase16 + q];
-                    sum_rungs(dk, w, false, buf(k + 1), radr);
-                    sum_rungs(dv, w, true, buf(k + 1) + kBufBytes, radr);
+                    if constexpr (INT) {
+                        sum_pairs(dk, w, false, buf(k + 1), radr);
+                        sum_pairs(dv, w, true, buf(k + 1) + kBufBytes, radr);
+                    } else {
+                        sum_rungs(dk, w, false, buf(k + 1), radr);
+                        sum_rungs(dv, w, true, buf(k + 1) + kBufBytes, radr);
+                    }
                 }
                 if (k + 1 < n_steps) put_w(k + 1);
                 publish<0>();
