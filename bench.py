@@ -28,6 +28,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 import workloads  # noqa: E402
@@ -373,6 +374,65 @@ def profile_pass(fa, name: str, dev):
     log(f"[{name}] profile pass done")
 
 
+PHASES = ("q and key near block", "key pass", "value near block", "value pass", "stores")
+RTC_MHZ = 100.0   # the GPU's real-time counter (s_memrealtime), a constant 100 MHz
+
+
+def phase_trace(name: str, dev, reps: int = 3):
+    """Per-workgroup phase timeline of the forward attention kernel (bf16 storage), every layer of
+    the workload, from the trace build (libfibattn_trace.so, which records stamps at the phase
+    boundaries of each workgroup): per phase the median and 90th percentile over workgroups (µs), the
+    spread of workgroup start and end times, the span from the first start to the last end (to be
+    read beside the kernel's duration in a kernel trace, a check of the clock), and when workgroups
+    end by their number of far steps."""
+    import fibonacci_offset_sparse_amd as fa
+    fa.LIB_PATH = fa.TRACE_LIB_PATH
+    fa.lib = fa._load()
+    w = workloads.WORKLOADS[name]
+    code = {"fixed": fa.SCHEDULE_FIXED, "linear": fa.SCHEDULE_LINEAR, "coprime": fa.SCHEDULE_COPRIME}
+    thetas = workloads.draw_theta(w.n_layers).tolist() if w.schedule == "learned" else None
+    base = fa.fibattn_base_offsets(fa.BASE_FIB) if w.base == "fib" else \
+        fa.fibattn_base_offsets(fa.BASE_POW2, workloads.pow2_max(w))
+    n_wg = w.B * w.Hkv * (w.Hq // w.Hkv // 4) * ((w.L + 63) // 64)
+    q_ = lambda a, f: float(np.quantile(a, f))
+    layers = []
+    for layer in range(w.n_layers):
+        alpha = fa.fibattn_alpha_from_theta(thetas[layer])[0] if thetas else \
+            fa.fibattn_alpha_schedule(code[w.schedule], layer, w.n_layers)
+        q, k, v = (x.to(dev) for x in workloads.draw(w, layer, with_grad=False))
+        for _ in range(reps):
+            fa.fibattn_fwd(q, k, v, alpha, w.W, base)
+        torch.cuda.synchronize()
+        # the traced call: only the attention kernel records, and its last launch is this one
+        fa.fibattn_fwd(q, k, v, alpha, w.W, base)
+        torch.cuda.synchronize()
+        rec = fa.fibattn_phase_trace_read(n_wg).astype(np.float64)
+        us = 1.0 / RTC_MHZ
+        t = rec[:, :6]
+        t0 = t[:, 0].min()
+        dur = np.diff(t, axis=1) * us
+        starts, ends = (t[:, 0] - t0) * us, (t[:, 5] - t0) * us
+        info = rec[:, 6].astype(np.uint64)
+        far = ((info >> np.uint64(16)) & np.uint64(0xff)).astype(int) - ((info >> np.uint64(24)) & np.uint64(0xff)).astype(int)
+        by_far = {int(f): {"workgroups": int((far == f).sum()), "end_median_us": q_(ends[far == f], 0.5)}
+                  for f in sorted(set(far.tolist()))}
+        layers.append({
+            "layer": layer, "alpha": alpha, "span_us": float(ends.max()),
+            "phases_us": {PHASES[j]: {"median": q_(dur[:, j], 0.5), "p90": q_(dur[:, j], 0.9)} for j in range(5)},
+            "start_us": {"p50": q_(starts, 0.5), "p90": q_(starts, 0.9), "max": float(starts.max())},
+            "end_us": {"p10": q_(ends, 0.1), "p50": q_(ends, 0.5), "p90": q_(ends, 0.9), "max": float(ends.max())},
+            "end_by_far_steps": by_far,
+        })
+        log(f"[{name}] layer {layer} alpha={alpha:.4f}: span {ends.max():.2f} us, "
+            + ", ".join(f"{PHASES[j]} {np.median(dur[:, j]):.2f}" for j in range(5)))
+        del q, k, v
+    summary = {PHASES[j]: {"median_over_layers_of_median": float(np.median([l["phases_us"][PHASES[j]]["median"] for l in layers])),
+                           "median_over_layers_of_p90": float(np.median([l["phases_us"][PHASES[j]]["p90"] for l in layers]))}
+               for j in range(5)}
+    return {"workload": name, "workgroups": n_wg, "clock_MHz": RTC_MHZ, "layers": layers, "summary": summary,
+            "span_us_mean": float(np.mean([l["span_us"] for l in layers]))}
+
+
 def time_steps(net: Layers, steps: int, warmup: int):
     for _ in range(warmup):
         net.step()
@@ -588,6 +648,9 @@ def main():
                     help="run the short counter-collection program instead of the timed bench")
     ap.add_argument("--stream-probe", action="store_true",
                     help="run only the streaming-bandwidth probe and print its JSON line")
+    ap.add_argument("--phase-trace", action="store_true",
+                    help="run the forward attention kernel's phase trace (libfibattn_trace.so) on every "
+                         "layer of --workload and print its JSON line instead of the timed bench")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -600,6 +663,9 @@ def main():
         return
     if args.stream_probe:
         print(json.dumps(stream_probe(torch.device("cuda:0"))), flush=True)
+        return
+    if args.phase_trace:
+        print(json.dumps({"phase_trace": phase_trace(args.workload, torch.device("cuda:0"))}), flush=True)
         return
 
     cpu = None

@@ -16,6 +16,8 @@ import numpy as np
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfibattn.so")
+# the same library with the forward attention kernel's phase trace compiled in (measurement only)
+TRACE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfibattn_trace.so")
 
 F32, BF16 = 0, 1
 DUP, INT, INTERP = 0, 1, 2
@@ -69,6 +71,7 @@ def _load() -> ctypes.CDLL:
                                                _P(_c_i32), _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                                _c_i32, _c_f64, _c_f64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                                _c_ptr, _c_ptr, _c_size, _c_ptr]),
+        "fibattn_phase_trace_read": (ctypes.c_int, [_P(ctypes.c_uint64), _c_i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -227,6 +230,14 @@ def fibattn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: float,
     return o, lse
 
 
+def fibattn_phase_trace_read(n_wg: int) -> np.ndarray:
+    """The forward attention kernel's phase records of its last launch, uint64 [n_wg, 8] (the trace
+    build only: load TRACE_LIB_PATH; other builds raise FibAttnError UNSUPPORTED)."""
+    out = np.zeros((int(n_wg), 8), dtype=np.uint64)
+    _check(lib.fibattn_phase_trace_read(out.ctypes.data_as(_P(ctypes.c_uint64)), int(n_wg)))
+    return out
+
+
 def fibattn_fwd_noalloc_max_bytes() -> int:
     return int(lib.fibattn_fwd_noalloc_max_bytes())
 
@@ -376,5 +387,5 @@ __all__ = [
     "fibattn_alpha_from_theta", "fibattn_round_offsets", "fibattn_plan", "fibattn_fwd_workspace_bytes", "fibattn_fwd",
     "fibattn_fwd_prep", "fibattn_fwd_attend", "fibattn_fwd_noalloc", "fibattn_fwd_noalloc_max_bytes", "fibattn_bwd_workspace_bytes", "fibattn_bwd",
     "fibattn_bwd_stages", "fibattn_bwd_reuses_fwd_prep", "fibattn_decode", "STAGE_PREP", "STAGE_QUERY", "STAGE_KEY", "STAGE_ALL",
-    "FibAttnError", "lib", "LIB_PATH",
+    "fibattn_phase_trace_read", "FibAttnError", "lib", "LIB_PATH", "TRACE_LIB_PATH",
 ]

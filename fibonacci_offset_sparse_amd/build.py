@@ -24,6 +24,10 @@ OUT = os.path.join(PKG, "libfibattn.so")
 # attention library)
 PROBE_SRC = "stream_probe.hip"
 PROBE_OUT = os.path.join(PKG, "libstreamprobe.so")
+# the same library with the forward attention kernel's phase trace compiled in (FIBATTN_PHASE_TRACE:
+# per-workgroup stamps read back by fibattn_phase_trace_read; `bench.py --phase-trace` loads it)
+TRACE_SRC = "fibattn_fwd_mfma.hip"
+TRACE_OUT = os.path.join(PKG, "libfibattn_trace.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
@@ -43,9 +47,10 @@ def hipcc() -> str:
     return exe
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, defines=()) -> str:
+    tag = "".join("_" + d.lower() for d in defines)
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + tag + ".o")
+    cmd = [hipcc(), *COMMON, *(f"-D{d}" for d in defines), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = DEVICE
     else:
@@ -67,12 +72,16 @@ def _link(objs, out):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
-        objs = list(ex.map(_compile, SOURCES + [PROBE_SRC]))
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + 2) as ex:
+        jobs = [ex.submit(_compile, s) for s in SOURCES + [PROBE_SRC]]
+        trace_job = ex.submit(_compile, TRACE_SRC, ("FIBATTN_PHASE_TRACE",))
+        objs = [j.result() for j in jobs]
+        trace_obj = trace_job.result()
     _link(objs[:-1], OUT)
     _link(objs[-1:], PROBE_OUT)
+    _link([trace_obj if s == TRACE_SRC else o for s, o in zip(SOURCES, objs[:-1])], TRACE_OUT)
     if verbose:
-        print(f"built {OUT} and {PROBE_OUT}")
+        print(f"built {OUT}, {PROBE_OUT} and {TRACE_OUT}")
     return OUT
 
 

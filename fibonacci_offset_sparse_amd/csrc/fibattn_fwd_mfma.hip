@@ -45,6 +45,7 @@
 //    then holds that head's keys and values for every tile that re-reads them, and each CU mixes
 //    early and late tiles.
 //  * q arrives by non-temporal LDS DMA (read once) and o and lse leave by non-temporal stores.
+#include "fibattn.h"
 #include "fibattn_mfma.h"
 
 namespace fibattn {
@@ -58,6 +59,38 @@ using namespace mx;
 // the scores and the 64 output accumulators without spilling (a spill reload is a vector-memory
 // load and would wait behind every staging load in flight).
 constexpr int kWgsPerCu = 4;
+
+// ---- phase trace (in the build with FIBATTN_PHASE_TRACE only) ----
+// Per workgroup of the attention kernel (wave 0), six stamps of the 100 MHz real-time counter:
+// start, key near block landed, key pass done, value near block landed, value pass done, outputs
+// stored (after a wait for the stores); then the tile and its counts of kept rungs and steps, and the
+// CU. In the usual build every PhaseClock call is empty.
+#ifdef FIBATTN_PHASE_TRACE
+constexpr int kTraceWgs = 65536;
+constexpr int kTraceWords = 8;
+__device__ uint64_t g_phase[kTraceWgs * kTraceWords];
+struct PhaseClock {
+    uint64_t t[6];
+    __device__ __forceinline__ void mark(int k) { t[k] = __builtin_amdgcn_s_memrealtime(); }
+    __device__ __forceinline__ void record(int tile, int n_steps, int kn, int n_reach) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        mark(5);
+        if (threadIdx.x == 0 && blockIdx.x < static_cast<unsigned>(kTraceWgs)) {
+            uint64_t* g = g_phase + static_cast<uint64_t>(blockIdx.x) * kTraceWords;
+#pragma unroll
+            for (int k = 0; k < 6; ++k) g[k] = t[k];
+            g[6] = static_cast<uint64_t>(tile) | (static_cast<uint64_t>(n_steps) << 16) |
+                   (static_cast<uint64_t>(kn) << 24) | (static_cast<uint64_t>(n_reach) << 32);
+            g[7] = static_cast<uint64_t>(__smid());
+        }
+    }
+};
+#else
+struct PhaseClock {
+    __device__ __forceinline__ void mark(int) {}
+    __device__ __forceinline__ void record(int, int, int, int) {}
+};
+#endif
 
 // ------------------------------------------------------------------------------------------------
 // prep_kv16: rotated keys and values as fp16 rows, plus the cos/sin table of every position. One
@@ -311,6 +344,8 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     const int i0 = tile * kTile;
     const int i = i0 + p;
     const bool active = i < L;
+    PhaseClock clk;
+    clk.mark(0);
 
     // kept rungs this tile reaches (a prefix: the reach grows with the rung), in steps of two
     int n_reach = 0;
@@ -406,6 +441,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
         }
     }
     publish<kStepDmas>();                               // the key near block has landed
+    clk.mark(1);
 
     // ---- phase A: scores of the lane's head x (base 2) ----
     // Far step k computes from buffer (k + 1) % 2 after issuing step k + 1 into the other buffer
@@ -486,6 +522,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
         }
     }
 
+    clk.mark(2);
     // ---- value near block into buffer 0 (unless it went ahead) and value far step kn into
     // buffer 1 (both free after the last barrier), under the softmax ----
     if (!near_ahead) st.near(vrs, lds0, jn);
@@ -546,6 +583,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
     for (int e = 0; e < 16; ++e) o[e] = (f4_t){0.f, 0.f, 0.f, 0.f};
     {
         publish<kStepDmas>();                           // the value near block has landed
+        clk.mark(3);
         // window group g: slot pt - 4g - kt + 64
         const int sv = pt - kt + kNear;
 #pragma unroll
@@ -584,6 +622,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
         }
     }
 
+    clk.mark(4);
     // ---- normalise and write: lane x holds dims 16x..16x+15 of heads 0..3 ----
     const float inv = 1.0f / l;
     float invh[4];
@@ -618,6 +657,7 @@ __global__ __launch_bounds__(kNT, kWgsPerCu) void fwd_mfma_kernel(FwdArgs A) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         fwd_tile_fp32(A, b, bg, h0, i0);
     }
+    clk.record(tile, n_steps, kn, n_reach);
 }
 
 }  // namespace
@@ -652,3 +692,23 @@ hipError_t launch_fwd_mfma(const FwdArgs& A0, hipStream_t s) {
 }
 
 }  // namespace fibattn
+
+extern "C" fibattn_status_t fibattn_phase_trace_read(uint64_t* out, int32_t n_wg) {
+#ifdef FIBATTN_PHASE_TRACE
+    if (out == nullptr || n_wg < 0 || n_wg > fibattn::kTraceWgs)
+        return static_cast<fibattn_status_t>(
+            fibattn::report_error(FIBATTN_ERR_INVALID, "phase trace: out is null or n_wg = %d outside 0..%d", n_wg,
+                                  fibattn::kTraceWgs));
+    const hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(fibattn::g_phase),
+                                             static_cast<size_t>(n_wg) * fibattn::kTraceWords * sizeof(uint64_t));
+    if (e != hipSuccess)
+        return static_cast<fibattn_status_t>(
+            fibattn::report_error(FIBATTN_ERR_HIP, "phase trace: %s", hipGetErrorString(e)));
+    return FIBATTN_OK;
+#else
+    (void)out;
+    (void)n_wg;
+    return static_cast<fibattn_status_t>(
+        fibattn::report_error(FIBATTN_ERR_UNSUPPORTED, "this library was built without the phase trace"));
+#endif
+}

@@ -306,6 +306,18 @@ fibattn_status_t fibattn_bwd_stages(int32_t stages, const void* q, const void* k
                                     void* dv, float* dalpha, float* dtheta, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* Phase trace of the bfloat16 forward attention kernel, for measurement only (no passage of the
+ * pages: it times the kernel that does §2 "Attended set" for bf16 storage). The library built with
+ * FIBATTN_PHASE_TRACE (libfibattn_trace.so) records, per workgroup of the kernel's last launch,
+ * eight 64-bit words: six stamps of the GPU's 100 MHz real-time counter (start; key near block
+ * landed; key pass done; value near block landed; value pass done; outputs stored), then
+ * tile | steps << 16 | near steps << 24 | kept rungs reached << 32, and the CU. Records of
+ * workgroups 65536 and up are not kept. fibattn_phase_trace_read copies the first n_wg records
+ * (0 <= n_wg <= 65536) to out (host, 8 n_wg words), a synchronous copy on the null stream: call it
+ * after the traced launch has finished. INVALID for a null out or n_wg out of range, HIP when the
+ * copy fails. Every other build returns UNSUPPORTED and touches nothing. */
+fibattn_status_t fibattn_phase_trace_read(uint64_t* out, int32_t n_wg);
+
 #ifdef __cplusplus
 }
 #endif

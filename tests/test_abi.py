@@ -244,3 +244,21 @@ def test_host_helpers_argument_checks():
         fa.fibattn_plan(2e9, 4, [1])
     assert fa.fibattn_status_string(99) == "unknown status"
     assert math.isfinite(fa.fibattn_alpha_schedule(fa.SCHEDULE_COPRIME, 3, 16))
+
+
+def test_phase_trace_reader_in_both_builds():
+    # the usual library has no trace and says so; the trace build exports the same functions and
+    # checks its arguments before touching the GPU
+    buf = (ctypes.c_uint64 * 8)()
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    f = lib.fibattn_phase_trace_read
+    f.restype, f.argtypes = ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]
+    assert f(buf, 1) == 2
+    tlib = ctypes.CDLL(fa.TRACE_LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(tlib, name), name
+    g = tlib.fibattn_phase_trace_read
+    g.restype, g.argtypes = ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]
+    assert g(None, 1) == 1
+    assert g(buf, -1) == 1
+    assert g(buf, 65537) == 1
