@@ -386,8 +386,7 @@ def phase_trace(name: str, dev, reps: int = 3):
     read beside the kernel's duration in a kernel trace, a check of the clock), and when workgroups
     end by their number of far steps."""
     import fibonacci_offset_sparse_amd as fa
-    fa.LIB_PATH = fa.TRACE_LIB_PATH
-    fa.lib = fa._load()
+    fa.lib = fa._load_from(fa.TRACE_LIB_PATH)
     w = workloads.WORKLOADS[name]
     code = {"fixed": fa.SCHEDULE_FIXED, "linear": fa.SCHEDULE_LINEAR, "coprime": fa.SCHEDULE_COPRIME}
     thetas = workloads.draw_theta(w.n_layers).tolist() if w.schedule == "learned" else None

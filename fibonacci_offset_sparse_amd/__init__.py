@@ -32,9 +32,14 @@ _P = ctypes.POINTER
 
 
 def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python fibonacci_offset_sparse_amd/build.py`")
-    lib = ctypes.CDLL(LIB_PATH)
+    return _load_from(LIB_PATH)
+
+
+def _load_from(path: str) -> ctypes.CDLL:
+    """The library at path with every entry point's signature set (the usual build or the trace build)."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python fibonacci_offset_sparse_amd/build.py`")
+    lib = ctypes.CDLL(path)
     sig = {
         "fibattn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "fibattn_last_error": (ctypes.c_char_p, []),
