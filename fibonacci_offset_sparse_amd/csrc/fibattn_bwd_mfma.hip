@@ -634,10 +634,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
                 const float sc = fmaf(t, dd, acc[2 * e] * qsc);
                 const bool ok = active && i >= A.off[n].a + A.off[n].interp;
                 s[4 * kWG + n] = ok ? sc : kNegInf;
-                sd[n] = ok ? dd : 0.f;
-                const float dv = accv[2 * e + 1] - accv[2 * e];
-                dp[4 * kWG + n] = fmaf(t, dv, accv[2 * e]);
-                dpd[n] = dv;
+                dp[4 * kWG + n] = fmaf(t, accv[2 * e + 1] - accv[2 * e], accv[2 * e]);
             }
         }
     };
@@ -815,20 +812,24 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     float delta = 0.f;
 #pragma unroll
     for (int y = 0; y < 4 * kWG + MAXK; ++y) delta = fmaf(s[y], dp[y], delta);
-    // dS = p (dP - delta) / sqrt(D), in place of dP; d(loss)/dt terms
+    // dS = p (dP - delta) / sqrt(D), in place of dP; d(loss)/dt terms, which only a call that
+    // asks for d(alpha) (PRECISE) sums: the other variants leave them out
     float dt[MAXK];
 #pragma unroll
     for (int y = 0; y < 4 * kWG + MAXK; ++y) dp[y] = s[y] * (dp[y] - delta) * A.scale;
+    if constexpr (PRECISE) {
 #pragma unroll
-    for (int n = 0; n < MAXK; ++n) {
-        // dS (q . (k_far - k_near)) / sqrt(D) in base 2: sd = (q . dk) log2(e) / sqrt(D), so
-        // (dS / sqrt(D)) sd ln2 sqrt(D) = dS (q . dk) / sqrt(D)
-        dt[n] = fmaf(dp[4 * kWG + n] * (kLn2 / A.scale), sd[n], s[4 * kWG + n] * dpd[n]);
-    }
-    // dS/sqrt(D), dP and the dt terms are in units of 2^-ed (do was scaled by it): dt to true units
-    if (wscaled) {
+        for (int n = 0; n < MAXK; ++n) {
+            // dS (q . (k_far - k_near)) / sqrt(D) in base 2: sd = (q . dk) log2(e) / sqrt(D), so
+            // (dS / sqrt(D)) sd ln2 sqrt(D) = dS (q . dk) / sqrt(D)
+            dt[n] = fmaf(dp[4 * kWG + n] * (kLn2 / A.scale), sd[n], s[4 * kWG + n] * dpd[n]);
+        }
+        // dS/sqrt(D), dP and the dt terms are in units of 2^-ed (do was scaled by it): dt to true
+        // units
+        if (wscaled) {
 #pragma unroll
-        for (int n = 0; n < MAXK; ++n) dt[n] *= pow2f(ed);
+            for (int n = 0; n < MAXK; ++n) dt[n] *= pow2f(ed);
+        }
     }
     // the key side's weights of this query: (p, dS/sqrt(D)) per window distance and per rung
     // (without the rung's coefficients), fp16 pairs, dS scaled by the row's 2^-es (its largest
@@ -1022,12 +1023,14 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
 
     // ---- d(loss)/dt partial sums of this workgroup (fixed order), and each head's largest dS
     // exponent over the tile ----
+    if constexpr (PRECISE) {
 #pragma unroll
-    for (int n = 0; n < MAXK; ++n) {
-        float v = active ? dt[n] : 0.f;
+        for (int n = 0; n < MAXK; ++n) {
+            float v = active ? dt[n] : 0.f;
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-        if (lane == 0) red[wave][n] = v;
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+            if (lane == 0) red[wave][n] = v;
+        }
     }
     {
         const int ms = head_max(es);
@@ -1057,7 +1060,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
             for (int y = 0; y < 4 * kWG + MAXK; ++y) wq[y] = mul_h2(wq[y], fs);
             store_w();
         }
-        if (threadIdx.x < static_cast<unsigned>(A.n_off)) {
+        if (PRECISE && threadIdx.x < static_cast<unsigned>(A.n_off)) {
             float v = 0.f;
             if (threadIdx.x < MAXK) v = ((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) + red[3][threadIdx.x];
             A.partial[static_cast<int64_t>(blockIdx.x) * kMaxOff + threadIdx.x] = v;
