@@ -208,12 +208,22 @@ INT_PLANS = [
 
 
 @pytest.mark.parametrize("W,offsets", INT_PLANS)
-def test_integer_offset_plans(W, offsets):
-    L = 300
-    q, k, v, do = (randn((2, 8, L, 64), 71, torch.bfloat16), randn((2, 2, L, 64), 72, torch.bfloat16),
-                   randn((2, 2, L, 64), 73, torch.bfloat16), randn((2, 8, L, 64), 74, torch.bfloat16))
+@pytest.mark.parametrize("L", [300, 1100])
+def test_integer_offset_plans(W, offsets, L):
+    B = 2 if L <= 300 else 1
+    q, k, v, do = (randn((B, 8, L, 64), 71, torch.bfloat16), randn((B, 2, L, 64), 72, torch.bfloat16),
+                   randn((B, 2, L, 64), 73, torch.bfloat16), randn((B, 8, L, 64), 74, torch.bfloat16))
     say(f"bwd integral plan W={W} offsets={offsets} L={L}")
-    compare(q, k, v, do, 1.0, W, offsets, f"int W={W} K={len(offsets)}", want_dalpha=False)
+    compare(q, k, v, do, 1.0, W, offsets, f"int W={W} K={len(offsets)} L={L}", want_dalpha=False)
+
+
+@pytest.mark.parametrize("Hq,Hkv,L", [(16, 2, 300), (8, 2, 65), (4, 1, 130)])
+def test_integer_offset_path_gqa_and_ragged(Hq, Hkv, L):
+    q, k, v, do = (randn((1, Hq, L, 64), 75, torch.bfloat16), randn((1, Hkv, L, 64), 76, torch.bfloat16),
+                   randn((1, Hkv, L, 64), 77, torch.bfloat16), randn((1, Hq, L, 64), 78, torch.bfloat16))
+    for W, offsets in ((2, [3, 5, 64, 65, 200]), (2, [3, 5, 8, 13, 21, 100, 200])):
+        say(f"bwd integral plan Hq={Hq} Hkv={Hkv} L={L} W={W} offsets={offsets}")
+        compare(q, k, v, do, 1.0, W, offsets, f"int Hq={Hq} L={L} K={len(offsets)}", want_dalpha=False)
 
 
 @pytest.mark.parametrize("name", ["l1024_linear_bf16", "l4096_coprime_bf16"])

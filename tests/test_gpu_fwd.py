@@ -170,6 +170,16 @@ def test_integer_offset_plans(W, offsets, L):
     compare(q, k, v, 1.0, W, offsets, f"int W={W} K={len(offsets)} L={L}")
 
 
+@pytest.mark.parametrize("Hq,Hkv,L", [(16, 2, 300), (8, 2, 65), (4, 1, 130)])
+def test_integer_offset_path_gqa_and_ragged(Hq, Hkv, L):
+    # a group of 8 query heads (two workgroups per tile), a tail one row past a tile, one KV head
+    q, k, v = (randn((1, Hq, L, 64), 64, torch.bfloat16), randn((1, Hkv, L, 64), 65, torch.bfloat16),
+               randn((1, Hkv, L, 64), 66, torch.bfloat16))
+    for W, offsets in ((2, [3, 5, 64, 65, 200]), (2, [3, 5, 8, 13, 21, 100, 200])):
+        say(f"integral plan Hq={Hq} Hkv={Hkv} L={L} W={W} offsets={offsets}")
+        compare(q, k, v, 1.0, W, offsets, f"int Hq={Hq} L={L} K={len(offsets)}")
+
+
 def test_grid_order_covers_every_tile_once():
     # B = 20 at the paper's head counts: 40 (batch, KV head) units of 16 tiles, 80 workgroup slots
     # per XCD, so the grid order takes one row of 32 slots in launch order, the next in reverse and
