@@ -1241,36 +1241,55 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     for (int q = 0; q < 4; ++q)
         radr[q] = INT ? blk_addr(rbase16 + q + (te & 1) * kBlkSlots, 0) ^ ((te >> 1) << 4)
                       : blk_addr(rbase16 + q + (te & 1) + (te >> 1) * (kBlkSlots + 2), 0);
-    auto sum_rungs = [&](f4_t (&acc)[4], const uint4 (&w)[4], bool use_p, const char* lds, const int (&radr)[4]) {
+    // A step's sums run as passes of 8 transposing reads and their products, each pass's reads
+    // issued before the previous pass's products, so that a wave multiplies with a pass of reads
+    // in flight (the empty asm with a memory clobber keeps the reads ahead of the products).
+    // Interpolated pass q0 (0 or 2): the terms of key rows q0 and q0 + 1 at element blocks 0..3.
+    auto rung_reads = [&](unsigned long long (&rv)[8], const char* lds, const int (&adr)[4], int q0) {
 #pragma unroll
-        for (int q0 = 0; q0 < 4; q0 += 2) {
-            unsigned long long rv[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int q = q0 + (u >> 2), nb = u & 3;
-                rv[u] = __builtin_bit_cast(unsigned long long, tr_read_h4(lds, radr[q] ^ (nb << 4)));
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int q = q0 + (u >> 2), nb = u & 3;
-                asm volatile("" : "+v"(rv[u]));
-                const uint32_t lo = static_cast<uint32_t>(rv[u]), hi = static_cast<uint32_t>(rv[u] >> 32);
-                const uint32_t w01 = use_p ? w[q].z : w[q].x, w23 = use_p ? w[q].w : w[q].y;
-                acc[nb][q] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, w01), __builtin_bit_cast(h2_t, lo), acc[nb][q], false);
-                acc[nb][q] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, w23), __builtin_bit_cast(h2_t, hi), acc[nb][q], false);
-            }
+        for (int u = 0; u < 8; ++u) {
+            const int q = q0 + (u >> 2), nb = u & 3;
+            rv[u] = __builtin_bit_cast(unsigned long long, tr_read_h4(lds, adr[q] ^ (nb << 4)));
         }
+    };
+    auto rung_products = [&](f4_t (&acc)[4], const uint4 (&w)[4], bool use_p, unsigned long long (&rv)[8], int q0) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int q = q0 + (u >> 2), nb = u & 3;
+            asm volatile("" : "+v"(rv[u]));
+            const uint32_t lo = static_cast<uint32_t>(rv[u]), hi = static_cast<uint32_t>(rv[u] >> 32);
+            const uint32_t w01 = use_p ? w[q].z : w[q].x, w23 = use_p ? w[q].w : w[q].y;
+            acc[nb][q] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, w01), __builtin_bit_cast(h2_t, lo), acc[nb][q], false);
+            acc[nb][q] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, w23), __builtin_bit_cast(h2_t, hi), acc[nb][q], false);
+        }
+    };
+    auto ahead = [] { asm volatile("" ::: "memory"); };
+    // dk and dv rung sums of one step: its rotated-query part at lds, its do part kBufBytes on
+    auto sum_rungs = [&](const uint4 (&w)[4], const char* lds, const int (&adr)[4]) {
+        unsigned long long ra[8], rb[8];
+        rung_reads(ra, lds, adr, 0);
+        rung_reads(rb, lds, adr, 2);
+        ahead();
+        rung_products(dk, w, false, ra, 0);
+        rung_reads(ra, lds + kBufBytes, adr, 0);
+        ahead();
+        rung_products(dk, w, false, rb, 2);
+        rung_reads(rb, lds + kBufBytes, adr, 2);
+        ahead();
+        rung_products(dv, w, true, ra, 0);
+        rung_products(dv, w, true, rb, 2);
     };
 
     // INT far steps: one read gives the two rungs' elements E(nb) and E(nb + 1) (nb even); the
     // weight word pairs the two rungs (dS halves in w.x, p halves in w.z)
-    auto sum_pairs = [&](f4_t (&acc)[4], const uint4 (&w)[4], bool use_p, const char* lds, const int (&radr)[4]) {
-        unsigned long long rv[8];
+    auto pair_reads = [&](unsigned long long (&rv)[8], const char* lds, const int (&adr)[4]) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int q = u >> 1, nb = 2 * (u & 1);
-            rv[u] = __builtin_bit_cast(unsigned long long, tr_read_h4(lds, radr[q] ^ (nb << 4)));
+            rv[u] = __builtin_bit_cast(unsigned long long, tr_read_h4(lds, adr[q] ^ (nb << 4)));
         }
+    };
+    auto pair_products = [&](f4_t (&acc)[4], const uint4 (&w)[4], bool use_p, unsigned long long (&rv)[8]) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int q = u >> 1, nb = 2 * (u & 1);
@@ -1280,6 +1299,14 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
             acc[nb][q] = __builtin_amdgcn_fdot2(wab, __builtin_bit_cast(h2_t, lo), acc[nb][q], false);
             acc[nb + 1][q] = __builtin_amdgcn_fdot2(wab, __builtin_bit_cast(h2_t, hi), acc[nb + 1][q], false);
         }
+    };
+    auto sum_pairs = [&](const uint4 (&w)[4], const char* lds, const int (&adr)[4]) {
+        unsigned long long ra[8], rb[8];
+        pair_reads(ra, lds, adr);
+        pair_reads(rb, lds + kBufBytes, adr);
+        ahead();
+        pair_products(dk, w, false, ra);
+        pair_products(dv, w, true, rb);
     };
 
     // ---- the query side scaled each head's rows of a query tile by powers of two of the tile's
@@ -1538,8 +1565,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
                 uint4 w[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) w[q] = wnear(k)[rbase16 + q];
-                sum_rungs(dk, w, false, lds0, nadr);
-                sum_rungs(dv, w, true, lds0 + kBufBytes, nadr);
+                sum_rungs(w, lds0, nadr);
             }
         }
         put_w(kn);
@@ -1561,11 +1587,9 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) w[q] = wst[k & 1][rbase16 + q];
                     if constexpr (INT) {
-                        sum_pairs(dk, w, false, buf(k + 1), radr);
-                        sum_pairs(dv, w, true, buf(k + 1) + kBufBytes, radr);
+                        sum_pairs(w, buf(k + 1), radr);
                     } else {
-                        sum_rungs(dk, w, false, buf(k + 1), radr);
-                        sum_rungs(dv, w, true, buf(k + 1) + kBufBytes, radr);
+                        sum_rungs(w, buf(k + 1), radr);
                     }
                 }
                 if (k + 1 < n_steps) put_w(k + 1);
