@@ -455,6 +455,29 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         const int pos = i0 + 16 * wave + (s & 15);
         return pos < L ? (static_cast<int64_t>(b) * A.Hq + h0 + (s >> 4)) * L + pos : -1;
     };
+    // The 8 linear-view chunks of the wave's 8 KB region of treg to rows of a [.., L, 64] fp16 or
+    // bf16 tensor (the rows lin_row names): all 8 LDS reads first, then 8 buffer stores of 1 KB
+    // contiguous per instruction. A slot past L stores at an offset beyond the buffer (4 heads' L
+    // rows from row (b Hq + h0) L: within 32 bits for L <= 2^20), which the hardware drops, so no
+    // branch splits the reads from one another. aux: 2 for non-temporal stores.
+    auto store_lin = [&](void* base, const char* treg, int aux) {
+        const __amdgpu_buffer_rsrc_t ors = rows_rsrc(base, (static_cast<int64_t>(b) * A.Hq + h0) * L, 4 * L);
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const uint4*>(treg + lin_view_addr(lane, u));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int sl = lin_slot(lane, u);
+            const int pos = i0 + 16 * wave + (sl & 15);
+            const int off = pos < L ? ((sl >> 4) * L + pos) * kRowBytes + (lane & 7) * 16 : -kRowBytes;
+            typedef int v4i_t __attribute__((ext_vector_type(4)));
+            const v4i_t d = {static_cast<int>(v[u].x), static_cast<int>(v[u].y), static_cast<int>(v[u].z), static_cast<int>(v[u].w)};
+            if (aux)
+                __builtin_amdgcn_raw_buffer_store_b128(d, ors, off, 0, 2);
+            else
+                __builtin_amdgcn_raw_buffer_store_b128(d, ors, off, 0, 0);
+        }
+    };
     uint4 qraw[8], draw[8];
     float4 ctq[4];                                      // cos/sin of pairs 8x..8x+7 at position i
     uint32_t flagged;                                   // nonzero: a staged row the lane checks lies outside fp16's range
@@ -784,13 +807,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
                     tscaled ? make_uint4(mul_h2(v[0], f), mul_h2(v[1], f), mul_h2(v[2], f), mul_h2(v[3], f))
                             : make_uint4(v[0], v[1], v[2], v[3]);
             }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const uint4 v = *reinterpret_cast<const uint4*>(treg + lin_view_addr(lane, u));
-                const int64_t row = lin_row(lin_slot(lane, u));
-                if (row >= 0)
-                    *reinterpret_cast<uint4*>(static_cast<f16_t*>(t ? A.do16 : A.qrot16) + row * kD + (lane & 7) * 8) = v;
-            }
+            store_lin(t ? A.do16 : A.qrot16, treg, 0);
         }
     }
 
@@ -1012,12 +1029,7 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
                 *reinterpret_cast<uint4*>(treg + row_view_addr(pq, r, 2 * x)) = lo;
                 *reinterpret_cast<uint4*>(treg + row_view_addr(pq, r, 2 * x + 1)) = hi;
             }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const uint4 v = *reinterpret_cast<const uint4*>(treg + lin_view_addr(lane, u));
-                const int64_t row = lin_row(lin_slot(lane, u));
-                if (row >= 0) store_nt(static_cast<bf16_t*>(A.dq) + row * kD + (lane & 7) * 8, v);
-            }
+            store_lin(A.dq, treg, 2);
         }
     }
 
