@@ -446,20 +446,12 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     auto buf = [&](int j) -> char* { return (j & 1) ? lds1 : lds0; };
     const int jn = i0 - kNear;                          // the near block's row at slot 0
 
-    // ---- prologue: q and do of the wave's 16 positions and 4 heads by LDS DMA into the wave's
-    // 8 KB of lds0 (q) and of lds1 (do), 1 KB contiguous per instruction (lane l lands on slot
-    // 8u + (l >> 3), physical chunk l & 7, and fetches the logical chunk the swizzle puts there),
-    // read back one row per lane; then the key and value near blocks and far step kn ----
-    // row of linear-view slot s (head h0 + (s >> 4), position i0 + 16w + (s & 15)), or -1 past L
-    auto lin_row = [&](int s) -> int64_t {
-        const int pos = i0 + 16 * wave + (s & 15);
-        return pos < L ? (static_cast<int64_t>(b) * A.Hq + h0 + (s >> 4)) * L + pos : -1;
-    };
-    // The 8 linear-view chunks of the wave's 8 KB region of treg to rows of a [.., L, 64] fp16 or
-    // bf16 tensor (the rows lin_row names): all 8 LDS reads first, then 8 buffer stores of 1 KB
-    // contiguous per instruction. A slot past L stores at an offset beyond the buffer (4 heads' L
-    // rows from row (b Hq + h0) L: within 32 bits for L <= 2^20), which the hardware drops, so no
-    // branch splits the reads from one another. aux: 2 for non-temporal stores.
+    // The 8 linear-view chunks of a wave's 8 KB region of treg to rows of a [.., L, 64] fp16 or
+    // bf16 tensor (linear-view slot s is head h0 + (s >> 4) at position i0 + 16w + (s & 15)): all
+    // 8 LDS reads first, then 8 buffer stores of 1 KB contiguous per instruction. A slot past L
+    // stores at an offset beyond the buffer (4 heads' L rows from row (b Hq + h0) L: within 32 bits
+    // for L <= 2^20), which the hardware drops, so no branch splits the reads from one another.
+    // aux: 2 for non-temporal stores.
     auto store_lin = [&](void* base, const char* treg, int aux) {
         const __amdgpu_buffer_rsrc_t ors = rows_rsrc(base, (static_cast<int64_t>(b) * A.Hq + h0) * L, 4 * L);
         uint4 v[8];
@@ -478,6 +470,11 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
                 __builtin_amdgcn_raw_buffer_store_b128(d, ors, off, 0, 0);
         }
     };
+
+    // ---- prologue: q and do of the wave's 16 positions and 4 heads by LDS DMA into the wave's
+    // 8 KB of lds0 (q) and of lds1 (do), 1 KB contiguous per instruction (lane l lands on slot
+    // 8u + (l >> 3), physical chunk l & 7, and fetches the logical chunk the swizzle puts there),
+    // read back one row per lane; then the key and value near blocks and far step kn ----
     uint4 qraw[8], draw[8];
     float4 ctq[4];                                      // cos/sin of pairs 8x..8x+7 at position i
     uint32_t flagged;                                   // nonzero: a staged row the lane checks lies outside fp16's range
@@ -955,12 +952,26 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
         for (int c = 0; c < kNW / 4; ++c)
             *reinterpret_cast<uint4*>(treg + (16 * x + pq) * (kNW * 4) + ((c ^ x) << 4)) =
                 make_uint4(wq[4 * c], wq[4 * c + 1], wq[4 * c + 2], wq[4 * c + 3]);
+        {
+            // 4 LDS reads, then 4 buffer stores over the 4 heads' rows (a slot past L stores
+            // beyond the buffer and is dropped, as in store_lin)
+            const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+                A.wwin + (static_cast<int64_t>(b) * A.Hq + h0) * L * kNW, 0, 4 * L * kNW * 4, kRsrcWord3);
+            uint4 v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int sl = 16 * u + (lane >> 2), c = lane & 3;
-            const uint4 v = *reinterpret_cast<const uint4*>(treg + sl * (kNW * 4) + ((c ^ u) << 4));
-            const int64_t row = lin_row(sl);
-            if (row >= 0) *reinterpret_cast<uint4*>(A.wwin + row * kNW + 4 * c) = v;
+            for (int u = 0; u < 4; ++u) {
+                const int sl = 16 * u + (lane >> 2), c = lane & 3;
+                v[u] = *reinterpret_cast<const uint4*>(treg + sl * (kNW * 4) + ((c ^ u) << 4));
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int sl = 16 * u + (lane >> 2), c = lane & 3;
+                const int pos = i0 + 16 * wave + (sl & 15);
+                const int off = pos < L ? ((sl >> 4) * L + pos) * (kNW * 4) + 16 * c : -(kNW * 4);
+                typedef int v4i_t __attribute__((ext_vector_type(4)));
+                const v4i_t d = {static_cast<int>(v[u].x), static_cast<int>(v[u].y), static_cast<int>(v[u].z), static_cast<int>(v[u].w)};
+                __builtin_amdgcn_raw_buffer_store_b128(d, wrs, off, 0, 0);
+            }
         }
         if (active) {
             uint32_t* rr = A.wrung + (static_cast<int64_t>(b) * A.Hq + h0 + x) * kNR * L + i;
