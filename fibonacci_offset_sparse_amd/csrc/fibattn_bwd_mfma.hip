@@ -1171,17 +1171,21 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     const int j0 = tile * kTile;
 
     // rungs some key row of the tile receives (query j + a < L): a prefix
+    // (loops unrolled over the matrix-core kernels' limit of 16 kept rungs: the offset table's
+    // scalar loads then go out together, where a loop to n_off waits for each in turn)
     int n_reach = 0;
-    for (int n = 0; n < A.n_off; ++n)
-        if (j0 + A.off[n].a < L) n_reach = n + 1;
+#pragma unroll
+    for (int n = 0; n < 16; ++n)
+        if (n < A.n_off && j0 + A.off[n].a < L) n_reach = n + 1;
     // near rungs: the prefix with a <= 63 (both query rows of every key row of the tile inside the
     // near block; INT: a <= 64, the one row). Pairs k < kn come from the near block (kn even, at
     // most 4; INT: for even k a group of the four rungs 2k .. 2k + 3, those past nn padding);
     // pairs kn .. n_far - 1 are far steps, pair k in buffer (k + 1) % 2, n_far odd so that the last
     // one sits in lds1; far pair k holds rungs 2k - ro and 2k - ro + 1 (ro = 0 unless INT).
     int n_near = 0;
-    for (int n = 0; n < n_reach; ++n)
-        if (A.off[n].a <= kNear - (INT ? 0 : 1)) n_near = n + 1;
+#pragma unroll
+    for (int n = 0; n < 16; ++n)
+        if (n < n_reach && A.off[n].a <= kNear - (INT ? 0 : 1)) n_near = n + 1;
     const int nn = INT ? min(n_near, 8) : 0;
     const int kn = INT ? 2 * ((nn + 3) >> 2) : min((n_near >> 1) & ~1, 4);
     const int ro = INT ? 2 * kn - nn : 0;
