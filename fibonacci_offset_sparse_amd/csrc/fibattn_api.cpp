@@ -47,6 +47,17 @@ struct Plan {
     OffsetSlot keep[kMaxOff] = {};
 };
 
+// The scan table of a plan's first kScanRungs kept rungs (RungScan).
+RungScan rung_scan(const Plan& plan) {
+    RungScan sc;
+    for (int n = 0; n < kScanRungs; ++n) {
+        const bool kept = n < plan.n_keep;
+        sc.a[n] = kept ? plan.keep[n].a : kScanPast;
+        sc.r[n] = kept ? plan.keep[n].a + plan.keep[n].interp : kScanPast;
+    }
+    return sc;
+}
+
 fibattn_status_t check_offsets(double alpha, int32_t W, const int32_t* offsets, int32_t K) {
     if (K < 0 || K > FIBATTN_MAX_K) return fail(FIBATTN_ERR_INVALID, "K = %d outside [0, %d]", K, FIBATTN_MAX_K);
     if (K > 0 && offsets == nullptr) return fail(FIBATTN_ERR_INVALID, "offsets is NULL");
@@ -386,6 +397,7 @@ fibattn_status_t fibattn_fwd_attend(const void* q, const void* k, const void* v,
     a.qscale = score_scale();
     a.fr = make_freq(rope_theta);
     std::memcpy(a.off, plan.keep, sizeof(plan.keep));
+    a.scan = rung_scan(plan);
     const hipError_t e = launch_fwd_attend(dtype, a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fwd_attend launch");
     return FIBATTN_OK;
@@ -526,6 +538,7 @@ fibattn_status_t fibattn_bwd_stages(int32_t stages, const void* q, const void* k
     a.dalpha_dtheta = static_cast<float>(dalpha_dtheta);
     a.fr = make_freq(rope_theta);
     std::memcpy(a.off, plan.keep, sizeof(plan.keep));
+    a.scan = rung_scan(plan);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;

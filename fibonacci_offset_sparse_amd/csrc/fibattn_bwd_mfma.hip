@@ -405,18 +405,21 @@ __global__ __launch_bounds__(kNT, 2) void bwd_q_mfma_kernel(BwdArgs A) {
     const int i = i0 + p;
     const bool active = i < L;
 
-    int n_reach = 0;
-    for (int n = 0; n < A.n_off; ++n)
-        if (i0 + kTile - 1 >= A.off[n].a + A.off[n].interp) n_reach = n + 1;
+    // (counted over the packed scan table, RungScan: a few wide scalar loads, where a loop over
+    // the offset table waits for each rung's load in turn)
+    int n_reach = 0, n_lo = 0;
+#pragma unroll
+    for (int n = 0; n < kScanRungs; ++n) {
+        n_reach += (A.scan.r[n] <= i0 + kTile - 1) ? 1 : 0;
+        n_lo += (A.scan.a[n] <= kNear - (INT ? 0 : 1)) ? 1 : 0;
+    }
     // near rungs: the prefix with a <= 63 (near and far rows inside the near block, key rows
     // i0 - 64 .. i0 + 63; INT: a <= 64, the one row). Steps k < kn come from the near block, kn
     // even: rung pairs 2k, 2k + 1, or (INT) for even k a group of the four rungs 2k .. 2k + 3
     // (those past nn are padding). Steps kn .. n_steps - 1 are far steps, step k in buffer
     // (k + 1) % 2, holding rungs 2k - ro and 2k - ro + 1 (ro = 0 unless INT). Products of step k
     // go to slots 2k and 2k + 1 (a near group: 2k .. 2k + 3).
-    int n_near = 0;
-    for (int n = 0; n < n_reach; ++n)
-        if (A.off[n].a <= kNear - (INT ? 0 : 1)) n_near = n + 1;
+    const int n_near = min(n_lo, n_reach);
     const int nn = INT ? min(n_near, 8) : 0;
     const int kn = INT ? 2 * ((nn + 3) >> 2) : (n_near >> 1) & ~1;
     const int ro = INT ? 2 * kn - nn : 0;
@@ -1171,21 +1174,20 @@ __global__ __launch_bounds__(kNT, 2) void bwd_k_dot_kernel(BwdArgs A) {
     const int j0 = tile * kTile;
 
     // rungs some key row of the tile receives (query j + a < L): a prefix
-    // (loops unrolled over the matrix-core kernels' limit of 16 kept rungs: the offset table's
-    // scalar loads then go out together, where a loop to n_off waits for each in turn)
-    int n_reach = 0;
+    // (counted over the packed scan table, RungScan: a few wide scalar loads, where a loop over
+    // the offset table waits for each rung's load in turn)
+    int n_reach = 0, n_lo = 0;
 #pragma unroll
-    for (int n = 0; n < 16; ++n)
-        if (n < A.n_off && j0 + A.off[n].a < L) n_reach = n + 1;
+    for (int n = 0; n < kScanRungs; ++n) {
+        n_reach += (j0 + A.scan.a[n] < L) ? 1 : 0;
+        n_lo += (A.scan.a[n] <= kNear - (INT ? 0 : 1)) ? 1 : 0;
+    }
     // near rungs: the prefix with a <= 63 (both query rows of every key row of the tile inside the
     // near block; INT: a <= 64, the one row). Pairs k < kn come from the near block (kn even, at
     // most 4; INT: for even k a group of the four rungs 2k .. 2k + 3, those past nn padding);
     // pairs kn .. n_far - 1 are far steps, pair k in buffer (k + 1) % 2, n_far odd so that the last
     // one sits in lds1; far pair k holds rungs 2k - ro and 2k - ro + 1 (ro = 0 unless INT).
-    int n_near = 0;
-#pragma unroll
-    for (int n = 0; n < 16; ++n)
-        if (n < n_reach && A.off[n].a <= kNear - (INT ? 0 : 1)) n_near = n + 1;
+    const int n_near = min(n_lo, n_reach);
     const int nn = INT ? min(n_near, 8) : 0;
     const int kn = INT ? 2 * ((nn + 3) >> 2) : min((n_near >> 1) & ~1, 4);
     const int ro = INT ? 2 * kn - nn : 0;

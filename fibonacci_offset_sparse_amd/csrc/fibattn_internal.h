@@ -28,6 +28,17 @@ struct OffsetSlot {
     int32_t f;       // base rung (d(alpha) weight)
 };
 
+// The first 16 kept rungs' floors and reach, packed for the matrix-core kernels' scans of the rungs
+// a tile reaches (a few wide scalar loads instead of one load of the offset table per rung). Both
+// are non-decreasing in the rung (the distances alpha f increase), so a count of entries under a
+// bound is the length of the prefix under it; entries past the kept rungs hold kScanPast.
+constexpr int kScanRungs = 16;
+constexpr int32_t kScanPast = 1 << 30;
+struct RungScan {
+    int32_t a[kScanRungs];   // floor(d) of kept rung n
+    int32_t r[kScanRungs];   // a + 1 for an interpolated rung, a for an integral one: its first query
+};
+
 // RoPE frequencies omega_j / (2 pi) as an unevaluated float sum hi + lo (double accuracy).
 struct RopeFreq {
     float hi[kPairs];
@@ -80,6 +91,7 @@ struct FwdArgs {
     float qscale;        // log2(e) / sqrt(D): scores kept in base 2
     RopeFreq fr;
     OffsetSlot off[kMaxOff];
+    RungScan scan;
 };
 
 struct BwdArgs {
@@ -104,6 +116,7 @@ struct BwdArgs {
     float dalpha_dtheta;
     RopeFreq fr;
     OffsetSlot off[kMaxOff];
+    RungScan scan;
     // matrix-core path (bfloat16 storage): staged rows from prep_kv16 (the forward's own), and
     // what the query-side kernel hands the key-side kernel; rows with dims permuted have element
     // 4m + c holding dim 16c + m
