@@ -77,6 +77,20 @@ def test_plan_bit_exact_on_random_and_learned_alphas():
         _plan_equal(a, 10, O.FIB_BASE)
 
 
+def test_kept_rungs_floors_and_reach_never_decrease():
+    # the matrix-core kernels count the rungs a tile reaches, and those its near block holds, from
+    # the kept rungs' floors and reach as counts under a bound: equal to the prefix lengths only
+    # because both sequences are non-decreasing (the distances alpha f increase with the rung)
+    rng = np.random.default_rng(11)
+    bases = [O.FIB_BASE, fa.fibattn_base_offsets(fa.BASE_POW2, 1024), fa.fibattn_base_offsets(fa.BASE_POW2, 2048)]
+    alphas = list(rng.uniform(0.05, 4.0, 3000)) + [0.5 + l / 15 for l in range(16)] + [1.0, 2.0, 1.5, 0.5]
+    for base in bases:
+        for alpha in alphas:
+            kind, fl, t, reach = fa.fibattn_plan(float(alpha), 12, base)
+            kept = kind != fa.DUP
+            assert (np.diff(fl[kept]) >= 0).all() and (np.diff(reach[kept]) >= 0).all(), (alpha, fl, reach)
+
+
 def test_plan_snaps_the_float64_traps():
     kind, fl, t, reach = fa.fibattn_plan(O.alpha_linear(5, 16), 12, [144])
     assert kind[0] == fa.INT and fl[0] == 120 and t[0] == 0.0
