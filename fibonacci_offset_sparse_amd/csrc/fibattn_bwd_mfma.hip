@@ -1726,7 +1726,7 @@ hipError_t launch_bwd_mfma(const BwdArgs& A0, bool want_dalpha, int stages, hipS
     A.q_fp32_wg = (stages & kStageQuery) ? static_cast<int32_t>(q_units * n_tiles) : 0;
     A.q_xcd_map = q_map;
     if (stages & kStageKey) {
-        A.xcd_map = (k_units % 8 == 0) ? 1 : 0;
+        A.xcd_map = (k_units % 32 == 0) ? 3 : (k_units % 8 == 0) ? 1 : 0;   // 3: heavy (low) key tiles first
         if (int_path_fits(A.off, A.n_off, 8))
             hipLaunchKernelGGL((bwd_k_dot_kernel<8, true>), dim3(static_cast<unsigned>(k_units * n_tiles)), dim3(kNT), 0, s,
                                A);

@@ -87,7 +87,8 @@ struct FwdArgs {
     void* o;             // [B, Hq, L, 64]
     float* lse;          // [B, Hq, L] or nullptr
     int32_t B, L, Hq, Hkv, G, W, n_off;
-    int32_t xcd_map;     // matrix-core kernels: 0 plain order, 1 each (batch, kv head) on one XCD, 2 also mix tiles per CU
+    int32_t xcd_map;     // matrix-core kernels: 0 plain order, 1 each (batch, kv head) on one XCD, 2 also mix tiles per CU,
+                         // 3 each unit on one XCD, groups of four units tile-major
     float qscale;        // log2(e) / sqrt(D): scores kept in base 2
     RopeFreq fr;
     OffsetSlot off[kMaxOff];
